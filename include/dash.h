@@ -1,0 +1,201 @@
+/*
+ * dash.h -- C ABI of the DashAttention forward library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method ("DashAttention: Differentiable and Adaptive Sparse Hierarchical
+ * Attention", explainer pages for arXiv 2605.18753, section "Technical
+ * summary") computes attention in three stages:
+ *   Stage 0  summaries of contiguous key blocks (chunks of block_size keys);
+ *   Stage 1  coarse scores of each query against the summaries and
+ *            w = alpha-entmax(gamma * zbar), a sparse probability vector over
+ *            blocks whose support size follows the scores; GQA query heads
+ *            that share a KV head average their probabilities;
+ *   Stage 2  softmax attention restricted to the routed blocks, with the
+ *            routing probability as a prior (added as a log bias before the
+ *            softmax); blocks of probability 0 are masked; the block holding
+ *            the query (near the diagonal, no summary yet) is handled apart.
+ * The pages state one fused kernel per stage, with prefill and incremental
+ * decoding ("Technical summary", Contributions, efficient GPU implementation).
+ *
+ * Fixed readings (the pages leave them open):
+ *   - summary s_j = (mean of block j's keys) . W_s, W_s a d x d float32 matrix,
+ *     row-major [d_in][d_out], shared by all heads;
+ *   - zbar_j = q . s_j / sqrt(d); entmax input x_j = (alpha - 1) gamma zbar_j;
+ *     p_j = [x_j - tau]_+^(1/(alpha-1)) with sum_j p_j = 1 (Tsallis entmax);
+ *   - causal attention: the routing candidates of a query at position i are
+ *     the complete blocks j < floor(i / block_size); the query's own block is
+ *     always attended (keys t <= i) with bias 0; a routed block adds
+ *     log pbar_j to q.k/sqrt(d); pbar is the mean of p over the heads of a
+ *     GQA group.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers unless stated; tensors are dense
+ *     row-major with the shapes given.  q, o: [B, H, n, d]; k, v:
+ *     [B, Hkv, kv_len, d] (one block of one head is a contiguous run).  Query
+ *     head h reads KV head h / (H / Hkv).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The library never allocates, frees or synchronises; the
+ *     caller owns every buffer, including workspaces.  Calls are re-entrant
+ *     across streams; concurrent calls must not share output buffers.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is launched and the status says why.  A failed launch is
+ *     reported as DASH_ERR_HIP; faults during execution surface at the
+ *     caller's next synchronisation.  Device data is never inspected: NaN and
+ *     Inf propagate.
+ *   - Results are bitwise reproducible for fixed inputs and launch shapes
+ *     (no floating-point atomics).
+ */
+#ifndef DASH_H_
+#define DASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DASH_OK = 0,
+  DASH_ERR_INVALID_ARG = 1,        /* null pointer, negative size, bad shape */
+  DASH_ERR_UNSUPPORTED = 2,        /* valid but not built (head_dim, block_size, ...) */
+  DASH_ERR_WORKSPACE_TOO_SMALL = 3,
+  DASH_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+} dash_status;
+
+typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
+
+/* Problem description shared by every call.
+ *   batch       B >= 1 sequences
+ *   n_heads     H query heads; n_kv_heads Hkv divides H; G = H / Hkv must be
+ *               1, 2, 4 or 8
+ *   head_dim    d: 64 or 128
+ *   block_size  key block ("chunk") size: 64 or 128
+ *   alpha       entmax exponent, 1 < alpha <= 2
+ *   gamma       routing scale, finite and > 0
+ *   dtype       element type of q, k, v and o (DASH_F32 or DASH_BF16); the
+ *               summaries and W_s are always float32 */
+typedef struct {
+  int32_t batch;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  float alpha;
+  float gamma;
+  int32_t dtype;
+} dash_params;
+
+/* Query tile of the prefill path: 64 consecutive positions of one sequence
+ * and one KV head (all G query heads of the group).  The routing result is
+ * stored per tile: the union of the tile's selected blocks and, for each
+ * selected block, the log prior of every position of the tile. */
+#define DASH_QUERY_TILE 64
+
+/* Storage of the routing result (Stage 1 -> Stage 2 hand-over), caller-owned.
+ * For prefill over n positions: n_qt = ceil(n / 64) tiles, nb = ceil(n / bs)
+ * blocks, QT = 64.  For decode (one query per sequence): n = 1, n_qt = 1,
+ * QT = 1, nb = ceil(max_len / bs).
+ *   tau          [B, H, n]            float; entmax threshold per (head, query),
+ *                                     NaN for queries without a candidate block
+ *   sel_count    [B, Hkv, n_qt]       int32; number of selected blocks
+ *   sel_idx      [B, Hkv, n_qt, nb]   int32; ascending selected block ids,
+ *                                     the first sel_count entries are valid
+ *   sel_logp     [B, Hkv, n_qt, nb, QT] float; log pbar(block, query) indexed
+ *                                     by BLOCK ID, -inf where pbar = 0; valid for
+ *                                     the candidate blocks of the tile
+ *   support_bits [B, H, n, ceil(nb/32)] uint32, optional (NULL = not written);
+ *                                     bit j set iff block j is in that head's own
+ *                                     entmax support (x_j > tau), before the GQA
+ *                                     average */
+typedef struct {
+  float* tau;
+  int32_t* sel_count;
+  int32_t* sel_idx;
+  float* sel_logp;
+  uint32_t* support_bits;
+} dash_route_buf;
+
+/* Element counts of each dash_route_buf array (not bytes). */
+typedef struct {
+  int64_t n_qt, nb, qt;
+  int64_t tau, sel_count, sel_idx, sel_logp, support_bits;
+} dash_route_sizes;
+
+const char* dash_status_string(dash_status s);
+
+/* Library version string, e.g. "dash-mi355x 0.1.0 gfx950". */
+const char* dash_version(void);
+
+/* Sizes of the prefill routing buffers for n query positions. */
+dash_status dash_route_sizes_prefill(const dash_params* p, int64_t n, dash_route_sizes* out);
+
+/* Sizes of the decode routing buffers for caches of max_len tokens. */
+dash_status dash_route_sizes_decode(const dash_params* p, int64_t max_len, dash_route_sizes* out);
+
+/* Workspace bytes needed by dash_prefill (n positions) and dash_decode
+ * (caches of max_len tokens).  The workspace must be 256-byte aligned. */
+dash_status dash_prefill_workspace_bytes(const dash_params* p, int64_t n, size_t* bytes);
+dash_status dash_decode_workspace_bytes(const dash_params* p, int64_t max_len, size_t* bytes);
+
+/* Stage 0 ("local chunk summarization"; summaries are computed once a chunk
+ * is complete and then cached).  For every sequence b, KV head g and block
+ * j in [blk_begin, blk_end): summ[b, g, j, :] = mean(k[b, g, j*bs:(j+1)*bs, :]) . w_s,
+ * accumulated in float32.
+ *   k      [B, Hkv, kv_len, d] dtype; (blk_end * bs) <= kv_len
+ *   w_s    [d, d] float32
+ *   summ   [B, Hkv, summ_blocks, d] float32, blk_end <= summ_blocks
+ * Blocks outside [blk_begin, blk_end) are left untouched. */
+dash_status dash_summarize(const dash_params* p, const void* k, int64_t kv_len, int64_t blk_begin,
+                           int64_t blk_end, const float* w_s, float* summ, int64_t summ_blocks,
+                           void* stream);
+
+/* Stage 1 for causal prefill of positions 0..n-1: coarse scores, alpha-entmax
+ * per (query, head), GQA average, per-tile union and compaction.
+ *   q      [B, H, n, d] dtype
+ *   summ   [B, Hkv, summ_blocks, d] float32 holding blocks 0 .. floor(n/bs)-1
+ *   route  buffers sized by dash_route_sizes_prefill(p, n) */
+dash_status dash_route(const dash_params* p, const void* q, int64_t n, const float* summ,
+                       int64_t summ_blocks, const dash_route_buf* route, void* stream);
+
+/* Stage 2 for causal prefill: for each query, softmax over the keys of its
+ * tile's selected blocks (logit q.k/sqrt(d) + sel_logp, -inf masks) and the
+ * keys t <= i of its own block (bias 0); o = weights . v.
+ *   q, o   [B, H, n, d] dtype;  k, v [B, Hkv, n, d] dtype
+ *   route  as written by dash_route (tau and support_bits are not read) */
+dash_status dash_attend(const dash_params* p, const void* q, const void* k, const void* v,
+                        int64_t n, const dash_route_buf* route, void* o, void* stream);
+
+/* Fused causal prefill: dash_summarize of blocks [0, floor(n/bs)) into summ,
+ * dash_route into the workspace, dash_attend into o.
+ *   summ   [B, Hkv, summ_blocks, d] float32, summ_blocks >= floor(n/bs)
+ *   ws     >= dash_prefill_workspace_bytes(p, n) bytes, 256-byte aligned */
+dash_status dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
+                         int64_t n, const float* w_s, float* summ, int64_t summ_blocks, void* o,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* One incremental decoding step for every sequence b: the query q[b] sits at
+ * position L = cache_len[b] - 1 and its key/value are already in the caches.
+ * Routes over the cached summaries of blocks j < floor(L / bs), attends to the
+ * selected blocks plus keys [floor(L/bs)*bs, L] of the own block, and, when
+ * cache_len[b] % bs == 0 (the step completes a block), writes the summary of
+ * block cache_len[b]/bs - 1 into summ.
+ *   q, o            [B, H, d] dtype
+ *   k_cache, v_cache [B, Hkv, max_len, d] dtype
+ *   cache_len       [B] int32 DEVICE array, 1 <= cache_len[b] <= max_len
+ *   summ            [B, Hkv, summ_blocks, d] float32, summ_blocks >= ceil(max_len/bs),
+ *                   read for blocks < floor((cache_len-1)/bs), written as above
+ *   route           optional (NULL = use the workspace): where the routing
+ *                   result goes, sized by dash_route_sizes_decode
+ *   ws              >= dash_decode_workspace_bytes(p, max_len) bytes
+ * Values of cache_len outside [1, max_len] are clamped into that range. */
+dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* cache_len, int64_t max_len,
+                        const float* w_s, float* summ, int64_t summ_blocks, void* o,
+                        const dash_route_buf* route, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H_ */

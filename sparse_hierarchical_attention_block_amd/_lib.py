@@ -1,0 +1,268 @@
+"""ctypes binding of libdash.so (the C ABI in include/dash.h).
+
+Argument marshalling only: torch tensors provide device memory and the HIP
+stream; every step of the computation runs in the library's gfx950 kernels.
+Each wrapper checks that tensors live on the GPU, are contiguous and hold at
+least the elements the call will touch (the C side cannot inspect device
+pointers), then calls the entry point of the same name and raises
+``DashError`` on a non-OK status.  There is no fallback: if the library is
+not built, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdash.so")
+
+DASH_OK, DASH_ERR_INVALID_ARG, DASH_ERR_UNSUPPORTED, DASH_ERR_WORKSPACE_TOO_SMALL, DASH_ERR_HIP = \
+    range(5)
+DASH_F32, DASH_BF16 = 0, 1
+QUERY_TILE = 64
+WS_ALIGN = 256
+
+
+class DashError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {dash_status_string(status)}")
+
+
+class dash_params(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("alpha", ctypes.c_float),
+                ("gamma", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class dash_route_buf(ctypes.Structure):
+    _fields_ = [("tau", ctypes.c_void_p), ("sel_count", ctypes.c_void_p),
+                ("sel_idx", ctypes.c_void_p), ("sel_logp", ctypes.c_void_p),
+                ("support_bits", ctypes.c_void_p)]
+
+
+class dash_route_sizes(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in
+                ("n_qt", "nb", "qt", "tau", "sel_count", "sel_idx", "sel_logp", "support_bits")]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                      "(python -m sparse_hierarchical_attention_block_amd.build)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.POINTER(dash_params)
+_R = ctypes.POINTER(dash_route_buf)
+_V = ctypes.c_void_p
+_I = ctypes.c_int64
+_lib.dash_status_string.restype = ctypes.c_char_p
+_lib.dash_status_string.argtypes = [ctypes.c_int]
+_lib.dash_version.restype = ctypes.c_char_p
+_lib.dash_version.argtypes = []
+for _name in ("dash_route_sizes_prefill", "dash_route_sizes_decode"):
+    getattr(_lib, _name).restype = ctypes.c_int
+    getattr(_lib, _name).argtypes = [_P, _I, ctypes.POINTER(dash_route_sizes)]
+for _name in ("dash_prefill_workspace_bytes", "dash_decode_workspace_bytes"):
+    getattr(_lib, _name).restype = ctypes.c_int
+    getattr(_lib, _name).argtypes = [_P, _I, ctypes.POINTER(ctypes.c_size_t)]
+_lib.dash_summarize.restype = ctypes.c_int
+_lib.dash_summarize.argtypes = [_P, _V, _I, _I, _I, _V, _V, _I, _V]
+_lib.dash_route.restype = ctypes.c_int
+_lib.dash_route.argtypes = [_P, _V, _I, _V, _I, _R, _V]
+_lib.dash_attend.restype = ctypes.c_int
+_lib.dash_attend.argtypes = [_P, _V, _V, _V, _I, _R, _V, _V]
+_lib.dash_prefill.restype = ctypes.c_int
+_lib.dash_prefill.argtypes = [_P, _V, _V, _V, _I, _V, _V, _I, _V, _V, ctypes.c_size_t, _V]
+_lib.dash_decode.restype = ctypes.c_int
+_lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _I, _V, _R, _V, ctypes.c_size_t, _V]
+
+EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
+            "dash_route_sizes_decode", "dash_prefill_workspace_bytes",
+            "dash_decode_workspace_bytes", "dash_summarize", "dash_route", "dash_attend",
+            "dash_prefill", "dash_decode")
+
+
+# ---------------------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------------------
+
+def make_params(batch, n_heads, n_kv_heads, head_dim, block_size, alpha, gamma, dtype):
+    """dtype: "bf16"/"f32", torch dtype, or DASH_* code."""
+    if dtype in ("bf16", torch.bfloat16):
+        code = DASH_BF16
+    elif dtype in ("f32", torch.float32):
+        code = DASH_F32
+    else:
+        code = int(dtype)
+    return dash_params(int(batch), int(n_heads), int(n_kv_heads), int(head_dim),
+                       int(block_size), float(alpha), float(gamma), code)
+
+
+def torch_dtype(p: dash_params):
+    return torch.bfloat16 if p.dtype == DASH_BF16 else torch.float32
+
+
+def _check(fn, status):
+    if status != DASH_OK:
+        raise DashError(fn, status)
+
+
+def _dev(t, name, numel, dtype=None):
+    """Device pointer of a GPU tensor holding >= numel elements."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def dash_status_string(status: int) -> str:
+    return _lib.dash_status_string(int(status)).decode()
+
+
+def dash_version() -> str:
+    return _lib.dash_version().decode()
+
+
+def dash_route_sizes_prefill(p, n):
+    out = dash_route_sizes()
+    _check("dash_route_sizes_prefill", _lib.dash_route_sizes_prefill(ctypes.byref(p), n,
+                                                                     ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in dash_route_sizes._fields_}
+
+
+def dash_route_sizes_decode(p, max_len):
+    out = dash_route_sizes()
+    _check("dash_route_sizes_decode", _lib.dash_route_sizes_decode(ctypes.byref(p), max_len,
+                                                                   ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in dash_route_sizes._fields_}
+
+
+def dash_prefill_workspace_bytes(p, n) -> int:
+    out = ctypes.c_size_t()
+    _check("dash_prefill_workspace_bytes",
+           _lib.dash_prefill_workspace_bytes(ctypes.byref(p), n, ctypes.byref(out)))
+    return out.value
+
+
+def dash_decode_workspace_bytes(p, max_len) -> int:
+    out = ctypes.c_size_t()
+    _check("dash_decode_workspace_bytes",
+           _lib.dash_decode_workspace_bytes(ctypes.byref(p), max_len, ctypes.byref(out)))
+    return out.value
+
+
+class RouteBuffers:
+    """Device tensors of a dash_route_buf (torch supplies the memory)."""
+
+    def __init__(self, sizes, device="cuda", bits=False):
+        self.sizes = sizes
+        self.tau = torch.empty(sizes["tau"], dtype=torch.float32, device=device)
+        self.sel_count = torch.empty(sizes["sel_count"], dtype=torch.int32, device=device)
+        self.sel_idx = torch.empty(sizes["sel_idx"], dtype=torch.int32, device=device)
+        self.sel_logp = torch.empty(sizes["sel_logp"], dtype=torch.float32, device=device)
+        self.support_bits = (torch.empty(sizes["support_bits"], dtype=torch.int32, device=device)
+                             if bits else None)
+
+    def struct(self):
+        s = self.sizes
+        return dash_route_buf(
+            _dev(self.tau, "tau", s["tau"], torch.float32),
+            _dev(self.sel_count, "sel_count", s["sel_count"], torch.int32),
+            _dev(self.sel_idx, "sel_idx", s["sel_idx"], torch.int32),
+            _dev(self.sel_logp, "sel_logp", s["sel_logp"], torch.float32),
+            None if self.support_bits is None else
+            _dev(self.support_bits, "support_bits", s["support_bits"], torch.int32))
+
+
+def workspace(nbytes, device="cuda"):
+    """A 256-byte aligned uint8 device buffer (torch's caching allocator
+    returns at least 512-byte aligned blocks)."""
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % WS_ALIGN == 0
+    return ws
+
+
+# ---------------------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------------------
+
+def dash_summarize(p, k, kv_len, blk_begin, blk_end, w_s, summ, summ_blocks, stream=None):
+    B, Hkv, d = p.batch, p.n_kv_heads, p.head_dim
+    _check("dash_summarize", _lib.dash_summarize(
+        ctypes.byref(p), _dev(k, "k", B * Hkv * kv_len * d, torch_dtype(p)), kv_len, blk_begin,
+        blk_end, _dev(w_s, "w_s", d * d, torch.float32),
+        _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
+        _stream(stream)))
+
+
+def dash_route(p, q, n, summ, summ_blocks, route: RouteBuffers, stream=None):
+    B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
+    if route.sizes != dash_route_sizes_prefill(p, n):
+        raise ValueError("route buffers were sized for another problem")
+    rb = route.struct()
+    _check("dash_route", _lib.dash_route(
+        ctypes.byref(p), _dev(q, "q", B * H * n * d, torch_dtype(p)), n,
+        _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
+        ctypes.byref(rb), _stream(stream)))
+
+
+def dash_attend(p, q, k, v, n, route: RouteBuffers, o, stream=None):
+    B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
+    if route.sizes != dash_route_sizes_prefill(p, n):
+        raise ValueError("route buffers were sized for another problem")
+    rb = route.struct()
+    dt = torch_dtype(p)
+    _check("dash_attend", _lib.dash_attend(
+        ctypes.byref(p), _dev(q, "q", B * H * n * d, dt), _dev(k, "k", B * Hkv * n * d, dt),
+        _dev(v, "v", B * Hkv * n * d, dt), n, ctypes.byref(rb), _dev(o, "o", B * H * n * d, dt),
+        _stream(stream)))
+
+
+def dash_prefill(p, q, k, v, n, w_s, summ, summ_blocks, o, ws, stream=None):
+    B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
+    dt = torch_dtype(p)
+    _check("dash_prefill", _lib.dash_prefill(
+        ctypes.byref(p), _dev(q, "q", B * H * n * d, dt), _dev(k, "k", B * Hkv * n * d, dt),
+        _dev(v, "v", B * Hkv * n * d, dt), n, _dev(w_s, "w_s", d * d, torch.float32),
+        _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
+        _dev(o, "o", B * H * n * d, dt), _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def dash_decode(p, q, k_cache, v_cache, cache_len, max_len, w_s, summ, summ_blocks, o,
+                ws, route: RouteBuffers | None = None, stream=None):
+    B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
+    dt = torch_dtype(p)
+    rb = None
+    if route is not None:
+        if route.sizes != dash_route_sizes_decode(p, max_len):
+            raise ValueError("route buffers were sized for another problem")
+        rb_struct = route.struct()
+        rb = ctypes.byref(rb_struct)
+    _check("dash_decode", _lib.dash_decode(
+        ctypes.byref(p), _dev(q, "q", B * H * d, dt),
+        _dev(k_cache, "k_cache", B * Hkv * max_len * d, dt),
+        _dev(v_cache, "v_cache", B * Hkv * max_len * d, dt),
+        _dev(cache_len, "cache_len", B, torch.int32), max_len,
+        _dev(w_s, "w_s", d * d, torch.float32),
+        _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
+        _dev(o, "o", B * H * d, dt), rb, _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
+        _stream(stream)))

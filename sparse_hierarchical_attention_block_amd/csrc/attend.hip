@@ -1,0 +1,352 @@
+// attend.hip -- Stage 2 of DashAttention for causal prefill ("prior-induced
+// sparse softmax", DashAttention explainer, Technical summary): attention of
+// each query restricted to the blocks its 64-position tile selected, with the
+// routing probability as a prior (logit q.k/sqrt(d) + log pbar), blocks of
+// probability 0 masked (-inf), and the query's own block attended causally
+// with bias 0 (the near-diagonal branch).  The pages' kernel is a modified
+// FlashAttention that walks the active chunks and adds the routing bias before
+// the softmax; this is a gfx950 design of that idea.
+//
+// bf16 kernel: one workgroup per (sequence, KV head, query tile) -- up to 8
+// waves; each wave owns 32 queries of one head of the group, so every K/V
+// chunk staged in LDS serves all G heads.  The walk goes over 64-key chunks:
+// own-block chunks first (so every running max is finite), then the selected
+// blocks.  Per chunk and wave:
+//   S^T (64 keys x 32 queries) = K Q^T     2 x 8 MFMA 32x32x16 (d = 128)
+//   online softmax in the exp2 domain, bias added per (query, block)
+//   O^T (d x 32 queries) += V^T P^T        4 x 4 MFMA 32x32x16
+// Keys are the MFMA rows of S^T, so the accumulator of S^T already has the
+// register layout of the P^T operand (the k index of the PV product is a
+// permutation of the chunk's keys, matched by how V^T is read from LDS).
+// V is transposed into LDS in 4x4 blocks while it is staged.
+#include "dash_internal.hpp"
+#include "device_common.hpp"
+
+namespace dash {
+
+constexpr int kQTa = DASH_QUERY_TILE;
+constexpr int kChunk = 64;
+
+struct AttendArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t n;
+  const int32_t* sel_count;
+  const int32_t* sel_idx;
+  const float* sel_logp;
+  int64_t n_qt, nb;
+  int H, Hkv, G, bs, B;
+  float scale_log2;   // log2(e) / sqrt(d)
+  int wg_per_tile;
+};
+
+// chunk c of the tile's walk -> first key and bias source
+struct ChunkRef {
+  int64_t key0;
+  int64_t block;   // -1 for own-block chunks (bias 0)
+  bool diag;       // chunk starting at the tile's first position: causal mask
+};
+
+__device__ __forceinline__ ChunkRef chunk_ref(int c, int n_own, int64_t own_c0, int cpb,
+                                              const int32_t* idx) {
+  ChunkRef r;
+  if (c < n_own) {
+    r.key0 = (own_c0 + c) * kChunk;
+    r.block = -1;
+    r.diag = c == n_own - 1;
+  } else {
+    const int cc = c - n_own;
+    const int64_t j = idx[cc / cpb];
+    r.key0 = j * (int64_t)(cpb * kChunk) + (cc % cpb) * kChunk;
+    r.block = j;
+    r.diag = false;
+  }
+  return r;
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16, MFMA
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(512) void attend_bf16_kernel(AttendArgs a) {
+  constexpr int KP = D + 8;        // K row pitch (elements)
+  constexpr int VP = kChunk + 4;   // V^T row pitch (elements)
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kChunk * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VP];
+
+  const int nthreads = blockDim.x;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int l32 = lane % 32, lh = lane / 32;
+
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
+  const int64_t tile_rank = blockIdx.x / a.wg_per_tile;
+  const int wi = blockIdx.x % a.wg_per_tile;
+  const int64_t qt = a.n_qt - 1 - tile_rank / nbg;   // heaviest tiles first
+  const int64_t bg = tile_rank % nbg;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int64_t p_begin = qt * kQTa;
+  const int64_t tile = bg * a.n_qt + qt;
+
+  const int gw = wi * 8 + wave;        // wave index within the tile
+  const int h = g * a.G + gw / 2;      // query head
+  const int half = gw % 2;
+  const int qloc = 32 * half + l32;    // query row within the tile
+  const int64_t qpos = p_begin + qloc;
+
+  const __bf16* qp = (const __bf16*)a.q + (((int64_t)b * a.H + h) * a.n) * D;
+  const __bf16* kp = (const __bf16*)a.k + (bg * a.n) * D;
+  const __bf16* vp = (const __bf16*)a.v + (bg * a.n) * D;
+
+  // Q^T operand fragments: column = query l32, k = d in [16 s + 8 lh, +8)
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (qpos < a.n) w = *(const u32x4*)(qp + qpos * D + 16 * s + 8 * lh);
+    qf[s] = as_bf16x8(w);
+  }
+
+  const int cpb = a.bs / kChunk;
+  const int64_t own_block = p_begin / a.bs;
+  const int64_t own_c0 = own_block * cpb;
+  const int n_own = (int)(qt - own_c0 + 1);
+  const int count = a.sel_count[tile];
+  const int32_t* idx = a.sel_idx + tile * a.nb;
+  const int n_chunks = n_own + count * cpb;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int c = 0; c < n_chunks; ++c) {
+    const ChunkRef cr = chunk_ref(c, n_own, own_c0, cpb, idx);
+    __syncthreads();
+    // ---- stage K (row-major) and V^T into LDS ----
+    for (int e = threadIdx.x; e < kChunk * (D / 8); e += nthreads) {
+      const int key = e / (D / 8), seg = e % (D / 8);
+      const int64_t kpos = cr.key0 + key;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (kpos < a.n) w = *(const u32x4*)(kp + kpos * D + seg * 8);
+      *(u32x4*)(Ks + key * KP + seg * 8) = w;
+    }
+    for (int e = threadIdx.x; e < (kChunk / 4) * (D / 4); e += nthreads) {
+      const int db = e % (D / 4), kb = e / (D / 4);
+      u32x2 in[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t kpos = cr.key0 + 4 * kb + r;
+        in[r] = (u32x2){0u, 0u};
+        if (kpos < a.n) in[r] = *(const u32x2*)(vp + kpos * D + 4 * db);
+      }
+      u32x2 o0 = {pack_lo(in[0].x, in[1].x), pack_lo(in[2].x, in[3].x)};
+      u32x2 o1 = {pack_hi(in[0].x, in[1].x), pack_hi(in[2].x, in[3].x)};
+      u32x2 o2 = {pack_lo(in[0].y, in[1].y), pack_lo(in[2].y, in[3].y)};
+      u32x2 o3 = {pack_hi(in[0].y, in[1].y), pack_hi(in[2].y, in[3].y)};
+      *(u32x2*)(Vt + (4 * db + 0) * VP + 4 * kb) = o0;
+      *(u32x2*)(Vt + (4 * db + 1) * VP + 4 * kb) = o1;
+      *(u32x2*)(Vt + (4 * db + 2) * VP + 4 * kb) = o2;
+      *(u32x2*)(Vt + (4 * db + 3) * VP + 4 * kb) = o3;
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T : two 32-key tiles ----
+    f32x16 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const u32x4 kw = *(const u32x4*)(Ks + (32 * kt + l32) * KP + 16 * s + 8 * lh);
+        st[kt] = mfma32(as_bf16x8(kw), qf[s], st[kt]);
+      }
+    }
+
+    // ---- online softmax (exp2 domain) ----
+    float bias2 = 0.f;
+    if (cr.block >= 0) bias2 = a.sel_logp[(tile * a.nb + cr.block) * kQTa + qloc] * kLog2e;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * kt + 8 * (i / 4) + 4 * lh + (i % 4);
+        float sv = fmaf(st[kt][i], a.scale_log2, bias2);
+        if (cr.diag && cr.key0 + key > qpos) sv = -INFINITY;
+        st[kt][i] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float corr = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = exp2f(st[kt][i] - m_use);
+        st[kt][i] = pv;
+        psum += pv;
+      }
+    psum += __shfl_xor(psum, 32, kWave);
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] *= corr;
+
+    // ---- O^T += V^T P^T : 4 k-steps of 16 keys ----
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = ks / 2, i0 = 8 * (ks % 2);
+      u32x4 pw;
+      pw.x = pack_bf16(st[kt][i0 + 0], st[kt][i0 + 1]);
+      pw.y = pack_bf16(st[kt][i0 + 2], st[kt][i0 + 3]);
+      pw.z = pack_bf16(st[kt][i0 + 4], st[kt][i0 + 5]);
+      pw.w = pack_bf16(st[kt][i0 + 6], st[kt][i0 + 7]);
+      const bf16x8 pf = as_bf16x8(pw);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const __bf16* vrow = Vt + (32 * dt + l32) * VP + 16 * ks + 4 * lh;
+        const u32x2 v0 = *(const u32x2*)(vrow);
+        const u32x2 v1 = *(const u32x2*)(vrow + 8);
+        const u32x4 vw = {v0.x, v0.y, v1.x, v1.y};
+        acc[dt] = mfma32(as_bf16x8(vw), pf, acc[dt]);
+      }
+    }
+  }
+
+  // ---- normalise and store: acc[dt][i] = O[query l32][32 dt + 8 (i/4) + 4 lh + i%4] ----
+  if (qpos < a.n) {
+    const float inv = 1.0f / l_run;
+    __bf16* op = (__bf16*)a.o + (((int64_t)b * a.H + h) * a.n + qpos) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        u32x2 w = {pack_bf16(acc[dt][4 * i4 + 0] * inv, acc[dt][4 * i4 + 1] * inv),
+                   pack_bf16(acc[dt][4 * i4 + 2] * inv, acc[dt][4 * i4 + 3] * inv)};
+        *(u32x2*)(op + 32 * dt + 8 * i4 + 4 * lh) = w;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// float32, plain FMAs (one thread per query of one head)
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
+  __shared__ float Ks[kChunk * D];
+  __shared__ float Vs[kChunk * D];
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
+  const int64_t rank = blockIdx.x / a.G;
+  const int hh = blockIdx.x % a.G;
+  const int64_t qt = a.n_qt - 1 - rank / nbg;
+  const int64_t bg = rank % nbg;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int h = g * a.G + hh;
+  const int64_t p_begin = qt * kQTa;
+  const int64_t tile = bg * a.n_qt + qt;
+  const int qloc = threadIdx.x;
+  const int64_t qpos = p_begin + qloc;
+  const float* kp = (const float*)a.k + (bg * a.n) * D;
+  const float* vp = (const float*)a.v + (bg * a.n) * D;
+
+  float qv[D], ov[D];
+  const float* qrow = (const float*)a.q + (((int64_t)b * a.H + h) * a.n + qpos) * D;
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    qv[c] = qpos < a.n ? qrow[c] : 0.f;
+    ov[c] = 0.f;
+  }
+  const int cpb = a.bs / kChunk;
+  const int64_t own_c0 = (p_begin / a.bs) * cpb;
+  const int n_own = (int)(qt - own_c0 + 1);
+  const int count = a.sel_count[tile];
+  const int32_t* idx = a.sel_idx + tile * a.nb;
+  const int n_chunks = n_own + count * cpb;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float scale = a.scale_log2;
+
+  for (int c = 0; c < n_chunks; ++c) {
+    const ChunkRef cr = chunk_ref(c, n_own, own_c0, cpb, idx);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kChunk * D; e += 64) {
+      const int64_t kpos = cr.key0 + e / D;
+      Ks[e] = kpos < a.n ? kp[cr.key0 * D + e] : 0.f;
+      Vs[e] = kpos < a.n ? vp[cr.key0 * D + e] : 0.f;
+    }
+    __syncthreads();
+    const float bias2 =
+        cr.block >= 0 ? a.sel_logp[(tile * a.nb + cr.block) * kQTa + qloc] * kLog2e : 0.f;
+    for (int key = 0; key < kChunk; ++key) {
+      if (cr.diag && cr.key0 + key > qpos) break;
+      float s = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < D; ++cc) s = fmaf(qv[cc], Ks[key * D + cc], s);
+      s = fmaf(s, scale, bias2);
+      const float m_new = fmaxf(m_run, s);
+      if (m_new == -INFINITY) continue;
+      const float corr = exp2f(m_run - m_new), p = exp2f(s - m_new);
+      l_run = l_run * corr + p;
+#pragma unroll
+      for (int cc = 0; cc < D; ++cc) ov[cc] = fmaf(p, Vs[key * D + cc], ov[cc] * corr);
+      m_run = m_new;
+    }
+  }
+  if (qpos < a.n) {
+    float* orow = (float*)a.o + (((int64_t)b * a.H + h) * a.n + qpos) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) orow[c] = ov[c] / l_run;
+  }
+}
+
+hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                                 int64_t n, const dash_route_buf& rb, void* o, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  AttendArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.n = n;
+  a.sel_count = rb.sel_count;
+  a.sel_idx = rb.sel_idx;
+  a.sel_logp = rb.sel_logp;
+  a.n_qt = (n + kQTa - 1) / kQTa;
+  a.nb = (n + s.bs - 1) / s.bs;
+  a.H = s.H;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.bs = s.bs;
+  a.B = s.B;
+  a.scale_log2 = kLog2e / sqrtf((float)s.d);
+  const int64_t tiles = a.n_qt * s.B * s.Hkv;
+  if (s.dtype == DASH_BF16) {
+    const int waves = 2 * s.G;                 // 32 queries x 1 head per wave
+    a.wg_per_tile = (waves + 7) / 8;
+    const int threads = (waves < 8 ? waves : 8) * kWave;
+    dim3 grid((unsigned)(tiles * a.wg_per_tile));
+    if (s.d == 64)
+      hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(threads), 0, st, a);
+    else
+      hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(threads), 0, st, a);
+  } else {
+    a.wg_per_tile = 1;
+    dim3 grid((unsigned)(tiles * s.G));
+    if (s.d == 64)
+      hipLaunchKernelGGL(attend_f32_kernel<64>, grid, dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL(attend_f32_kernel<128>, grid, dim3(64), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dash

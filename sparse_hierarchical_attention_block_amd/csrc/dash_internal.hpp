@@ -1,0 +1,48 @@
+// dash_internal.hpp -- host-side launchers shared between the C ABI layer
+// (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dash.h"
+
+namespace dash {
+
+// Validated problem shape.
+struct Shape {
+  int B, H, Hkv, G, d, bs;
+  float alpha, gamma;
+  int dtype;  // dash_dtype
+};
+
+// Stage 0: summaries of blocks [blk_begin, blk_end) for every (b, kv head).
+hipError_t launch_summarize(const Shape& s, const void* k, int64_t kv_len, int64_t blk_begin,
+                            int64_t blk_end, const float* w_s, float* summ, int64_t summ_blocks,
+                            hipStream_t st);
+
+// Stage 1, causal prefill of positions 0..n-1.
+hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const float* summ,
+                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st);
+
+// Stage 2, causal prefill.
+hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                                 int64_t n, const dash_route_buf& rb, void* o, hipStream_t st);
+
+// Decode workspace layout (byte offsets from the workspace base).
+struct DecodeLayout {
+  int64_t nb;          // ceil(max_len / bs)
+  int64_t ncand_max;   // (max_len - 1) / bs
+  int64_t n_split;     // splits of the (own + selected) block list
+  size_t off_x, off_tau, off_count, off_idx, off_logp, off_part, total;
+};
+DecodeLayout decode_layout(const Shape& s, int64_t max_len);
+constexpr int kDecodeSplit = 16;   // list entries (blocks) per split
+
+// One decode step (route, attend, combine, summary update).
+hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const void* vc,
+                         const int32_t* cache_len, int64_t max_len, const float* w_s, float* summ,
+                         int64_t summ_blocks, void* o, const dash_route_buf& rb,
+                         const DecodeLayout& L, char* ws, hipStream_t st);
+
+}  // namespace dash

@@ -1,0 +1,98 @@
+// device_common.hpp -- small device helpers shared by the gfx950 kernels of
+// the DashAttention library: element types, wave64 reductions and MFMA
+// fragment types.  Nothing here is used by the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dash {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- element access --------------------------------------------------------
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// bf16 bits <-> float (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// pack the low halves / high halves of two words: (a.lo, b.lo) and (a.hi, b.hi)
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+// two floats -> packed bf16 pair (round to nearest even), x in the low half
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 r;
+  r.x = (__bf16)x;
+  r.y = (__bf16)y;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---- wave64 reductions (fixed order, deterministic) -------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// reductions over aligned groups of `width` lanes (width a power of two <= 64)
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float group_max(float v, int width) {
+  for (int o = width >> 1; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float group_min(float v, int width) {
+  for (int o = width >> 1; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// ---- MFMA (gfx950) ------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, C 16x16.  Lane l holds row
+// (l % 16) of A / column (l % 16) of B with k = 8 * (l / 16) + [0, 8), and
+// C[4 * (l / 16) + i][l % 16] in element i.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16_bf16: A 32x16, B 16x32, C 32x32.  Lane l holds row
+// (l % 32) of A / column (l % 32) of B with k = 8 * (l / 32) + [0, 8), and
+// C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32] in element i.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace dash

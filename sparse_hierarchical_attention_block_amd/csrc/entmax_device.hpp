@@ -1,0 +1,97 @@
+// entmax_device.hpp -- alpha-entmax threshold on the GPU (Stage 1, "entmax
+// chunk routing", DashAttention explainer: w = alpha-entmax(gamma * zbar),
+// support size set by the scores).
+//
+// With inputs in threshold units x_j = (alpha - 1) gamma zbar_j, the
+// probabilities are p_j = [x_j - tau]_+^e, e = 1/(alpha-1), where tau is the
+// root of f(tau) = sum_j [x_j - tau]_+^e - 1.  f is convex and decreasing, so
+// Newton steps started at tau0 = max_j x_j - 1 (where f >= 0) stay left of
+// the root and increase monotonically.  For e = 2 (alpha = 1.5) and e = 1
+// (alpha = 2) each step also solves f = 0 exactly on the current support
+// {x_j > tau}; that solution is accepted as soon as it keeps the whole
+// support above it, which makes it the (unique) root.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace dash {
+
+enum EntmaxMode : int { kSparsemax = 1, kEntmax15 = 2, kEntmaxQuartic = 4, kEntmaxGeneral = 0 };
+
+__host__ __device__ inline int entmax_mode(float alpha) {
+  if (alpha == 2.0f) return kSparsemax;
+  if (alpha == 1.5f) return kEntmax15;
+  if (alpha == 1.25f) return kEntmaxQuartic;
+  return kEntmaxGeneral;
+}
+
+// y^e for y > 0
+__device__ __forceinline__ float entmax_pow(float y, int mode, float e) {
+  if (mode == kEntmax15) return y * y;
+  if (mode == kSparsemax) return y;
+  if (mode == kEntmaxQuartic) { float y2 = y * y; return y2 * y2; }
+  return exp2f(e * __log2f(y));
+}
+
+// log(y^e) for y > 0
+__device__ __forceinline__ float entmax_logpow(float y, int mode, float e) {
+  float l = __logf(y);
+  if (mode == kEntmax15) return 2.f * l;
+  if (mode == kSparsemax) return l;
+  if (mode == kEntmaxQuartic) return 4.f * l;
+  return e * l;
+}
+
+// Threshold of one row whose n values are spread over a group of `width`
+// consecutive lanes (lane `sub` of the group reads get(sub), get(sub+width),
+// ...).  Every lane of the group returns the same tau.  `get(j)` reads x_j.
+template <typename Get>
+__device__ float entmax_tau(Get get, int n, int sub, int width, int mode, float e) {
+  float xmax = -INFINITY;
+  for (int j = sub; j < n; j += width) xmax = fmaxf(xmax, get(j));
+  xmax = group_max(xmax, width);
+  float tau = xmax - 1.0f;
+  for (int it = 0; it < 64; ++it) {
+    float k = 0.f, s1 = 0.f, s2 = 0.f, ymin = INFINITY;
+    for (int j = sub; j < n; j += width) {
+      float y = get(j) - tau;
+      if (y > 0.f) {
+        k += 1.f;
+        ymin = fminf(ymin, y);
+        if (mode == kEntmax15) { s1 += y; s2 = fmaf(y, y, s2); }
+        else if (mode == kSparsemax) { s1 += y; }
+        else if (mode == kEntmaxQuartic) { float y2 = y * y; s1 = fmaf(y2, y, s1); s2 = fmaf(y2, y2, s2); }
+        else { float l = __log2f(y); s1 += exp2f((e - 1.f) * l); s2 += exp2f(e * l); }
+      }
+    }
+    k = group_sum(k, width);
+    s1 = group_sum(s1, width);
+    s2 = group_sum(s2, width);
+    ymin = group_min(ymin, width);
+    float step;
+    if (mode == kSparsemax) {
+      // sum_S (y - d) = 1  ->  d = (s1 - 1) / k: Michelot's step, exact once S is the support
+      step = (s1 - 1.f) / k;
+      tau += step;
+      if (step < ymin) break;
+    } else if (mode == kEntmax15) {
+      // sum_S (y - d)^2 = 1: k d^2 - 2 s1 d + (s2 - 1) = 0, smaller root in stable form
+      float disc = s1 * s1 - k * (s2 - 1.f);
+      if (disc >= 0.f) {
+        float d = (s2 - 1.f) / (s1 + sqrtf(disc));
+        if (d < ymin) { tau += d; break; }
+      }
+      step = (s2 - 1.f) / (2.f * s1);
+      tau += step;
+      if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
+    } else {
+      // Newton: f = s2 - 1, f' = -e s1  (s1 = sum y^(e-1), s2 = sum y^e)
+      step = (s2 - 1.f) / (e * s1);
+      tau += step;
+      if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
+    }
+  }
+  return tau;
+}
+
+}  // namespace dash

@@ -1,0 +1,117 @@
+// summarize.hip -- Stage 0 of DashAttention ("local chunk summarization",
+// DashAttention explainer, Technical summary): one summary per complete key
+// block, s_j = mean(k of block j) . W_s, accumulated in float32.  A chunk's
+// summary is computed once, when the chunk is complete, and cached.
+//
+// HBM-bound scan: every key of a complete block is read once (bs * d * elt
+// bytes per block); W_s (64 KB at d = 128) stays in L2.
+#include "dash_internal.hpp"
+#include "device_common.hpp"
+
+namespace dash {
+
+constexpr int kSumThreads = 256;
+
+// Summary of one block.  kb points at the block's first key row (bs rows of
+// D elements), out at the D floats of its summary.  All 256 threads call it.
+template <typename T, int D>
+__device__ void summarize_block(const T* __restrict__ kb, int bs, const float* __restrict__ w_s,
+                                float* __restrict__ out) {
+  constexpr int RG = kSumThreads / D;  // row groups
+  __shared__ float part[RG][D];
+  __shared__ float mean[D];
+  const int c = threadIdx.x % D, rg = threadIdx.x / D;
+  float acc = 0.f;
+  for (int t = rg; t < bs; t += RG) acc += to_f32(kb[(int64_t)t * D + c]);
+  part[rg][c] = acc;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) s += part[r][c];
+    mean[c] = s * (1.0f / (float)bs);
+  }
+  __syncthreads();
+  float o = 0.f;
+  for (int r = rg; r < D; r += RG) o = fmaf(mean[r], w_s[r * D + c], o);
+  part[rg][c] = o;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) s += part[r][c];
+    out[c] = s;
+  }
+  __syncthreads();
+}
+
+// grid.x = nblk * B * Hkv
+template <typename T, int D>
+__global__ __launch_bounds__(kSumThreads) void summarize_kernel(
+    const T* __restrict__ k, int64_t kv_len, int bs, int64_t blk_begin, int64_t nblk,
+    const float* __restrict__ w_s, float* __restrict__ summ, int64_t summ_blocks) {
+  const int64_t u = blockIdx.x;
+  const int64_t j = blk_begin + u % nblk, bg = u / nblk;
+  summarize_block<T, D>(k + (bg * kv_len + j * bs) * D, bs, w_s,
+                        summ + (bg * summ_blocks + j) * D);
+}
+
+// Decode: the step that makes cache_len[b] a multiple of bs completes block
+// cache_len[b] / bs - 1; grid.x = B * Hkv.
+template <typename T, int D>
+__global__ __launch_bounds__(kSumThreads) void summarize_completed_kernel(
+    const T* __restrict__ k, int64_t max_len, int Hkv, int bs, const int32_t* __restrict__ cache_len,
+    const float* __restrict__ w_s, float* __restrict__ summ, int64_t summ_blocks) {
+  const int64_t bg = blockIdx.x;
+  const int b = (int)(bg / Hkv);
+  int64_t len = cache_len[b];
+  len = len < 1 ? 1 : (len > max_len ? max_len : len);
+  if (len % bs != 0) return;
+  const int64_t j = len / bs - 1;
+  summarize_block<T, D>(k + (bg * max_len + j * bs) * D, bs, w_s,
+                        summ + (bg * summ_blocks + j) * D);
+}
+
+template <typename T, int D>
+static hipError_t summarize_t(const Shape& s, const void* k, int64_t kv_len, int64_t b0,
+                              int64_t b1, const float* w_s, float* summ, int64_t sb,
+                              hipStream_t st) {
+  const int64_t nblk = b1 - b0;
+  dim3 grid((unsigned)(nblk * s.B * s.Hkv));
+  hipLaunchKernelGGL((summarize_kernel<T, D>), grid, dim3(kSumThreads), 0, st,
+                     (const T*)k, kv_len, s.bs, b0, nblk, w_s, summ, sb);
+  return hipGetLastError();
+}
+
+hipError_t launch_summarize(const Shape& s, const void* k, int64_t kv_len, int64_t blk_begin,
+                            int64_t blk_end, const float* w_s, float* summ, int64_t summ_blocks,
+                            hipStream_t st) {
+  if (blk_end <= blk_begin) return hipSuccess;
+  if (s.dtype == DASH_BF16)
+    return s.d == 64 ? summarize_t<__bf16, 64>(s, k, kv_len, blk_begin, blk_end, w_s, summ,
+                                               summ_blocks, st)
+                     : summarize_t<__bf16, 128>(s, k, kv_len, blk_begin, blk_end, w_s, summ,
+                                                summ_blocks, st);
+  return s.d == 64 ? summarize_t<float, 64>(s, k, kv_len, blk_begin, blk_end, w_s, summ,
+                                            summ_blocks, st)
+                   : summarize_t<float, 128>(s, k, kv_len, blk_begin, blk_end, w_s, summ,
+                                             summ_blocks, st);
+}
+
+hipError_t launch_summarize_completed(const Shape& s, const void* kc, int64_t max_len,
+                                      const int32_t* cache_len, const float* w_s, float* summ,
+                                      int64_t summ_blocks, hipStream_t st) {
+  dim3 grid((unsigned)(s.B * s.Hkv));
+#define DASH_SC(T, D)                                                                       \
+  hipLaunchKernelGGL((summarize_completed_kernel<T, D>), grid, dim3(kSumThreads), 0, st,    \
+                     (const T*)kc, max_len, s.Hkv, s.bs, cache_len, w_s, summ, summ_blocks)
+  if (s.dtype == DASH_BF16) {
+    if (s.d == 64) DASH_SC(__bf16, 64); else DASH_SC(__bf16, 128);
+  } else {
+    if (s.d == 64) DASH_SC(float, 64); else DASH_SC(float, 128);
+  }
+#undef DASH_SC
+  return hipGetLastError();
+}
+
+}  // namespace dash

@@ -17,3 +17,13 @@ def pytest_configure(config):
 def _oracle_built():
     import oracle
     oracle._load()
+
+
+def pytest_collection_modifyitems(config, items):
+    import torch
+    if torch.cuda.is_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU in this environment")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

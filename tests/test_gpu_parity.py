@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Small cases run every row through the oracle (several query tiles, ragged
+tails, batch > 1, GQA groups 1/2/4/8, head dims 64/128, blocks 64/128,
+alpha 1.25/1.5/2, fp32 and bf16).  Full-size workloads are in
+test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import (TOL, check_list, check_supports, check_tau, dev, params, run_decode,
+                         run_prefill, run_prefill_fused, tile_union_ref, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+QT = 64
+
+
+def tiny(**kw):
+    return W.get("tiny").replace(**kw)
+
+
+PREFILL_CASES = {
+    "tiny_f32_sparse": tiny(gamma=8.0),
+    "tiny_f32_dense": tiny(gamma=1.0),
+    "tiny_bf16": tiny(dtype="bf16", gamma=8.0),
+    "gqa4_d128_bs64": W.get("prefill_8k").replace(seq_len=2048),
+    "gqa4_d128_bs128": W.get("prefill_64k").replace(seq_len=2048, gamma=2.0),
+    "gqa8_d64_alpha2": tiny(n_heads=16, n_kv_heads=2, seq_len=1536, dtype="bf16", alpha=2.0,
+                            gamma=6.0, planted=True),
+    "gqa2_alpha125_ragged": W.get("prefill_8k").replace(n_heads=4, n_kv_heads=2, seq_len=1000,
+                                                        alpha=1.25, gamma=4.0),
+    "batch3_ragged_f32": tiny(batch=3, seq_len=700, n_heads=4, n_kv_heads=1, gamma=5.0),
+    "alpha175_general": tiny(seq_len=640, dtype="bf16", alpha=1.75, gamma=6.0),
+}
+
+
+def oracle_prefill(w, inp, nb):
+    r = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["w_s"], bs=w.block_size, alpha=w.alpha,
+                       gamma=w.gamma, nb_out=nb, want=("o", "tau", "x", "pbar"))
+    B, N, H, Hkv = w.batch, w.seq_len, w.n_heads, w.n_kv_heads
+    return {"o": r["o"].reshape(B, N, H, -1).transpose(0, 2, 1, 3),
+            "tau": r["tau"].reshape(B, N, H), "x": r["x"].reshape(B, N, H, nb),
+            "pbar": r["pbar"].reshape(B, N, Hkv, nb), "summ": r["summ"]}
+
+
+def compare_prefill(w, g, ref):
+    B, H, Hkv, N, bs, G = w.batch, w.n_heads, w.n_kv_heads, w.seq_len, w.block_size, w.group
+    nb = -(-N // bs)
+    tol = TOL[w.dtype]
+    # Stage 0
+    np.testing.assert_allclose(g["summ"], ref["summ"], rtol=1e-5, atol=2e-5)
+    # Stage 1: thresholds and per-head supports
+    check_tau(g["tau"].transpose(0, 2, 1), ref["tau"])
+    pos = np.arange(N)
+    ncand = np.tile(pos // bs, B)
+    bits = g["bits"].transpose(0, 2, 1, 3).reshape(B * N, H, nb)
+    check_supports(bits, ref["x"].reshape(B * N, H, nb), ref["tau"].reshape(B * N, H), ncand)
+    # tile lists and log priors
+    n_qt = -(-N // QT)
+    for b in range(B):
+        for gg in range(Hkv):
+            for qt in range(n_qt):
+                p0, p1 = qt * QT, min(N, qt * QT + QT)
+                t = p0 // bs
+                hs = slice(gg * G, gg * G + G)
+                union, solid, near = tile_union_ref(ref["pbar"][b, p0:p1, gg, :t],
+                                                    ref["x"][b, p0:p1, hs, :t],
+                                                    ref["tau"][b, p0:p1, hs], G)
+                cnt = g["count"][b, gg, qt]
+                check_list(cnt, g["idx"][b, gg, qt], union, solid, near)
+                lst = g["idx"][b, gg, qt, :cnt]
+                with np.errstate(over="ignore"):
+                    pg = np.exp(g["logp"][b, gg, qt, lst, : p1 - p0]).T      # [P, listed]
+                np.testing.assert_allclose(pg, ref["pbar"][b, p0:p1, gg][:, lst], atol=2e-5)
+    # Stage 2 output
+    err = np.abs(g["o"] - ref["o"]).max()
+    assert err <= tol, f"output max-abs error {err:.3e} > {tol}"
+    return err
+
+
+@pytest.mark.parametrize("case", list(PREFILL_CASES))
+def test_prefill_parity(case):
+    w = PREFILL_CASES[case]
+    print(f"[prefill parity] {case}: {w}", flush=True)
+    inp = W.make_prefill(w)
+    nb = -(-w.seq_len // w.block_size)
+    g = run_prefill(w, inp)
+    ref = oracle_prefill(w, inp, nb)
+    err = compare_prefill(w, g, ref)
+    # the fused entry point runs the same kernels
+    fused = run_prefill_fused(w, inp)
+    np.testing.assert_array_equal(fused, g["o"])
+    print(f"  max-abs err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 200])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_short_and_ragged(n, dtype):
+    w = tiny(seq_len=n, dtype=dtype, n_heads=4, n_kv_heads=2, gamma=3.0)
+    print(f"[prefill ragged] n={n} {dtype}", flush=True)
+    inp = W.make_prefill(w)
+    ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["w_s"], bs=w.block_size,
+                         alpha=w.alpha, gamma=w.gamma)
+    got = run_prefill_fused(w, inp)
+    err = np.abs(got.transpose(0, 2, 1, 3).reshape(n, 4, -1) - ref["o"]).max()
+    assert err <= TOL[dtype], err
+
+
+def test_attend_given_oracle_route():
+    """Stage 2 alone: feed the oracle's routing (lists and log pbar) to
+    dash_attend, so routing flips cannot mask an attend error."""
+    import sparse_hierarchical_attention_block_amd as dash
+    w = W.get("prefill_8k").replace(seq_len=1536)
+    inp = W.make_prefill(w)
+    B, H, Hkv, N, d, bs = w.batch, w.n_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block_size
+    nb = N // bs
+    ref = oracle_prefill(w, inp, nb)
+    p = params(w)
+    sizes = dash.dash_route_sizes_prefill(p, N)
+    n_qt = sizes["n_qt"]
+    count = np.zeros((B, Hkv, n_qt), np.int32)
+    idx = np.zeros((B, Hkv, n_qt, nb), np.int32)
+    logp = np.full((B, Hkv, n_qt, nb, QT), -np.inf, np.float32)
+    for b in range(B):
+        for g in range(Hkv):
+            for qt in range(n_qt):
+                pb = ref["pbar"][b, qt * QT:(qt + 1) * QT, g]              # [QT, nb]
+                lst = np.flatnonzero((pb > 0).any(0))
+                count[b, g, qt] = len(lst)
+                idx[b, g, qt, :len(lst)] = lst
+                with np.errstate(divide="ignore"):
+                    logp[b, g, qt] = np.log(pb).T
+    rb = dash.RouteBuffers(sizes, dev())
+    rb.sel_count.copy_(torch.from_numpy(count.ravel()))
+    rb.sel_idx.copy_(torch.from_numpy(idx.ravel()))
+    rb.sel_logp.copy_(torch.from_numpy(logp.ravel()))
+    q, k, v = (to_dev(inp[x], "bf16") for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    dash.dash_attend(p, q, k, v, N, rb, o)
+    torch.cuda.synchronize()
+    err = np.abs(o.float().cpu().numpy() - ref["o"]).max()
+    assert err <= TOL["bf16"], err
+
+
+def test_unselected_values_do_not_matter():
+    """Zero-probability blocks are masked: changing V of every block that a
+    tile neither selected nor owns leaves that tile's outputs bit-identical."""
+    w = W.get("prefill_8k").replace(seq_len=2048)
+    inp = W.make_prefill(w)
+    g1 = run_prefill(w, inp, bits=False)
+    N, bs, G = w.seq_len, w.block_size, w.group
+    qt, gg = N // QT - 1, 3
+    used = np.zeros(N // bs, bool)
+    used[g1["idx"][0, gg, qt, :g1["count"][0, gg, qt]]] = True
+    used[(qt * QT) // bs] = True
+    assert (~used).any()
+    v2 = inp["v"].copy()
+    for j in np.flatnonzero(~used):
+        v2[0, gg, j * bs:(j + 1) * bs] = 7.0
+    g2 = run_prefill(w, dict(inp, v=v2), bits=False)
+    rows = slice(qt * QT, qt * QT + QT)
+    heads = slice(gg * G, gg * G + G)
+    np.testing.assert_array_equal(g1["o"][0, heads, rows], g2["o"][0, heads, rows])
+    assert not np.array_equal(g1["o"], g2["o"])      # other tiles did read those blocks
+
+
+def test_deterministic():
+    w = W.get("prefill_8k").replace(seq_len=2048)
+    inp = W.make_prefill(w)
+    a = run_prefill_fused(w, inp)
+    b = run_prefill_fused(w, inp)
+    np.testing.assert_array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------------------
+
+DECODE_CASES = {
+    "tiny_f32_ragged": (tiny(batch=7, gamma=8.0, kind="decode"),
+                        [1, 63, 64, 65, 300, 1000, 1024]),
+    "tiny_bf16_ragged": (tiny(batch=4, gamma=8.0, kind="decode", dtype="bf16"),
+                         [1024, 640, 129, 2]),
+    "gqa4_d128": (W.get("decode_32k").replace(batch=4, seq_len=4096, count_lo=4, count_hi=40),
+                  [4096, 4000, 2049, 64]),
+    "gqa8_loguniform": (W.get("decode_128k").replace(batch=2, seq_len=8192, count_hi=64),
+                        [8192, 5555]),
+    "bs128_alpha2": (W.get("decode_32k").replace(batch=3, seq_len=3072, block_size=128,
+                                                 alpha=2.0, gamma=3.0, count_lo=2, count_hi=12),
+                     [3072, 3000, 130]),
+}
+
+
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_parity(case):
+    w, lens = DECODE_CASES[case]
+    print(f"[decode parity] {case}: {w} lens={lens}", flush=True)
+    inp = W.make_decode(w, cache_len=lens)
+    B, H, Hkv, d, bs, G = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, w.group
+    Lmax = inp["k_cache"].shape[2]
+    nb = -(-Lmax // bs)
+    lens = np.asarray(lens)
+    # summary cache holds exactly the blocks complete before each new token
+    summ = oracle.summaries(inp["k_cache"], inp["w_s"], bs, Lmax // bs)
+    for b in range(B):
+        summ[b, :, (lens[b] - 1) // bs:] = 0.0
+    g = run_decode(w, inp, summ_np=summ)
+    ref = oracle.decode(inp["q"], inp["k_cache"], inp["v_cache"], lens, inp["w_s"], bs=bs,
+                        alpha=w.alpha, gamma=w.gamma, nb_out=nb, want=("o", "tau", "x", "pbar"))
+    check_tau(g["tau"], ref["tau"])
+    ncand = (lens - 1) // bs
+    check_supports(g["bits"], ref["x"], ref["tau"], ncand)
+    for b in range(B):
+        for gg in range(Hkv):
+            hs = slice(gg * G, gg * G + G)
+            t = ncand[b]
+            union, solid, near = tile_union_ref(ref["pbar"][b:b + 1, gg, :t],
+                                                ref["x"][b:b + 1, hs, :t], ref["tau"][b:b + 1, hs], G)
+            cnt = g["count"][b, gg]
+            check_list(cnt, g["idx"][b, gg], union, solid, near)
+            lst = g["idx"][b, gg, :cnt]
+            np.testing.assert_allclose(np.exp(g["logp"][b, gg, lst]), ref["pbar"][b, gg, lst],
+                                       atol=2e-5)
+    err = np.abs(g["o"] - ref["o"]).max()
+    assert err <= TOL[w.dtype], f"decode max-abs err {err:.3e}"
+    # summary written exactly when the step completes a block
+    for b in range(B):
+        blk = lens[b] // bs - 1
+        after, before = g["summ"][b], g["summ_before"][b]
+        changed = np.flatnonzero(np.abs(after - before).max(axis=(0, 2)) > 0)
+        if lens[b] % bs == 0:
+            np.testing.assert_allclose(after[:, blk], ref["new_summary"][b], rtol=1e-5, atol=2e-5)
+            assert set(changed.tolist()) <= {blk}
+        else:
+            assert changed.size == 0
+    print(f"  max-abs err {err:.3e}", flush=True)
+
+
+def test_decode_matches_prefill_last_row():
+    """decode(L) is row L-1 of a causal prefill over the first L tokens."""
+    w = W.get("prefill_8k").replace(seq_len=1024)
+    inp = W.make_prefill(w)
+    pre = run_prefill_fused(w, inp)
+    L = 1024
+    wd = w.replace(kind="decode")
+    dinp = {"q": inp["q"][:, :, L - 1], "k_cache": inp["k"], "v_cache": inp["v"],
+            "cache_len": np.array([L], np.int32), "w_s": inp["w_s"]}
+    g = run_decode(wd, dinp, route=False)
+    err = np.abs(g["o"][0] - pre[0, :, L - 1]).max()
+    assert err <= TOL["bf16"], err

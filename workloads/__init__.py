@@ -21,6 +21,7 @@ when ``plant_per_head`` is set -- for the single new query.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import json
 import math
@@ -166,6 +167,12 @@ def prefill_plan(w: Workload, b: int, g: int):
     return plan
 
 
+def _pool_map(fn, items):
+    workers = min(16, os.cpu_count() or 1, max(len(items), 1))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fn, items))
+
+
 def make_prefill(w: Workload, batches=None):
     """q [B', H, N, d], k, v [B', Hkv, N, d], w_s [d, d] as float32 arrays."""
     B, H, Hkv, N, d, bs, G = w.batch, w.n_heads, w.n_kv_heads, w.seq_len, w.head_dim, \
@@ -174,26 +181,28 @@ def make_prefill(w: Workload, batches=None):
     q = np.empty((len(batches), H, N, d), np.float32)
     k = np.empty((len(batches), Hkv, N, d), np.float32)
     v = np.empty((len(batches), Hkv, N, d), np.float32)
-    for bi, b in enumerate(batches):
-        for g in range(Hkv):
-            kk = _rng(w.seed, _T_K, b, g).standard_normal((N, d), dtype=np.float32)
-            v[bi, g] = _cast(w, _rng(w.seed, _T_V, b, g).standard_normal((N, d), dtype=np.float32))
-            if w.planted:
-                plan = prefill_plan(w, b, g)
-                for t, (u, rel) in enumerate(plan):
-                    for j in rel:
-                        kk[j * bs:(j + 1) * bs] += 3.0 * u
-            k[bi, g] = _cast(w, kk)
-            for hh in range(G):
-                h = g * G + hh
-                eps = _rng(w.seed, _T_Q, b, h).standard_normal((N, d), dtype=np.float32)
-                if w.planted:
-                    qq = 0.1 * eps
-                    for t, (u, _) in enumerate(plan):
-                        qq[t * bs:(t + 1) * bs] += 3.0 * u
-                else:
-                    qq = eps
-                q[bi, h] = _cast(w, qq)
+
+    def unit(item):
+        bi, b, g = item
+        kk = _rng(w.seed, _T_K, b, g).standard_normal((N, d), dtype=np.float32)
+        v[bi, g] = _cast(w, _rng(w.seed, _T_V, b, g).standard_normal((N, d), dtype=np.float32))
+        plan = prefill_plan(w, b, g) if w.planted else []
+        for u, rel in plan:
+            for j in rel:
+                kk[j * bs:(j + 1) * bs] += 3.0 * u
+        k[bi, g] = _cast(w, kk)
+        for hh in range(G):
+            h = g * G + hh
+            eps = _rng(w.seed, _T_Q, b, h).standard_normal((N, d), dtype=np.float32)
+            if plan:
+                qq = 0.1 * eps
+                for t, (u, _) in enumerate(plan):
+                    qq[t * bs:(t + 1) * bs] += 3.0 * u
+            else:
+                qq = eps
+            q[bi, h] = _cast(w, qq)
+
+    _pool_map(unit, [(bi, b, g) for bi, b in enumerate(batches) for g in range(Hkv)])
     return {"q": q, "k": k, "v": v, "w_s": w_s(w)}
 
 
@@ -226,22 +235,25 @@ def make_decode(w: Workload, batches=None, cache_len=None):
     q = np.empty((len(batches), H, d), np.float32)
     kc = np.empty((len(batches), Hkv, Lmax, d), np.float32)
     vc = np.empty((len(batches), Hkv, Lmax, d), np.float32)
-    for bi, b in enumerate(batches):
-        for g in range(Hkv):
-            kk = _rng(w.seed, _T_K, b, g).standard_normal((Lmax, d), dtype=np.float32)
-            vc[bi, g] = _cast(w, _rng(w.seed, _T_V, b, g).standard_normal((Lmax, d),
-                                                                            dtype=np.float32))
-            plans = decode_plan(w, b, g) if w.planted else []
-            for u, rel in plans:
-                for j in rel:
-                    kk[j * bs:(j + 1) * bs] += 3.0 * u
-            kc[bi, g] = _cast(w, kk)
-            for hh in range(G):
-                h = g * G + hh
-                eps = _rng(w.seed, _T_Q, b, h).standard_normal(d, dtype=np.float32)
-                if plans:
-                    u = plans[hh if w.plant_per_head else 0][0]
-                    q[bi, h] = _cast(w, 3.0 * u + 0.1 * eps)
-                else:
-                    q[bi, h] = _cast(w, eps)
+
+    def unit(item):
+        bi, b, g = item
+        kk = _rng(w.seed, _T_K, b, g).standard_normal((Lmax, d), dtype=np.float32)
+        vc[bi, g] = _cast(w, _rng(w.seed, _T_V, b, g).standard_normal((Lmax, d),
+                                                                        dtype=np.float32))
+        plans = decode_plan(w, b, g) if w.planted else []
+        for u, rel in plans:
+            for j in rel:
+                kk[j * bs:(j + 1) * bs] += 3.0 * u
+        kc[bi, g] = _cast(w, kk)
+        for hh in range(G):
+            h = g * G + hh
+            eps = _rng(w.seed, _T_Q, b, h).standard_normal(d, dtype=np.float32)
+            if plans:
+                u = plans[hh if w.plant_per_head else 0][0]
+                q[bi, h] = _cast(w, 3.0 * u + 0.1 * eps)
+            else:
+                q[bi, h] = _cast(w, eps)
+
+    _pool_map(unit, [(bi, b, g) for bi, b in enumerate(batches) for g in range(Hkv)])
     return {"q": q, "k_cache": kc, "v_cache": vc, "cache_len": lens, "w_s": w_s(w)}
