@@ -1,0 +1,290 @@
+"""Benchmark of the DashAttention forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_8k]
+
+A step is one fused causal prefill (dash_prefill: Stage 0 summaries, Stage 1
+entmax routing, Stage 2 prior-induced sparse attention) over the workload's
+synthetic batch, inputs resident in HBM.  ``value`` is prefill tokens/s
+(B * N / step time).  The same line carries:
+  roofline      the attend kernel (the dominant one): selected-tile MFMA flops
+                per launch / its average launch time (HIP events on the stream
+                it runs on) against the 2.5 PFLOP/s dense bf16 peak;
+  stages        per-stage kernel times (each entry point timed alone);
+  decode        one batched decode step (dash_decode) on the 32 x 32K decode
+                workload: microseconds per step and selected-KV GB/s against
+                the 8 TB/s HBM peak;
+  cpu_baseline  the fp64 CPU oracle timed on this host's cores on a bounded
+                sample of the same workload, scaled to tokens/s.
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tok/s + decode step µs at ~75% block sparsity; % HBM/MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+QT = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_prefill_8k_traffic.txt")
+ATTEND_SRC = os.path.join(ROOT, "sparse_hierarchical_attention_block_amd", "csrc", "attend.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_8k")
+    ap.add_argument("--decode-workload", default="decode_32k")
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--dense", action="store_true",
+                    help="also time the in-house dense causal attention (all blocks, zero prior)")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="launch one device copy of this many MiB (HBM-counter calibration)")
+    return ap.parse_args()
+
+
+def events_time(fn, steps, warmup, torch):
+    """Average milliseconds of fn() over `steps` calls on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def traffic_for_attend():
+    """HBM bytes per attend launch from the committed counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    src = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()
+    if kv.get("attend_hip_sha256") != src:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def prefill_bench(args, torch, dash, W):
+    w = W.get(args.workload)
+    if args.alpha is not None:
+        w = w.replace(alpha=args.alpha)
+    dev = torch.device("cuda:0")
+    inp = W.make_prefill(w)
+    B, H, Hkv, N, d, bs, G = w.batch, w.n_heads, w.n_kv_heads, w.seq_len, w.head_dim, \
+        w.block_size, w.group
+    p = dash.make_params(B, H, Hkv, d, bs, w.alpha, w.gamma, w.dtype)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(inp[x]).to(dev, tdt) for x in ("q", "k", "v"))
+    ws_mat = torch.from_numpy(inp["w_s"]).to(dev)
+    nb = N // bs
+    summ = torch.zeros(B * Hkv * nb * d, dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    ws = dash.workspace(dash.dash_prefill_workspace_bytes(p, N), dev)
+    del inp
+
+    step = lambda: dash.dash_prefill(p, q, k, v, N, ws_mat, summ, nb, o, ws)  # noqa: E731
+    ms_step = events_time(step, args.steps, args.warmup, torch)
+
+    # stage-wise launches of the same kernels
+    sizes = dash.dash_route_sizes_prefill(p, N)
+    rb = dash.RouteBuffers(sizes, dev)
+    t_sum = events_time(lambda: dash.dash_summarize(p, k, N, 0, nb, ws_mat, summ, nb),
+                        args.steps, 2, torch)
+    t_route = events_time(lambda: dash.dash_route(p, q, N, summ, nb, rb), args.steps, 2, torch)
+    o2 = torch.empty_like(q)
+    t_att = events_time(lambda: dash.dash_attend(p, q, k, v, N, rb, o2), args.steps, 2, torch)
+
+    count = rb.sel_count.view(B, Hkv, -1).cpu().numpy().astype(np.int64)
+    n_qt = count.shape[2]
+    qt = np.arange(n_qt)
+    cand = (qt * QT) // bs                                 # routing candidates per tile
+    cpb = bs // 64
+    own_chunks = qt - (qt * QT // bs) * cpb + 1            # own-block 64-key chunks walked
+    chunks = (count * cpb + own_chunks[None, None, :]).sum()
+    flops_per_chunk = 4.0 * G * QT * 64 * d                # QK^T + PV for G*64 rows x 64 keys
+    att_flops = float(chunks) * flops_per_chunk
+    dense_chunks = float(B * Hkv) * (cand * cpb + own_chunks).sum()
+    tile_union_density = float((count + 1).sum() / (B * Hkv * (cand + 1).sum()))
+    achieved = att_flops / (t_att * 1e-3) / 1e12
+    traffic = traffic_for_attend()
+    res = {
+        "workload": w, "ms_step": ms_step, "tok_s": B * N / (ms_step * 1e-3),
+        "stages_ms": {"summarize": t_sum, "route": t_route, "attend": t_att},
+        "attend_flops": att_flops, "attend_tflops": achieved,
+        "tile_union_density": tile_union_density,
+        "selected_chunk_fraction": float(chunks) / dense_chunks,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if args.dense:
+        rbd = dash.RouteBuffers(sizes, dev)
+        rbd.sel_count.copy_(torch.from_numpy(np.broadcast_to(cand, (B * Hkv, n_qt)).astype(
+            np.int32).ravel()))
+        idx = np.broadcast_to(np.arange(nb, dtype=np.int32), (B * Hkv * n_qt, nb))
+        rbd.sel_idx.copy_(torch.from_numpy(np.ascontiguousarray(idx).ravel()))
+        rbd.sel_logp.zero_()
+        t_dense = events_time(lambda: dash.dash_attend(p, q, k, v, N, rbd, o2), args.steps, 2,
+                              torch)
+        res["dense_attend_ms"] = t_dense
+        res["dense_tok_s"] = B * N / (t_dense * 1e-3)
+        res["dense_tflops"] = dense_chunks * flops_per_chunk / (t_dense * 1e-3) / 1e12
+    return res
+
+
+def decode_bench(args, torch, dash, W):
+    w = W.get(args.decode_workload)
+    dev = torch.device("cuda:0")
+    B, H, Hkv, d, bs, L = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, w.seq_len
+    p = dash.make_params(B, H, Hkv, d, bs, w.alpha, w.gamma, w.dtype)
+    kc = torch.empty((B, Hkv, L, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    q = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    for b0 in range(0, B, 8):
+        part = W.make_decode(w, batches=range(b0, min(B, b0 + 8)))
+        kc[b0:b0 + 8] = torch.from_numpy(part["k_cache"]).to(dev, torch.bfloat16)
+        vc[b0:b0 + 8] = torch.from_numpy(part["v_cache"]).to(dev, torch.bfloat16)
+        q[b0:b0 + 8] = torch.from_numpy(part["q"]).to(dev, torch.bfloat16)
+        w_s = part["w_s"]
+        del part
+    ws_mat = torch.from_numpy(w_s).to(dev)
+    nb = L // bs
+    summ = torch.zeros(B * Hkv * nb * d, dtype=torch.float32, device=dev)
+    dash.dash_summarize(p, kc, L, 0, nb, ws_mat, summ, nb)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    ws = dash.workspace(dash.dash_decode_workspace_bytes(p, L), dev)
+    rb = dash.RouteBuffers(dash.dash_route_sizes_decode(p, L), dev)
+    step = lambda: dash.dash_decode(p, q, kc, vc, lens, L, ws_mat, summ, nb, o, ws,  # noqa
+                                    route=rb)
+    ms = events_time(step, args.steps, args.warmup, torch)
+    count = rb.sel_count.cpu().numpy().astype(np.int64)
+    own_len = (L - 1) % bs + 1
+    sel_bytes = float(((count * bs + own_len) * d * 2 * 2).sum())
+    ncand = (L - 1) // bs
+    density = float((count + 1).sum() / (B * Hkv * (ncand + 1)))
+    summ_bytes = float(B * Hkv * ncand * d * 4)
+    gbs = sel_bytes / (ms * 1e-3) / 1e9
+    return {"workload": w, "us_per_step": ms * 1e3, "selected_kv_bytes": sel_bytes,
+            "block_density": density,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "scope": "selected K/V bytes / whole decode step"},
+            "all_bytes_gbs": round((sel_bytes + summ_bytes) / (ms * 1e-3) / 1e9, 1)}
+
+
+def cpu_baseline(args, W, min_seconds=10.0):
+    """The CPU oracle on the same workload (all query positions and heads),
+    repeated until at least `min_seconds` of CPU work; tokens/s = positions
+    processed / seconds (input generation excluded)."""
+    import oracle
+    w = W.get(args.workload)
+    if args.alpha is not None:
+        w = w.replace(alpha=args.alpha)
+    inp = W.make_prefill(w)
+    threads = oracle.max_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill(inp["q"], inp["k"], inp["v"], inp["w_s"], bs=w.block_size,
+                       alpha=w.alpha, gamma=w.gamma)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 100:
+            break
+    return {"value": round(reps * w.batch * w.seq_len / dt, 1), "unit": "tok/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"whole workload ({w.batch} x {w.seq_len} positions, {w.n_heads} heads) "
+                      f"x {reps} repeats, fp64 C/OpenMP, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_hierarchical_attention_block_amd as dash
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calib_mb:
+        n = args.copy_calib_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    pre = prefill_bench(args, torch, dash, W)
+    dec = None if args.no_decode else decode_bench(args, torch, dash, W)
+    cpu = None if args.no_cpu else cpu_baseline(args, W)
+    w = pre["workload"]
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tok_s"], 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: causal prefill B={w.batch} N={w.seq_len} "
+                               f"H={w.n_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
+                               f"block={w.block_size} alpha={w.alpha} gamma={w.gamma}",
+                   "global_batch": w.batch, "seq_len": w.seq_len,
+                   "tile_union_block_density": round(pre["tile_union_density"], 4),
+                   "parallelism": "single GPU"},
+        "roofline": pre["roofline"],
+        "stages_ms": {k2: round(v2, 4) for k2, v2 in pre["stages_ms"].items()},
+        "attend_gflop": round(pre["attend_flops"] / 1e9, 2),
+    }
+    if "dense_tok_s" in pre:
+        line["dense_attend"] = {"ms": round(pre["dense_attend_ms"], 4),
+                                "tok_s": round(pre["dense_tok_s"], 1),
+                                "tflops": round(pre["dense_tflops"], 1)}
+    if dec is not None:
+        dw = dec["workload"]
+        line["decode"] = {"workload": f"{dw.name}: batch {dw.batch} x {dw.seq_len} context, "
+                                      f"H={dw.n_heads} Hkv={dw.n_kv_heads} block={dw.block_size}",
+                          "us_per_step": round(dec["us_per_step"], 2),
+                          "block_density": round(dec["block_density"], 4),
+                          "selected_kv_gb": round(dec["selected_kv_bytes"] / 1e9, 4),
+                          "roofline": dec["roofline"],
+                          "all_bytes_gbs": dec["all_bytes_gbs"]}
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
