@@ -66,7 +66,7 @@ bool route_lds_ok(const Shape& s, int64_t n) {
   int64_t pp = 64;
   while (pp > 1 && pp * s.G * pitch * 4 > 64 * 1024) pp >>= 1;
   while (pp * s.G < 16) pp <<= 1;
-  while (pp * s.G > 256) pp >>= 1;
+  while (pp * s.G > 64) pp >>= 1;
   const int64_t lds = (pp * s.G * pitch + pp * s.G) * 4 + (pitch - 4) * 4;
   return lds <= 160 * 1024;
 }

@@ -69,14 +69,96 @@ __device__ __forceinline__ ChunkRef chunk_ref(int c, int n_own, int64_t own_c0, 
 // ------------------------------------------------------------------------------------------
 // bf16, MFMA
 // ------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(512) void attend_bf16_kernel(AttendArgs a) {
-  constexpr int KP = D + 8;        // K row pitch (elements)
-  constexpr int VP = kChunk + 4;   // V^T row pitch (elements)
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kChunk * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VP];
+// Staging of one 64-key chunk: K row-major [64][D + 8], V transposed [D][64 + 4]
+// (bf16).  NT threads; each thread owns KPT 16-byte pieces of K and VPT 4x4
+// blocks of V.
+template <int D, int NT>
+struct ChunkStage {
+  static constexpr int KP = D + 8;
+  static constexpr int VP = kChunk + 4;
+  static constexpr int KTOT = kChunk * (D / 8);          // 16-byte pieces of K
+  static constexpr int VTOT = (kChunk / 4) * (D / 4);    // 4x4 blocks of V
+  static constexpr int KPT = (KTOT + NT - 1) / NT;
+  static constexpr int VPT = (VTOT + NT - 1) / NT;
+  u32x4 kr[KPT];
+  u32x2 vr[VPT][4];
 
-  const int nthreads = blockDim.x;
+  __device__ __forceinline__ void load(const __bf16* kp, const __bf16* vp, int64_t key0,
+                                       int64_t n) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = threadIdx.x + i * NT;
+      const int key = e / (D / 8), seg = e % (D / 8);
+      const int64_t kpos = key0 + key;
+      kr[i] = (u32x4){0u, 0u, 0u, 0u};
+      if ((KTOT % NT == 0 || e < KTOT) && kpos < n) kr[i] = *(const u32x4*)(kp + kpos * D + seg * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = threadIdx.x + i * NT;
+      const int db = e % (D / 4), kb = e / (D / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t kpos = key0 + 4 * kb + r;
+        vr[i][r] = (u32x2){0u, 0u};
+        if ((VTOT % NT == 0 || e < VTOT) && kpos < n)
+          vr[i][r] = *(const u32x2*)(vp + kpos * D + 4 * db);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* Ks, __bf16* Vt) const {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = threadIdx.x + i * NT;
+      const int key = e / (D / 8), seg = e % (D / 8);
+      if (KTOT % NT == 0 || e < KTOT) *(u32x4*)(Ks + key * KP + seg * 8) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = threadIdx.x + i * NT;
+      if (VTOT % NT != 0 && e >= VTOT) continue;
+      const int db = e % (D / 4), kb = e / (D / 4);
+      const u32x2* in = vr[i];
+      const u32x2 o0 = {pack_lo(in[0].x, in[1].x), pack_lo(in[2].x, in[3].x)};
+      const u32x2 o1 = {pack_hi(in[0].x, in[1].x), pack_hi(in[2].x, in[3].x)};
+      const u32x2 o2 = {pack_lo(in[0].y, in[1].y), pack_lo(in[2].y, in[3].y)};
+      const u32x2 o3 = {pack_hi(in[0].y, in[1].y), pack_hi(in[2].y, in[3].y)};
+      *(u32x2*)(Vt + (4 * db + 0) * VP + 4 * kb) = o0;
+      *(u32x2*)(Vt + (4 * db + 1) * VP + 4 * kb) = o1;
+      *(u32x2*)(Vt + (4 * db + 2) * VP + 4 * kb) = o2;
+      *(u32x2*)(Vt + (4 * db + 3) * VP + 4 * kb) = o3;
+    }
+  }
+};
+
+// Rescale the running output only when a row max grows by more than 2^8:
+// exp2(s - m_ref) then stays <= 256, exact in float32 and in bf16's range.
+constexpr float kLazyRescale = 8.0f;
+
+// S^T (64 keys x 32 queries) = K Q^T for one staged chunk: two 32-key tiles.
+template <int D, int KP>
+__device__ __forceinline__ void chunk_scores(const __bf16* Kc, const bf16x8 (&qf)[D / 16], int l32,
+                                             int lh, f32x16 (&st)[2]) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 kw = *(const u32x4*)(Kc + (32 * kt + l32) * KP + 16 * s + 8 * lh);
+      st[kt] = mfma32(as_bf16x8(kw), qf[s], st[kt]);
+    }
+  }
+}
+
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
+  using Stage = ChunkStage<D, NT>;
+  constexpr int KP = Stage::KP, VP = Stage::VP;
+  constexpr int NBUF = 3;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][kChunk * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[NBUF][D * VP];
+
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int l32 = lane % 32, lh = lane / 32;
 
@@ -89,10 +171,10 @@ __global__ __launch_bounds__(512) void attend_bf16_kernel(AttendArgs a) {
   const int64_t p_begin = qt * kQTa;
   const int64_t tile = bg * a.n_qt + qt;
 
-  const int gw = wi * 8 + wave;        // wave index within the tile
-  const int h = g * a.G + gw / 2;      // query head
+  const int gw = wi * (NT / kWave) + wave;   // wave index within the tile
+  const int h = g * a.G + gw / 2;            // query head
   const int half = gw % 2;
-  const int qloc = 32 * half + l32;    // query row within the tile
+  const int qloc = 32 * half + l32;          // query row within the tile
   const int64_t qpos = p_begin + qloc;
 
   const __bf16* qp = (const __bf16*)a.q + (((int64_t)b * a.H + h) * a.n) * D;
@@ -109,100 +191,94 @@ __global__ __launch_bounds__(512) void attend_bf16_kernel(AttendArgs a) {
   }
 
   const int cpb = a.bs / kChunk;
-  const int64_t own_block = p_begin / a.bs;
-  const int64_t own_c0 = own_block * cpb;
+  const int64_t own_c0 = (p_begin / a.bs) * cpb;
   const int n_own = (int)(qt - own_c0 + 1);
   const int count = a.sel_count[tile];
   const int32_t* idx = a.sel_idx + tile * a.nb;
   const int n_chunks = n_own + count * cpb;
+  const float* logp_tile = a.sel_logp + tile * a.nb * kQTa;
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
+  // Chunk c sits in LDS buffer c % 3; chunk c+1 is already staged and chunk
+  // c+2's K/V are in flight from HBM into registers.  The waves form two
+  // groups that walk the same chunks half a phase apart: group A computes
+  // chunk c's scores after the barrier, group B computed them before it (at
+  // the end of the previous iteration).  A SIMD hosts one wave of each group,
+  // so one wave's softmax VALU work overlaps the other wave's MFMAs.
+  const bool late = wave >= NT / kWave / 2;   // group B
+  Stage stage;
+  ChunkRef cr_cur = chunk_ref(0, n_own, own_c0, cpb, idx), cr_nx, cr_nx2;
+  stage.load(kp, vp, cr_cur.key0, a.n);
+  stage.store(Ks[0], Vt[0]);
+  if (n_chunks > 1) {
+    cr_nx = chunk_ref(1, n_own, own_c0, cpb, idx);
+    stage.load(kp, vp, cr_nx.key0, a.n);
+    stage.store(Ks[1], Vt[1]);
+  }
+  if (n_chunks > 2) {
+    cr_nx2 = chunk_ref(2, n_own, own_c0, cpb, idx);
+    stage.load(kp, vp, cr_nx2.key0, a.n);
+  }
+  __syncthreads();
+  f32x16 st[2];
+  if (late) chunk_scores<D, KP>(Ks[0], qf, l32, lh, st);
+
+  int bcur = 0;
   for (int c = 0; c < n_chunks; ++c) {
-    const ChunkRef cr = chunk_ref(c, n_own, own_c0, cpb, idx);
-    __syncthreads();
-    // ---- stage K (row-major) and V^T into LDS ----
-    for (int e = threadIdx.x; e < kChunk * (D / 8); e += nthreads) {
-      const int key = e / (D / 8), seg = e % (D / 8);
-      const int64_t kpos = cr.key0 + key;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (kpos < a.n) w = *(const u32x4*)(kp + kpos * D + seg * 8);
-      *(u32x4*)(Ks + key * KP + seg * 8) = w;
-    }
-    for (int e = threadIdx.x; e < (kChunk / 4) * (D / 4); e += nthreads) {
-      const int db = e % (D / 4), kb = e / (D / 4);
-      u32x2 in[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t kpos = cr.key0 + 4 * kb + r;
-        in[r] = (u32x2){0u, 0u};
-        if (kpos < a.n) in[r] = *(const u32x2*)(vp + kpos * D + 4 * db);
-      }
-      u32x2 o0 = {pack_lo(in[0].x, in[1].x), pack_lo(in[2].x, in[3].x)};
-      u32x2 o1 = {pack_hi(in[0].x, in[1].x), pack_hi(in[2].x, in[3].x)};
-      u32x2 o2 = {pack_lo(in[0].y, in[1].y), pack_lo(in[2].y, in[3].y)};
-      u32x2 o3 = {pack_hi(in[0].y, in[1].y), pack_hi(in[2].y, in[3].y)};
-      *(u32x2*)(Vt + (4 * db + 0) * VP + 4 * kb) = o0;
-      *(u32x2*)(Vt + (4 * db + 1) * VP + 4 * kb) = o1;
-      *(u32x2*)(Vt + (4 * db + 2) * VP + 4 * kb) = o2;
-      *(u32x2*)(Vt + (4 * db + 3) * VP + 4 * kb) = o3;
-    }
-    __syncthreads();
+    const int bnx = bcur == NBUF - 1 ? 0 : bcur + 1;
+    const int bnx2 = bnx == NBUF - 1 ? 0 : bnx + 1;
+    if (!late) chunk_scores<D, KP>(Ks[bcur], qf, l32, lh, st);
 
-    // ---- S^T = K Q^T : two 32-key tiles ----
-    f32x16 st[2];
+    // ---- online softmax of chunk c, exp2 domain: logit2 = s * scale_log2 + bias2 ----
+    const float bias2 =
+        cr_cur.block >= 0 ? logp_tile[cr_cur.block * kQTa + qloc] * kLog2e : 0.f;
+    if (cr_cur.diag) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const u32x4 kw = *(const u32x4*)(Ks + (32 * kt + l32) * KP + 16 * s + 8 * lh);
-        st[kt] = mfma32(as_bf16x8(kw), qf[s], st[kt]);
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * kt + 8 * (i / 4) + 4 * lh + (i % 4);
+          if (cr_cur.key0 + key > qpos) st[kt][i] = -INFINITY;
+        }
     }
-
-    // ---- online softmax (exp2 domain) ----
-    float bias2 = 0.f;
-    if (cr.block >= 0) bias2 = a.sel_logp[(tile * a.nb + cr.block) * kQTa + qloc] * kLog2e;
-    float mx = -INFINITY;
+    float smax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 32 * kt + 8 * (i / 4) + 4 * lh + (i % 4);
-        float sv = fmaf(st[kt][i], a.scale_log2, bias2);
-        if (cr.diag && cr.key0 + key > qpos) sv = -INFINITY;
-        st[kt][i] = sv;
-        mx = fmaxf(mx, sv);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float corr = exp2f(m_run - m_use);
+      for (int i = 0; i < 16; ++i) smax = fmaxf(smax, st[kt][i]);
+    smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+    const float cmax = fmaf(smax, a.scale_log2, bias2);   // -inf when all masked
+    if (__any(cmax > m_ref + kLazyRescale)) {
+      const float m_new = fmaxf(m_ref, cmax);
+      const float corr = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= corr;
+      m_ref = m_new;
+    }
+    const float off = m_ref == -INFINITY ? 0.f : bias2 - m_ref;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = exp2f(st[kt][i] - m_use);
+        const float pv = fast_exp2(fmaf(st[kt][i], a.scale_log2, off));
         st[kt][i] = pv;
         psum += pv;
       }
     psum += __shfl_xor(psum, 32, kWave);
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] *= corr;
+    l_run += psum;
 
     // ---- O^T += V^T P^T : 4 k-steps of 16 keys ----
+    const __bf16* Vc = Vt[bcur];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kt = ks / 2, i0 = 8 * (ks % 2);
@@ -214,13 +290,32 @@ __global__ __launch_bounds__(512) void attend_bf16_kernel(AttendArgs a) {
       const bf16x8 pf = as_bf16x8(pw);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const __bf16* vrow = Vt + (32 * dt + l32) * VP + 16 * ks + 4 * lh;
+        const __bf16* vrow = Vc + (32 * dt + l32) * VP + 16 * ks + 4 * lh;
         const u32x2 v0 = *(const u32x2*)(vrow);
         const u32x2 v1 = *(const u32x2*)(vrow + 8);
         const u32x4 vw = {v0.x, v0.y, v1.x, v1.y};
         acc[dt] = mfma32(as_bf16x8(vw), pf, acc[dt]);
       }
     }
+    if (late && c + 1 < n_chunks) {
+      __builtin_amdgcn_sched_barrier(0);
+      chunk_scores<D, KP>(Ks[bnx], qf, l32, lh, st);
+    }
+
+    // chunk c+2 into the buffer chunk c-1 used (every wave is past it)
+    if (c + 2 < n_chunks) stage.store(Ks[bnx2], Vt[bnx2]);
+    __syncthreads();
+    if (c + 3 < n_chunks) {
+      const ChunkRef cr3 = chunk_ref(c + 3, n_own, own_c0, cpb, idx);
+      stage.load(kp, vp, cr3.key0, a.n);
+      cr_cur = cr_nx;
+      cr_nx = cr_nx2;
+      cr_nx2 = cr3;
+    } else {
+      cr_cur = cr_nx;
+      cr_nx = cr_nx2;
+    }
+    bcur = bnx;
   }
 
   // ---- normalise and store: acc[dt][i] = O[query l32][32 dt + 8 (i/4) + 4 lh + i%4] ----
@@ -294,7 +389,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
       s = fmaf(s, scale, bias2);
       const float m_new = fmaxf(m_run, s);
       if (m_new == -INFINITY) continue;
-      const float corr = exp2f(m_run - m_new), p = exp2f(s - m_new);
+      const float corr = fast_exp2(m_run - m_new), p = fast_exp2(s - m_new);
       l_run = l_run * corr + p;
 #pragma unroll
       for (int cc = 0; cc < D; ++cc) ov[cc] = fmaf(p, Vs[key * D + cc], ov[cc] * corr);
@@ -334,10 +429,13 @@ hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, c
     a.wg_per_tile = (waves + 7) / 8;
     const int threads = (waves < 8 ? waves : 8) * kWave;
     dim3 grid((unsigned)(tiles * a.wg_per_tile));
-    if (s.d == 64)
-      hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, dim3(threads), 0, st, a);
-    else
-      hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, dim3(threads), 0, st, a);
+#define DASH_AT(D, NT) hipLaunchKernelGGL((attend_bf16_kernel<D, NT>), grid, dim3(NT), 0, st, a)
+    if (s.d == 64) {
+      if (threads == 128) DASH_AT(64, 128); else if (threads == 256) DASH_AT(64, 256); else DASH_AT(64, 512);
+    } else {
+      if (threads == 128) DASH_AT(128, 128); else if (threads == 256) DASH_AT(128, 256); else DASH_AT(128, 512);
+    }
+#undef DASH_AT
   } else {
     a.wg_per_tile = 1;
     dim3 grid((unsigned)(tiles * s.G));

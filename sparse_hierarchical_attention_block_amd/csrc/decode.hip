@@ -51,38 +51,56 @@ struct DecodeArgs {
   float e, scale, scale_log2;
 };
 
+__device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
+
 __device__ __forceinline__ int64_t clamp_len(int32_t v, int64_t max_len) {
   int64_t l = v;
   return l < 1 ? 1 : (l > max_len ? max_len : l);
 }
 
 // ---- 1. coarse scores ------------------------------------------------------------------------
+// One thread per cached summary j; the row is read with 16-byte loads (32
+// floats in flight per batch) and serves all G heads, whose queries sit in LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_scores_kernel(DecodeArgs a) {
-  __shared__ float Ss[64 * (D + 1)];
-  __shared__ float qs[8 * D];
+__global__ __launch_bounds__(64) void decode_scores_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float qs[8][D];
   const int64_t bg = blockIdx.y;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
   const int64_t ncand = (len - 1) / a.bs;
   const int64_t j0 = (int64_t)blockIdx.x * 64;
   if (j0 >= ncand) return;
-  const float* sb = a.summ + (bg * a.summ_blocks + j0) * D;
-  for (int e = threadIdx.x; e < 64 * D; e += 256) {
-    const int r = e / D, c = e % D;
-    Ss[r * (D + 1) + c] = (j0 + r < ncand) ? sb[e] : 0.f;
-  }
   const T* qb = (const T*)a.q + ((int64_t)b * a.H + g * a.G) * D;
-  for (int e = threadIdx.x; e < a.G * D; e += 256) qs[e] = to_f32(qb[e]);
+  for (int e = threadIdx.x; e < a.G * D; e += 64) qs[e / D][e % D] = to_f32(qb[e]);
   __syncthreads();
-  const int jl = threadIdx.x % 64;
-  if (j0 + jl >= ncand) return;
-  for (int h = threadIdx.x / 64; h < a.G; h += 4) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) acc = fmaf(qs[h * D + c], Ss[jl * (D + 1) + c], acc);
-    a.x[((int64_t)b * a.H + g * a.G + h) * a.nb + j0 + jl] = acc * a.scale;
+  const int64_t j = j0 + threadIdx.x;
+  if (j >= ncand) return;
+  const float* srow = a.summ + (bg * a.summ_blocks + j) * D;
+  float acc[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) acc[h] = 0.f;
+#pragma unroll
+  for (int c0 = 0; c0 < D; c0 += 32) {
+    f32x4 sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = *(const f32x4*)(srow + c0 + 4 * i);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      if (h < a.G) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x4 qv = *(const f32x4*)(&qs[h][c0 + 4 * i]);
+          acc[h] = fmaf(qv.x, sv[i].x, acc[h]);
+          acc[h] = fmaf(qv.y, sv[i].y, acc[h]);
+          acc[h] = fmaf(qv.z, sv[i].z, acc[h]);
+          acc[h] = fmaf(qv.w, sv[i].w, acc[h]);
+        }
+      }
+    }
   }
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+    if (h < a.G) a.x[((int64_t)b * a.H + g * a.G + h) * a.nb + j] = acc[h] * a.scale;
 }
 
 // ---- 2. threshold, GQA average, union, compaction ------------------------------------------
@@ -183,18 +201,40 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
     for (int c64 = 0; c64 < a.bs / 64; ++c64) {
       const int64_t key0 = j * a.bs + 64 * c64;
       if (key0 >= len) break;
+      // Issue every load of the chunk before any use.  Addresses are clamped
+      // to the last valid key, so each load stays in bounds and reads finite
+      // data; keys >= len are masked below (score -inf, probability 0).
+      u32x4 kw[4][D / 32];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int64_t key = min64(key0 + 16 * kt + l16, len - 1);
+#pragma unroll
+        for (int sp = 0; sp < D / 32; ++sp)
+          kw[kt][sp] = *(const u32x4*)(kb + key * D + 32 * sp + 8 * lg);
+      }
+      // V rows this lane needs: k = 8 lg + e' <-> key 32 ks + 16 (e'/4) + 4 lg + e'%4,
+      // DPL consecutive d starting at DPL * l16
+      uint32_t vin[2][8][DPL / 2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int ep = 0; ep < 8; ++ep) {
+          const int64_t key = min64(key0 + 32 * ks + 16 * (ep / 4) + 4 * lg + (ep % 4), len - 1);
+          if constexpr (DPL == 8) {
+            const u32x4 t = *(const u32x4*)(vb + key * D + DPL * l16);
+            vin[ks][ep][0] = t.x; vin[ks][ep][1] = t.y; vin[ks][ep][2] = t.z; vin[ks][ep][3] = t.w;
+          } else {
+            const u32x2 t = *(const u32x2*)(vb + key * D + DPL * l16);
+            vin[ks][ep][0] = t.x; vin[ks][ep][1] = t.y;
+          }
+        }
       // S^T = K Q^T: st[kt][i] = S[query l16][key 16 kt + 4 lg + i]
       f32x4 st[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         st[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        const int64_t key = key0 + 16 * kt + l16;
 #pragma unroll
-        for (int sp = 0; sp < D / 32; ++sp) {
-          u32x4 w = {0u, 0u, 0u, 0u};
-          if (key < len) w = *(const u32x4*)(kb + key * D + 32 * sp + 8 * lg);
-          st[kt] = mfma16(as_bf16x8(w), qf[sp], st[kt]);
-        }
+        for (int sp = 0; sp < D / 32; ++sp) st[kt] = mfma16(as_bf16x8(kw[kt][sp]), qf[sp], st[kt]);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -210,13 +250,13 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = exp2f(m_run - m_use);
+      const float corr = fast_exp2(m_run - m_use);
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = exp2f(st[kt][i] - m_use);
+          const float pv = fast_exp2(st[kt][i] - m_use);
           st[kt][i] = pv;
           psum += pv;
         }
@@ -231,43 +271,26 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < DPL; ++c) acc[c][i] *= ci;
       }
-      // O += P V over two 32-key steps; k = 8 lg + e' <-> key 32 ks + 16 (e'/4) + 4 lg + e'%4
+      // O += P V over two 32-key steps
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4 pw = {pack_bf16(st[2 * ks][0], st[2 * ks][1]), pack_bf16(st[2 * ks][2], st[2 * ks][3]),
                     pack_bf16(st[2 * ks + 1][0], st[2 * ks + 1][1]),
                     pack_bf16(st[2 * ks + 1][2], st[2 * ks + 1][3])};
         const bf16x8 pf = as_bf16x8(pw);
-        // rows of V this lane needs, DPL consecutive d starting at DPL * l16
-        uint32_t vin[8][DPL / 2];
-#pragma unroll
-        for (int ep = 0; ep < 8; ++ep) {
-          const int64_t key = key0 + 32 * ks + 16 * (ep / 4) + 4 * lg + (ep % 4);
-#pragma unroll
-          for (int w = 0; w < DPL / 2; ++w) vin[ep][w] = 0u;
-          if (key < len) {
-            if constexpr (DPL == 8) {
-              const u32x4 t = *(const u32x4*)(vb + key * D + DPL * l16);
-              vin[ep][0] = t.x; vin[ep][1] = t.y; vin[ep][2] = t.z; vin[ep][3] = t.w;
-            } else {
-              const u32x2 t = *(const u32x2*)(vb + key * D + DPL * l16);
-              vin[ep][0] = t.x; vin[ep][1] = t.y;
-            }
-          }
-        }
 #pragma unroll
         for (int c = 0; c < DPL; ++c) {
           u32x4 vw;
           if (c % 2 == 0) {
-            vw.x = pack_lo(vin[0][c / 2], vin[1][c / 2]);
-            vw.y = pack_lo(vin[2][c / 2], vin[3][c / 2]);
-            vw.z = pack_lo(vin[4][c / 2], vin[5][c / 2]);
-            vw.w = pack_lo(vin[6][c / 2], vin[7][c / 2]);
+            vw.x = pack_lo(vin[ks][0][c / 2], vin[ks][1][c / 2]);
+            vw.y = pack_lo(vin[ks][2][c / 2], vin[ks][3][c / 2]);
+            vw.z = pack_lo(vin[ks][4][c / 2], vin[ks][5][c / 2]);
+            vw.w = pack_lo(vin[ks][6][c / 2], vin[ks][7][c / 2]);
           } else {
-            vw.x = pack_hi(vin[0][c / 2], vin[1][c / 2]);
-            vw.y = pack_hi(vin[2][c / 2], vin[3][c / 2]);
-            vw.z = pack_hi(vin[4][c / 2], vin[5][c / 2]);
-            vw.w = pack_hi(vin[6][c / 2], vin[7][c / 2]);
+            vw.x = pack_hi(vin[ks][0][c / 2], vin[ks][1][c / 2]);
+            vw.y = pack_hi(vin[ks][2][c / 2], vin[ks][3][c / 2]);
+            vw.z = pack_hi(vin[ks][4][c / 2], vin[ks][5][c / 2]);
+            vw.w = pack_hi(vin[ks][6][c / 2], vin[ks][7][c / 2]);
           }
           // C[query 4 lg + i][col l16] with col l16 <-> d = DPL * l16 + c
           acc[c] = mfma16(pf, as_bf16x8(vw), acc[c]);
@@ -293,7 +316,7 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
     for (int w = 0; w < 4; ++w) M = fmaxf(M, ms[w][qr]);
     float L = 0.f, O = 0.f;
     for (int w = 0; w < 4; ++w) {
-      const float f = ms[w][qr] == -INFINITY ? 0.f : exp2f(ms[w][qr] - M);
+      const float f = ms[w][qr] == -INFINITY ? 0.f : fast_exp2(ms[w][qr] - M);
       L += ls[w][qr] * f;
       O += os[w][qr][d] * f;
     }
@@ -346,7 +369,7 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
           const float sv = sc[qr][kk];
           if (sv == -INFINITY) continue;
           const float m_new = fmaxf(m_run, sv);
-          const float corr = exp2f(m_run - m_new), p = exp2f(sv - m_new);
+          const float corr = fast_exp2(m_run - m_new), p = fast_exp2(sv - m_new);
           l_run = l_run * corr + p;
           for (int c = 0; c < D / 32; ++c) ov[c] = fmaf(p, vb[(key0 + kk) * D + dl + 32 * c], ov[c] * corr);
           m_run = m_new;
@@ -378,7 +401,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int d = threadIdx.x;
   for (int s = 0; s < ns; ++s) {
     const float ms = part[s * stride];
-    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
     L += part[s * stride + 1] * f;
     O += part[s * stride + 2 + d] * f;
   }
@@ -439,7 +462,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
 
   if (L.ncand_max > 0) {
     dim3 g1((unsigned)((L.ncand_max + 63) / 64), nbg);
-#define DASH_DS(T, D) hipLaunchKernelGGL((decode_scores_kernel<T, D>), g1, dim3(256), 0, st, a)
+#define DASH_DS(T, D) hipLaunchKernelGGL((decode_scores_kernel<T, D>), g1, dim3(64), 0, st, a)
     if (bf16) { if (s.d == 64) DASH_DS(__bf16, 64); else DASH_DS(__bf16, 128); }
     else { if (s.d == 64) DASH_DS(float, 64); else DASH_DS(float, 128); }
 #undef DASH_DS

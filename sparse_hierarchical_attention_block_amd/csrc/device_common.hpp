@@ -48,6 +48,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// 2^x with the hardware instruction (v_exp_f32): no denormal-range fix-up,
+// results below 2^-126 flush to zero, which softmax weights can afford.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---- wave64 reductions (fixed order, deterministic) -------------------------
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -94,4 +94,80 @@ __device__ float entmax_tau(Get get, int n, int sub, int width, int mode, float 
   return tau;
 }
 
+// Reductions over the lanes that hold one row.
+struct GroupReduce {   // `width` consecutive lanes
+  int width;
+  __device__ float sum(float v) const { return group_sum(v, width); }
+  __device__ float max(float v) const { return group_max(v, width); }
+  __device__ float min(float v) const { return group_min(v, width); }
+};
+struct Stride16Reduce {   // lanes l, l^16, l^32, l^48 (one MFMA 16x16 C-fragment row)
+  __device__ float sum(float v) const {
+    v += __shfl_xor(v, 16, kWave);
+    return v + __shfl_xor(v, 32, kWave);
+  }
+  __device__ float max(float v) const {
+    v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    return fmaxf(v, __shfl_xor(v, 32, kWave));
+  }
+  __device__ float min(float v) const {
+    v = fminf(v, __shfl_xor(v, 16, kWave));
+    return fminf(v, __shfl_xor(v, 32, kWave));
+  }
+};
+
+// Same threshold with the row held in registers: each lane of the row's lane
+// set holds VPL of its values (-inf for absent entries); `red` reduces over
+// that lane set.  Only the first nact4 groups of four values are visited
+// (nact4 is uniform across the wave, so the skipped groups cost no VALU).
+template <int VPL, int mode, typename Red>
+__device__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int nact4 = VPL / 4) {
+  float xmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+    if (i / 4 < nact4) xmax = fmaxf(xmax, xv[i]);
+  xmax = red.max(xmax);
+  float tau = xmax - 1.0f;
+  for (int it = 0; it < 64; ++it) {
+    float k = 0.f, s1 = 0.f, s2 = 0.f, ymin = INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      if (i / 4 >= nact4) continue;
+      const float y = xv[i] - tau;
+      const bool in = y > 0.f;
+      const float yp = in ? y : 0.f;
+      k += in ? 1.f : 0.f;
+      ymin = fminf(ymin, in ? y : INFINITY);
+      if constexpr (mode == kEntmax15) { s1 += yp; s2 = fmaf(yp, yp, s2); }
+      else if constexpr (mode == kSparsemax) { s1 += yp; }
+      else if constexpr (mode == kEntmaxQuartic) { const float y2 = yp * yp; s1 = fmaf(y2, yp, s1); s2 = fmaf(y2, y2, s2); }
+      else if (in) { const float l = __log2f(y); s1 += exp2f((e - 1.f) * l); s2 += exp2f(e * l); }
+    }
+    k = red.sum(k);
+    s1 = red.sum(s1);
+    s2 = red.sum(s2);
+    ymin = red.min(ymin);
+    float step;
+    if constexpr (mode == kSparsemax) {
+      step = (s1 - 1.f) / k;
+      tau += step;
+      if (step < ymin) break;
+    } else if constexpr (mode == kEntmax15) {
+      const float disc = s1 * s1 - k * (s2 - 1.f);
+      if (disc >= 0.f) {
+        const float d = (s2 - 1.f) / (s1 + sqrtf(disc));
+        if (d < ymin) { tau += d; break; }
+      }
+      step = (s2 - 1.f) / (2.f * s1);
+      tau += step;
+      if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
+    } else {
+      step = (s2 - 1.f) / (e * s1);
+      tau += step;
+      if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
+    }
+  }
+  return tau;
+}
+
 }  // namespace dash

@@ -26,6 +26,7 @@ namespace dash {
 
 constexpr int kRouteThreads = 256;
 constexpr int kQT = DASH_QUERY_TILE;
+constexpr int kRouteMaxRowTiles = 4;   // rows per pass <= 64
 
 struct RouteArgs {
   const void* q;
@@ -49,7 +50,10 @@ struct RouteArgs {
 __host__ __device__ inline int round_up16(int x) { return (x + 15) & ~15; }
 
 // ---- step 1, bf16: MFMA with a 3-way bf16 split of the summaries ----------------
-template <int D>
+// Wave w computes candidate tiles w, w+4, ... against every row tile of the
+// pass; the pass's Q fragments are loaded once up front and the next
+// candidate tile's summaries are prefetched while the current one is used.
+template <int D, int MAXRT>
 __device__ void route_scores_bf16(const RouteArgs& a, float* X, int t, int64_t bg, int b, int g,
                                   int64_t pos0, int R) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -57,47 +61,67 @@ __device__ void route_scores_bf16(const RouteArgs& a, float* X, int t, int64_t b
   const __bf16* q = (const __bf16*)a.q;
   const int CT = round_up16(t) / 16;
   constexpr int KS = D / 32;
-  for (int ct = wave; ct < CT; ct += kRouteThreads / kWave) {
+  const int RT = R / 16;
+  if (wave >= CT) return;
+  // Q^T fragments of every row tile: column = row l16, k = d in [32 s + 8 lg, +8)
+  bf16x8 qf[MAXRT][KS];
+#pragma unroll
+  for (int rt = 0; rt < MAXRT; ++rt) {
+    const int row = rt * 16 + l16;
+    const int m = row / a.G, h = row % a.G;
+    const int64_t pos = pos0 + m;
+    const __bf16* qrow = q + (((int64_t)b * a.H + g * a.G + h) * a.n + pos) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 qv = {0u, 0u, 0u, 0u};
+      if (rt < RT && pos < a.n) qv = *(const u32x4*)(qrow + 32 * s + 8 * lg);
+      qf[rt][s] = as_bf16x8(qv);
+    }
+  }
+  auto load_s = [&](int ct, f32x4 (&v)[KS][2]) {
     const int cand = ct * 16 + l16;
-    const float* srow = a.summ + (bg * a.summ_blocks + cand) * D;
+    const float* srow = a.summ + (bg * a.summ_blocks + (cand < t ? cand : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      v[s][0] = *(const f32x4*)(srow + 32 * s + 8 * lg);
+      v[s][1] = *(const f32x4*)(srow + 32 * s + 8 * lg + 4);
+      if (cand >= t) v[s][0] = v[s][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  f32x4 sv[KS][2];
+  load_s(wave, sv);
+  for (int ct = wave; ct < CT; ct += kRouteThreads / kWave) {
     bf16x8 hi[KS], mid[KS], lo[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-      if (cand < t) {
-        v0 = *(const f32x4*)(srow + 32 * s + 8 * lg);
-        v1 = *(const f32x4*)(srow + 32 * s + 8 * lg + 4);
-      }
-      float xv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const float xv[8] = {sv[s][0].x, sv[s][0].y, sv[s][0].z, sv[s][0].w,
+                           sv[s][1].x, sv[s][1].y, sv[s][1].z, sv[s][1].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        __bf16 h = (__bf16)xv[i];
-        float r1 = xv[i] - (float)h;
-        __bf16 m = (__bf16)r1;
-        float r2 = r1 - (float)m;
+        const __bf16 h = (__bf16)xv[i];
+        const float r1 = xv[i] - (float)h;
+        const __bf16 m = (__bf16)r1;
         hi[s][i] = h;
         mid[s][i] = m;
-        lo[s][i] = (__bf16)r2;
+        lo[s][i] = (__bf16)(r1 - (float)m);
       }
     }
-    for (int rt = 0; rt < R / 16; ++rt) {
-      const int row = rt * 16 + l16;
-      const int m = row / a.G, h = row % a.G;
-      const int64_t pos = pos0 + m;
-      const __bf16* qrow = q + (((int64_t)b * a.H + g * a.G + h) * a.n + pos) * D;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int ct_next = ct + kRouteThreads / kWave;
+    if (ct_next < CT) load_s(ct_next, sv);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 qv = {0u, 0u, 0u, 0u};
-        if (pos < a.n) qv = *(const u32x4*)(qrow + 32 * s + 8 * lg);
-        bf16x8 qf = as_bf16x8(qv);
-        acc = mfma16(lo[s], qf, acc);
-        acc = mfma16(mid[s], qf, acc);
-        acc = mfma16(hi[s], qf, acc);
+    for (int rt = 0; rt < MAXRT; ++rt) {
+      if (rt < RT) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          acc = mfma16(lo[s], qf[rt][s], acc);
+          acc = mfma16(mid[s], qf[rt][s], acc);
+          acc = mfma16(hi[s], qf[rt][s], acc);
+        }
+        // C[cand 4*lg + i][row l16]
+        const f32x4 outv = {acc.x * a.scale, acc.y * a.scale, acc.z * a.scale, acc.w * a.scale};
+        *(f32x4*)(X + (rt * 16 + l16) * a.pitch + ct * 16 + 4 * lg) = outv;
       }
-      // C[cand 4*lg + i][row l16]
-      f32x4 outv = {acc.x * a.scale, acc.y * a.scale, acc.z * a.scale, acc.w * a.scale};
-      *(f32x4*)(X + row * a.pitch + ct * 16 + 4 * lg) = outv;
     }
   }
 }
@@ -121,7 +145,7 @@ __device__ void route_scores_f32(const RouteArgs& a, float* X, int t, int64_t bg
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int VPL, int MODE>
 __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs a) {
   extern __shared__ float smem[];
   const int R = a.PP * a.G;
@@ -157,18 +181,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs 
   for (int pp = 0; pp < npos; pp += a.PP) {
     const int64_t pos0 = p_begin + pp;
     __syncthreads();
-    if constexpr (sizeof(T) == 2) route_scores_bf16<D>(a, X, t, bg, b, g, pos0, R);
+    if constexpr (sizeof(T) == 2) route_scores_bf16<D, kRouteMaxRowTiles>(a, X, t, bg, b, g, pos0, R);
     else route_scores_f32<D>(a, X, t, bg, b, g, pos0, R);
     __syncthreads();
 
-    // step 2: threshold per row
-    {
+    const int np = min(a.PP, npos - pp);
+    if constexpr (VPL > 0) {
+      // steps 2-3 with the row in registers: lane `sub` of the row's group
+      // holds x_{sub + lpr*i}; the G rows of a position are adjacent groups,
+      // so the GQA sum is a shuffle over G * lpr lanes.
       const int row = threadIdx.x / lpr, sub = threadIdx.x % lpr;
       const float* xr = X + row * a.pitch;
-      const float tau = entmax_tau([&](int j) { return xr[j]; }, t, sub, lpr, a.mode, a.e);
+      float xv[VPL];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int j = sub + lpr * i;
+        xv[i] = j < t ? xr[j] : -INFINITY;
+      }
+      const float tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{lpr}, a.e);
       const int m = row / a.G, h = row % a.G;
       const int64_t pos = pos0 + m;
-      if (sub == 0) tau_s[row] = tau;
       if (pos < a.n) {
         const int64_t r = ((int64_t)b * a.H + g * a.G + h) * a.n + pos;
         if (sub == 0) a.tau[r] = tau;
@@ -182,22 +214,66 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs 
             a.bits[r * a.nwords + w] = word;
           }
       }
-    }
-    __syncthreads();
-
-    // step 3: GQA average, log prior, tile-union flags
-    const int np = min(a.PP, npos - pp);
-    for (int idx = threadIdx.x; idx < t * np; idx += kRouteThreads) {
-      const int j = idx / np, m = idx % np;
-      float pb = 0.f;
-      for (int h = 0; h < a.G; ++h) {
-        const int row = m * a.G + h;
-        const float y = X[row * a.pitch + j] - tau_s[row];
-        if (y > 0.f) pb += entmax_pow(y, a.mode, a.e);
+      float* pv = xv;   // p overwrites x
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const float y = xv[i] - tau;
+        pv[i] = y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
       }
-      pb *= invG;
-      a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? __logf(pb) : -INFINITY;
-      if (pb > 0.f) uflag[j] = 1;
+      for (int o = lpr; o < lpr * a.G; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) pv[i] += __shfl_xor(pv[i], o, kWave);
+      // every head's lanes now hold the group sum; head h writes the blocks
+      // with i % G == h
+      if (m < np) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          const int j = sub + lpr * i;
+          if (i % a.G == h && j < t) {
+            const float pb = pv[i] * invG;
+            a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? __logf(pb) : -INFINITY;
+            if (pb > 0.f) uflag[j] = 1;
+          }
+        }
+      }
+    } else {
+      static_assert(VPL > 0 || MODE == kEntmaxGeneral, "the LDS path takes the mode at run time");
+      // step 2: threshold per row (row read from LDS on every iteration)
+      {
+        const int row = threadIdx.x / lpr, sub = threadIdx.x % lpr;
+        const float* xr = X + row * a.pitch;
+        const float tau = entmax_tau([&](int j) { return xr[j]; }, t, sub, lpr, a.mode, a.e);
+        const int m = row / a.G, h = row % a.G;
+        const int64_t pos = pos0 + m;
+        if (sub == 0) tau_s[row] = tau;
+        if (pos < a.n) {
+          const int64_t r = ((int64_t)b * a.H + g * a.G + h) * a.n + pos;
+          if (sub == 0) a.tau[r] = tau;
+          if (a.bits)
+            for (int w = sub; w < a.nwords; w += lpr) {
+              uint32_t word = 0u;
+              for (int i = 0; i < 32; ++i) {
+                const int j = w * 32 + i;
+                if (j < t && xr[j] > tau) word |= 1u << i;
+              }
+              a.bits[r * a.nwords + w] = word;
+            }
+        }
+      }
+      __syncthreads();
+      // step 3: GQA average, log prior, tile-union flags
+      for (int idx = threadIdx.x; idx < t * np; idx += kRouteThreads) {
+        const int j = idx / np, m = idx % np;
+        float pb = 0.f;
+        for (int h = 0; h < a.G; ++h) {
+          const int row = m * a.G + h;
+          const float y = X[row * a.pitch + j] - tau_s[row];
+          if (y > 0.f) pb += entmax_pow(y, a.mode, a.e);
+        }
+        pb *= invG;
+        a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? __logf(pb) : -INFINITY;
+        if (pb > 0.f) uflag[j] = 1;
+      }
     }
   }
   __syncthreads();
@@ -218,13 +294,237 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs 
   }
 }
 
+
+// ------------------------------------------------------------------------------------------
+// Tile-resident variant for up to 128 candidates (bf16 queries): the whole
+// tile's scores stay in MFMA accumulator registers.  The workgroup splits
+// the tile's summaries once into three bf16 planes in LDS; wave w owns RTW
+// 16-row tiles (one for G <= 4, so a tile of 64 G rows runs on 4 G waves and
+// each SIMD keeps several waves to hide VALU latency) and computes X^T = S Q^T for every
+// candidate tile with MFMA 16x16x32.  In the accumulator a row's values sit in
+// lanes l16, l16+16, l16+32, l16+48, so the entmax reductions are two lane
+// swaps; the G heads of a position are adjacent rows (lanes differing in the
+// low bits of l16), so the GQA sum is log2(G) more swaps.
+// ------------------------------------------------------------------------------------------
+constexpr int kTileMaxCT = 8;   // candidate tiles of 16
+
+template <int D, int MODE, int RTW>
+__global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char tsm[];
+  constexpr int SP = D + 8;                       // plane row pitch (bf16)
+  constexpr int KS = D / 32;
+  const int TP = a.pitch;                         // candidate rows per plane (x16)
+  __bf16* planes = (__bf16*)tsm;                  // [3][TP][SP]: hi, mid, lo
+  int* uflag = (int*)(tsm + (size_t)3 * TP * SP * 2);
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int l16 = lane % 16, lg = lane / 16;
+  const int nthreads = blockDim.x;
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
+  const int64_t qt = a.n_qt - 1 - blockIdx.x / nbg;   // heaviest tiles first
+  const int64_t bg = blockIdx.x % nbg;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int64_t p_begin = qt * kQT;
+  const int t = (int)(p_begin / a.bs);
+  const int64_t tile = bg * a.n_qt + qt;
+  const int G = a.G;
+
+  if (t == 0) {
+    const int npos = (int)min((int64_t)kQT, a.n - p_begin);
+    for (int idx = threadIdx.x; idx < npos * G; idx += nthreads) {
+      const int m = idx / G, h = idx % G;
+      const int64_t r = ((int64_t)b * a.H + g * G + h) * a.n + p_begin + m;
+      a.tau[r] = __builtin_nanf("");
+      if (a.bits)
+        for (int w = 0; w < a.nwords; ++w) a.bits[r * a.nwords + w] = 0u;
+    }
+    if (threadIdx.x == 0) a.sel_count[tile] = 0;
+    return;
+  }
+  const int CT = (t + 15) / 16;
+
+  // ---- stage the summaries, split into hi + mid + lo bf16 ----
+  // (batches of 8 loads per thread are issued before any is consumed)
+  const int n4 = CT * 16 * (D / 4);
+  for (int e0 = threadIdx.x; e0 < n4; e0 += 8 * nthreads) {
+    f32x4 vb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * nthreads;
+      const int cand = e / (D / 4), c4 = e % (D / 4);
+      vb[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (e < n4 && cand < t) vb[u] = *(const f32x4*)(a.summ + (bg * a.summ_blocks + cand) * D + 4 * c4);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * nthreads;
+      if (e >= n4) break;
+      const int cand = e / (D / 4), c4 = e % (D / 4);
+      const float xs[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+      uint32_t hw[2], mw[2], lw[2];
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        float hv[2], mv[2], lv[2];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const float x = xs[2 * p2 + q2];
+          const float h = (float)(__bf16)x;
+          const float r1 = x - h;
+          const float m = (float)(__bf16)r1;
+          hv[q2] = h;
+          mv[q2] = m;
+          lv[q2] = r1 - m;
+        }
+        hw[p2] = pack_bf16(hv[0], hv[1]);
+        mw[p2] = pack_bf16(mv[0], mv[1]);
+        lw[p2] = pack_bf16(lv[0], lv[1]);
+      }
+      const int off = cand * SP + 4 * c4;
+      *(u32x2*)(planes + off) = (u32x2){hw[0], hw[1]};
+      *(u32x2*)(planes + (size_t)TP * SP + off) = (u32x2){mw[0], mw[1]};
+      *(u32x2*)(planes + (size_t)2 * TP * SP + off) = (u32x2){lw[0], lw[1]};
+    }
+  }
+  for (int j = threadIdx.x; j < TP; j += nthreads) uflag[j] = 0;
+
+  // ---- Q^T fragments of the wave's RTW row tiles ----
+  const __bf16* q = (const __bf16*)a.q;
+  bf16x8 qf[RTW][KS];
+  int64_t rpos[RTW];
+  int rh[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    const int r = 16 * RTW * wave + 16 * rt + l16;
+    const int m = r / G, h = r % G;
+    rpos[rt] = p_begin + m;
+    rh[rt] = h;
+    const __bf16* qrow = q + (((int64_t)b * a.H + g * G + h) * a.n + rpos[rt]) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 qv = {0u, 0u, 0u, 0u};
+      if (rpos[rt] < a.n) qv = *(const u32x4*)(qrow + 32 * s + 8 * lg);
+      qf[rt][s] = as_bf16x8(qv);
+    }
+  }
+  __syncthreads();
+
+  // ---- scores: X[rt][ct][i] = x(row 16 rt + l16, cand 16 ct + 4 lg + i) ----
+  f32x4 X[RTW][kTileMaxCT];
+#pragma unroll
+  for (int ct = 0; ct < kTileMaxCT; ++ct) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) X[rt][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (ct < CT) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int off = (16 * ct + l16) * SP + 32 * s + 8 * lg;
+        const bf16x8 hi = as_bf16x8(*(const u32x4*)(planes + off));
+        const bf16x8 mid = as_bf16x8(*(const u32x4*)(planes + (size_t)TP * SP + off));
+        const bf16x8 lo = as_bf16x8(*(const u32x4*)(planes + (size_t)2 * TP * SP + off));
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+          X[rt][ct] = mfma16(lo, qf[rt][s], X[rt][ct]);
+          X[rt][ct] = mfma16(mid, qf[rt][s], X[rt][ct]);
+          X[rt][ct] = mfma16(hi, qf[rt][s], X[rt][ct]);
+        }
+      }
+    }
+  }
+
+  const float invG = 1.0f / (float)G;
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    float xv[4 * kTileMaxCT];
+#pragma unroll
+    for (int ct = 0; ct < kTileMaxCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[4 * ct + i] = (16 * ct + 4 * lg + i < t) ? X[rt][ct][i] * a.scale : -INFINITY;
+    const float tau = entmax_tau_reg<4 * kTileMaxCT, MODE>(xv, Stride16Reduce{}, a.e, CT);
+    const int64_t pos = rpos[rt];
+    const int h = rh[rt];
+    const int64_t rglob = ((int64_t)b * a.H + g * G + h) * a.n + pos;
+    if (a.bits) {
+      // per-head support bits: ballots give, for each (ct, i), the bit of
+      // every (row, lg) pair
+      uint32_t chunk[kTileMaxCT];
+#pragma unroll
+      for (int ct = 0; ct < kTileMaxCT; ++ct) {
+        chunk[ct] = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t mk = __ballot(xv[4 * ct + i] > tau);
+#pragma unroll
+          for (int l2 = 0; l2 < 4; ++l2)
+            chunk[ct] |= (uint32_t)((mk >> (16 * l2 + l16)) & 1ull) << (4 * l2 + i);
+        }
+      }
+      if (lg == 0 && pos < a.n)
+        for (int w = 0; w < a.nwords; ++w) {
+          uint32_t word = 0u;
+#pragma unroll
+          for (int ct = 0; ct < kTileMaxCT; ++ct)
+            if (ct / 2 == w) word |= chunk[ct] << (16 * (ct % 2));
+          a.bits[rglob * a.nwords + w] = word;
+        }
+    }
+    if (lg == 0 && pos < a.n) a.tau[rglob] = tau;
+    // p, GQA sum over the G adjacent rows (lanes differing in l16's low bits)
+#pragma unroll
+    for (int ct = 0; ct < kTileMaxCT; ++ct) {
+      if (ct < CT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = xv[4 * ct + i] - tau;
+          xv[4 * ct + i] = y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
+        }
+        for (int o = 1; o < G; o <<= 1)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xv[4 * ct + i] += __shfl_xor(xv[4 * ct + i], o, kWave);
+      }
+    }
+    if (pos < a.n) {
+      const int mloc = (int)(pos - p_begin);
+      float* lp = a.sel_logp + tile * a.nb * kQT + mloc;
+#pragma unroll
+      for (int ct = 0; ct < kTileMaxCT; ++ct) {
+        if (ct < CT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = 16 * ct + 4 * lg + i;
+            if (j < t && (4 * ct + i) % G == h) {
+              const float pb = xv[4 * ct + i] * invG;
+              lp[j * kQT] = pb > 0.f ? __logf(pb) : -INFINITY;
+              if (pb > 0.f) uflag[j] = 1;
+            }
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- compaction (ascending block ids) ----
+  if (threadIdx.x < kWave) {
+    int base = 0;
+    for (int j0 = 0; j0 < t; j0 += kWave) {
+      const int j = j0 + lane;
+      const bool f = j < t && uflag[j] != 0;
+      const uint64_t mask = __ballot(f);
+      if (f) a.sel_idx[tile * a.nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
+      base += __popcll(mask);
+    }
+    if (lane == 0) a.sel_count[tile] = base;
+  }
+}
+
 // positions per pass: largest power of two in [16/G, 64] whose score buffer
 // fits the LDS budget
 static int route_pp(int G, int pitch, size_t budget) {
   int pp = 64;
   while (pp > 1 && (size_t)pp * G * pitch * 4 > budget) pp >>= 1;
   while (pp * G < 16) pp <<= 1;
-  while (pp * G > kRouteThreads) pp >>= 1;
+  while (pp * G > 16 * kRouteMaxRowTiles) pp >>= 1;
   return pp;
 }
 
@@ -253,18 +553,70 @@ hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const 
   a.e = 1.0f / (s.alpha - 1.0f);
   a.scale = (s.alpha - 1.0f) * s.gamma / sqrtf((float)s.d);
   const int t_max = (int)(((a.n_qt - 1) * kQT) / s.bs);
+  if (s.dtype == DASH_BF16 && t_max <= 16 * kTileMaxCT) {
+    // tile-resident path: one wave per 64 rows of the tile
+    a.pitch = round_up16(t_max > 0 ? t_max : 1);
+    const size_t lds_t = (size_t)3 * a.pitch * (s.d + 8) * 2 + (size_t)a.pitch * 4;
+    dim3 grid_t((unsigned)(a.n_qt * s.B * s.Hkv));
+    const int rtw = s.G <= 4 ? 1 : 2;                 // row tiles per wave
+    const int threads = kWave * (4 * s.G / rtw);      // 64 G rows / (16 rtw) waves
+#define DASH_RTT3(D, M, R)                                                                  \
+  do {                                                                                      \
+    if (lds_t > 64 * 1024)                                                                  \
+      (void)hipFuncSetAttribute((const void*)route_tile_kernel<D, M, R>,                    \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_t);     \
+    hipLaunchKernelGGL((route_tile_kernel<D, M, R>), grid_t, dim3(threads), lds_t, st, a);  \
+  } while (0)
+#define DASH_RTT(D, M)                                   \
+  do {                                                   \
+    if (rtw == 1) DASH_RTT3(D, M, 1); else DASH_RTT3(D, M, 2); \
+  } while (0)
+#define DASH_RTT2(D)                                                          \
+  do {                                                                        \
+    if (a.mode == kEntmax15) DASH_RTT(D, kEntmax15);                          \
+    else if (a.mode == kSparsemax) DASH_RTT(D, kSparsemax);                   \
+    else if (a.mode == kEntmaxQuartic) DASH_RTT(D, kEntmaxQuartic);           \
+    else DASH_RTT(D, kEntmaxGeneral);                                         \
+  } while (0)
+    if (s.d == 64) DASH_RTT2(64); else DASH_RTT2(128);
+#undef DASH_RTT2
+#undef DASH_RTT
+#undef DASH_RTT3
+    return hipGetLastError();
+  }
   a.pitch = round_up16(t_max > 0 ? t_max : 1) + 4;
   a.PP = route_pp(s.G, a.pitch, 64 * 1024);
   const size_t lds = ((size_t)a.PP * s.G * a.pitch + (size_t)a.PP * s.G) * 4 +
                      (size_t)round_up16(t_max > 0 ? t_max : 1) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.n_qt * s.B * s.Hkv));
-#define DASH_RT(T, D)                                                                   \
-  do {                                                                                  \
-    if (lds > 64 * 1024)                                                                \
-      (void)hipFuncSetAttribute((const void*)route_prefill_kernel<T, D>,                \
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);   \
-    hipLaunchKernelGGL((route_prefill_kernel<T, D>), grid, dim3(kRouteThreads), lds, st, a); \
+  // register path: the row's candidates fit VPL per lane and a position's
+  // G rows share one wave
+  const int lpr = kRouteThreads / (a.PP * s.G);
+  const int need = (t_max + lpr - 1) / lpr;
+  int vpl = 0;
+  if (lpr * s.G <= kWave) vpl = need <= 8 ? 8 : need <= 16 ? 16 : need <= 32 ? 32 : 0;
+#define DASH_RT3(T, D, V, M)                                                               \
+  do {                                                                                     \
+    if (lds > 64 * 1024)                                                                   \
+      (void)hipFuncSetAttribute((const void*)route_prefill_kernel<T, D, V, M>,             \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);      \
+    hipLaunchKernelGGL((route_prefill_kernel<T, D, V, M>), grid, dim3(kRouteThreads), lds, st, \
+                       a);                                                                 \
+  } while (0)
+#define DASH_RT2(T, D, V)                                          \
+  do {                                                             \
+    if (a.mode == kEntmax15) DASH_RT3(T, D, V, kEntmax15);         \
+    else if (a.mode == kSparsemax) DASH_RT3(T, D, V, kSparsemax);  \
+    else if (a.mode == kEntmaxQuartic) DASH_RT3(T, D, V, kEntmaxQuartic); \
+    else DASH_RT3(T, D, V, kEntmaxGeneral);                        \
+  } while (0)
+#define DASH_RT(T, D)                                              \
+  do {                                                             \
+    if (vpl == 8) DASH_RT2(T, D, 8);                               \
+    else if (vpl == 16) DASH_RT2(T, D, 16);                        \
+    else if (vpl == 32) DASH_RT2(T, D, 32);                        \
+    else DASH_RT3(T, D, 0, kEntmaxGeneral);                        \
   } while (0)
   if (s.dtype == DASH_BF16) {
     if (s.d == 64) DASH_RT(__bf16, 64); else DASH_RT(__bf16, 128);
@@ -272,6 +624,8 @@ hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const 
     if (s.d == 64) DASH_RT(float, 64); else DASH_RT(float, 128);
   }
 #undef DASH_RT
+#undef DASH_RT2
+#undef DASH_RT3
   return hipGetLastError();
 }
 

@@ -3,8 +3,10 @@
 // block, s_j = mean(k of block j) . W_s, accumulated in float32.  A chunk's
 // summary is computed once, when the chunk is complete, and cached.
 //
-// HBM-bound scan: every key of a complete block is read once (bs * d * elt
-// bytes per block); W_s (64 KB at d = 128) stays in L2.
+// HBM-bound scan: every key of a complete block is read once with 16-byte
+// loads (bs * d * elt bytes per block).  A workgroup summarises up to NB
+// blocks of one (sequence, KV head) so W_s (64 KB at d = 128, L2-resident) is
+// read once per NB blocks.
 #include "dash_internal.hpp"
 #include "device_common.hpp"
 
@@ -12,48 +14,94 @@ namespace dash {
 
 constexpr int kSumThreads = 256;
 
-// Summary of one block.  kb points at the block's first key row (bs rows of
-// D elements), out at the D floats of its summary.  All 256 threads call it.
-template <typename T, int D>
-__device__ void summarize_block(const T* __restrict__ kb, int bs, const float* __restrict__ w_s,
-                                float* __restrict__ out) {
-  constexpr int RG = kSumThreads / D;  // row groups
+// Summaries of nblk <= NB consecutive blocks.  kb points at the first key row
+// of the first block (rows of D elements, blocks of bs rows, contiguous), out
+// at the first summary (D floats per block, contiguous).  All 256 threads call.
+template <typename T, int D, int NB>
+__device__ void summarize_blocks(const T* __restrict__ kb, int nblk, int bs,
+                                 const float* __restrict__ w_s, float* __restrict__ out) {
+  constexpr int EPV = 16 / sizeof(T);       // elements per 16-byte load
+  constexpr int CH = D / EPV;               // 16-byte chunks per row
+  constexpr int RG = kSumThreads / CH;      // row groups
   __shared__ float part[RG][D];
-  __shared__ float mean[D];
-  const int c = threadIdx.x % D, rg = threadIdx.x / D;
-  float acc = 0.f;
-  for (int t = rg; t < bs; t += RG) acc += to_f32(kb[(int64_t)t * D + c]);
-  part[rg][c] = acc;
-  __syncthreads();
-  if (threadIdx.x < D) {
-    float s = 0.f;
+  __shared__ float mean[NB][D];
+  const int ch = threadIdx.x % CH, rg = threadIdx.x / CH;
+  for (int bi = 0; bi < nblk; ++bi) {
+    const T* blk = kb + (int64_t)bi * bs * D;
+    float acc[EPV];
 #pragma unroll
-    for (int r = 0; r < RG; ++r) s += part[r][c];
-    mean[c] = s * (1.0f / (float)bs);
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+#pragma unroll 4
+    for (int t = rg; t < bs; t += RG) {
+      const u32x4 w = *(const u32x4*)(blk + (int64_t)t * D + ch * EPV);
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_lo(ww[e]);
+          acc[2 * e + 1] += bf16_hi(ww[e]);
+        }
+      } else {
+        acc[0] += __uint_as_float(w.x);
+        acc[1] += __uint_as_float(w.y);
+        acc[2] += __uint_as_float(w.z);
+        acc[3] += __uint_as_float(w.w);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) part[rg][ch * EPV + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < D) {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) s += part[r][threadIdx.x];
+      mean[bi][threadIdx.x] = s * (1.0f / (float)bs);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  float o = 0.f;
-  for (int r = rg; r < D; r += RG) o = fmaf(mean[r], w_s[r * D + c], o);
-  part[rg][c] = o;
+  // projection: out[bi][c] = sum_r mean[bi][r] * W_s[r][c], r split over the
+  // 256 / D row groups; W_s is read once for all blocks
+  constexpr int PG = kSumThreads / D;
+  const int c = threadIdx.x % D, pg = threadIdx.x / D;
+  float o[NB];
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi) o[bi] = 0.f;
+#pragma unroll 8
+  for (int r = pg; r < D; r += PG) {
+    const float wv = w_s[r * D + c];
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) o[bi] = fmaf(mean[bi][r], wv, o[bi]);
+  }
+  // `part` is reused as [PG][NB][D]
+  static_assert(RG >= PG * NB, "LDS scratch too small");
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi) (&part[0][0])[(pg * NB + bi) * D + c] = o[bi];
   __syncthreads();
   if (threadIdx.x < D) {
-    float s = 0.f;
+    for (int bi = 0; bi < nblk; ++bi) {
+      float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < RG; ++r) s += part[r][c];
-    out[c] = s;
+      for (int q = 0; q < PG; ++q) s += (&part[0][0])[(q * NB + bi) * D + threadIdx.x];
+      out[bi * D + threadIdx.x] = s;
+    }
   }
   __syncthreads();
 }
 
-// grid.x = nblk * B * Hkv
+constexpr int kSumNB = 4;
+
+// grid.x = ceil(nblk / NB) * B * Hkv
 template <typename T, int D>
 __global__ __launch_bounds__(kSumThreads) void summarize_kernel(
     const T* __restrict__ k, int64_t kv_len, int bs, int64_t blk_begin, int64_t nblk,
     const float* __restrict__ w_s, float* __restrict__ summ, int64_t summ_blocks) {
+  const int64_t ngrp = (nblk + kSumNB - 1) / kSumNB;
   const int64_t u = blockIdx.x;
-  const int64_t j = blk_begin + u % nblk, bg = u / nblk;
-  summarize_block<T, D>(k + (bg * kv_len + j * bs) * D, bs, w_s,
-                        summ + (bg * summ_blocks + j) * D);
+  const int64_t grp = u % ngrp, bg = u / ngrp;
+  const int64_t j = blk_begin + grp * kSumNB;
+  const int here = (int)min((int64_t)kSumNB, nblk - grp * kSumNB);
+  summarize_blocks<T, D, kSumNB>(k + (bg * kv_len + j * bs) * D, here, bs, w_s,
+                                 summ + (bg * summ_blocks + j) * D);
 }
 
 // Decode: the step that makes cache_len[b] a multiple of bs completes block
@@ -68,8 +116,8 @@ __global__ __launch_bounds__(kSumThreads) void summarize_completed_kernel(
   len = len < 1 ? 1 : (len > max_len ? max_len : len);
   if (len % bs != 0) return;
   const int64_t j = len / bs - 1;
-  summarize_block<T, D>(k + (bg * max_len + j * bs) * D, bs, w_s,
-                        summ + (bg * summ_blocks + j) * D);
+  summarize_blocks<T, D, 1>(k + (bg * max_len + j * bs) * D, 1, bs, w_s,
+                            summ + (bg * summ_blocks + j) * D);
 }
 
 template <typename T, int D>
@@ -77,7 +125,7 @@ static hipError_t summarize_t(const Shape& s, const void* k, int64_t kv_len, int
                               int64_t b1, const float* w_s, float* summ, int64_t sb,
                               hipStream_t st) {
   const int64_t nblk = b1 - b0;
-  dim3 grid((unsigned)(nblk * s.B * s.Hkv));
+  dim3 grid((unsigned)(((nblk + kSumNB - 1) / kSumNB) * s.B * s.Hkv));
   hipLaunchKernelGGL((summarize_kernel<T, D>), grid, dim3(kSumThreads), 0, st,
                      (const T*)k, kv_len, s.bs, b0, nblk, w_s, summ, sb);
   return hipGetLastError();
