@@ -162,14 +162,17 @@ dash_status dash_route(const dash_params* p, const void* q, int64_t n, const flo
  * tile's selected blocks (logit q.k/sqrt(d) + sel_logp, -inf masks) and the
  * keys t <= i of its own block (bias 0); o = weights . v.
  *   q, o   [B, H, n, d] dtype;  k, v [B, Hkv, n, d] dtype
- *   route  as written by dash_route (tau and support_bits are not read) */
+ *   route  as written by dash_route (tau and support_bits are not read)
+ * DASH_ERR_UNSUPPORTED when one (sequence, KV head)'s keys span 2 GiB or more
+ * ((n + 64) * d * element size >= 2^31). */
 dash_status dash_attend(const dash_params* p, const void* q, const void* k, const void* v,
                         int64_t n, const dash_route_buf* route, void* o, void* stream);
 
 /* Fused causal prefill: dash_summarize of blocks [0, floor(n/bs)) into summ,
  * dash_route into the workspace, dash_attend into o.
  *   summ   [B, Hkv, summ_blocks, d] float32, summ_blocks >= floor(n/bs)
- *   ws     >= dash_prefill_workspace_bytes(p, n) bytes, 256-byte aligned */
+ *   ws     >= dash_prefill_workspace_bytes(p, n) bytes, 256-byte aligned
+ * Same size limit as dash_attend. */
 dash_status dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
                          int64_t n, const float* w_s, float* summ, int64_t summ_blocks, void* o,
                          void* ws, size_t ws_bytes, void* stream);

@@ -47,6 +47,13 @@ dash_status hip_status(hipError_t e) { return e == hipSuccess ? DASH_OK : DASH_E
 // grid sizes must fit the 32-bit x dimension
 bool grid_ok(int64_t blocks) { return blocks >= 0 && blocks < ((int64_t)1 << 31); }
 
+// the prefill attend kernel addresses one sequence's keys / values through a
+// buffer resource with a 31-bit byte range
+bool seq_bytes_ok(const Shape& s, int64_t n) {
+  const int64_t elt = s.dtype == DASH_BF16 ? 2 : 4;
+  return (n + 64) * s.d * elt < ((int64_t)1 << 31);
+}
+
 void prefill_sizes(const Shape& s, int64_t n, dash_route_sizes* r) {
   r->n_qt = (n + kQT - 1) / kQT;
   r->nb = (n + s.bs - 1) / s.bs;
@@ -192,7 +199,8 @@ dash_status dash_attend(const dash_params* p, const void* q, const void* k, cons
       !route->sel_logp)
     return DASH_ERR_INVALID_ARG;
   if (n == 0) return DASH_OK;
-  if (!grid_ok(((n + kQT - 1) / kQT) * s.B * s.H)) return DASH_ERR_UNSUPPORTED;
+  if (!grid_ok(((n + kQT - 1) / kQT) * s.B * s.H) || !seq_bytes_ok(s, n))
+    return DASH_ERR_UNSUPPORTED;
   return hip_status(dash::launch_attend_prefill(s, q, k, v, n, *route, o, (hipStream_t)stream));
 }
 
@@ -208,7 +216,7 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
   const PrefillLayout L = prefill_layout(s, n);
   if (!ws || ((uintptr_t)ws % kAlign) != 0) return DASH_ERR_INVALID_ARG;
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE_TOO_SMALL;
-  if (!route_lds_ok(s, n)) return DASH_ERR_UNSUPPORTED;
+  if (!route_lds_ok(s, n) || !seq_bytes_ok(s, n)) return DASH_ERR_UNSUPPORTED;
   if (!grid_ok(((n + kQT - 1) / kQT) * s.B * s.H) || !grid_ok((n / s.bs) * s.B * s.Hkv))
     return DASH_ERR_UNSUPPORTED;
   char* base = (char*)ws;

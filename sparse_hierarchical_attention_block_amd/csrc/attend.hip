@@ -70,8 +70,12 @@ __device__ __forceinline__ ChunkRef chunk_ref(int c, int n_own, int64_t own_c0, 
 // bf16, MFMA
 // ------------------------------------------------------------------------------------------
 // Staging of one 64-key chunk: K row-major [64][D + 8], V transposed [D][64 + 4]
-// (bf16).  NT threads; each thread owns KPT 16-byte pieces of K and VPT 4x4
-// blocks of V.
+// (bf16), and the chunk's 64 per-query biases (float, log pbar of the chunk's
+// block; 0 for own-block chunks).  NT threads; each thread owns KPT 16-byte
+// pieces of K and VPT 4x4 blocks of V; lanes 0..15 of wave 0 own the bias.
+// Loads go through buffer resources, so keys at or past n read as zeros
+// without branches, and the bias rides the same in-order load queue as K/V
+// (no wait on it can stall on a younger K/V load).
 template <int D, int NT>
 struct ChunkStage {
   static constexpr int KP = D + 8;
@@ -82,16 +86,18 @@ struct ChunkStage {
   static constexpr int VPT = (VTOT + NT - 1) / NT;
   u32x4 kr[KPT];
   u32x2 vr[VPT][4];
+  u32x4 br;
 
-  __device__ __forceinline__ void load(const __bf16* kp, const __bf16* vp, int64_t key0,
-                                       int64_t n) {
+  // key0: first key of the chunk; block: its block id, -1 for an own-block
+  // chunk.  rk / rv cover one sequence's keys / values, rb the tile's bias rows.
+  __device__ __forceinline__ void load(buf_rsrc rk, buf_rsrc rv, buf_rsrc rb, int64_t key0,
+                                       int block) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int e = threadIdx.x + i * NT;
       const int key = e / (D / 8), seg = e % (D / 8);
-      const int64_t kpos = key0 + key;
-      kr[i] = (u32x4){0u, 0u, 0u, 0u};
-      if ((KTOT % NT == 0 || e < KTOT) && kpos < n) kr[i] = *(const u32x4*)(kp + kpos * D + seg * 8);
+      const uint32_t off = (uint32_t)((key0 + key) * (D * 2) + seg * 16);
+      if (KTOT % NT == 0 || e < KTOT) kr[i] = buf_load16(rk, off);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -99,14 +105,17 @@ struct ChunkStage {
       const int db = e % (D / 4), kb = e / (D / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t kpos = key0 + 4 * kb + r;
-        vr[i][r] = (u32x2){0u, 0u};
-        if ((VTOT % NT == 0 || e < VTOT) && kpos < n)
-          vr[i][r] = *(const u32x2*)(vp + kpos * D + 4 * db);
+        const uint32_t off = (uint32_t)((key0 + 4 * kb + r) * (D * 2) + db * 8);
+        if (VTOT % NT == 0 || e < VTOT) vr[i][r] = buf_load8(rv, off);
       }
     }
+    if (threadIdx.x < kWave) {   // wave-uniform
+      br = (u32x4){0u, 0u, 0u, 0u};
+      if (block >= 0)
+        br = buf_load16(rb, (uint32_t)block * (kQTa * 4) + (threadIdx.x % 16) * 16);
+    }
   }
-  __device__ __forceinline__ void store(__bf16* Ks, __bf16* Vt) const {
+  __device__ __forceinline__ void store(__bf16* Ks, __bf16* Vt, float* Bs) const {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int e = threadIdx.x + i * NT;
@@ -128,28 +137,13 @@ struct ChunkStage {
       *(u32x2*)(Vt + (4 * db + 2) * VP + 4 * kb) = o2;
       *(u32x2*)(Vt + (4 * db + 3) * VP + 4 * kb) = o3;
     }
+    if (threadIdx.x < kQTa / 4) *(u32x4*)(Bs + 4 * threadIdx.x) = br;
   }
 };
 
 // Rescale the running output only when a row max grows by more than 2^8:
 // exp2(s - m_ref) then stays <= 256, exact in float32 and in bf16's range.
 constexpr float kLazyRescale = 8.0f;
-
-// S^T (64 keys x 32 queries) = K Q^T for one staged chunk: two 32-key tiles.
-template <int D, int KP>
-__device__ __forceinline__ void chunk_scores(const __bf16* Kc, const bf16x8 (&qf)[D / 16], int l32,
-                                             int lh, f32x16 (&st)[2]) {
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const u32x4 kw = *(const u32x4*)(Kc + (32 * kt + l32) * KP + 16 * s + 8 * lh);
-      st[kt] = mfma32(as_bf16x8(kw), qf[s], st[kt]);
-    }
-  }
-}
 
 template <int D, int NT>
 __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
@@ -158,6 +152,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   constexpr int NBUF = 3;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][kChunk * KP];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[NBUF][D * VP];
+  __shared__ __attribute__((aligned(16))) float Bs[NBUF][kQTa];
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int l32 = lane % 32, lh = lane / 32;
@@ -178,8 +173,10 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   const int64_t qpos = p_begin + qloc;
 
   const __bf16* qp = (const __bf16*)a.q + (((int64_t)b * a.H + h) * a.n) * D;
-  const __bf16* kp = (const __bf16*)a.k + (bg * a.n) * D;
-  const __bf16* vp = (const __bf16*)a.v + (bg * a.n) * D;
+  const uint32_t seq_bytes = (uint32_t)(a.n * (D * 2));
+  const buf_rsrc rk = make_rsrc((const __bf16*)a.k + (bg * a.n) * D, seq_bytes);
+  const buf_rsrc rv = make_rsrc((const __bf16*)a.v + (bg * a.n) * D, seq_bytes);
+  const buf_rsrc rb = make_rsrc(a.sel_logp + tile * a.nb * kQTa, (uint32_t)(a.nb * kQTa * 4));
 
   // Q^T operand fragments: column = query l32, k = d in [16 s + 8 lh, +8)
   bf16x8 qf[D / 16];
@@ -190,13 +187,22 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     qf[s] = as_bf16x8(w);
   }
 
-  const int cpb = a.bs / kChunk;
-  const int64_t own_c0 = (p_begin / a.bs) * cpb;
+  const int cpb_log = a.bs == 2 * kChunk ? 1 : 0;   // chunks per block: 1 or 2
+  const int64_t own_c0 = (p_begin / a.bs) << cpb_log;
   const int n_own = (int)(qt - own_c0 + 1);
   const int count = a.sel_count[tile];
-  const int32_t* idx = a.sel_idx + tile * a.nb;
-  const int n_chunks = n_own + count * cpb;
-  const float* logp_tile = a.sel_logp + tile * a.nb * kQTa;
+  const int n_chunks = n_own + (count << cpb_log);
+  // the tile's selected block ids; chunk c >= n_own belongs to entry
+  // (c - n_own) >> cpb_log, other offsets fall outside the range and read 0
+  const buf_rsrc ri = make_rsrc(a.sel_idx + tile * a.nb, (uint32_t)(count * 4));
+  auto sel_block = [&](int c) -> uint32_t {
+    return buf_load4(ri, (uint32_t)(((c - n_own) >> cpb_log) * 4));
+  };
+  // chunk c (block id j when selected) -> first key, bias block (-1: own block)
+  auto key0_of = [&](int c, int j) -> int64_t {
+    return c < n_own ? (own_c0 + c) * kChunk
+                     : ((int64_t)j << cpb_log) * kChunk + ((c - n_own) & cpb_log) * kChunk;
+  };
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -206,45 +212,69 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   float m_ref = -INFINITY, l_run = 0.f;
 
   // Chunk c sits in LDS buffer c % 3; chunk c+1 is already staged and chunk
-  // c+2's K/V are in flight from HBM into registers.  The waves form two
-  // groups that walk the same chunks half a phase apart: group A computes
-  // chunk c's scores after the barrier, group B computed them before it (at
-  // the end of the previous iteration).  A SIMD hosts one wave of each group,
-  // so one wave's softmax VALU work overlaps the other wave's MFMAs.
-  const bool late = wave >= NT / kWave / 2;   // group B
+  // c+2's K/V/bias are in flight from HBM into registers, preceded in the
+  // load queue by the block id of chunk c+3.
   Stage stage;
-  ChunkRef cr_cur = chunk_ref(0, n_own, own_c0, cpb, idx), cr_nx, cr_nx2;
-  stage.load(kp, vp, cr_cur.key0, a.n);
-  stage.store(Ks[0], Vt[0]);
-  if (n_chunks > 1) {
-    cr_nx = chunk_ref(1, n_own, own_c0, cpb, idx);
-    stage.load(kp, vp, cr_nx.key0, a.n);
-    stage.store(Ks[1], Vt[1]);
+  for (int c = 0; c < 2 && c < n_chunks; ++c) {
+    const int j = __builtin_amdgcn_readfirstlane(sel_block(c));
+    stage.load(rk, rv, rb, key0_of(c, j), c < n_own ? -1 : j);
+    stage.store(Ks[c], Vt[c], Bs[c]);
   }
+  uint32_t jv = 0;
   if (n_chunks > 2) {
-    cr_nx2 = chunk_ref(2, n_own, own_c0, cpb, idx);
-    stage.load(kp, vp, cr_nx2.key0, a.n);
+    const int j = __builtin_amdgcn_readfirstlane(sel_block(2));
+    jv = sel_block(3);
+    stage.load(rk, rv, rb, key0_of(2, j), 2 < n_own ? -1 : j);
   }
+  // Q fragments and the first chunks have landed: with nothing of the
+  // prologue pending, the loop's waits only ever cover its own loads
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  f32x16 st[2];
-  if (late) chunk_scores<D, KP>(Ks[0], qf, l32, lh, st);
 
   int bcur = 0;
   for (int c = 0; c < n_chunks; ++c) {
     const int bnx = bcur == NBUF - 1 ? 0 : bcur + 1;
     const int bnx2 = bnx == NBUF - 1 ? 0 : bnx + 1;
-    if (!late) chunk_scores<D, KP>(Ks[bcur], qf, l32, lh, st);
+
+    // ---- S^T (64 keys x 32 queries) = K Q^T: two 32-key tiles ----
+    const __bf16* Kc = Ks[bcur];
+    u32x4 kw[2][D / 16];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        kw[kt][s] = *(const u32x4*)(Kc + (32 * kt + l32) * KP + 16 * s + 8 * lh);
+    f32x16 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) st[kt] = mfma32(as_bf16x8(kw[kt][s]), qf[s], st[kt]);
+    }
+
+    // V^T fragments of the chunk, read while the scores are computed
+    const __bf16* Vc = Vt[bcur];
+    u32x4 vw[4][D / 32];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const __bf16* vrow = Vc + (32 * dt + l32) * VP + 16 * ks + 4 * lh;
+        const u32x2 v0 = *(const u32x2*)(vrow);
+        const u32x2 v1 = *(const u32x2*)(vrow + 8);
+        vw[ks][dt] = (u32x4){v0.x, v0.y, v1.x, v1.y};
+      }
 
     // ---- online softmax of chunk c, exp2 domain: logit2 = s * scale_log2 + bias2 ----
-    const float bias2 =
-        cr_cur.block >= 0 ? logp_tile[cr_cur.block * kQTa + qloc] * kLog2e : 0.f;
-    if (cr_cur.diag) {
+    const float bias2 = Bs[bcur][qloc] * kLog2e;
+    if (c == n_own - 1) {   // the diagonal chunk starts at the tile's first position
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * kt + 8 * (i / 4) + 4 * lh + (i % 4);
-          if (cr_cur.key0 + key > qpos) st[kt][i] = -INFINITY;
+          if (key > qloc) st[kt][i] = -INFINITY;
         }
     }
     float smax = -INFINITY;
@@ -266,54 +296,37 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     }
     const float off = m_ref == -INFINITY ? 0.f : bias2 - m_ref;
     float psum = 0.f;
+    bf16x8 pf[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = ks / 2, i0 = 8 * (ks % 2);
+      float pv[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(st[kt][i], a.scale_log2, off));
-        st[kt][i] = pv;
-        psum += pv;
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = fast_exp2(fmaf(st[kt][i0 + e], a.scale_log2, off));
+        psum += pv[e];
       }
+      const u32x4 pw = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
+                        pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
+      pf[ks] = as_bf16x8(pw);
+    }
     psum += __shfl_xor(psum, 32, kWave);
     l_run += psum;
 
     // ---- O^T += V^T P^T : 4 k-steps of 16 keys ----
-    const __bf16* Vc = Vt[bcur];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kt = ks / 2, i0 = 8 * (ks % 2);
-      u32x4 pw;
-      pw.x = pack_bf16(st[kt][i0 + 0], st[kt][i0 + 1]);
-      pw.y = pack_bf16(st[kt][i0 + 2], st[kt][i0 + 3]);
-      pw.z = pack_bf16(st[kt][i0 + 4], st[kt][i0 + 5]);
-      pw.w = pack_bf16(st[kt][i0 + 6], st[kt][i0 + 7]);
-      const bf16x8 pf = as_bf16x8(pw);
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const __bf16* vrow = Vc + (32 * dt + l32) * VP + 16 * ks + 4 * lh;
-        const u32x2 v0 = *(const u32x2*)(vrow);
-        const u32x2 v1 = *(const u32x2*)(vrow + 8);
-        const u32x4 vw = {v0.x, v0.y, v1.x, v1.y};
-        acc[dt] = mfma32(as_bf16x8(vw), pf, acc[dt]);
-      }
-    }
-    if (late && c + 1 < n_chunks) {
-      __builtin_amdgcn_sched_barrier(0);
-      chunk_scores<D, KP>(Ks[bnx], qf, l32, lh, st);
-    }
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma32(as_bf16x8(vw[ks][dt]), pf[ks], acc[dt]);
 
     // chunk c+2 into the buffer chunk c-1 used (every wave is past it)
-    if (c + 2 < n_chunks) stage.store(Ks[bnx2], Vt[bnx2]);
+    if (c + 2 < n_chunks) stage.store(Ks[bnx2], Vt[bnx2], Bs[bnx2]);
     __syncthreads();
-    if (c + 3 < n_chunks) {
-      const ChunkRef cr3 = chunk_ref(c + 3, n_own, own_c0, cpb, idx);
-      stage.load(kp, vp, cr3.key0, a.n);
-      cr_cur = cr_nx;
-      cr_nx = cr_nx2;
-      cr_nx2 = cr3;
-    } else {
-      cr_cur = cr_nx;
-      cr_nx = cr_nx2;
+    const int c3 = c + 3;
+    if (c3 < n_chunks) {
+      const int j = __builtin_amdgcn_readfirstlane(jv);
+      jv = sel_block(c3 + 1);
+      stage.load(rk, rv, rb, key0_of(c3, j), c3 < n_own ? -1 : j);
     }
     bcur = bnx;
   }

@@ -52,6 +52,26 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
 // results below 2^-126 flush to zero, which softmax weights can afford.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- buffer loads with hardware range checking -----------------------------
+// A raw buffer resource covers `bytes` bytes from `base`; a load whose byte
+// offset lies at or beyond that size returns zeros and touches no memory,
+// which replaces per-element bounds branches on ragged tails.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr int kBufFlags = 0x00020000;   // gfx9 raw-buffer dword 3 (32-bit data format)
+
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kBufFlags);
+}
+__device__ __forceinline__ u32x4 buf_load16(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // ---- wave64 reductions (fixed order, deterministic) -------------------------
 
 __device__ __forceinline__ float wave_sum(float v) {
