@@ -191,7 +191,9 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
  *   route           optional (NULL = use the workspace): where the routing
  *                   result goes, sized by dash_route_sizes_decode
  *   ws              >= dash_decode_workspace_bytes(p, max_len) bytes
- * Values of cache_len outside [1, max_len] are clamped into that range. */
+ * Values of cache_len outside [1, max_len] are clamped into that range.
+ * DASH_ERR_UNSUPPORTED when (max_len + 64) * d * element size >= 2^31, when
+ * B * Hkv > 65535, or for bf16 when B * Hkv > 8192. */
 dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* cache_len, int64_t max_len,
                         const float* w_s, float* summ, int64_t summ_blocks, void* o,

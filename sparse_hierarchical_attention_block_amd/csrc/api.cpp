@@ -47,8 +47,8 @@ dash_status hip_status(hipError_t e) { return e == hipSuccess ? DASH_OK : DASH_E
 // grid sizes must fit the 32-bit x dimension
 bool grid_ok(int64_t blocks) { return blocks >= 0 && blocks < ((int64_t)1 << 31); }
 
-// the prefill attend kernel addresses one sequence's keys / values through a
-// buffer resource with a 31-bit byte range
+// the attend kernels address one (sequence, KV head)'s keys / values through
+// a buffer resource with a 31-bit byte range
 bool seq_bytes_ok(const Shape& s, int64_t n) {
   const int64_t elt = s.dtype == DASH_BF16 ? 2 : 4;
   return (n + 64) * s.d * elt < ((int64_t)1 << 31);
@@ -247,8 +247,11 @@ dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache
   const dash::DecodeLayout L = dash::decode_layout(s, max_len);
   if (!ws || ((uintptr_t)ws % kAlign) != 0) return DASH_ERR_INVALID_ARG;
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE_TOO_SMALL;
-  if ((int64_t)s.G * L.nb * 4 > 160 * 1024) return DASH_ERR_UNSUPPORTED;
+  if ((int64_t)s.G * L.nb * 4 > 160 * 1024 || !seq_bytes_ok(s, max_len))
+    return DASH_ERR_UNSUPPORTED;
   if (!grid_ok(L.n_split) || (int64_t)s.B * s.Hkv > 65535) return DASH_ERR_UNSUPPORTED;
+  if (s.dtype == DASH_BF16 && (int64_t)s.B * s.Hkv > dash::kDecodeMaxBg)
+    return DASH_ERR_UNSUPPORTED;
   dash_route_buf rb = {nullptr, nullptr, nullptr, nullptr, nullptr};
   if (route) rb = *route;
   return hip_status(dash::launch_decode(s, q, k_cache, v_cache, cache_len, max_len, w_s, summ,

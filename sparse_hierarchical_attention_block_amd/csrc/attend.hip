@@ -252,6 +252,10 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) st[kt] = mfma32(as_bf16x8(kw[kt][s]), qf[s], st[kt]);
     }
+    // issue all 2 x D/16 K-fragment reads before the first MFMA (mask 0x100:
+    // LDS reads, 0x008: MFMA), so LDS latency is paid once per chunk
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
 
     // V^T fragments of the chunk, read while the scores are computed
     const __bf16* Vc = Vt[bcur];

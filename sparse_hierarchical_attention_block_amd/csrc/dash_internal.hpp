@@ -38,6 +38,8 @@ struct DecodeLayout {
 };
 DecodeLayout decode_layout(const Shape& s, int64_t max_len);
 constexpr int kDecodeSplit = 16;   // list entries (blocks) per split
+constexpr int kDecodeMaxBg = 8192; // sequences x KV heads of one bf16 decode call
+constexpr int kMaxDevices = 64;    // per-device launch-shape caches
 
 // One decode step (route, attend, combine, summary update).
 hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const void* vc,

@@ -17,6 +17,8 @@
 //                      transposed 8x8 in registers
 //   4. decode_combine  log-sum-exp merge of the splits in a fixed order
 //   5. when cache_len[b] % bs == 0 the completed block's summary is written.
+#include <atomic>
+
 #include "dash_internal.hpp"
 #include "device_common.hpp"
 #include "entmax_device.hpp"
@@ -47,11 +49,12 @@ struct DecodeArgs {
   int64_t n_split;
   int nwords;
   int H, Hkv, G, bs, B;
+  int bs_log;        // log2(bs)
   int mode;
   float e, scale, scale_log2;
 };
 
-__device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
+__host__ __device__ inline int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
 
 __device__ __forceinline__ int64_t clamp_len(int32_t v, int64_t max_len) {
   int64_t l = v;
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(64) void decode_scores_kernel(DecodeArgs a) {
   const int64_t bg = blockIdx.y;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
-  const int64_t ncand = (len - 1) / a.bs;
+  const int64_t ncand = (len - 1) >> a.bs_log;
   const int64_t j0 = (int64_t)blockIdx.x * 64;
   if (j0 >= ncand) return;
   const T* qb = (const T*)a.q + ((int64_t)b * a.H + g * a.G) * D;
@@ -104,12 +107,17 @@ __global__ __launch_bounds__(64) void decode_scores_kernel(DecodeArgs a) {
 }
 
 // ---- 2. threshold, GQA average, union, compaction ------------------------------------------
+// One workgroup per (sequence, KV head), one wave per query head.  With VPL > 0
+// the wave keeps its row of scores in registers (VPL per lane, candidate j in
+// lane j % 64, slot j / 64) and solves for tau there (MODE: entmax_mode of
+// alpha); VPL = 0 walks the row in memory for lists longer than 64 * 32.
+template <int VPL, int MODE>
 __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
   extern __shared__ float Ps[];   // [G][nb]
   const int64_t bg = blockIdx.x;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
-  const int ncand = (int)((len - 1) / a.bs);
+  const int ncand = (int)((len - 1) >> a.bs_log);
   const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
   const int64_t row = (int64_t)b * a.H + g * a.G + hh;
   const float* xr = a.x + row * a.nb;
@@ -120,20 +128,50 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
     if (threadIdx.x == 0) a.count[bg] = 0;
     return;
   }
-  const float tau = entmax_tau([&](int j) { return xr[j]; }, ncand, lane, kWave, a.mode, a.e);
-  if (lane == 0) a.tau[row] = tau;
-  if (a.bits)
-    for (int w = lane; w < a.nwords; w += kWave) {
-      uint32_t word = 0u;
-      for (int i = 0; i < 32; ++i) {
-        const int j = w * 32 + i;
-        if (j < ncand && xr[j] > tau) word |= 1u << i;
-      }
-      a.bits[row * a.nwords + w] = word;
+  if constexpr (VPL > 0) {
+    float xv[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int j = lane + kWave * i;
+      xv[i] = j < ncand ? xr[j] : -INFINITY;
     }
-  for (int j = lane; j < ncand; j += kWave) {
-    const float y = xr[j] - tau;
-    Ps[hh * a.nb + j] = y > 0.f ? entmax_pow(y, a.mode, a.e) : 0.f;
+    const int nact4 = (ncand + 4 * kWave - 1) / (4 * kWave);
+    const float tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{kWave}, a.e, nact4);
+    if (lane == 0) a.tau[row] = tau;
+    if (a.bits) {
+      // candidate j = 64 i + lane sits in bit lane of the ballot of slot i
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const uint64_t m = __ballot(xv[i] > tau);   // -inf slots never pass
+        if (lane == 0) {
+          if (2 * i < a.nwords) a.bits[row * a.nwords + 2 * i] = (uint32_t)m;
+          if (2 * i + 1 < a.nwords) a.bits[row * a.nwords + 2 * i + 1] = (uint32_t)(m >> 32);
+        }
+      }
+      for (int w = 2 * VPL + lane; w < a.nwords; w += kWave) a.bits[row * a.nwords + w] = 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int j = lane + kWave * i;
+      const float y = xv[i] - tau;
+      if (j < ncand) Ps[hh * a.nb + j] = y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
+    }
+  } else {
+    const float tau = entmax_tau([&](int j) { return xr[j]; }, ncand, lane, kWave, a.mode, a.e);
+    if (lane == 0) a.tau[row] = tau;
+    if (a.bits)
+      for (int w = lane; w < a.nwords; w += kWave) {
+        uint32_t word = 0u;
+        for (int i = 0; i < 32; ++i) {
+          const int j = w * 32 + i;
+          if (j < ncand && xr[j] > tau) word |= 1u << i;
+        }
+        a.bits[row * a.nwords + w] = word;
+      }
+    for (int j = lane; j < ncand; j += kWave) {
+      const float y = xr[j] - tau;
+      Ps[hh * a.nb + j] = y > 0.f ? entmax_pow(y, a.mode, a.e) : 0.f;
+    }
   }
   __syncthreads();
   const float invG = 1.0f / (float)a.G;
@@ -159,35 +197,56 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
 }
 
 // ---- 3. split-K attend (bf16, MFMA) ----------------------------------------------------------
+// One work item: split s of the list of (sequence, KV head) bgi, i.e. entries
+// [s * kDecodeSplit, (s + 1) * kDecodeSplit) of [own block, selected blocks...].
+// All 256 threads call; ms / ls / os are the workgroup's merge buffers.
 template <int D>
-__global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
+                                            float (&ms)[4][16], float (&ls)[4][16],
+                                            float (&os)[4][8][D]) {
   constexpr int DPL = D / 16;   // d columns per lane in the PV product
-  __shared__ float ms[4][16], ls[4][16];
-  __shared__ float os[4][16][D];
-  const int s = blockIdx.x;
-  const int64_t bg = blockIdx.y;
-  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
-  const int64_t len = clamp_len(a.cache_len[b], a.max_len);
-  const int64_t own = (len - 1) / a.bs;
-  const int count = a.count[bg];
-  const int n_entries = 1 + count;
-  if (s * kDecodeSplit >= n_entries) return;
+  const int64_t bg = bgi;
+  const int b = bgi / a.Hkv, g = bgi % a.Hkv;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int l16 = lane % 16, lg = lane / 16;
+  // Everything the K/V addresses depend on arrives with one vector load:
+  // lanes 0..kPerWave-1 read this wave's block ids e = s * kDecodeSplit +
+  // wave + 4 i (slots clamped into the list buffer; ids past the list's end
+  // are never used), lane kPerWave the list length, the other lanes the
+  // sequence length.  Biases are read later, behind the K/V loads.
+  constexpr int kPerWave = kDecodeSplit / 4;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int32_t meta;
+  {
+    const int64_t slot = min64(max(s * kDecodeSplit + wv + 4 * lane - 1, 0), a.nb - 1);
+    const int32_t* src = lane < kPerWave    ? a.idx + bg * a.nb + slot
+                         : lane == kPerWave ? a.count + bg
+                                            : a.cache_len + b;
+    meta = *src;
+  }
+  int32_t jraw[kPerWave];
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) jraw[i] = __builtin_amdgcn_readlane(meta, i);
+  const int count = __builtin_amdgcn_readlane(meta, kPerWave);
+  const int64_t len = clamp_len(__builtin_amdgcn_readlane(meta, kPerWave + 1), a.max_len);
+  const int64_t own = (len - 1) >> a.bs_log;
+  const int n_entries = 1 + count;
 
-  const __bf16* kb = (const __bf16*)a.kc + bg * a.max_len * D;
-  const __bf16* vb = (const __bf16*)a.vc + bg * a.max_len * D;
+  // K/V of this (sequence, KV head) through buffer resources sized to the
+  // current length: keys >= len read as zeros (and are masked below)
+  const uint32_t len_bytes = (uint32_t)(len * (D * 2));
+  const buf_rsrc rk = make_rsrc((const __bf16*)a.kc + bg * a.max_len * D, len_bytes);
+  const buf_rsrc rv = make_rsrc((const __bf16*)a.vc + bg * a.max_len * D, len_bytes);
 
-  // Q^T operand: column = query head l16 (< G), k = d in [32 s' + 8 lg, +8)
+  // Q^T operand: column = query head l16 (< G), k = d in [32 s' + 8 lg, +8);
+  // columns l16 >= G fall outside the resource and read as zeros
   bf16x8 qf[D / 32];
   {
-    const __bf16* qrow = (const __bf16*)a.q + ((int64_t)b * a.H + g * a.G + l16) * D;
+    const buf_rsrc rq =
+        make_rsrc((const __bf16*)a.q + ((int64_t)b * a.H + g * a.G) * D, (uint32_t)(a.G * D * 2));
 #pragma unroll
-    for (int sp = 0; sp < D / 32; ++sp) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (l16 < a.G) w = *(const u32x4*)(qrow + 32 * sp + 8 * lg);
-      qf[sp] = as_bf16x8(w);
-    }
+    for (int sp = 0; sp < D / 32; ++sp)
+      qf[sp] = as_bf16x8(buf_load16(rq, (uint32_t)(l16 * D + 32 * sp + 8 * lg) * 2));
   }
   f32x4 acc[DPL];
 #pragma unroll
@@ -195,23 +254,23 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   const int e_end = min(n_entries, (s + 1) * kDecodeSplit);
-  for (int e = s * kDecodeSplit + wave; e < e_end; e += 4) {
-    const int64_t j = e == 0 ? own : (int64_t)a.idx[bg * a.nb + e - 1];
-    const float bias2 = e == 0 ? 0.f : a.logp[bg * a.nb + j] * kLog2e;
-    for (int c64 = 0; c64 < a.bs / 64; ++c64) {
-      const int64_t key0 = j * a.bs + 64 * c64;
+#pragma unroll
+  for (int ei = 0; ei < kPerWave; ++ei) {
+    const int e = s * kDecodeSplit + wv + 4 * ei;
+    if (e >= e_end) break;
+    const int64_t j = e == 0 ? own : (int64_t)jraw[ei];
+    for (int c64 = 0; c64 < (a.bs >> 6); ++c64) {
+      const int64_t key0 = (j << a.bs_log) + 64 * c64;
       if (key0 >= len) break;
-      // Issue every load of the chunk before any use.  Addresses are clamped
-      // to the last valid key, so each load stays in bounds and reads finite
-      // data; keys >= len are masked below (score -inf, probability 0).
+      // Issue every load of the chunk before any use (32-bit byte offsets
+      // from the chunk's first key).
+      const uint32_t c0 = (uint32_t)(key0 * (D * 2));
       u32x4 kw[4][D / 32];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int64_t key = min64(key0 + 16 * kt + l16, len - 1);
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int sp = 0; sp < D / 32; ++sp)
-          kw[kt][sp] = *(const u32x4*)(kb + key * D + 32 * sp + 8 * lg);
-      }
+          kw[kt][sp] = buf_load16(rk, c0 + (16 * kt + l16) * (D * 2) + (32 * sp + 8 * lg) * 2);
       // V rows this lane needs: k = 8 lg + e' <-> key 32 ks + 16 (e'/4) + 4 lg + e'%4,
       // DPL consecutive d starting at DPL * l16
       uint32_t vin[2][8][DPL / 2];
@@ -219,15 +278,20 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int ep = 0; ep < 8; ++ep) {
-          const int64_t key = min64(key0 + 32 * ks + 16 * (ep / 4) + 4 * lg + (ep % 4), len - 1);
+          const uint32_t off =
+              c0 + (32 * ks + 16 * (ep / 4) + 4 * lg + (ep % 4)) * (D * 2) + DPL * l16 * 2;
           if constexpr (DPL == 8) {
-            const u32x4 t = *(const u32x4*)(vb + key * D + DPL * l16);
+            const u32x4 t = buf_load16(rv, off);
             vin[ks][ep][0] = t.x; vin[ks][ep][1] = t.y; vin[ks][ep][2] = t.z; vin[ks][ep][3] = t.w;
           } else {
-            const u32x2 t = *(const u32x2*)(vb + key * D + DPL * l16);
+            const u32x2 t = buf_load8(rv, off);
             vin[ks][ep][0] = t.x; vin[ks][ep][1] = t.y;
           }
         }
+      const float bias2 = e == 0 ? 0.f : a.logp[bg * a.nb + j] * kLog2e;
+      // keep every load of the chunk ahead of the first use: one HBM latency
+      // per chunk instead of one per dependent group of loads
+      __builtin_amdgcn_sched_barrier(0);
       // S^T = K Q^T: st[kt][i] = S[query l16][key 16 kt + 4 lg + i]
       f32x4 st[4];
 #pragma unroll
@@ -299,15 +363,17 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- merge the 4 waves in a fixed order ----
+  // ---- merge the 4 waves in a fixed order (query rows 4 lg + i < 8 hold the G <= 8 heads) ----
   if (lane < 16) {
     ms[wave][lane] = m_run;
     ls[wave][lane] = l_run;
   }
+  if (lg < 2) {
 #pragma unroll
-  for (int c = 0; c < DPL; ++c)
+    for (int c = 0; c < DPL; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) os[wave][4 * lg + i][DPL * l16 + c] = acc[c][i];
+      for (int i = 0; i < 4; ++i) os[wave][4 * lg + i][DPL * l16 + c] = acc[c][i];
+  }
   __syncthreads();
   float* part = a.part + ((bg * a.n_split + s) * a.G) * (D + 2);
   for (int e = threadIdx.x; e < a.G * D; e += 256) {
@@ -323,6 +389,59 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
     float* pr = part + qr * (D + 2);
     if (d == 0) { pr[0] = M; pr[1] = L; }
     pr[2 + d] = O;
+  }
+  __syncthreads();   // the merge buffers are reused by the next item
+}
+
+// Persistent grid (as many workgroups as fit on the GPU at once): every
+// workgroup derives the work items from the list lengths -- item ranges
+// pre[bg] .. pre[bg+1] with ceil((1 + count[bg]) / kDecodeSplit) items per
+// (sequence, KV head) -- and takes items blockIdx.x, + gridDim.x, ...  No
+// workgroup is launched for a split past its list, so none holds a slot
+// waiting only to find it has nothing to do.
+template <int D>
+__global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
+  __shared__ float ms[4][16], ls[4][16];
+  __shared__ float os[4][8][D];
+  __shared__ int pre[kDecodeMaxBg + 1];
+  __shared__ int wsum[4];
+  const int nbg = a.B * a.Hkv;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  // exclusive prefix of the item counts: 256 contiguous ranges, then a scan
+  // of the range totals
+  const int per = (nbg + 255) / 256;
+  const int i0 = min(nbg, (int)threadIdx.x * per), i1 = min(nbg, i0 + per);
+  int tot = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int ns = (a.count[i] + kDecodeSplit) / kDecodeSplit;   // ceil((1 + count) / split)
+    pre[i] = ns;
+    tot += ns;
+  }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - tot;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+  for (int i = i0; i < i1; ++i) {
+    const int ns = pre[i];
+    pre[i] = run;
+    run += ns;
+  }
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  if (threadIdx.x == 0) pre[nbg] = total;
+  __syncthreads();
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    int lo = 0, hi = nbg;   // pre[lo] <= it < pre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= it) lo = mid; else hi = mid;
+    }
+    decode_item<D>(a, lo, it - pre[lo], ms, ls, os);
   }
 }
 
@@ -384,28 +503,80 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
   }
 }
 
-// ---- 4. combine --------------------------------------------------------------------------
+// ---- 4. combine ----------------------------------------------------------------------------
+// One workgroup per (sequence, KV head): the ns split maxima and sums of all
+// G heads are read at once into LDS, then each thread merges its outputs over
+// the splits with the loads of several splits in flight.  Fixed order in s.
+constexpr int kCombineThreads = 256;
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
-  const int64_t bh = blockIdx.x;
-  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-  const int g = h / a.G, qr = h % a.G;
-  const int64_t bg = (int64_t)b * a.Hkv + g;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a) {
+  extern __shared__ float wts[];   // [ns][G] weights exp2(m_s - M), [ns][G] l_s, [G] 1 / L
+  const int bgi = blockIdx.x;
+  const int64_t bg = bgi;
+  const int b = bgi / a.Hkv, g = bgi % a.Hkv;
   const int n_entries = 1 + a.count[bg];
   const int ns = (n_entries + kDecodeSplit - 1) / kDecodeSplit;
-  const float* part = a.part + (bg * a.n_split * a.G + qr) * (D + 2);
-  const int64_t stride = (int64_t)a.G * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part[s * stride]);
-  float L = 0.f, O = 0.f;
-  const int d = threadIdx.x;
-  for (int s = 0; s < ns; ++s) {
-    const float ms = part[s * stride];
-    const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-    L += part[s * stride + 1] * f;
-    O += part[s * stride + 2 + d] * f;
+  const int G = a.G;
+  const int64_t stride = (int64_t)G * (D + 2);   // one split: G rows of [m, l, o(D)]
+  const float* part = a.part + bg * a.n_split * stride;
+  float* ls = wts + ns * G;
+  float* inv_l = ls + ns * G;
+  for (int e = threadIdx.x; e < ns * G; e += kCombineThreads) {
+    const float* pr = part + (e / G) * stride + (e % G) * (D + 2);
+    wts[e] = pr[0];
+    ls[e] = pr[1];
   }
-  ((T*)a.o)[bh * D + d] = from_f32<T>(O / L);
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int qr = threadIdx.x;
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, wts[sp * G + qr]);
+    float L = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float m = wts[sp * G + qr];
+      const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
+      wts[sp * G + qr] = f;
+      L += ls[sp * G + qr] * f;
+    }
+    inv_l[qr] = 1.0f / L;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += kCombineThreads) {
+    const int qr = e / D, d = e % D;
+    const float* col = part + qr * (D + 2) + 2 + d;
+    float O = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= ns; sp += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = col[(sp + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) O += v[u] * wts[(sp + u) * G + qr];
+    }
+    for (; sp < ns; ++sp) O += col[sp * stride] * wts[sp * G + qr];
+    ((T*)a.o)[((int64_t)b * a.H + g * G + qr) * D + d] = from_f32<T>(O * inv_l[qr]);
+  }
+}
+
+// Workgroups of decode_attend_bf16_kernel<D> resident on the current device at
+// once (cached per device).
+template <int D>
+static int persistent_grid() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int g = cache[dev].load(std::memory_order_relaxed);
+  if (g == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, (const void*)decode_attend_bf16_kernel<D>, 256, 0) != hipSuccess)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    g = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+    cache[dev].store(g, std::memory_order_relaxed);
+  }
+  return g;
 }
 
 DecodeLayout decode_layout(const Shape& s, int64_t max_len) {
@@ -452,6 +623,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   a.Hkv = s.Hkv;
   a.G = s.G;
   a.bs = s.bs;
+  a.bs_log = s.bs == 128 ? 7 : 6;
   a.B = s.B;
   a.mode = entmax_mode(s.alpha);
   a.e = 1.0f / (s.alpha - 1.0f);
@@ -468,21 +640,44 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
 #undef DASH_DS
   }
   const size_t lds = sizeof(float) * s.G * L.nb;
-  if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute((const void*)decode_route_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(decode_route_kernel, dim3(nbg), dim3(64 * s.G), lds, st, a);
+  {
+    // rows of up to 64 * VPL candidates stay in registers
+    const int64_t nc = L.ncand_max;
+    const int vpl = nc <= 256 ? 4 : nc <= 512 ? 8 : nc <= 1024 ? 16 : nc <= 2048 ? 32 : 0;
+    const int mode = entmax_mode(s.alpha);
+    const void* fn = (const void*)decode_route_kernel<0, kEntmaxGeneral>;
+#define DASH_RK(V)                                                                    \
+  fn = mode == kSparsemax       ? (const void*)decode_route_kernel<V, kSparsemax>     \
+       : mode == kEntmax15      ? (const void*)decode_route_kernel<V, kEntmax15>      \
+       : mode == kEntmaxQuartic ? (const void*)decode_route_kernel<V, kEntmaxQuartic> \
+                                : (const void*)decode_route_kernel<V, kEntmaxGeneral>
+    if (vpl == 4) DASH_RK(4); else if (vpl == 8) DASH_RK(8); else if (vpl == 16) DASH_RK(16);
+    else if (vpl == 32) DASH_RK(32);
+#undef DASH_RK
+    if (lds > 64 * 1024)
+      (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    void* kargs[] = {&a};
+    hipError_t e2 = hipLaunchKernel(fn, dim3(nbg), dim3(64 * s.G), kargs, lds, st);
+    if (e2 != hipSuccess) return e2;
+  }
 
   dim3 g3((unsigned)L.n_split, nbg);
   if (bf16) {
-    if (s.d == 64) hipLaunchKernelGGL(decode_attend_bf16_kernel<64>, g3, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(decode_attend_bf16_kernel<128>, g3, dim3(256), 0, st, a);
+    const int64_t items_max = (int64_t)nbg * L.n_split;
+    if (s.d == 64)
+      hipLaunchKernelGGL(decode_attend_bf16_kernel<64>,
+                         dim3((unsigned)min64(items_max, persistent_grid<64>())), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(decode_attend_bf16_kernel<128>,
+                         dim3((unsigned)min64(items_max, persistent_grid<128>())), dim3(256), 0, st, a);
   } else {
     if (s.d == 64) hipLaunchKernelGGL(decode_attend_f32_kernel<64>, g3, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(decode_attend_f32_kernel<128>, g3, dim3(256), 0, st, a);
   }
-  dim3 g4((unsigned)(s.B * s.H));
-#define DASH_DC(T, D) hipLaunchKernelGGL((decode_combine_kernel<T, D>), g4, dim3(D), 0, st, a)
+  dim3 g4(nbg);
+  const size_t lds4 = sizeof(float) * (2 * L.n_split + 1) * s.G;
+#define DASH_DC(T, D) \
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), g4, dim3(kCombineThreads), lds4, st, a)
   if (bf16) { if (s.d == 64) DASH_DC(__bf16, 64); else DASH_DC(__bf16, 128); }
   else { if (s.d == 64) DASH_DC(float, 64); else DASH_DC(float, 128); }
 #undef DASH_DC
