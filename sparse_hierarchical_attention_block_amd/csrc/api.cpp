@@ -71,7 +71,7 @@ bool route_lds_ok(const Shape& s, int64_t n) {
   const int64_t t_max = ((n_qt - 1) * kQT) / s.bs;
   const int64_t pitch = ((t_max > 0 ? t_max : 1) + 15) / 16 * 16 + 4;
   int64_t pp = 64;
-  while (pp > 1 && pp * s.G * pitch * 4 > 64 * 1024) pp >>= 1;
+  while (pp > 1 && pp * s.G * pitch * 4 > DASH_ROUTE_X_BUDGET) pp >>= 1;
   while (pp * s.G < 16) pp <<= 1;
   while (pp * s.G > 64) pp >>= 1;
   const int64_t lds = (pp * s.G * pitch + pp * s.G) * 4 + (pitch - 4) * 4;

@@ -37,6 +37,15 @@ struct DecodeLayout {
   size_t off_x, off_tau, off_count, off_idx, off_logp, off_part, total;
 };
 DecodeLayout decode_layout(const Shape& s, int64_t max_len);
+// Prefill routing, pass-based path (rows longer than 128 candidates): threads
+// per workgroup and the LDS bytes its per-pass score buffer may use.
+#ifndef DASH_ROUTE_PASS_THREADS
+#define DASH_ROUTE_PASS_THREADS 512
+#endif
+#ifndef DASH_ROUTE_X_BUDGET
+#define DASH_ROUTE_X_BUDGET (80 * 1024)
+#endif
+
 constexpr int kDecodeSplit = 16;   // list entries (blocks) per split
 constexpr int kDecodeMaxBg = 8192; // sequences x KV heads of one bf16 decode call
 constexpr int kMaxDevices = 64;    // per-device launch-shape caches

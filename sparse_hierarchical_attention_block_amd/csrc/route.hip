@@ -8,12 +8,14 @@
 // One workgroup per (sequence, KV head, query tile of 64 positions), heaviest
 // tiles (most candidate blocks) first.  Candidates of tile qt are the complete
 // blocks j < floor(64 qt / bs).  Rows are (position, head of the group)
-// pairs; they are processed in passes of PP positions:
+// pairs; for tiles with more than 128 candidates (or float32 queries) they are
+// processed in passes of PP positions, PP as large as an 80 KB LDS score
+// buffer allows:
 //   1. scores X[row][j] = scale * q_row . s_j into an LDS buffer; bf16 queries
 //      use MFMA 16x16x32 with the float32 summaries split into three bf16
 //      parts (hi + mid + lo carries 24 mantissa bits), float32 queries use
 //      plain FMAs;
-//   2. tau per row (entmax_device.hpp), lanes-per-row = 256 / rows;
+//   2. tau per row (entmax_device.hpp), lanes-per-row = threads / rows;
 //   3. pbar per (position, block) = mean over the group's heads of
 //      [x - tau]_+^e, written as log pbar (-inf for 0) into sel_logp, and the
 //      tile-union flags.
@@ -24,7 +26,8 @@
 
 namespace dash {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRoutePassThreads = DASH_ROUTE_PASS_THREADS;   // pass-based path
+constexpr size_t kRouteXBudget = DASH_ROUTE_X_BUDGET;         // its LDS score buffer
 constexpr int kQT = DASH_QUERY_TILE;
 constexpr int kRouteMaxRowTiles = 4;   // rows per pass <= 64
 
@@ -50,10 +53,10 @@ struct RouteArgs {
 __host__ __device__ inline int round_up16(int x) { return (x + 15) & ~15; }
 
 // ---- step 1, bf16: MFMA with a 3-way bf16 split of the summaries ----------------
-// Wave w computes candidate tiles w, w+4, ... against every row tile of the
-// pass; the pass's Q fragments are loaded once up front and the next
-// candidate tile's summaries are prefetched while the current one is used.
-template <int D, int MAXRT>
+// Wave w computes candidate tiles w, w + NT/64, ... against every row tile of
+// the pass; the pass's Q fragments are loaded once up front.  (Prefetching the
+// next tile's summaries would cost the registers that keep two waves per SIMD.)
+template <int D, int MAXRT, int NT>
 __device__ void route_scores_bf16(const RouteArgs& a, float* X, int t, int64_t bg, int b, int g,
                                   int64_t pos0, int R) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -88,9 +91,9 @@ __device__ void route_scores_bf16(const RouteArgs& a, float* X, int t, int64_t b
       if (cand >= t) v[s][0] = v[s][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
   };
-  f32x4 sv[KS][2];
-  load_s(wave, sv);
-  for (int ct = wave; ct < CT; ct += kRouteThreads / kWave) {
+  for (int ct = wave; ct < CT; ct += NT / kWave) {
+    f32x4 sv[KS][2];
+    load_s(ct, sv);
     bf16x8 hi[KS], mid[KS], lo[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -106,8 +109,6 @@ __device__ void route_scores_bf16(const RouteArgs& a, float* X, int t, int64_t b
         lo[s][i] = (__bf16)(r1 - (float)m);
       }
     }
-    const int ct_next = ct + kRouteThreads / kWave;
-    if (ct_next < CT) load_s(ct_next, sv);
 #pragma unroll
     for (int rt = 0; rt < MAXRT; ++rt) {
       if (rt < RT) {
@@ -127,11 +128,11 @@ __device__ void route_scores_bf16(const RouteArgs& a, float* X, int t, int64_t b
 }
 
 // ---- step 1, float32: plain FMAs -----------------------------------------------------
-template <int D>
+template <int D, int NT>
 __device__ void route_scores_f32(const RouteArgs& a, float* X, int t, int64_t bg, int b, int g,
                                  int64_t pos0, int R) {
   const float* q = (const float*)a.q;
-  for (int idx = threadIdx.x; idx < R * t; idx += kRouteThreads) {
+  for (int idx = threadIdx.x; idx < R * t; idx += NT) {
     const int row = idx / t, j = idx % t;
     const int m = row / a.G, h = row % a.G;
     const int64_t pos = pos0 + m;
@@ -145,8 +146,8 @@ __device__ void route_scores_f32(const RouteArgs& a, float* X, int t, int64_t bg
   }
 }
 
-template <typename T, int D, int VPL, int MODE>
-__global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs a) {
+template <typename T, int D, int VPL, int MODE, int NT, int RT>
+__global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
   extern __shared__ float smem[];
   const int R = a.PP * a.G;
   float* X = smem;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs 
   const int64_t tile = bg * a.n_qt + qt;
 
   if (t == 0) {
-    for (int idx = threadIdx.x; idx < npos * a.G; idx += kRouteThreads) {
+    for (int idx = threadIdx.x; idx < npos * a.G; idx += NT) {
       const int m = idx / a.G, h = idx % a.G;
       const int64_t r = ((int64_t)b * a.H + g * a.G + h) * a.n + p_begin + m;
       a.tau[r] = __builtin_nanf("");
@@ -174,15 +175,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs 
     return;
   }
 
-  for (int j = threadIdx.x; j < t; j += kRouteThreads) uflag[j] = 0;
-  const int lpr = kRouteThreads / R;   // lanes per row in step 2
+  for (int j = threadIdx.x; j < t; j += NT) uflag[j] = 0;
+  const int lpr = NT / R;   // lanes per row in step 2
   const float invG = 1.0f / (float)a.G;
 
   for (int pp = 0; pp < npos; pp += a.PP) {
     const int64_t pos0 = p_begin + pp;
     __syncthreads();
-    if constexpr (sizeof(T) == 2) route_scores_bf16<D, kRouteMaxRowTiles>(a, X, t, bg, b, g, pos0, R);
-    else route_scores_f32<D>(a, X, t, bg, b, g, pos0, R);
+    if constexpr (sizeof(T) == 2) route_scores_bf16<D, RT, NT>(a, X, t, bg, b, g, pos0, R);
+    else route_scores_f32<D, NT>(a, X, t, bg, b, g, pos0, R);
     __syncthreads();
 
     const int np = min(a.PP, npos - pp);
@@ -198,7 +199,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs 
         const int j = sub + lpr * i;
         xv[i] = j < t ? xr[j] : -INFINITY;
       }
-      const float tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{lpr}, a.e);
+      // slots 4 k .. 4 k + 3 hold candidates [4 k lpr, 4 (k + 1) lpr): only the
+      // groups below t are visited
+      const int nact4 = (t + 4 * lpr - 1) / (4 * lpr);
+      const float tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{lpr}, a.e, nact4);
       const int m = row / a.G, h = row % a.G;
       const int64_t pos = pos0 + m;
       if (pos < a.n) {
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(RouteArgs 
       }
       __syncthreads();
       // step 3: GQA average, log prior, tile-union flags
-      for (int idx = threadIdx.x; idx < t * np; idx += kRouteThreads) {
+      for (int idx = threadIdx.x; idx < t * np; idx += NT) {
         const int j = idx / np, m = idx % np;
         float pb = 0.f;
         for (int h = 0; h < a.G; ++h) {
@@ -584,25 +588,35 @@ hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const 
 #undef DASH_RTT3
     return hipGetLastError();
   }
+  // pass-based path: NT threads, PP positions per pass with their score rows
+  // in an LDS buffer of at most kRouteXBudget bytes
   a.pitch = round_up16(t_max > 0 ? t_max : 1) + 4;
-  a.PP = route_pp(s.G, a.pitch, 64 * 1024);
+  constexpr int NT = kRoutePassThreads;
+  a.PP = route_pp(s.G, a.pitch, kRouteXBudget);
   const size_t lds = ((size_t)a.PP * s.G * a.pitch + (size_t)a.PP * s.G) * 4 +
                      (size_t)round_up16(t_max > 0 ? t_max : 1) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.n_qt * s.B * s.Hkv));
   // register path: the row's candidates fit VPL per lane and a position's
   // G rows share one wave
-  const int lpr = kRouteThreads / (a.PP * s.G);
+  const int lpr = NT / (a.PP * s.G);
   const int need = (t_max + lpr - 1) / lpr;
   int vpl = 0;
-  if (lpr * s.G <= kWave) vpl = need <= 8 ? 8 : need <= 16 ? 16 : need <= 32 ? 32 : 0;
-#define DASH_RT3(T, D, V, M)                                                               \
-  do {                                                                                     \
-    if (lds > 64 * 1024)                                                                   \
-      (void)hipFuncSetAttribute((const void*)route_prefill_kernel<T, D, V, M>,             \
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);      \
-    hipLaunchKernelGGL((route_prefill_kernel<T, D, V, M>), grid, dim3(kRouteThreads), lds, st, \
-                       a);                                                                 \
+  if (lpr * s.G <= kWave)
+    vpl = need <= 8 ? 8 : need <= 16 ? 16 : need <= 32 ? 32 : (need <= 64 && NT <= 256) ? 64 : 0;
+  const int rt_pass = a.PP * s.G / 16;   // row tiles per pass: 1, 2 or 4
+#define DASH_RT4(T, D, V, M, R)                                                                 \
+  do {                                                                                          \
+    if (lds > 64 * 1024)                                                                        \
+      (void)hipFuncSetAttribute((const void*)route_prefill_kernel<T, D, V, M, NT, R>,           \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);           \
+    hipLaunchKernelGGL((route_prefill_kernel<T, D, V, M, NT, R>), grid, dim3(NT), lds, st, a);  \
+  } while (0)
+#define DASH_RT3(T, D, V, M)                                                  \
+  do {                                                                        \
+    if (rt_pass == 1) DASH_RT4(T, D, V, M, 1);                                \
+    else if (rt_pass == 2) DASH_RT4(T, D, V, M, 2);                           \
+    else DASH_RT4(T, D, V, M, 4);                                             \
   } while (0)
 #define DASH_RT2(T, D, V)                                          \
   do {                                                             \
@@ -616,6 +630,7 @@ hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const 
     if (vpl == 8) DASH_RT2(T, D, 8);                               \
     else if (vpl == 16) DASH_RT2(T, D, 16);                        \
     else if (vpl == 32) DASH_RT2(T, D, 32);                        \
+    else if (vpl == 64) DASH_RT2(T, D, 64);                        \
     else DASH_RT3(T, D, 0, kEntmaxGeneral);                        \
   } while (0)
   if (s.dtype == DASH_BF16) {
@@ -626,6 +641,7 @@ hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const 
 #undef DASH_RT
 #undef DASH_RT2
 #undef DASH_RT3
+#undef DASH_RT4
   return hipGetLastError();
 }
 
