@@ -4,10 +4,16 @@
 //
 // With inputs in threshold units x_j = (alpha - 1) gamma zbar_j, the
 // probabilities are p_j = [x_j - tau]_+^e, e = 1/(alpha-1), where tau is the
-// root of f(tau) = sum_j [x_j - tau]_+^e - 1.  f is convex and decreasing, so
-// Newton steps started at tau0 = max_j x_j - 1 (where f >= 0) stay left of
-// the root and increase monotonically.  For e = 2 (alpha = 1.5) and e = 1
-// (alpha = 2) each step also solves f = 0 exactly on the current support
+// root of f(tau) = sum_j [x_j - tau]_+^e - 1, equivalently of
+// phi(tau) = ||[x - tau]_+||_e - 1.  phi is convex and decreasing in tau (a
+// norm, nondecreasing in each nonnegative argument, of convex decreasing
+// functions), so Newton steps on phi started at tau0 = max_j x_j - 1 (where
+// phi >= 0) stay left of the root and increase monotonically.  On a fixed
+// support phi is close to linear (exactly linear when the support's values
+// are equal), so these steps need fewer passes than Newton on f: with
+// S_e = sum y^e and S_{e-1} = sum y^(e-1) over y = [x - tau]_+, the step is
+// (S_e - S_e^(1 - 1/e)) / S_{e-1}.  For e = 2 (alpha = 1.5) and e = 1
+// (alpha = 2) each pass also solves f = 0 exactly on the current support
 // {x_j > tau}; that solution is accepted as soon as it keeps the whole
 // support above it, which makes it the (unique) root.
 #pragma once
@@ -23,6 +29,15 @@ __host__ __device__ inline int entmax_mode(float alpha) {
   if (alpha == 1.5f) return kEntmax15;
   if (alpha == 1.25f) return kEntmaxQuartic;
   return kEntmaxGeneral;
+}
+
+// Newton step on phi = (sum y^e)^(1/e) - 1 from se = sum y^e, se1 = sum y^(e-1)
+__device__ __forceinline__ float entmax_norm_step(float se, float se1, int mode, float e) {
+  float root;   // se^(1 - 1/e)
+  if (mode == kEntmax15) root = sqrtf(se);
+  else if (mode == kEntmaxQuartic) { const float r = sqrtf(se); root = r * sqrtf(r); }
+  else root = exp2f((1.f - 1.f / e) * __log2f(se));
+  return (se - root) / se1;
 }
 
 // y^e for y > 0
@@ -81,12 +96,12 @@ __device__ float entmax_tau(Get get, int n, int sub, int width, int mode, float 
         float d = (s2 - 1.f) / (s1 + sqrtf(disc));
         if (d < ymin) { tau += d; break; }
       }
-      step = (s2 - 1.f) / (2.f * s1);
+      step = entmax_norm_step(s2, s1, mode, e);
       tau += step;
       if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
     } else {
-      // Newton: f = s2 - 1, f' = -e s1  (s1 = sum y^(e-1), s2 = sum y^e)
-      step = (s2 - 1.f) / (e * s1);
+      // s1 = sum y^(e-1), s2 = sum y^e
+      step = entmax_norm_step(s2, s1, mode, e);
       tau += step;
       if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
     }
@@ -158,11 +173,11 @@ __device__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int na
         const float d = (s2 - 1.f) / (s1 + sqrtf(disc));
         if (d < ymin) { tau += d; break; }
       }
-      step = (s2 - 1.f) / (2.f * s1);
+      step = entmax_norm_step(s2, s1, mode, e);
       tau += step;
       if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
     } else {
-      step = (s2 - 1.f) / (e * s1);
+      step = entmax_norm_step(s2, s1, mode, e);
       tau += step;
       if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
     }
