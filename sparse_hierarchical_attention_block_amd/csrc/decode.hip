@@ -6,17 +6,20 @@
 // Per sequence b the new query sits at position L = cache_len[b] - 1:
 //   1. decode_scores   x[b,h,j] = (alpha-1) gamma q_h . s_j / sqrt(d) for the
 //                      cached summaries j < floor(L / bs)  (HBM scan of the
-//                      float32 summary cache, 64 blocks per workgroup)
+//                      float32 summary cache, 64 blocks per workgroup); one
+//                      more workgroup per (sequence, KV head) writes the
+//                      summary of the block the step completes, if any
+//                      (cache_len[b] % bs == 0)
 //   2. decode_route    one wave per query head finds tau; the G heads of a KV
 //                      head average p; the union is compacted into an
 //                      ascending list with log pbar per listed block
 //   3. decode_attend   split-K over the list [own block, selected blocks...],
-//                      16 entries per workgroup, 4 waves; MFMA 16x16x32 with
-//                      the G query heads as MFMA rows (padded to 16); K and V
-//                      stream from HBM straight into registers, V is
-//                      transposed 8x8 in registers
+//                      16 entries per work item, a persistent grid walking
+//                      the items, 4 waves; MFMA 16x16x32 with the G query
+//                      heads as MFMA rows (padded to 16); K and V stream from
+//                      HBM straight into registers, V is transposed 8x8 in
+//                      registers
 //   4. decode_combine  log-sum-exp merge of the splits in a fixed order
-//   5. when cache_len[b] % bs == 0 the completed block's summary is written.
 #include <atomic>
 
 #include "dash_internal.hpp"
@@ -45,6 +48,8 @@ struct DecodeArgs {
   float* logp;       // [B, Hkv, nb]  by block id
   uint32_t* bits;    // [B, H, nwords] or null
   float* part;       // [B, Hkv, n_split, G, D + 2]
+  float* summ_w;     // the summary cache, written for a block this step completes
+  const float* w_s;
   int64_t nb;
   int64_t n_split;
   int nwords;
@@ -64,12 +69,94 @@ __device__ __forceinline__ int64_t clamp_len(int32_t v, int64_t max_len) {
 // ---- 1. coarse scores ------------------------------------------------------------------------
 // One thread per cached summary j; the row is read with 16-byte loads (32
 // floats in flight per batch) and serves all G heads, whose queries sit in LDS.
+// Summary of one complete block by a 64-thread workgroup, float32 throughout:
+// column sums with 16-byte loads (thread = 16-byte column chunk x row group,
+// every load of a thread in flight together), reduced over the row groups in
+// LDS, then the projection by W_s with 16-byte loads of W_s rows (thread =
+// 4 consecutive output columns x a share of the rows), reduced again in LDS.
+// sh holds at least 9 D floats.
+template <typename T, int D>
+__device__ void summarize_block_64(const T* __restrict__ kb, int bs, const float* __restrict__ w_s,
+                                   float* __restrict__ out, float* sh) {
+  constexpr int EPV = 16 / sizeof(T);   // elements per 16-byte load
+  constexpr int CH = D / EPV;           // 16-byte chunks per key row
+  constexpr int RG = 64 / CH;           // row groups
+  const int t = threadIdx.x;
+  {
+    const int ch = t % CH, rg = t / CH;
+    float acc[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+#pragma unroll 4
+    for (int r = rg; r < bs; r += RG) {
+      const u32x4 w = *(const u32x4*)(kb + (int64_t)r * D + ch * EPV);
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_lo(ww[e]);
+          acc[2 * e + 1] += bf16_hi(ww[e]);
+        }
+      } else {
+        acc[0] += __uint_as_float(w.x);
+        acc[1] += __uint_as_float(w.y);
+        acc[2] += __uint_as_float(w.z);
+        acc[3] += __uint_as_float(w.w);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) sh[rg * D + ch * EPV + e] = acc[e];
+  }
+  __syncthreads();
+  float* mean = sh + 8 * D;
+  for (int c = t; c < D; c += 64) {
+    float sum = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < RG; ++g2) sum += sh[g2 * D + c];
+    mean[c] = sum * (1.0f / (float)bs);
+  }
+  __syncthreads();
+  constexpr int CQ = D / 4;    // column quads
+  constexpr int RP = 64 / CQ;  // row shares
+  const int cq = t % CQ, rp = t / CQ;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int r = rp; r < D; r += RP) {
+    const f32x4 wv = *(const f32x4*)(w_s + r * D + 4 * cq);
+    const float m = mean[r];
+    o.x = fmaf(m, wv.x, o.x);
+    o.y = fmaf(m, wv.y, o.y);
+    o.z = fmaf(m, wv.z, o.z);
+    o.w = fmaf(m, wv.w, o.w);
+  }
+  *(f32x4*)(sh + rp * D + 4 * cq) = o;   // sh rows < RP <= 4 do not overlap mean
+  __syncthreads();
+  for (int c = t; c < D; c += 64) {
+    float sum = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < RP; ++p2) sum += sh[p2 * D + c];
+    out[c] = sum;
+  }
+}
+
+// grid.x = ceil(ncand_max / 64) + 1: the last column of workgroups writes the
+// summary of the block this step completes, if any (cache_len[b] % bs == 0
+// completes block cache_len[b] / bs - 1); it overlaps the score scan.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_scores_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float qs[8][D];
   const int64_t bg = blockIdx.y;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
+  if (blockIdx.x == gridDim.x - 1) {
+    if (len % a.bs == 0) {
+      const int64_t j = len / a.bs - 1;
+      __shared__ __attribute__((aligned(16))) float sh[9 * D];
+      summarize_block_64<T, D>((const T*)a.kc + (bg * a.max_len + j * a.bs) * D, a.bs, a.w_s,
+                               a.summ_w + (bg * a.summ_blocks + j) * D, sh);
+    }
+    return;
+  }
   const int64_t ncand = (len - 1) >> a.bs_log;
   const int64_t j0 = (int64_t)blockIdx.x * 64;
   if (j0 >= ncand) return;
@@ -390,6 +477,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
     if (d == 0) { pr[0] = M; pr[1] = L; }
     pr[2 + d] = O;
   }
+
   __syncthreads();   // the merge buffers are reused by the next item
 }
 
@@ -504,58 +592,66 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
 }
 
 // ---- 4. combine ----------------------------------------------------------------------------
-// One workgroup per (sequence, KV head): the ns split maxima and sums of all
-// G heads are read at once into LDS, then each thread merges its outputs over
-// the splits with the loads of several splits in flight.  Fixed order in s.
+// grid (ceil(G D / 256), B Hkv): workgroup x merges outputs [256 x, 256 x + 256)
+// of the G heads x D columns of one (sequence, KV head), one output per
+// thread.  The split maxima and sums of the heads it covers are staged in LDS
+// and turned into weights exp2(m_s - M) by one thread per head; every thread
+// then reads its column of all ns splits, 16 loads in flight.  Fixed order in s.
 constexpr int kCombineThreads = 256;
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a) {
-  extern __shared__ float wts[];   // [ns][G] weights exp2(m_s - M), [ns][G] l_s, [G] 1 / L
-  const int bgi = blockIdx.x;
+  extern __shared__ float wts[];   // [HPW][ns] weights, [HPW][ns] l_s, [HPW] 1 / L
+  constexpr int HPW = kCombineThreads / D;   // heads per workgroup (D <= 256)
+  const int bgi = blockIdx.y;
   const int64_t bg = bgi;
   const int b = bgi / a.Hkv, g = bgi % a.Hkv;
   const int n_entries = 1 + a.count[bg];
   const int ns = (n_entries + kDecodeSplit - 1) / kDecodeSplit;
   const int G = a.G;
-  const int64_t stride = (int64_t)G * (D + 2);   // one split: G rows of [m, l, o(D)]
+  const int q0 = blockIdx.x * HPW;                 // first head of this workgroup
+  const int64_t stride = (int64_t)G * (D + 2);     // one split: G rows of [m, l, o(D)]
   const float* part = a.part + bg * a.n_split * stride;
-  float* ls = wts + ns * G;
-  float* inv_l = ls + ns * G;
-  for (int e = threadIdx.x; e < ns * G; e += kCombineThreads) {
-    const float* pr = part + (e / G) * stride + (e % G) * (D + 2);
-    wts[e] = pr[0];
-    ls[e] = pr[1];
+  float* ls = wts + HPW * ns;
+  float* inv_l = ls + HPW * ns;
+  for (int e = threadIdx.x; e < HPW * ns; e += kCombineThreads) {
+    const int hq = e / ns, sp = e % ns;
+    if (q0 + hq < G) {
+      const float* pr = part + sp * stride + (q0 + hq) * (D + 2);
+      wts[e] = pr[0];
+      ls[e] = pr[1];
+    }
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int qr = threadIdx.x;
+  if (threadIdx.x < HPW && q0 + (int)threadIdx.x < G) {
+    float* w = wts + threadIdx.x * ns;
+    const float* l = ls + threadIdx.x * ns;
     float M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, wts[sp * G + qr]);
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, w[sp]);
     float L = 0.f;
     for (int sp = 0; sp < ns; ++sp) {
-      const float m = wts[sp * G + qr];
-      const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-      wts[sp * G + qr] = f;
-      L += ls[sp * G + qr] * f;
+      const float f = w[sp] == -INFINITY ? 0.f : fast_exp2(w[sp] - M);
+      w[sp] = f;
+      L += l[sp] * f;
     }
-    inv_l[qr] = 1.0f / L;
+    inv_l[threadIdx.x] = 1.0f / L;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += kCombineThreads) {
-    const int qr = e / D, d = e % D;
-    const float* col = part + qr * (D + 2) + 2 + d;
-    float O = 0.f;
-    int sp = 0;
-    for (; sp + 8 <= ns; sp += 8) {
-      float v[8];
+  const int hq = threadIdx.x / D, d = threadIdx.x % D;
+  const int qr = q0 + hq;
+  if (qr >= G) return;
+  const float* col = part + qr * (D + 2) + 2 + d;
+  const float* w = wts + hq * ns;
+  float O = 0.f;
+  int sp = 0;
+  for (; sp + 16 <= ns; sp += 16) {
+    float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = col[(sp + u) * stride];
+    for (int u = 0; u < 16; ++u) v[u] = col[(sp + u) * stride];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) O += v[u] * wts[(sp + u) * G + qr];
-    }
-    for (; sp < ns; ++sp) O += col[sp * stride] * wts[sp * G + qr];
-    ((T*)a.o)[((int64_t)b * a.H + g * G + qr) * D + d] = from_f32<T>(O * inv_l[qr]);
+    for (int u = 0; u < 16; ++u) O += v[u] * w[sp + u];
   }
+  for (; sp < ns; ++sp) O += col[sp * stride] * w[sp];
+  ((T*)a.o)[((int64_t)b * a.H + g * G + qr) * D + d] = from_f32<T>(O * inv_l[hq]);
 }
 
 // Workgroups of decode_attend_bf16_kernel<D> resident on the current device at
@@ -616,6 +712,8 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   a.logp = rb.sel_logp ? rb.sel_logp : (float*)(ws + L.off_logp);
   a.bits = rb.support_bits;
   a.part = (float*)(ws + L.off_part);
+  a.summ_w = summ;
+  a.w_s = w_s;
   a.nb = L.nb;
   a.n_split = L.n_split;
   a.nwords = (int)((L.nb + 31) / 32);
@@ -633,7 +731,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   const unsigned nbg = (unsigned)(s.B * s.Hkv);
 
   if (L.ncand_max > 0) {
-    dim3 g1((unsigned)((L.ncand_max + 63) / 64), nbg);
+    dim3 g1((unsigned)((L.ncand_max + 63) / 64 + 1), nbg);
 #define DASH_DS(T, D) hipLaunchKernelGGL((decode_scores_kernel<T, D>), g1, dim3(64), 0, st, a)
     if (bf16) { if (s.d == 64) DASH_DS(__bf16, 64); else DASH_DS(__bf16, 128); }
     else { if (s.d == 64) DASH_DS(float, 64); else DASH_DS(float, 128); }
@@ -674,8 +772,9 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
     if (s.d == 64) hipLaunchKernelGGL(decode_attend_f32_kernel<64>, g3, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(decode_attend_f32_kernel<128>, g3, dim3(256), 0, st, a);
   }
-  dim3 g4(nbg);
-  const size_t lds4 = sizeof(float) * (2 * L.n_split + 1) * s.G;
+  const int hpw = kCombineThreads / s.d;
+  dim3 g4((unsigned)((s.G + hpw - 1) / hpw), nbg);
+  const size_t lds4 = sizeof(float) * (2 * L.n_split + 1) * hpw;
 #define DASH_DC(T, D) \
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), g4, dim3(kCombineThreads), lds4, st, a)
   if (bf16) { if (s.d == 64) DASH_DC(__bf16, 64); else DASH_DC(__bf16, 128); }
@@ -683,6 +782,8 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
 #undef DASH_DC
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // with candidates the score kernel wrote the completed block's summary
+  if (L.ncand_max > 0) return hipSuccess;
   return launch_summarize_completed(s, kc, max_len, cache_len, w_s, summ, summ_blocks, st);
 }
 
