@@ -46,7 +46,7 @@ DecodeLayout decode_layout(const Shape& s, int64_t max_len);
 #define DASH_ROUTE_X_BUDGET (80 * 1024)
 #endif
 
-constexpr int kDecodeSplit = 16;   // list entries (blocks) per split
+constexpr int kDecodeSplit = 32;   // list entries (blocks) per split (8 per wave)
 constexpr int kDecodeMaxBg = 8192; // sequences x KV heads of one bf16 decode call
 constexpr int kMaxDevices = 64;    // per-device launch-shape caches
 

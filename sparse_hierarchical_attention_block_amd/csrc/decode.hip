@@ -14,7 +14,7 @@
 //                      head average p; the union is compacted into an
 //                      ascending list with log pbar per listed block
 //   3. decode_attend   split-K over the list [own block, selected blocks...],
-//                      16 entries per work item, a persistent grid walking
+//                      32 entries per work item, a persistent grid walking
 //                      the items, 4 waves; MFMA 16x16x32 with the G query
 //                      heads as MFMA rows (padded to 16); K and V stream from
 //                      HBM straight into registers, V is transposed 8x8 in
