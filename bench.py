@@ -71,9 +71,10 @@ def events_time(fn, steps, warmup, torch):
     return start.elapsed_time(end) / steps
 
 
-def traffic_for_attend():
+def traffic_for_attend(workload):
     """HBM bytes per attend launch from the committed counter summary, or None
-    when the kernel source changed since the counters were taken."""
+    when the counters were taken on another workload or the kernel source
+    changed since they were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -82,7 +83,7 @@ def traffic_for_attend():
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
     src = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()
-    if kv.get("attend_hip_sha256") != src:
+    if kv.get("attend_hip_sha256") != src or kv.get("workload") != workload:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -132,7 +133,7 @@ def prefill_bench(args, torch, dash, W):
     dense_chunks = float(B * Hkv) * (cand * cpb + own_chunks).sum()
     tile_union_density = float((count + 1).sum() / (B * Hkv * (cand + 1).sum()))
     achieved = att_flops / (t_att * 1e-3) / 1e12
-    traffic = traffic_for_attend()
+    traffic = traffic_for_attend(w.name)
     res = {
         "workload": w, "ms_step": ms_step, "tok_s": B * N / (ms_step * 1e-3),
         "stages_ms": {"summarize": t_sum, "route": t_route, "attend": t_att},
