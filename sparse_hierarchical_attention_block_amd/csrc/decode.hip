@@ -4,33 +4,34 @@
 // summary, Stage 0 and Contributions).
 //
 // Per sequence b the new query sits at position L = cache_len[b] - 1:
-//   1. decode_scores   x[b,h,j] = (alpha-1) gamma q_h . s_j / sqrt(d) for the
-//                      cached summaries j < floor(L / bs)  (HBM scan of the
-//                      float32 summary cache, 64 blocks per workgroup); one
-//                      more workgroup per (sequence, KV head) writes the
-//                      summary of the block the step completes, if any
-//                      (cache_len[b] % bs == 0)
-//   2. decode_route    one wave per query head finds tau; the G heads of a KV
+//   1. scores          x[b,h,j] = (alpha-1) gamma q_h . s_j / sqrt(d) for the
+//                      cached summaries j < floor(L / bs): a coalesced scan of
+//                      the float32 summary cache with MFMA 4x4x1 f32
+//   2. route           one wave per query head finds tau; the G heads of a KV
 //                      head average p; the union is compacted into an
 //                      ascending list with log pbar per listed block
+//      (1 and 2 run as one kernel, decode_select, when there are enough
+//      (sequence, KV head) pairs to fill the GPU with one workgroup each;
+//      otherwise as decode_scores + decode_route)
 //   3. decode_attend   split-K over the list [own block, selected blocks...],
 //                      32 entries per work item, a persistent grid walking
 //                      the items, 4 waves; MFMA 16x16x32 with the G query
 //                      heads as MFMA rows (padded to 16); K and V stream from
 //                      HBM straight into registers, V is transposed 8x8 in
 //                      registers
-//   4. decode_combine  log-sum-exp merge of the splits in a fixed order
+//   4. decode_combine  log-sum-exp merge of the splits in a fixed order; one
+//                      more workgroup per (sequence, KV head) writes the
+//                      summary of the block the step completes, if any
+//                      (cache_len[b] % bs == 0), off the critical path
 #include <atomic>
+#include <type_traits>
 
 #include "dash_internal.hpp"
 #include "device_common.hpp"
 #include "entmax_device.hpp"
+#include "summarize_device.hpp"
 
 namespace dash {
-
-hipError_t launch_summarize_completed(const Shape& s, const void* kc, int64_t max_len,
-                                      const int32_t* cache_len, const float* w_s, float* summ,
-                                      int64_t summ_blocks, hipStream_t st);
 
 struct DecodeArgs {
   const void* q;
@@ -55,6 +56,7 @@ struct DecodeArgs {
   int nwords;
   int H, Hkv, G, bs, B;
   int bs_log;        // log2(bs)
+  int xpitch;        // fused score/route kernel: LDS row pitch of the scores
   int mode;
   float e, scale, scale_log2;
 };
@@ -67,137 +69,203 @@ __device__ __forceinline__ int64_t clamp_len(int32_t v, int64_t max_len) {
 }
 
 // ---- 1. coarse scores ------------------------------------------------------------------------
-// One thread per cached summary j; the row is read with 16-byte loads (32
-// floats in flight per batch) and serves all G heads, whose queries sit in LDS.
-// Summary of one complete block by a 64-thread workgroup, float32 throughout:
-// column sums with 16-byte loads (thread = 16-byte column chunk x row group,
-// every load of a thread in flight together), reduced over the row groups in
-// LDS, then the projection by W_s with 16-byte loads of W_s rows (thread =
-// 4 consecutive output columns x a share of the rows), reduced again in LDS.
-// sh holds at least 9 D floats.
-template <typename T, int D>
-__device__ void summarize_block_64(const T* __restrict__ kb, int bs, const float* __restrict__ w_s,
-                                   float* __restrict__ out, float* sh) {
-  constexpr int EPV = 16 / sizeof(T);   // elements per 16-byte load
-  constexpr int CH = D / EPV;           // 16-byte chunks per key row
-  constexpr int RG = 64 / CH;           // row groups
-  const int t = threadIdx.x;
+// x[h][j] = scale * q_h . s_j over the float32 summary rows of one (sequence,
+// KV head), in groups of 16 rows.  Lane l = 16 rq + 4 ks + m loads row
+// 4 rq + m of a group, floats 16 u + 4 ks + [0, 4) for u < D / 16, so one
+// load instruction covers 16 rows x 64 contiguous bytes.  MFMA 4x4x1 f32
+// block (rq, ks) multiplies these rows by the heads 4 hs + m of head set hs
+// (B operand from the same lane) over that d slice; two row rotations add
+// the four ks partial sums, after which lane (rq, 0, m) holds x of rows
+// 4 rq + i, head 4 hs + m in element i.  The wave takes groups g_first,
+// g_first + g_step, ... < g_end, NG of them in flight; x of row j, head h
+// goes to out[h * pitch + j] (rows < ncand only).
+template <typename T, int D, int NG>
+__device__ __forceinline__ void score_groups(const DecodeArgs& a, int64_t bg, int64_t row0,
+                                             int ncand, int g_first, int g_step, int g_end,
+                                             float* out, int64_t pitch) {
+  constexpr int NU = D / 16;
+  constexpr bool kBf16 = sizeof(T) == 2;
+  const int lane = threadIdx.x % kWave;
+  const int rq = lane >> 4, ks = (lane >> 2) & 3, m = lane & 3;
+  const int G = a.G;
+  // B operand q[head 4 hs + m][16 u + 4 ks + t]; heads >= G fall outside the
+  // resource and read as zeros.  bf16 stays packed until use.
+  typedef typename std::conditional<kBf16, u32x2, f32x4>::type QW;
+  QW qw[2][NU];
   {
-    const int ch = t % CH, rg = t / CH;
-    float acc[EPV];
+    const buf_rsrc rq_ = make_rsrc((const T*)a.q + row0 * D, (uint32_t)(G * D * sizeof(T)));
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
-#pragma unroll 4
-    for (int r = rg; r < bs; r += RG) {
-      const u32x4 w = *(const u32x4*)(kb + (int64_t)r * D + ch * EPV);
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16_lo(ww[e]);
-          acc[2 * e + 1] += bf16_hi(ww[e]);
+      for (int u = 0; u < NU; ++u) {
+        const uint32_t off = (uint32_t)(((4 * hs + m) * D + 16 * u + 4 * ks) * sizeof(T));
+        if constexpr (kBf16) qw[hs][u] = buf_load8(rq_, off);
+        else qw[hs][u] = __builtin_bit_cast(f32x4, buf_load16(rq_, off));
+      }
+  }
+  const buf_rsrc rs = make_rsrc(a.summ + bg * a.summ_blocks * D, (uint32_t)(ncand * D * 4));
+  for (int g0 = g_first; g0 < g_end; g0 += g_step * NG) {
+    // rows past ncand read as zeros; their scores are never stored
+    f32x4 sv[NG][NU];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const uint32_t r = (uint32_t)(16 * (g0 + g_step * gi) + 4 * rq + m);
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        sv[gi][u] = __builtin_bit_cast(f32x4, buf_load16(rs, (r * D + 16 * u + 4 * ks) * 4));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      if (hs * 4 >= G) break;
+      f32x4 acc[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) acc[gi] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        float qf[4];
+        if constexpr (kBf16) {
+          qf[0] = bf16_lo(qw[hs][u].x); qf[1] = bf16_hi(qw[hs][u].x);
+          qf[2] = bf16_lo(qw[hs][u].y); qf[3] = bf16_hi(qw[hs][u].y);
+        } else {
+          qf[0] = qw[hs][u].x; qf[1] = qw[hs][u].y; qf[2] = qw[hs][u].z; qf[3] = qw[hs][u].w;
         }
-      } else {
-        acc[0] += __uint_as_float(w.x);
-        acc[1] += __uint_as_float(w.y);
-        acc[2] += __uint_as_float(w.z);
-        acc[3] += __uint_as_float(w.w);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          acc[gi] = mfma4x4(sv[gi][u].x, qf[0], acc[gi]);
+          acc[gi] = mfma4x4(sv[gi][u].y, qf[1], acc[gi]);
+          acc[gi] = mfma4x4(sv[gi][u].z, qf[2], acc[gi]);
+          acc[gi] = mfma4x4(sv[gi][u].w, qf[3], acc[gi]);
+        }
+      }
+      const int head = 4 * hs + m;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[gi][t] += row_ror<8>(acc[gi][t]);
+          acc[gi][t] += row_ror<4>(acc[gi][t]);
+        }
+        const int j0 = 16 * (g0 + g_step * gi) + 4 * rq;
+        if (g0 + g_step * gi < g_end && ks == 0 && head < G) {
+          float* o = out + head * pitch + j0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (j0 + t < ncand) o[t] = acc[gi][t] * a.scale;
+        }
       }
     }
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) sh[rg * D + ch * EPV + e] = acc[e];
-  }
-  __syncthreads();
-  float* mean = sh + 8 * D;
-  for (int c = t; c < D; c += 64) {
-    float sum = 0.f;
-#pragma unroll
-    for (int g2 = 0; g2 < RG; ++g2) sum += sh[g2 * D + c];
-    mean[c] = sum * (1.0f / (float)bs);
-  }
-  __syncthreads();
-  constexpr int CQ = D / 4;    // column quads
-  constexpr int RP = 64 / CQ;  // row shares
-  const int cq = t % CQ, rp = t / CQ;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int r = rp; r < D; r += RP) {
-    const f32x4 wv = *(const f32x4*)(w_s + r * D + 4 * cq);
-    const float m = mean[r];
-    o.x = fmaf(m, wv.x, o.x);
-    o.y = fmaf(m, wv.y, o.y);
-    o.z = fmaf(m, wv.z, o.z);
-    o.w = fmaf(m, wv.w, o.w);
-  }
-  *(f32x4*)(sh + rp * D + 4 * cq) = o;   // sh rows < RP <= 4 do not overlap mean
-  __syncthreads();
-  for (int c = t; c < D; c += 64) {
-    float sum = 0.f;
-#pragma unroll
-    for (int p2 = 0; p2 < RP; ++p2) sum += sh[p2 * D + c];
-    out[c] = sum;
   }
 }
 
-// grid.x = ceil(ncand_max / 64) + 1: the last column of workgroups writes the
-// summary of the block this step completes, if any (cache_len[b] % bs == 0
-// completes block cache_len[b] / bs - 1); it overlaps the score scan.
+// Score kernel for the two-kernel path: grid (ceil(ncand_max / 256), B Hkv),
+// 4 waves x 4 groups = 256 rows per workgroup.
+constexpr int kScoreThreads = 256;
+constexpr int kScoreGroups = 4;
+constexpr int kScoreRows = kScoreThreads / kWave * kScoreGroups * 16;
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_scores_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) float qs[8][D];
+__global__ __launch_bounds__(kScoreThreads) void decode_scores_kernel(DecodeArgs a) {
   const int64_t bg = blockIdx.y;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
-  if (blockIdx.x == gridDim.x - 1) {
-    if (len % a.bs == 0) {
-      const int64_t j = len / a.bs - 1;
-      __shared__ __attribute__((aligned(16))) float sh[9 * D];
-      summarize_block_64<T, D>((const T*)a.kc + (bg * a.max_len + j * a.bs) * D, a.bs, a.w_s,
-                               a.summ_w + (bg * a.summ_blocks + j) * D, sh);
-    }
-    return;
-  }
-  const int64_t ncand = (len - 1) >> a.bs_log;
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
-  if (j0 >= ncand) return;
-  const T* qb = (const T*)a.q + ((int64_t)b * a.H + g * a.G) * D;
-  for (int e = threadIdx.x; e < a.G * D; e += 64) qs[e / D][e % D] = to_f32(qb[e]);
-  __syncthreads();
-  const int64_t j = j0 + threadIdx.x;
-  if (j >= ncand) return;
-  const float* srow = a.summ + (bg * a.summ_blocks + j) * D;
-  float acc[8];
-#pragma unroll
-  for (int h = 0; h < 8; ++h) acc[h] = 0.f;
-#pragma unroll
-  for (int c0 = 0; c0 < D; c0 += 32) {
-    f32x4 sv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = *(const f32x4*)(srow + c0 + 4 * i);
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      if (h < a.G) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const f32x4 qv = *(const f32x4*)(&qs[h][c0 + 4 * i]);
-          acc[h] = fmaf(qv.x, sv[i].x, acc[h]);
-          acc[h] = fmaf(qv.y, sv[i].y, acc[h]);
-          acc[h] = fmaf(qv.z, sv[i].z, acc[h]);
-          acc[h] = fmaf(qv.w, sv[i].w, acc[h]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < 8; ++h)
-    if (h < a.G) a.x[((int64_t)b * a.H + g * a.G + h) * a.nb + j] = acc[h] * a.scale;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int ncand = (int)((len - 1) >> a.bs_log);
+  const int gb = blockIdx.x * (kScoreRows / 16);
+  const int ge = min((ncand + 15) >> 4, gb + kScoreRows / 16);
+  if (gb >= ge) return;
+  const int64_t row0 = (int64_t)b * a.H + g * a.G;
+  score_groups<T, D, kScoreGroups>(a, bg, row0, ncand, gb + wave, kScoreThreads / kWave, ge,
+                                   a.x + row0 * a.nb, a.nb);
 }
 
 // ---- 2. threshold, GQA average, union, compaction ------------------------------------------
+constexpr int kMaxRouteWaves = 8;   // routing workgroups have at most 512 threads
+
+// Row of query head `row` with no candidate: tau is NaN, no support bit set.
+__device__ __forceinline__ void route_row_empty(const DecodeArgs& a, int64_t row) {
+  const int lane = threadIdx.x % kWave;
+  if (lane == 0) a.tau[row] = __builtin_nanf("");
+  if (a.bits)
+    for (int w = lane; w < a.nwords; w += kWave) a.bits[row * a.nwords + w] = 0u;
+}
+
+// One wave: tau of a row whose candidates sit in registers (candidate j in
+// lane j % 64, slot j / 64; -inf past ncand), the support bits, and the
+// probabilities [x - tau]_+^e into prow[0, ncand).
+template <int VPL, int MODE>
+__device__ __forceinline__ void route_row_reg(const DecodeArgs& a, int64_t row, int ncand,
+                                              float (&xv)[VPL], float* prow) {
+  const int lane = threadIdx.x % kWave;
+  const int nact4 = (ncand + 4 * kWave - 1) / (4 * kWave);
+  const float tau = entmax_tau_reg<VPL, MODE>(xv, WaveReduce{}, a.e, nact4);
+  if (lane == 0) a.tau[row] = tau;
+  if (a.bits) {
+    // candidate j = 64 i + lane sits in bit lane of the ballot of slot i
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const uint64_t m = __ballot(xv[i] > tau);   // -inf slots never pass
+      if (lane == 0) {
+        if (2 * i < a.nwords) a.bits[row * a.nwords + 2 * i] = (uint32_t)m;
+        if (2 * i + 1 < a.nwords) a.bits[row * a.nwords + 2 * i + 1] = (uint32_t)(m >> 32);
+      }
+    }
+    for (int w = 2 * VPL + lane; w < a.nwords; w += kWave) a.bits[row * a.nwords + w] = 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = lane + kWave * i;
+    const float y = xv[i] - tau;
+    if (j < ncand) prow[j] = y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
+  }
+}
+
+// All threads of the workgroup, after the G rows of probabilities are in
+// Ps[h * pitch + j]: pbar = mean over the heads, log pbar per candidate, and
+// the ascending list of blocks with pbar > 0.  Wave w owns a contiguous range
+// of candidates (a multiple of 64): it counts its blocks, the counts are
+// prefixed across waves, and each wave writes its part of the list.
+__device__ __forceinline__ void route_union(const DecodeArgs& a, int64_t bg, int ncand, float* Ps,
+                                            int pitch) {
+  __shared__ int wcount[kMaxRouteWaves];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  const int span = (ncand + nw * kWave - 1) / (nw * kWave) * kWave;
+  const int jb = wave * span, je = min(ncand, jb + span);
+  const float invG = 1.0f / (float)a.G;
+  int cnt = 0;
+  for (int j0 = jb; j0 < je; j0 += kWave) {
+    const int j = j0 + lane;
+    float pb = 0.f;
+    if (j < je) {
+      for (int h = 0; h < a.G; ++h) pb += Ps[h * pitch + j];
+      pb *= invG;
+      a.logp[bg * a.nb + j] = pb > 0.f ? __logf(pb) : -INFINITY;
+      Ps[j] = pb;   // column j is only touched by this lane
+    }
+    cnt += __popcll(__ballot(pb > 0.f));
+  }
+  if (lane == 0) wcount[wave] = cnt;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int c = wcount[w];
+    base += w < wave ? c : 0;
+    total += c;
+  }
+  for (int j0 = jb; j0 < je; j0 += kWave) {
+    const int j = j0 + lane;
+    const bool f = j < je && Ps[j] > 0.f;
+    const uint64_t mask = __ballot(f);
+    if (f) a.idx[bg * a.nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
+    base += __popcll(mask);
+  }
+  if (threadIdx.x == 0) a.count[bg] = total;
+}
+
 // One workgroup per (sequence, KV head), one wave per query head.  With VPL > 0
-// the wave keeps its row of scores in registers (VPL per lane, candidate j in
-// lane j % 64, slot j / 64) and solves for tau there (MODE: entmax_mode of
-// alpha); VPL = 0 walks the row in memory for lists longer than 64 * 32.
+// the wave keeps its row of scores in registers (VPL per lane) and solves for
+// tau there (MODE: entmax_mode of alpha); VPL = 0 walks the row in memory for
+// lists longer than 64 * 32.
 template <int VPL, int MODE>
 __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
   extern __shared__ float Ps[];   // [G][nb]
@@ -209,9 +277,7 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
   const int64_t row = (int64_t)b * a.H + g * a.G + hh;
   const float* xr = a.x + row * a.nb;
   if (ncand == 0) {
-    if (lane == 0) a.tau[row] = __builtin_nanf("");
-    if (a.bits)
-      for (int w = lane; w < a.nwords; w += kWave) a.bits[row * a.nwords + w] = 0u;
+    route_row_empty(a, row);
     if (threadIdx.x == 0) a.count[bg] = 0;
     return;
   }
@@ -222,27 +288,7 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
       const int j = lane + kWave * i;
       xv[i] = j < ncand ? xr[j] : -INFINITY;
     }
-    const int nact4 = (ncand + 4 * kWave - 1) / (4 * kWave);
-    const float tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{kWave}, a.e, nact4);
-    if (lane == 0) a.tau[row] = tau;
-    if (a.bits) {
-      // candidate j = 64 i + lane sits in bit lane of the ballot of slot i
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const uint64_t m = __ballot(xv[i] > tau);   // -inf slots never pass
-        if (lane == 0) {
-          if (2 * i < a.nwords) a.bits[row * a.nwords + 2 * i] = (uint32_t)m;
-          if (2 * i + 1 < a.nwords) a.bits[row * a.nwords + 2 * i + 1] = (uint32_t)(m >> 32);
-        }
-      }
-      for (int w = 2 * VPL + lane; w < a.nwords; w += kWave) a.bits[row * a.nwords + w] = 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int j = lane + kWave * i;
-      const float y = xv[i] - tau;
-      if (j < ncand) Ps[hh * a.nb + j] = y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
-    }
+    route_row_reg<VPL, MODE>(a, row, ncand, xv, Ps + hh * a.nb);
   } else {
     const float tau = entmax_tau([&](int j) { return xr[j]; }, ncand, lane, kWave, a.mode, a.e);
     if (lane == 0) a.tau[row] = tau;
@@ -261,26 +307,55 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  const float invG = 1.0f / (float)a.G;
-  for (int j = threadIdx.x; j < ncand; j += blockDim.x) {
-    float pb = 0.f;
-    for (int h = 0; h < a.G; ++h) pb += Ps[h * a.nb + j];
-    pb *= invG;
-    a.logp[bg * a.nb + j] = pb > 0.f ? __logf(pb) : -INFINITY;
-    Ps[j] = pb;   // column j is only touched by this thread
+  route_union(a, bg, ncand, Ps, (int)a.nb);
+}
+
+// ---- 1+2 fused (bf16): scores and routing of one (sequence, KV head) per workgroup ----------
+// For many (sequence, KV head) pairs with rows of at most 2048 candidates.
+// The scores go to LDS instead of HBM and the routing needs no second launch:
+// 8 waves scan the summaries (score_groups), then wave h < G finds tau of
+// head h in registers, and the workgroup forms pbar, log pbar and the block
+// list.
+constexpr int kSelectThreads = 512;
+constexpr int kSelectWaves = kSelectThreads / kWave;
+constexpr int kSelectGroups = 4;
+#ifndef DASH_SELECT_MIN_PAIRS
+#define DASH_SELECT_MIN_PAIRS 128
+#endif
+constexpr int kSelectMinPairs = DASH_SELECT_MIN_PAIRS;
+
+template <int D, int VPL, int MODE>
+__global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];   // [G][xpitch] x, then p
+  const int pitch = a.xpitch;
+  const int64_t bg = blockIdx.x;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int G = a.G;
+  const int64_t len = clamp_len(a.cache_len[b], a.max_len);
+  const int ncand = (int)((len - 1) >> a.bs_log);
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t row0 = (int64_t)b * a.H + g * G;
+  if (ncand == 0) {
+    if (wave < G) route_row_empty(a, row0 + wave);
+    if (threadIdx.x == 0) a.count[bg] = 0;
+    return;
+  }
+  score_groups<__bf16, D, kSelectGroups>(a, bg, row0, ncand, wave, kSelectWaves,
+                                         (ncand + 15) >> 4, xs, pitch);
+  __syncthreads();
+  if (wave < G) {
+    float* prow = xs + wave * pitch;
+    float xv[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int j = lane + kWave * i;
+      xv[i] = j < ncand ? prow[j] : -INFINITY;
+    }
+    route_row_reg<VPL, MODE>(a, row0 + wave, ncand, xv, prow);
   }
   __syncthreads();
-  if (threadIdx.x < kWave) {
-    int base = 0;
-    for (int j0 = 0; j0 < ncand; j0 += kWave) {
-      const int j = j0 + lane;
-      const bool f = j < ncand && Ps[j] > 0.f;
-      const uint64_t mask = __ballot(f);
-      if (f) a.idx[bg * a.nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
-      base += __popcll(mask);
-    }
-    if (lane == 0) a.count[bg] = base;
-  }
+  route_union(a, bg, ncand, xs, pitch);
 }
 
 // ---- 3. split-K attend (bf16, MFMA) ----------------------------------------------------------
@@ -602,9 +677,21 @@ template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a) {
   extern __shared__ float wts[];   // [HPW][ns] weights, [HPW][ns] l_s, [HPW] 1 / L
   constexpr int HPW = kCombineThreads / D;   // heads per workgroup (D <= 256)
+  static_assert(kCombineThreads == kSumThreads, "summary column runs summarize_blocks");
   const int bgi = blockIdx.y;
   const int64_t bg = bgi;
   const int b = bgi / a.Hkv, g = bgi % a.Hkv;
+  if (blockIdx.x == gridDim.x - 1) {
+    // the step that makes cache_len[b] a multiple of bs completes block
+    // cache_len[b] / bs - 1: its summary, for the next steps' routing
+    const int64_t len = clamp_len(a.cache_len[b], a.max_len);
+    if ((len & (a.bs - 1)) == 0) {
+      const int64_t j = (len >> a.bs_log) - 1;
+      summarize_blocks<T, D, 1>((const T*)a.kc + (bg * a.max_len + j * a.bs) * D, 1, a.bs, a.w_s,
+                                a.summ_w + (bg * a.summ_blocks + j) * D);
+    }
+    return;
+  }
   const int n_entries = 1 + a.count[bg];
   const int ns = (n_entries + kDecodeSplit - 1) / kDecodeSplit;
   const int G = a.G;
@@ -697,6 +784,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
                          int64_t summ_blocks, void* o, const dash_route_buf& rb,
                          const DecodeLayout& L, char* ws, hipStream_t st) {
   DecodeArgs a;
+  a.xpitch = 0;
   a.q = q;
   a.kc = kc;
   a.vc = vc;
@@ -730,19 +818,46 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   const bool bf16 = s.dtype == DASH_BF16;
   const unsigned nbg = (unsigned)(s.B * s.Hkv);
 
-  if (L.ncand_max > 0) {
-    dim3 g1((unsigned)((L.ncand_max + 63) / 64 + 1), nbg);
-#define DASH_DS(T, D) hipLaunchKernelGGL((decode_scores_kernel<T, D>), g1, dim3(64), 0, st, a)
-    if (bf16) { if (s.d == 64) DASH_DS(__bf16, 64); else DASH_DS(__bf16, 128); }
-    else { if (s.d == 64) DASH_DS(float, 64); else DASH_DS(float, 128); }
+  // rows of up to 64 * VPL candidates stay in registers
+  const int64_t nc = L.ncand_max;
+  const int vpl = nc <= 256 ? 4 : nc <= 512 ? 8 : nc <= 1024 ? 16 : nc <= 2048 ? 32 : 0;
+  const int mode = entmax_mode(s.alpha);
+  // one fused workgroup per (sequence, KV head) only keeps the GPU's memory
+  // system busy with enough of them; otherwise the scan is spread over
+  // ceil(ncand / 256) workgroups per pair and routed by a second kernel
+  const bool fused = bf16 && vpl > 0 && (int64_t)nbg >= kSelectMinPairs;
+  if (fused) {
+    a.xpitch = (int)((nc + 15) / 16 * 16);
+    const size_t lds_sel = sizeof(float) * (size_t)s.G * a.xpitch;
+    const void* fn = nullptr;
+#define DASH_SK(D, V)                                                                        \
+  fn = mode == kSparsemax       ? (const void*)decode_select_kernel<D, V, kSparsemax>        \
+       : mode == kEntmax15      ? (const void*)decode_select_kernel<D, V, kEntmax15>         \
+       : mode == kEntmaxQuartic ? (const void*)decode_select_kernel<D, V, kEntmaxQuartic>    \
+                                : (const void*)decode_select_kernel<D, V, kEntmaxGeneral>
+#define DASH_SKD(D)                                                                          \
+  do {                                                                                       \
+    if (vpl == 4) DASH_SK(D, 4); else if (vpl == 8) DASH_SK(D, 8);                           \
+    else if (vpl == 16) DASH_SK(D, 16); else DASH_SK(D, 32);                                 \
+  } while (0)
+    if (s.d == 64) DASH_SKD(64); else DASH_SKD(128);
+#undef DASH_SKD
+#undef DASH_SK
+    if (lds_sel > 64 * 1024)
+      (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_sel);
+    void* kargs[] = {&a};
+    hipError_t e1 = hipLaunchKernel(fn, dim3(nbg), dim3(kSelectThreads), kargs, lds_sel, st);
+    if (e1 != hipSuccess) return e1;
+  } else {
+    if (L.ncand_max > 0) {
+      dim3 g1((unsigned)((L.ncand_max + kScoreRows - 1) / kScoreRows), nbg);
+#define DASH_DS(T, D) \
+  hipLaunchKernelGGL((decode_scores_kernel<T, D>), g1, dim3(kScoreThreads), 0, st, a)
+      if (bf16) { if (s.d == 64) DASH_DS(__bf16, 64); else DASH_DS(__bf16, 128); }
+      else { if (s.d == 64) DASH_DS(float, 64); else DASH_DS(float, 128); }
 #undef DASH_DS
-  }
-  const size_t lds = sizeof(float) * s.G * L.nb;
-  {
-    // rows of up to 64 * VPL candidates stay in registers
-    const int64_t nc = L.ncand_max;
-    const int vpl = nc <= 256 ? 4 : nc <= 512 ? 8 : nc <= 1024 ? 16 : nc <= 2048 ? 32 : 0;
-    const int mode = entmax_mode(s.alpha);
+    }
+    const size_t lds = sizeof(float) * s.G * L.nb;
     const void* fn = (const void*)decode_route_kernel<0, kEntmaxGeneral>;
 #define DASH_RK(V)                                                                    \
   fn = mode == kSparsemax       ? (const void*)decode_route_kernel<V, kSparsemax>     \
@@ -773,7 +888,8 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
     else hipLaunchKernelGGL(decode_attend_f32_kernel<128>, g3, dim3(256), 0, st, a);
   }
   const int hpw = kCombineThreads / s.d;
-  dim3 g4((unsigned)((s.G + hpw - 1) / hpw), nbg);
+  // one more column of workgroups writes the completed blocks' summaries
+  dim3 g4((unsigned)((s.G + hpw - 1) / hpw + 1), nbg);
   const size_t lds4 = sizeof(float) * (2 * L.n_split + 1) * hpw;
 #define DASH_DC(T, D) \
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), g4, dim3(kCombineThreads), lds4, st, a)
@@ -782,9 +898,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
 #undef DASH_DC
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // with candidates the score kernel wrote the completed block's summary
-  if (L.ncand_max > 0) return hipSuccess;
-  return launch_summarize_completed(s, kc, max_len, cache_len, w_s, summ, summ_blocks, st);
+  return hipSuccess;
 }
 
 }  // namespace dash

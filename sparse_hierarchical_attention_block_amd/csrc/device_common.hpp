@@ -89,6 +89,32 @@ __device__ __forceinline__ float wave_min(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
   return v;
 }
+// Wave-wide reductions on DPP instead of LDS permutes: within each row of 16
+// lanes (quad_perm 1,0,3,2 and 2,3,0,1, then half-row and row mirrors every
+// lane holds its row's result), then row 0 into row 1 and row 2 into row 3
+// (row_bcast:15), then lane 31 into rows 2 and 3 (row_bcast:31); lane 63 ends
+// with the whole wave's result, which every lane reads.  Fixed order: all
+// lanes get the same bits.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_src(float v, float old) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_dpp(float v, Op op, float ident) {
+  v = op(v, dpp_src<0xB1>(v, ident));         // quad_perm [1,0,3,2]
+  v = op(v, dpp_src<0x4E>(v, ident));         // quad_perm [2,3,0,1]
+  v = op(v, dpp_src<0x141>(v, ident));        // row_half_mirror
+  v = op(v, dpp_src<0x140>(v, ident));        // row_mirror
+  v = op(v, dpp_src<0x142, 0xA>(v, ident));   // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_src<0x143, 0xC>(v, ident));   // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+struct DppAdd { __device__ float operator()(float x, float y) const { return x + y; } };
+struct DppMax { __device__ float operator()(float x, float y) const { return fmaxf(x, y); } };
+struct DppMin { __device__ float operator()(float x, float y) const { return fminf(x, y); } };
+
 // reductions over aligned groups of `width` lanes (width a power of two <= 64)
 __device__ __forceinline__ float group_sum(float v, int width) {
   for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -103,6 +129,14 @@ __device__ __forceinline__ float group_min(float v, int width) {
   return v;
 }
 
+// value of lane (l + N) mod 16 within lane l's row of 16 lanes (DPP row_ror);
+// summing v, ror 8 and then ror 4 adds up the four lanes l mod 4 + 4 i of a row
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, false));
+}
+
 // ---- MFMA (gfx950) ------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, C 16x16.  Lane l holds row
 // (l % 16) of A / column (l % 16) of B with k = 8 * (l / 16) + [0, 8), and
@@ -115,6 +149,13 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32] in element i.
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_4x4x1_16b_f32: 16 independent 4x4 products with k = 1.  Block
+// b = l / 4; lane l holds A_b[l % 4] and B_b[l % 4], and C_b[i][l % 4] in
+// element i.
+__device__ __forceinline__ f32x4 mfma4x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -116,6 +116,11 @@ struct GroupReduce {   // `width` consecutive lanes
   __device__ float max(float v) const { return group_max(v, width); }
   __device__ float min(float v) const { return group_min(v, width); }
 };
+struct WaveReduce {   // all 64 lanes of the wave (DPP)
+  __device__ float sum(float v) const { return wave_reduce_dpp(v, DppAdd{}, 0.f); }
+  __device__ float max(float v) const { return wave_reduce_dpp(v, DppMax{}, -INFINITY); }
+  __device__ float min(float v) const { return wave_reduce_dpp(v, DppMin{}, INFINITY); }
+};
 struct Stride16Reduce {   // lanes l, l^16, l^32, l^48 (one MFMA 16x16 C-fragment row)
   __device__ float sum(float v) const {
     v += __shfl_xor(v, 16, kWave);

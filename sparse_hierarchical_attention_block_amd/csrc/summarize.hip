@@ -29,22 +29,6 @@ __global__ __launch_bounds__(kSumThreads) void summarize_kernel(
                                  summ + (bg * summ_blocks + j) * D);
 }
 
-// Decode: the step that makes cache_len[b] a multiple of bs completes block
-// cache_len[b] / bs - 1; grid.x = B * Hkv.
-template <typename T, int D>
-__global__ __launch_bounds__(kSumThreads) void summarize_completed_kernel(
-    const T* __restrict__ k, int64_t max_len, int Hkv, int bs, const int32_t* __restrict__ cache_len,
-    const float* __restrict__ w_s, float* __restrict__ summ, int64_t summ_blocks) {
-  const int64_t bg = blockIdx.x;
-  const int b = (int)(bg / Hkv);
-  int64_t len = cache_len[b];
-  len = len < 1 ? 1 : (len > max_len ? max_len : len);
-  if (len % bs != 0) return;
-  const int64_t j = len / bs - 1;
-  summarize_blocks<T, D, 1>(k + (bg * max_len + j * bs) * D, 1, bs, w_s,
-                            summ + (bg * summ_blocks + j) * D);
-}
-
 template <typename T, int D>
 static hipError_t summarize_t(const Shape& s, const void* k, int64_t kv_len, int64_t b0,
                               int64_t b1, const float* w_s, float* summ, int64_t sb,
@@ -69,22 +53,6 @@ hipError_t launch_summarize(const Shape& s, const void* k, int64_t kv_len, int64
                                             summ_blocks, st)
                    : summarize_t<float, 128>(s, k, kv_len, blk_begin, blk_end, w_s, summ,
                                              summ_blocks, st);
-}
-
-hipError_t launch_summarize_completed(const Shape& s, const void* kc, int64_t max_len,
-                                      const int32_t* cache_len, const float* w_s, float* summ,
-                                      int64_t summ_blocks, hipStream_t st) {
-  dim3 grid((unsigned)(s.B * s.Hkv));
-#define DASH_SC(T, D)                                                                       \
-  hipLaunchKernelGGL((summarize_completed_kernel<T, D>), grid, dim3(kSumThreads), 0, st,    \
-                     (const T*)kc, max_len, s.Hkv, s.bs, cache_len, w_s, summ, summ_blocks)
-  if (s.dtype == DASH_BF16) {
-    if (s.d == 64) DASH_SC(__bf16, 64); else DASH_SC(__bf16, 128);
-  } else {
-    if (s.d == 64) DASH_SC(float, 64); else DASH_SC(float, 128);
-  }
-#undef DASH_SC
-  return hipGetLastError();
 }
 
 }  // namespace dash

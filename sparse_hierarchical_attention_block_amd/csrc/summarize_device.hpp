@@ -1,8 +1,8 @@
 // summarize_device.hpp -- the block-summary routine of Stage 0 of
 // DashAttention ("local chunk summarization", DashAttention explainer,
 // Technical summary): s_j = mean(k of block j) . W_s, accumulated in float32.
-// Used by the prefill summary kernel and by the decode step that completes a
-// block.
+// Used by the summary kernel of dash_summarize and dash_prefill, and by the
+// decode step for the block it completes.
 //
 // HBM-bound scan: every key of a block is read once with 16-byte loads
 // (bs * d * elt bytes per block); the projection reads W_s (d x d float32,
@@ -27,6 +27,13 @@ __device__ void summarize_blocks(const T* __restrict__ kb, int nblk, int bs,
   __shared__ float part[RG][D];
   __shared__ float mean[NB][D];
   const int ch = threadIdx.x % CH, rg = threadIdx.x / CH;
+  // this thread's W_s entries (column c, rows pg + PG i), loaded before the
+  // keys so that both arrive in one memory round trip
+  constexpr int PG = kSumThreads / D;
+  const int c = threadIdx.x % D, pg = threadIdx.x / D;
+  float wcol[D / PG];
+#pragma unroll
+  for (int i = 0; i < D / PG; ++i) wcol[i] = w_s[(pg + PG * i) * D + c];
   for (int bi = 0; bi < nblk; ++bi) {
     const T* blk = kb + (int64_t)bi * bs * D;
     float acc[EPV];
@@ -62,16 +69,14 @@ __device__ void summarize_blocks(const T* __restrict__ kb, int nblk, int bs,
   }
   // projection: out[bi][c] = sum_r mean[bi][r] * W_s[r][c], r split over the
   // 256 / D row groups; W_s is read once for all blocks
-  constexpr int PG = kSumThreads / D;
-  const int c = threadIdx.x % D, pg = threadIdx.x / D;
   float o[NB];
 #pragma unroll
   for (int bi = 0; bi < NB; ++bi) o[bi] = 0.f;
-#pragma unroll 8
-  for (int r = pg; r < D; r += PG) {
-    const float wv = w_s[r * D + c];
 #pragma unroll
-    for (int bi = 0; bi < NB; ++bi) o[bi] = fmaf(mean[bi][r], wv, o[bi]);
+  for (int i = 0; i < D / PG; ++i) {
+    const int r = pg + PG * i;
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) o[bi] = fmaf(mean[bi][r], wcol[i], o[bi]);
   }
   // `part` is reused as [PG][NB][D]
   static_assert(RG >= PG * NB, "LDS scratch too small");

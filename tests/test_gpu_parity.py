@@ -193,6 +193,13 @@ DECODE_CASES = {
     "bs128_alpha2": (W.get("decode_32k").replace(batch=3, seq_len=3072, block_size=128,
                                                  alpha=2.0, gamma=3.0, count_lo=2, count_hi=12),
                      [3072, 3000, 130]),
+    # 512 < candidates <= 1024 (16 register slots per lane), two heads per group
+    "gqa2_slots16": (W.get("decode_32k").replace(batch=2, n_heads=4, n_kv_heads=2, seq_len=49152),
+                     [49152, 33001]),
+    # more than 2048 candidates: scores and routing as two kernels, the row in memory
+    "long_row_in_memory": (W.get("decode_32k").replace(batch=1, n_heads=4, n_kv_heads=1,
+                                                       seq_len=139264),
+                           [139264]),
 }
 
 
