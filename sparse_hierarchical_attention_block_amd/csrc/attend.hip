@@ -286,7 +286,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) smax = fmaxf(smax, st[kt][i]);
-    smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+    smax = xor_reduce<32>(smax, DppMax{});
     const float cmax = fmaf(smax, a.scale_log2, bias2);   // -inf when all masked
     if (__any(cmax > m_ref + kLazyRescale)) {
       const float m_new = fmaxf(m_ref, cmax);
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
                         pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
       pf[ks] = as_bf16x8(pw);
     }
-    psum += __shfl_xor(psum, 32, kWave);
+    psum = xor_reduce<32>(psum, DppAdd{});
     l_run += psum;
 
     // ---- O^T += V^T P^T : 4 k-steps of 16 keys ----

@@ -472,8 +472,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
           st[kt][i] = sv;
           mx = fmaxf(mx, sv);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = xor_reduce<32>(xor_reduce<16>(mx, DppMax{}), DppMax{});
       const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float corr = fast_exp2(m_run - m_use);
@@ -486,8 +485,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
           st[kt][i] = pv;
           psum += pv;
         }
-      psum += __shfl_xor(psum, 16, kWave);
-      psum += __shfl_xor(psum, 32, kWave);
+      psum = xor_reduce<32>(xor_reduce<16>(psum, DppAdd{}), DppAdd{});
       l_run = l_run * corr + psum;
       m_run = m_new;
       // acc rows are queries 4 lg + i: their correction lives in lane 4 lg + i

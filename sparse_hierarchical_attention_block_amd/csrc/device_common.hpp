@@ -72,50 +72,83 @@ __device__ __forceinline__ uint32_t buf_load4(buf_rsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// ---- wave64 reductions (fixed order, deterministic) -------------------------
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-// Wave-wide reductions on DPP instead of LDS permutes: within each row of 16
-// lanes (quad_perm 1,0,3,2 and 2,3,0,1, then half-row and row mirrors every
-// lane holds its row's result), then row 0 into row 1 and row 2 into row 3
-// (row_bcast:15), then lane 31 into rows 2 and 3 (row_bcast:31); lane 63 ends
-// with the whole wave's result, which every lane reads.  Fixed order: all
-// lanes get the same bits.
-template <int CTRL, int ROW_MASK = 0xF>
+// ---- cross-lane exchange without LDS (DPP and gfx950 permlane swaps) -------
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
 __device__ __forceinline__ float dpp_src(float v, float old) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
                                                                __builtin_bit_cast(int, v), CTRL,
-                                                               ROW_MASK, 0xF, false));
+                                                               ROW_MASK, BANK_MASK, false));
 }
+// (v of lane l & ~M, v of lane l | M) for M = 16 (v_permlane16_swap) or 32
+// (v_permlane32_swap): the lower and upper partner of every lane
+template <int M>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  static_assert(M == 16 || M == 32, "permlane swaps exchange 16- or 32-lane halves");
+  const unsigned iv = __builtin_bit_cast(unsigned, v);
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
+    lo = __builtin_bit_cast(float, (unsigned)r[0]);
+    hi = __builtin_bit_cast(float, (unsigned)r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(iv, iv, false, false);
+    lo = __builtin_bit_cast(float, (unsigned)r[0]);
+    hi = __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+}
+// v of lane l ^ M (M a power of two below 64): DPP quad_perm for 1 and 2,
+// row_shl / row_shr by 4 on alternate banks of four lanes for 4, row_ror by 8
+// for 8, permlane swaps for 16 and 32
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (M == 1) return dpp_src<0xB1>(v, v);            // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_src<0x4E>(v, v);       // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) {
+    const float t = dpp_src<0x104, 0xF, 0x5>(v, v);           // banks 0, 2: lane + 4
+    return dpp_src<0x114, 0xF, 0xA>(v, t);                     // banks 1, 3: lane - 4
+  } else if constexpr (M == 8) return dpp_src<0x128>(v, v);    // row_ror:8
+  else {
+    float lo, hi;
+    lane_pair<M>(v, lo, hi);
+    return (__lane_id() & M) ? lo : hi;
+  }
+}
+// op(v, v of lane l ^ M): both lanes of a pair get the same bits (op is
+// commutative; for 16 and 32 the lower lane's value is always the left operand)
+template <int M, typename Op>
+__device__ __forceinline__ float xor_reduce(float v, Op op) {
+  if constexpr (M >= 16) {
+    float lo, hi;
+    lane_pair<M>(v, lo, hi);
+    return op(lo, hi);
+  } else {
+    return op(v, lane_xor<M>(v));
+  }
+}
+// the same over aligned groups of `width` lanes (a power of two <= 64),
+// partners at distance 1, 2, 4, ... in that order
 template <typename Op>
-__device__ __forceinline__ float wave_reduce_dpp(float v, Op op, float ident) {
-  v = op(v, dpp_src<0xB1>(v, ident));         // quad_perm [1,0,3,2]
-  v = op(v, dpp_src<0x4E>(v, ident));         // quad_perm [2,3,0,1]
-  v = op(v, dpp_src<0x141>(v, ident));        // row_half_mirror
-  v = op(v, dpp_src<0x140>(v, ident));        // row_mirror
-  v = op(v, dpp_src<0x142, 0xA>(v, ident));   // row_bcast:15 into rows 1 and 3
-  v = op(v, dpp_src<0x143, 0xC>(v, ident));   // row_bcast:31 into rows 2 and 3
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+__device__ __forceinline__ float group_reduce(float v, int width, Op op) {
+  if (width > 1) v = xor_reduce<1>(v, op);
+  if (width > 2) v = xor_reduce<2>(v, op);
+  if (width > 4) v = xor_reduce<4>(v, op);
+  if (width > 8) v = xor_reduce<8>(v, op);
+  if (width > 16) v = xor_reduce<16>(v, op);
+  if (width > 32) v = xor_reduce<32>(v, op);
+  return v;
 }
 struct DppAdd { __device__ float operator()(float x, float y) const { return x + y; } };
 struct DppMax { __device__ float operator()(float x, float y) const { return fmaxf(x, y); } };
 struct DppMin { __device__ float operator()(float x, float y) const { return fminf(x, y); } };
 
-// reductions over aligned groups of `width` lanes (width a power of two <= 64)
+// Wave-wide reductions on DPP and permlane swaps: every lane gets the same
+// bits; for latency-bound code with few waves per SIMD.
+__device__ __forceinline__ float wave_sum(float v) { return group_reduce(v, kWave, DppAdd{}); }
+__device__ __forceinline__ float wave_max(float v) { return group_reduce(v, kWave, DppMax{}); }
+__device__ __forceinline__ float wave_min(float v) { return group_reduce(v, kWave, DppMin{}); }
+
+// Reductions over aligned groups of `width` lanes (a power of two <= 64)
+// through LDS permutes (ds_bpermute): in kernels whose VALU is the busy unit
+// these cost less than DPP chains, which add VALU work and wait states.
 __device__ __forceinline__ float group_sum(float v, int width) {
   for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;

@@ -116,10 +116,10 @@ struct GroupReduce {   // `width` consecutive lanes
   __device__ float max(float v) const { return group_max(v, width); }
   __device__ float min(float v) const { return group_min(v, width); }
 };
-struct WaveReduce {   // all 64 lanes of the wave (DPP)
-  __device__ float sum(float v) const { return wave_reduce_dpp(v, DppAdd{}, 0.f); }
-  __device__ float max(float v) const { return wave_reduce_dpp(v, DppMax{}, -INFINITY); }
-  __device__ float min(float v) const { return wave_reduce_dpp(v, DppMin{}, INFINITY); }
+struct WaveReduce {   // all 64 lanes of the wave
+  __device__ float sum(float v) const { return wave_sum(v); }
+  __device__ float max(float v) const { return wave_max(v); }
+  __device__ float min(float v) const { return wave_min(v); }
 };
 struct Stride16Reduce {   // lanes l, l^16, l^32, l^48 (one MFMA 16x16 C-fragment row)
   __device__ float sum(float v) const {
@@ -139,31 +139,41 @@ struct Stride16Reduce {   // lanes l, l^16, l^32, l^48 (one MFMA 16x16 C-fragmen
 // Same threshold with the row held in registers: each lane of the row's lane
 // set holds VPL of its values (-inf for absent entries); `red` reduces over
 // that lane set.  Only the first nact4 groups of four values are visited
-// (nact4 is uniform across the wave, so the skipped groups cost no VALU).
+// (nact4 is uniform across the wave, so the skipped groups cost no VALU, and
+// the loop leaves at the first inactive group).
 template <int VPL, int mode, typename Red>
 __device__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int nact4 = VPL / 4) {
   float xmax = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i)
-    if (i / 4 < nact4) xmax = fmaxf(xmax, xv[i]);
+  for (int g4 = 0; g4 < VPL / 4; ++g4) {
+    if (g4 >= nact4) break;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) xmax = fmaxf(xmax, xv[4 * g4 + ii]);
+  }
   xmax = red.max(xmax);
   float tau = xmax - 1.0f;
   for (int it = 0; it < 64; ++it) {
-    float k = 0.f, s1 = 0.f, s2 = 0.f, ymin = INFINITY;
+    float s1 = 0.f, s2 = 0.f, ymin = INFINITY;
+    int kc = 0;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      if (i / 4 >= nact4) continue;
-      const float y = xv[i] - tau;
-      const bool in = y > 0.f;
-      const float yp = in ? y : 0.f;
-      k += in ? 1.f : 0.f;
-      ymin = fminf(ymin, in ? y : INFINITY);
-      if constexpr (mode == kEntmax15) { s1 += yp; s2 = fmaf(yp, yp, s2); }
-      else if constexpr (mode == kSparsemax) { s1 += yp; }
-      else if constexpr (mode == kEntmaxQuartic) { const float y2 = yp * yp; s1 = fmaf(y2, yp, s1); s2 = fmaf(y2, y2, s2); }
-      else if (in) { const float l = __log2f(y); s1 += exp2f((e - 1.f) * l); s2 += exp2f(e * l); }
+    for (int g4 = 0; g4 < VPL / 4; ++g4) {
+      if (g4 >= nact4) break;   // the active groups come first
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const float y = xv[4 * g4 + ii] - tau;
+        const bool in = y > 0.f;
+        const float yp = fmaxf(y, 0.f);
+        kc += in ? 1 : 0;
+        // min(ymin, y over the support) as v_med3(z, ymin, -inf): no NaN
+        // quieting of the loop-carried ymin as fminf would need
+        ymin = __builtin_amdgcn_fmed3f(in ? y : INFINITY, ymin, -INFINITY);
+        if constexpr (mode == kEntmax15) { s1 += yp; s2 = fmaf(yp, yp, s2); }
+        else if constexpr (mode == kSparsemax) { s1 += yp; }
+        else if constexpr (mode == kEntmaxQuartic) { const float y2 = yp * yp; s1 = fmaf(y2, yp, s1); s2 = fmaf(y2, y2, s2); }
+        else if (in) { const float l = __log2f(y); s1 += exp2f((e - 1.f) * l); s2 += exp2f(e * l); }
+      }
     }
-    k = red.sum(k);
+    float k = red.sum((float)kc);
     s1 = red.sum(s1);
     s2 = red.sum(s2);
     ymin = red.min(ymin);

@@ -224,17 +224,32 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
         const float y = xv[i] - tau;
         pv[i] = y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
       }
-      for (int o = lpr; o < lpr * a.G; o <<= 1)
+      // GQA sum as a reduce-scatter over the G rows of a position (lanes
+      // lpr apart): at the step over bit `bit` of h a lane keeps the half of
+      // its slots whose bit agrees with its own h and sends the other half
+      // to its partner.  Afterwards slot s (low log2 G bits clear) holds the
+      // sum for slot s | h, which this lane then writes.
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) pv[i] += __shfl_xor(pv[i], o, kWave);
-      // every head's lanes now hold the group sum; head h writes the blocks
-      // with i % G == h
+      for (int bb = 0; bb < 3; ++bb) {
+        const int bit = 1 << bb;
+        if (bit < a.G) {
+          const bool up = (h & bit) != 0;
+#pragma unroll
+          for (int s2 = 0; s2 < VPL; ++s2) {
+            if ((s2 & (2 * bit - 1)) != 0 || (s2 >> 2) >= nact4) continue;
+            const float lo = pv[s2], hi = pv[s2 | bit];
+            const float send = up ? lo : hi, keep = up ? hi : lo;
+            pv[s2] = keep + __shfl_xor(send, lpr * bit, kWave);
+          }
+        }
+      }
       if (m < np) {
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-          const int j = sub + lpr * i;
-          if (i % a.G == h && j < t) {
-            const float pb = pv[i] * invG;
+        for (int s2 = 0; s2 < VPL; ++s2) {
+          if (s2 % a.G != 0 || (s2 >> 2) >= nact4) continue;
+          const int j = sub + lpr * (s2 | h);
+          if (j < t) {
+            const float pb = pv[s2] * invG;
             a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? __logf(pb) : -INFINITY;
             if (pb > 0.f) uflag[j] = 1;
           }
@@ -473,35 +488,46 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
         }
     }
     if (lg == 0 && pos < a.n) a.tau[rglob] = tau;
-    // p, GQA sum over the G adjacent rows (lanes differing in l16's low bits)
+    // p of this row's slots (slot s = 4 ct + i <-> candidate 16 ct + 4 lg + i)
 #pragma unroll
     for (int ct = 0; ct < kTileMaxCT; ++ct) {
-      if (ct < CT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float y = xv[4 * ct + i] - tau;
-          xv[4 * ct + i] = y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const float y = xv[4 * ct + i] - tau;
+        xv[4 * ct + i] = ct < CT && y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
+      }
+    }
+    // GQA sum as a reduce-scatter over the G rows of a position (lanes whose
+    // l16 differ in the bits of h = l16 % G): at the step over bit `bit` a
+    // lane keeps the half of its slots whose bit agrees with its own h and
+    // sends the other half to its partner.  Afterwards slot s (low log2 G
+    // bits clear) holds the sum for slot s | h, which this lane then writes.
+#pragma unroll
+    for (int bb = 0; bb < 3; ++bb) {
+      const int bit = 1 << bb;
+      if (bit < G) {
+        const bool up = (h & bit) != 0;
+#pragma unroll
+        for (int s2 = 0; s2 < 4 * kTileMaxCT; ++s2) {
+          if ((s2 & (2 * bit - 1)) != 0 || (s2 >> 2) >= CT) continue;
+          const float lo = xv[s2], hi = xv[s2 | bit];
+          const float send = up ? lo : hi, keep = up ? hi : lo;
+          xv[s2] = keep + __shfl_xor(send, bit, kWave);
         }
-        for (int o = 1; o < G; o <<= 1)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) xv[4 * ct + i] += __shfl_xor(xv[4 * ct + i], o, kWave);
       }
     }
     if (pos < a.n) {
       const int mloc = (int)(pos - p_begin);
       float* lp = a.sel_logp + tile * a.nb * kQT + mloc;
 #pragma unroll
-      for (int ct = 0; ct < kTileMaxCT; ++ct) {
-        if (ct < CT) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = 16 * ct + 4 * lg + i;
-            if (j < t && (4 * ct + i) % G == h) {
-              const float pb = xv[4 * ct + i] * invG;
-              lp[j * kQT] = pb > 0.f ? __logf(pb) : -INFINITY;
-              if (pb > 0.f) uflag[j] = 1;
-            }
-          }
+      for (int s2 = 0; s2 < 4 * kTileMaxCT; ++s2) {
+        if (s2 % G != 0 || (s2 >> 2) >= CT) continue;
+        const int slot = s2 | h;
+        const int j = 16 * (slot >> 2) + 4 * lg + (slot & 3);
+        if (j < t) {
+          const float pb = xv[s2] * invG;
+          lp[j * kQT] = pb > 0.f ? __logf(pb) : -INFINITY;
+          if (pb > 0.f) uflag[j] = 1;
         }
       }
     }
