@@ -17,8 +17,9 @@
 //   O^T (d x 32 queries) += V^T P^T        4 x 4 MFMA 32x32x16
 // Keys are the MFMA rows of S^T, so the accumulator of S^T already has the
 // register layout of the P^T operand (the k index of the PV product is a
-// permutation of the chunk's keys, matched by how V^T is read from LDS).
-// V is transposed into LDS in 4x4 blocks while it is staged.
+// permutation of the chunk's keys).  V is transposed into LDS in 4x4 blocks
+// while it is staged, with the keys of each group of 16 stored in the order
+// of that permutation, so every V^T operand fragment is one 16-byte read.
 #include "dash_internal.hpp"
 #include "device_common.hpp"
 
@@ -69,7 +70,8 @@ __device__ __forceinline__ ChunkRef chunk_ref(int c, int n_own, int64_t own_c0, 
 // ------------------------------------------------------------------------------------------
 // bf16, MFMA
 // ------------------------------------------------------------------------------------------
-// Staging of one 64-key chunk: K row-major [64][D + 8], V transposed [D][64 + 4]
+// Staging of one 64-key chunk: K row-major [64][D + 8], V transposed [D][64 + 8]
+// (keys permuted within each group of 16, see store())
 // (bf16), and the chunk's 64 per-query biases (float, log pbar of the chunk's
 // block; 0 for own-block chunks).  NT threads; each thread owns KPT 16-byte
 // pieces of K and VPT 4x4 blocks of V; lanes 0..15 of wave 0 own the bias.
@@ -79,7 +81,7 @@ __device__ __forceinline__ ChunkRef chunk_ref(int c, int n_own, int64_t own_c0, 
 template <int D, int NT>
 struct ChunkStage {
   static constexpr int KP = D + 8;
-  static constexpr int VP = kChunk + 4;
+  static constexpr int VP = kChunk + 8;   // 144-byte rows: 16-byte aligned, 36-bank shift
   static constexpr int KTOT = kChunk * (D / 8);          // 16-byte pieces of K
   static constexpr int VTOT = (kChunk / 4) * (D / 4);    // 4x4 blocks of V
   static constexpr int KPT = (KTOT + NT - 1) / NT;
@@ -132,14 +134,25 @@ struct ChunkStage {
       const u32x2 o1 = {pack_hi(in[0].x, in[1].x), pack_hi(in[2].x, in[3].x)};
       const u32x2 o2 = {pack_lo(in[0].y, in[1].y), pack_lo(in[2].y, in[3].y)};
       const u32x2 o3 = {pack_hi(in[0].y, in[1].y), pack_hi(in[2].y, in[3].y)};
-      *(u32x2*)(Vt + (4 * db + 0) * VP + 4 * kb) = o0;
-      *(u32x2*)(Vt + (4 * db + 1) * VP + 4 * kb) = o1;
-      *(u32x2*)(Vt + (4 * db + 2) * VP + 4 * kb) = o2;
-      *(u32x2*)(Vt + (4 * db + 3) * VP + 4 * kb) = o3;
+      // keys 16 m + 8 a + 4 b + [0, 4) go to columns 16 m + 8 b + 4 a + [0, 4):
+      // the 8 keys one lane needs for a PV k-step become one 16-byte run
+      const int col = 16 * (kb / 4) + 8 * (kb % 2) + 4 * ((kb / 2) % 2);
+      *(u32x2*)(Vt + (4 * db + 0) * VP + col) = o0;
+      *(u32x2*)(Vt + (4 * db + 1) * VP + col) = o1;
+      *(u32x2*)(Vt + (4 * db + 2) * VP + col) = o2;
+      *(u32x2*)(Vt + (4 * db + 3) * VP + col) = o3;
     }
     if (threadIdx.x < kQTa / 4) *(u32x4*)(Bs + 4 * threadIdx.x) = br;
   }
 };
+
+// Workgroup barrier that orders LDS accesses only: global loads issued before
+// it stay in flight (__syncthreads would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Rescale the running output only when a row max grows by more than 2^8:
 // exp2(s - m_ref) then stays <= 256, exact in float32 and in bf16's range.
@@ -214,22 +227,35 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   // Chunk c sits in LDS buffer c % 3; chunk c+1 is already staged and chunk
   // c+2's K/V/bias are in flight from HBM into registers, preceded in the
   // load queue by the block id of chunk c+3.
-  Stage stage;
-  for (int c = 0; c < 2 && c < n_chunks; ++c) {
-    const int j = __builtin_amdgcn_readfirstlane(sel_block(c));
-    stage.load(rk, rv, rb, key0_of(c, j), c < n_own ? -1 : j);
-    stage.store(Ks[c], Vt[c], Bs[c]);
+  // Prologue: the block ids of chunks 0..3 arrive with one load (slots of
+  // own-block chunks and past the list read as 0 and are not used), chunks 0
+  // and 1 are loaded together, then chunk 2's loads stay in flight into the
+  // loop behind an LDS-only barrier.
+  uint32_t j4[4];
+  {
+    // chunk c >= n_own belongs to list entry (c - n_own) >> cpb_log
+    u32x4 w4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) j4[c] = 0u;
+    if (n_own < 4 && count > 0) w4 = buf_load16(ri, 0u);
+    const uint32_t wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = (c - n_own) >> cpb_log;   // uniform; negative for own chunks
+      uint32_t jj = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) jj = e == q ? wv[q] : jj;
+      j4[c] = __builtin_amdgcn_readfirstlane(jj);
+    }
   }
-  uint32_t jv = 0;
-  if (n_chunks > 2) {
-    const int j = __builtin_amdgcn_readfirstlane(sel_block(2));
-    jv = sel_block(3);
-    stage.load(rk, rv, rb, key0_of(2, j), 2 < n_own ? -1 : j);
-  }
-  // Q fragments and the first chunks have landed: with nothing of the
-  // prologue pending, the loop's waits only ever cover its own loads
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  Stage stage, stage1;
+  if (n_chunks > 0) stage.load(rk, rv, rb, key0_of(0, (int)j4[0]), 0 < n_own ? -1 : (int)j4[0]);
+  if (n_chunks > 1) stage1.load(rk, rv, rb, key0_of(1, (int)j4[1]), 1 < n_own ? -1 : (int)j4[1]);
+  if (n_chunks > 0) stage.store(Ks[0], Vt[0], Bs[0]);
+  if (n_chunks > 1) stage1.store(Ks[1], Vt[1], Bs[1]);
+  uint32_t jv = j4[3];
+  if (n_chunks > 2) stage.load(rk, rv, rb, key0_of(2, (int)j4[2]), 2 < n_own ? -1 : (int)j4[2]);
+  lds_barrier();
 
   int bcur = 0;
   for (int c = 0; c < n_chunks; ++c) {
@@ -264,10 +290,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const __bf16* vrow = Vc + (32 * dt + l32) * VP + 16 * ks + 4 * lh;
-        const u32x2 v0 = *(const u32x2*)(vrow);
-        const u32x2 v1 = *(const u32x2*)(vrow + 8);
-        vw[ks][dt] = (u32x4){v0.x, v0.y, v1.x, v1.y};
+        vw[ks][dt] = *(const u32x4*)(Vc + (32 * dt + l32) * VP + 16 * ks + 8 * lh);
       }
 
     // ---- online softmax of chunk c, exp2 domain: logit2 = s * scale_log2 + bias2 ----
