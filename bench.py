@@ -43,8 +43,11 @@ ATTEND_SRC = os.path.join(ROOT, "sparse_hierarchical_attention_block_amd", "csrc
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 200 untimed steps bring the GPU to its steady clock before the timed
+    # steps (5 warmup steps of this workload are ~1.5 ms of work, during which
+    # the clock is still ramping)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefill_8k")
     ap.add_argument("--decode-workload", default="decode_32k")
     ap.add_argument("--alpha", type=float, default=None)
