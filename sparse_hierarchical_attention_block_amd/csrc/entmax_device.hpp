@@ -116,6 +116,26 @@ struct GroupReduce {   // `width` consecutive lanes
   __device__ float max(float v) const { return group_max(v, width); }
   __device__ float min(float v) const { return group_min(v, width); }
 };
+// Reductions over aligned groups of W consecutive lanes (W = 2 ... 16, known
+// at compile time) on DPP within the lane's row of 16: quad_perm for
+// partners 1 and 2, then the half-row and row mirrors (after the quad
+// steps every lane of a quad holds the same value, so mirrored partners
+// complete the group).  Every lane of a group gets the same bits.
+template <int W>
+struct DppGroupReduce {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "DPP group of 2..16 lanes");
+  template <typename Op>
+  __device__ static float run(float v, Op op) {
+    v = op(v, dpp_src<0xB1>(v, v));
+    if constexpr (W > 2) v = op(v, dpp_src<0x4E>(v, v));
+    if constexpr (W > 4) v = op(v, dpp_src<0x141>(v, v));
+    if constexpr (W > 8) v = op(v, dpp_src<0x140>(v, v));
+    return v;
+  }
+  __device__ float sum(float v) const { return run(v, DppAdd{}); }
+  __device__ float max(float v) const { return run(v, DppMax{}); }
+  __device__ float min(float v) const { return run(v, DppMin{}); }
+};
 struct WaveReduce {   // all 64 lanes of the wave
   __device__ float sum(float v) const { return wave_sum(v); }
   __device__ float max(float v) const { return wave_max(v); }

@@ -202,7 +202,10 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
       // slots 4 k .. 4 k + 3 hold candidates [4 k lpr, 4 (k + 1) lpr): only the
       // groups below t are visited
       const int nact4 = (t + 4 * lpr - 1) / (4 * lpr);
-      const float tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{lpr}, a.e, nact4);
+      constexpr int LPR = NT / (16 * RT);   // lanes per row: NT / rows per pass
+      float tau;
+      if constexpr (LPR <= 16) tau = entmax_tau_reg<VPL, MODE>(xv, DppGroupReduce<LPR>{}, a.e, nact4);
+      else tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{lpr}, a.e, nact4);
       const int m = row / a.G, h = row % a.G;
       const int64_t pos = pos0 + m;
       if (pos < a.n) {
