@@ -136,6 +136,17 @@ __device__ __forceinline__ float group_reduce(float v, int width, Op op) {
   if (width > 32) v = xor_reduce<32>(v, op);
   return v;
 }
+// lane_xor for a distance that is a compile-time constant after unrolling
+__device__ __forceinline__ float lane_xor_c(float v, int m) {
+  switch (m) {
+    case 1: return lane_xor<1>(v);
+    case 2: return lane_xor<2>(v);
+    case 4: return lane_xor<4>(v);
+    case 8: return lane_xor<8>(v);
+    case 16: return lane_xor<16>(v);
+    default: return lane_xor<32>(v);
+  }
+}
 struct DppAdd { __device__ float operator()(float x, float y) const { return x + y; } };
 struct DppMax { __device__ float operator()(float x, float y) const { return fmaxf(x, y); } };
 struct DppMin { __device__ float operator()(float x, float y) const { return fminf(x, y); } };

@@ -188,6 +188,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
 
     const int np = min(a.PP, npos - pp);
     if constexpr (VPL > 0) {
+      constexpr int LPR = NT / (16 * RT);   // lanes per row: NT / rows per pass
       // steps 2-3 with the row in registers: lane `sub` of the row's group
       // holds x_{sub + lpr*i}; the G rows of a position are adjacent groups,
       // so the GQA sum is a shuffle over G * lpr lanes.
@@ -202,7 +203,6 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
       // slots 4 k .. 4 k + 3 hold candidates [4 k lpr, 4 (k + 1) lpr): only the
       // groups below t are visited
       const int nact4 = (t + 4 * lpr - 1) / (4 * lpr);
-      constexpr int LPR = NT / (16 * RT);   // lanes per row: NT / rows per pass
       float tau;
       if constexpr (LPR <= 16) tau = entmax_tau_reg<VPL, MODE>(xv, DppGroupReduce<LPR>{}, a.e, nact4);
       else tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{lpr}, a.e, nact4);
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
             if ((s2 & (2 * bit - 1)) != 0 || (s2 >> 2) >= nact4) continue;
             const float lo = pv[s2], hi = pv[s2 | bit];
             const float send = up ? lo : hi, keep = up ? hi : lo;
-            pv[s2] = keep + __shfl_xor(send, lpr * bit, kWave);
+            pv[s2] = keep + lane_xor_c(send, LPR * bit);
           }
         }
       }
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
           if ((s2 & (2 * bit - 1)) != 0 || (s2 >> 2) >= CT) continue;
           const float lo = xv[s2], hi = xv[s2 | bit];
           const float send = up ? lo : hi, keep = up ? hi : lo;
-          xv[s2] = keep + __shfl_xor(send, bit, kWave);
+          xv[s2] = keep + lane_xor_c(send, bit);
         }
       }
     }
