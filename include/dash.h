@@ -169,9 +169,7 @@ dash_status dash_attend(const dash_params* p, const void* q, const void* k, cons
                         int64_t n, const dash_route_buf* route, void* o, void* stream);
 
 /* Fused causal prefill: dash_summarize of blocks [0, floor(n/bs)) into summ,
- * dash_route into the workspace, dash_attend into o.  For bf16 the workspace
- * also holds the summaries split into three bf16 rows (written with them),
- * which the routing kernels read instead of splitting on every pass.
+ * dash_route into the workspace, dash_attend into o.
  *   summ   [B, Hkv, summ_blocks, d] float32, summ_blocks >= floor(n/bs)
  *   ws     >= dash_prefill_workspace_bytes(p, n) bytes, 256-byte aligned
  * Same size limit as dash_attend. */

@@ -79,7 +79,7 @@ bool route_lds_ok(const Shape& s, int64_t n) {
 }
 
 struct PrefillLayout {
-  size_t off_tau, off_count, off_idx, off_logp, off_planes, total;
+  size_t off_tau, off_count, off_idx, off_logp, total;
 };
 
 PrefillLayout prefill_layout(const Shape& s, int64_t n) {
@@ -91,9 +91,6 @@ PrefillLayout prefill_layout(const Shape& s, int64_t n) {
   L.off_count = off; off = align_up(off + 4 * (size_t)r.sel_count);
   L.off_idx = off;   off = align_up(off + 4 * (size_t)r.sel_idx);
   L.off_logp = off;  off = align_up(off + 4 * (size_t)r.sel_logp);
-  // the complete blocks' summaries split into three bf16 rows for routing
-  L.off_planes = off;
-  if (s.dtype == DASH_BF16) off = align_up(off + 2 * (size_t)3 * s.d * s.B * s.Hkv * (n / s.bs));
   L.total = off;
   return L;
 }
@@ -230,12 +227,8 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
   rb.sel_logp = (float*)(base + L.off_logp);
   rb.support_bits = nullptr;
   hipStream_t hs = (hipStream_t)stream;
-  __bf16* planes = s.dtype == DASH_BF16 ? (__bf16*)(base + L.off_planes) : nullptr;
-  const int64_t nfull = n / s.bs;
-  hipError_t e =
-      dash::launch_summarize(s, k, n, 0, nfull, w_s, summ, summ_blocks, hs, planes, nfull);
-  if (e == hipSuccess)
-    e = dash::launch_route_prefill(s, q, n, summ, summ_blocks, rb, hs, planes, nfull);
+  hipError_t e = dash::launch_summarize(s, k, n, 0, n / s.bs, w_s, summ, summ_blocks, hs);
+  if (e == hipSuccess) e = dash::launch_route_prefill(s, q, n, summ, summ_blocks, rb, hs);
   if (e == hipSuccess) e = dash::launch_attend_prefill(s, q, k, v, n, rb, o, hs);
   return hip_status(e);
 }

@@ -17,18 +17,13 @@ struct Shape {
 };
 
 // Stage 0: summaries of blocks [blk_begin, blk_end) for every (b, kv head).
-// With `planes` (bf16 [B, Hkv, planes_blocks, 3, d]) each summary is also
-// written as hi / mid / lo bf16 rows for the routing kernels.
 hipError_t launch_summarize(const Shape& s, const void* k, int64_t kv_len, int64_t blk_begin,
                             int64_t blk_end, const float* w_s, float* summ, int64_t summ_blocks,
-                            hipStream_t st, __bf16* planes = nullptr, int64_t planes_blocks = 0);
+                            hipStream_t st);
 
-// Stage 1, causal prefill of positions 0..n-1.  `planes` (optional, bf16
-// queries only): the summaries' bf16 split as written by launch_summarize;
-// without it the routing kernels split the float32 summaries themselves.
+// Stage 1, causal prefill of positions 0..n-1.
 hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const float* summ,
-                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st,
-                                const __bf16* planes = nullptr, int64_t planes_blocks = 0);
+                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st);
 
 // Stage 2, causal prefill.
 hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,

@@ -48,8 +48,6 @@ struct RouteArgs {
   float e, scale;
   int PP;      // positions per pass
   int pitch;   // X row pitch in floats (multiple of 4)
-  const __bf16* planes;   // optional [B, Hkv, planes_blocks, 3, D]: summaries as hi / mid / lo
-  int64_t planes_blocks;
 };
 
 __host__ __device__ inline int round_up16(int x) { return (x + 15) & ~15; }
@@ -94,37 +92,21 @@ __device__ void route_scores_bf16(const RouteArgs& a, float* X, int t, int64_t b
     }
   };
   for (int ct = wave; ct < CT; ct += NT / kWave) {
+    f32x4 sv[KS][2];
+    load_s(ct, sv);
     bf16x8 hi[KS], mid[KS], lo[KS];
-    if (a.planes) {
-      // the split was written with the summaries: three 16-byte loads per k-step
-      const int cand = ct * 16 + l16;
-      const __bf16* prow = a.planes + (bg * a.planes_blocks + (cand < t ? cand : 0)) * 3 * D;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 h4 = *(const u32x4*)(prow + 32 * s + 8 * lg);
-        u32x4 m4 = *(const u32x4*)(prow + D + 32 * s + 8 * lg);
-        u32x4 l4 = *(const u32x4*)(prow + 2 * D + 32 * s + 8 * lg);
-        if (cand >= t) h4 = m4 = l4 = (u32x4){0u, 0u, 0u, 0u};
-        hi[s] = as_bf16x8(h4);
-        mid[s] = as_bf16x8(m4);
-        lo[s] = as_bf16x8(l4);
-      }
-    } else {
-      f32x4 sv[KS][2];
-      load_s(ct, sv);
+    for (int s = 0; s < KS; ++s) {
+      const float xv[8] = {sv[s][0].x, sv[s][0].y, sv[s][0].z, sv[s][0].w,
+                           sv[s][1].x, sv[s][1].y, sv[s][1].z, sv[s][1].w};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const float xv[8] = {sv[s][0].x, sv[s][0].y, sv[s][0].z, sv[s][0].w,
-                             sv[s][1].x, sv[s][1].y, sv[s][1].z, sv[s][1].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const __bf16 h = (__bf16)xv[i];
-          const float r1 = xv[i] - (float)h;
-          const __bf16 m = (__bf16)r1;
-          hi[s][i] = h;
-          mid[s][i] = m;
-          lo[s][i] = (__bf16)(r1 - (float)m);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)xv[i];
+        const float r1 = xv[i] - (float)h;
+        const __bf16 m = (__bf16)r1;
+        hi[s][i] = h;
+        mid[s][i] = m;
+        lo[s][i] = (__bf16)(r1 - (float)m);
       }
     }
 #pragma unroll
@@ -385,30 +367,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
 
   // ---- stage the summaries, split into hi + mid + lo bf16 ----
   // (batches of 8 loads per thread are issued before any is consumed)
-  const int n4 = a.planes ? 0 : CT * 16 * (D / 4);
-  if (a.planes) {   // already split: copy the three rows of each candidate
-    const int n8 = 3 * CT * 16 * (D / 8);
-    const __bf16* pbase = a.planes + bg * a.planes_blocks * 3 * D;
-    for (int e0 = threadIdx.x; e0 < n8; e0 += 8 * nthreads) {
-      u32x4 vb[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * nthreads;
-        const int c8 = e % (D / 8), rest = e / (D / 8);
-        const int cand = rest % (CT * 16), pl = rest / (CT * 16);
-        vb[u] = (u32x4){0u, 0u, 0u, 0u};
-        if (e < n8 && cand < t) vb[u] = *(const u32x4*)(pbase + (cand * 3 + pl) * D + 8 * c8);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * nthreads;
-        if (e >= n8) break;
-        const int c8 = e % (D / 8), rest = e / (D / 8);
-        const int cand = rest % (CT * 16), pl = rest / (CT * 16);
-        *(u32x4*)(planes + (size_t)pl * TP * SP + cand * SP + 8 * c8) = vb[u];
-      }
-    }
-  }
+  const int n4 = CT * 16 * (D / 4);
   for (int e0 = threadIdx.x; e0 < n4; e0 += 8 * nthreads) {
     f32x4 vb[8];
 #pragma unroll
@@ -603,16 +562,13 @@ static int route_pp(int G, int pitch, size_t budget) {
 }
 
 hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const float* summ,
-                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st,
-                                const __bf16* planes, int64_t planes_blocks) {
+                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   RouteArgs a;
   a.q = q;
   a.n = n;
   a.summ = summ;
   a.summ_blocks = summ_blocks;
-  a.planes = s.dtype == DASH_BF16 ? planes : nullptr;
-  a.planes_blocks = planes_blocks;
   a.tau = rb.tau;
   a.sel_count = rb.sel_count;
   a.sel_idx = rb.sel_idx;

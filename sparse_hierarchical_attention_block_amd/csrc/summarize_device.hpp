@@ -17,13 +17,10 @@ constexpr int kSumThreads = 256;
 
 // Summaries of nblk <= NB consecutive blocks.  kb points at the first key row
 // of the first block (rows of D elements, blocks of bs rows, contiguous), out
-// at the first summary (D floats per block, contiguous).  With `planes`, each
-// summary is also written split into three bf16 rows [hi, mid, lo] (3 D per
-// block) whose sum is the float32 value.  All 256 threads call.
+// at the first summary (D floats per block, contiguous).  All 256 threads call.
 template <typename T, int D, int NB>
 __device__ void summarize_blocks(const T* __restrict__ kb, int nblk, int bs,
-                                 const float* __restrict__ w_s, float* __restrict__ out,
-                                 __bf16* __restrict__ planes = nullptr) {
+                                 const float* __restrict__ w_s, float* __restrict__ out) {
   constexpr int EPV = 16 / sizeof(T);       // elements per 16-byte load
   constexpr int CH = D / EPV;               // 16-byte chunks per row
   constexpr int RG = kSumThreads / CH;      // row groups
@@ -92,15 +89,6 @@ __device__ void summarize_blocks(const T* __restrict__ kb, int nblk, int bs,
 #pragma unroll
       for (int q = 0; q < PG; ++q) s += (&part[0][0])[(q * NB + bi) * D + threadIdx.x];
       out[bi * D + threadIdx.x] = s;
-      if (planes) {   // s = hi + mid + lo in bf16 (24 mantissa bits), for MFMA scoring
-        const __bf16 h = (__bf16)s;
-        const float r1 = s - (float)h;
-        const __bf16 m = (__bf16)r1;
-        __bf16* pb = planes + (size_t)bi * 3 * D + threadIdx.x;
-        pb[0] = h;
-        pb[D] = m;
-        pb[2 * D] = (__bf16)(r1 - (float)m);
-      }
     }
   }
   __syncthreads();
