@@ -196,6 +196,18 @@ DECODE_CASES = {
     # 512 < candidates <= 1024 (16 register slots per lane), two heads per group
     "gqa2_slots16": (W.get("decode_32k").replace(batch=2, n_heads=4, n_kv_heads=2, seq_len=49152),
                      [49152, 33001]),
+    # at least 128 (sequence, KV head) pairs: scores and routing fused per pair,
+    # lengths with no candidate, block completions and ragged tails
+    "fused_gqa4_d128": (W.get("decode_32k").replace(batch=16, seq_len=3000, count_lo=4,
+                                                    count_hi=30),
+                        [1, 2, 63, 64, 65, 127, 128, 129, 500, 1000, 1024, 2047, 2048, 2049,
+                         2999, 3000]),
+    "fused_gqa2_d64": (W.get("decode_32k").replace(batch=32, n_heads=8, n_kv_heads=4,
+                                                   head_dim=64, seq_len=1500, count_lo=2,
+                                                   count_hi=16),
+                       [1500 - 37 * i for i in range(32)]),
+    "fused_gqa8": (W.get("decode_128k").replace(batch=16, seq_len=2000, count_hi=24),
+                   [2000 - 61 * i for i in range(16)]),
     # more than 2048 candidates: scores and routing as two kernels, the row in memory
     "long_row_in_memory": (W.get("decode_32k").replace(batch=1, n_heads=4, n_kv_heads=1,
                                                        seq_len=139264),
