@@ -564,7 +564,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
   __shared__ float ms[4][16], ls[4][16];
   __shared__ float os[4][8][D];
-  __shared__ int pre[kDecodeMaxBg + 1];
+  extern __shared__ int pre[];   // [B Hkv + 1], sized at launch
   __shared__ int wsum[4];
   const int nbg = a.B * a.Hkv;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -740,22 +740,25 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
 }
 
 // Workgroups of decode_attend_bf16_kernel<D> resident on the current device at
-// once (cached per device).
+// once with `lds` bytes of dynamic LDS (cached per device and 4 KB step of lds).
+constexpr int kLdsSteps = (kDecodeMaxBg + 1) * 4 / 4096 + 1;
 template <int D>
-static int persistent_grid() {
-  static std::atomic<int> cache[kMaxDevices];
+static int persistent_grid(size_t lds) {
+  static std::atomic<int> cache[kMaxDevices][kLdsSteps];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  int g = cache[dev].load(std::memory_order_relaxed);
+  const int step = (int)(lds / 4096);
+  lds = (size_t)(step + 1) * 4096;   // occupancy of the step's upper end
+  int g = cache[dev][step].load(std::memory_order_relaxed);
   if (g == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, (const void*)decode_attend_bf16_kernel<D>, 256, 0) != hipSuccess)
+            &per_cu, (const void*)decode_attend_bf16_kernel<D>, 256, lds) != hipSuccess)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
     g = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
-    cache[dev].store(g, std::memory_order_relaxed);
+    cache[dev][step].store(g, std::memory_order_relaxed);
   }
   return g;
 }
@@ -875,12 +878,15 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   dim3 g3((unsigned)L.n_split, nbg);
   if (bf16) {
     const int64_t items_max = (int64_t)nbg * L.n_split;
+    const size_t lds_pre = sizeof(int) * ((size_t)nbg + 1);   // the item prefix
     if (s.d == 64)
       hipLaunchKernelGGL(decode_attend_bf16_kernel<64>,
-                         dim3((unsigned)min64(items_max, persistent_grid<64>())), dim3(256), 0, st, a);
+                         dim3((unsigned)min64(items_max, persistent_grid<64>(lds_pre))), dim3(256),
+                         lds_pre, st, a);
     else
       hipLaunchKernelGGL(decode_attend_bf16_kernel<128>,
-                         dim3((unsigned)min64(items_max, persistent_grid<128>())), dim3(256), 0, st, a);
+                         dim3((unsigned)min64(items_max, persistent_grid<128>(lds_pre))), dim3(256),
+                         lds_pre, st, a);
   } else {
     if (s.d == 64) hipLaunchKernelGGL(decode_attend_f32_kernel<64>, g3, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(decode_attend_f32_kernel<128>, g3, dim3(256), 0, st, a);
