@@ -156,11 +156,70 @@ struct Stride16Reduce {   // lanes l, l^16, l^32, l^48 (one MFMA 16x16 C-fragmen
   }
 };
 
+// Support statistics of the register-held values at tau: count, s1, s2 and
+// the smallest positive y = x - tau (MODE as in entmax_tau).  Only the first
+// nact4 groups of four values are visited (nact4 is uniform across the wave,
+// so the skipped groups cost no VALU, and the loop leaves at the first
+// inactive group).
+template <int VPL, int mode>
+__device__ __forceinline__ void entmax_accumulate(const float (&xv)[VPL], float tau, float e,
+                                                  int nact4, int& kc, float& s1, float& s2,
+                                                  float& ymin) {
+  kc = 0;
+  s1 = 0.f;
+  s2 = 0.f;
+  ymin = INFINITY;
+#pragma unroll
+  for (int g4 = 0; g4 < VPL / 4; ++g4) {
+    if (g4 >= nact4) break;   // the active groups come first
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const float y = xv[4 * g4 + ii] - tau;
+      const bool in = y > 0.f;
+      const float yp = fmaxf(y, 0.f);
+      kc += in ? 1 : 0;
+      // min(ymin, y over the support) as v_med3(z, ymin, -inf): no NaN
+      // quieting of the loop-carried ymin as fminf would need
+      ymin = __builtin_amdgcn_fmed3f(in ? y : INFINITY, ymin, -INFINITY);
+      if constexpr (mode == kEntmax15) { s1 += yp; s2 = fmaf(yp, yp, s2); }
+      else if constexpr (mode == kSparsemax) { s1 += yp; }
+      else if constexpr (mode == kEntmaxQuartic) { const float y2 = yp * yp; s1 = fmaf(y2, yp, s1); s2 = fmaf(y2, y2, s2); }
+      else if (in) { const float l = __log2f(y); s1 += exp2f((e - 1.f) * l); s2 += exp2f(e * l); }
+    }
+  }
+}
+
+// One update of tau from the statistics of the row's support at tau (k, s1,
+// s2, ymin as above); true once tau is final.  Sparsemax: Michelot's step,
+// exact once the support is stable; alpha = 1.5: the closed-form root on the
+// current support when it keeps the whole support above it, else a Newton
+// step on the e-norm form; other alpha: the Newton step.
+template <int mode>
+__device__ __forceinline__ bool entmax_update(float k, float s1, float s2, float ymin, float e,
+                                              float& tau) {
+  if constexpr (mode == kSparsemax) {
+    const float step = (s1 - 1.f) / k;
+    tau += step;
+    return step < ymin;
+  } else if constexpr (mode == kEntmax15) {
+    const float disc = s1 * s1 - k * (s2 - 1.f);
+    if (disc >= 0.f) {
+      const float d = (s2 - 1.f) / (s1 + sqrtf(disc));
+      if (d < ymin) { tau += d; return true; }
+    }
+    const float step = entmax_norm_step(s2, s1, mode, e);
+    tau += step;
+    return !(step > 1e-7f * fmaxf(1.f, fabsf(tau)));
+  } else {
+    const float step = entmax_norm_step(s2, s1, mode, e);
+    tau += step;
+    return !(step > 1e-7f * fmaxf(1.f, fabsf(tau)));
+  }
+}
+
 // Same threshold with the row held in registers: each lane of the row's lane
 // set holds VPL of its values (-inf for absent entries); `red` reduces over
-// that lane set.  Only the first nact4 groups of four values are visited
-// (nact4 is uniform across the wave, so the skipped groups cost no VALU, and
-// the loop leaves at the first inactive group).
+// that lane set.
 template <int VPL, int mode, typename Red>
 __device__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int nact4 = VPL / 4) {
   float xmax = -INFINITY;
@@ -173,49 +232,14 @@ __device__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int na
   xmax = red.max(xmax);
   float tau = xmax - 1.0f;
   for (int it = 0; it < 64; ++it) {
-    float s1 = 0.f, s2 = 0.f, ymin = INFINITY;
-    int kc = 0;
-#pragma unroll
-    for (int g4 = 0; g4 < VPL / 4; ++g4) {
-      if (g4 >= nact4) break;   // the active groups come first
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const float y = xv[4 * g4 + ii] - tau;
-        const bool in = y > 0.f;
-        const float yp = fmaxf(y, 0.f);
-        kc += in ? 1 : 0;
-        // min(ymin, y over the support) as v_med3(z, ymin, -inf): no NaN
-        // quieting of the loop-carried ymin as fminf would need
-        ymin = __builtin_amdgcn_fmed3f(in ? y : INFINITY, ymin, -INFINITY);
-        if constexpr (mode == kEntmax15) { s1 += yp; s2 = fmaf(yp, yp, s2); }
-        else if constexpr (mode == kSparsemax) { s1 += yp; }
-        else if constexpr (mode == kEntmaxQuartic) { const float y2 = yp * yp; s1 = fmaf(y2, yp, s1); s2 = fmaf(y2, y2, s2); }
-        else if (in) { const float l = __log2f(y); s1 += exp2f((e - 1.f) * l); s2 += exp2f(e * l); }
-      }
-    }
-    float k = red.sum((float)kc);
+    int kc;
+    float s1, s2, ymin;
+    entmax_accumulate<VPL, mode>(xv, tau, e, nact4, kc, s1, s2, ymin);
+    const float k = red.sum((float)kc);
     s1 = red.sum(s1);
     s2 = red.sum(s2);
     ymin = red.min(ymin);
-    float step;
-    if constexpr (mode == kSparsemax) {
-      step = (s1 - 1.f) / k;
-      tau += step;
-      if (step < ymin) break;
-    } else if constexpr (mode == kEntmax15) {
-      const float disc = s1 * s1 - k * (s2 - 1.f);
-      if (disc >= 0.f) {
-        const float d = (s2 - 1.f) / (s1 + sqrtf(disc));
-        if (d < ymin) { tau += d; break; }
-      }
-      step = entmax_norm_step(s2, s1, mode, e);
-      tau += step;
-      if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
-    } else {
-      step = entmax_norm_step(s2, s1, mode, e);
-      tau += step;
-      if (!(step > 1e-7f * fmaxf(1.f, fabsf(tau)))) break;
-    }
+    if (entmax_update<mode>(k, s1, s2, ymin, e, tau)) break;
   }
   return tau;
 }
