@@ -8,7 +8,9 @@ The arithmetic lives in ``dash_oracle.c`` (plain C, IEEE double, OpenMP over
 query rows), which follows the DashAttention explainer pages (gist.science,
 arXiv 2605.18753), "Technical summary": Stage 0 (local chunk summarization),
 Stage 1 (entmax chunk routing, w = alpha-entmax(gamma * zbar)) and Stage 2
-(prior-induced sparse softmax).  This module only marshals numpy arrays.
+(prior-induced sparse softmax).  Stage 0 pools a block uniformly, or, given
+a summary query q_bar per KV head, by scaled dot-product attention of q_bar
+over the block's keys.  This module only marshals numpy arrays.
 
 Parity pins (all in ``tests/test_oracle_*.py``): closed-form sparsemax and
 1.5-entmax values, an independent SLSQP solve of the Tsallis-entmax problem,
@@ -44,7 +46,8 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if (not os.path.exists(_LIB)
+                or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         dp = ctypes.POINTER(ctypes.c_double)
@@ -54,7 +57,8 @@ def _load():
         lib.oracle_entmax.argtypes = [dp, ctypes.c_int, ctypes.c_double, ctypes.c_int, dp]
         lib.oracle_summaries.restype = None
         lib.oracle_summaries.argtypes = [fp, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
-                                         ctypes.c_int, ctypes.c_int, ctypes.c_int64, fp, dp]
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int64, fp, fp,
+                                         dp]
         lib.oracle_forward_rows.restype = ctypes.c_int
         lib.oracle_forward_rows.argtypes = [
             fp, ip, ip, ctypes.c_int64, fp, fp, ctypes.c_int64, ctypes.c_int64,
@@ -95,17 +99,25 @@ def entmax_of_scores(y, alpha: float, method: str = "auto"):
     return entmax((alpha - 1.0) * y, alpha, method)
 
 
-def summaries(k, w_s, bs: int, nblocks: int):
-    """Stage 0 summaries of blocks [0, nblocks): k [B, Hkv, L, d] -> [B, Hkv, nblocks, d]."""
+def summaries(k, w_s, bs: int, nblocks: int, q_bar=None):
+    """Stage 0 summaries of blocks [0, nblocks): k [B, Hkv, L, d] -> [B, Hkv, nblocks, d].
+
+    ``q_bar`` None pools each block uniformly; a [Hkv, d] array pools it by
+    scaled dot-product attention of that head's summary query over the keys."""
     k = np.ascontiguousarray(k, dtype=np.float32)
     w_s = np.ascontiguousarray(w_s, dtype=np.float32)
     B, Hkv, L, d = k.shape
+    if q_bar is not None:
+        q_bar = np.ascontiguousarray(q_bar, dtype=np.float32)
+        if q_bar.shape != (Hkv, d):
+            raise ValueError("q_bar must be [Hkv, d]")
     if nblocks * bs > L:
         raise ValueError("summaries requested for incomplete blocks")
     out = np.zeros((B, Hkv, max(nblocks, 0), d), dtype=np.float64)
     if nblocks > 0:
         _load().oracle_summaries(_ptr(k, ctypes.c_float), B, Hkv, L, d, bs, nblocks,
-                                 _ptr(w_s, ctypes.c_float), _ptr(out, ctypes.c_double))
+                                 _ptr(w_s, ctypes.c_float), _ptr(q_bar, ctypes.c_float),
+                                 _ptr(out, ctypes.c_double))
     return out
 
 
@@ -153,7 +165,8 @@ def forward_rows(q_rows, row_b, row_pos, k, v, summ, *, n_heads: int, bs: int, a
 
 
 def prefill(q, k, v, w_s, *, bs: int, alpha: float, gamma: float, causal: bool = True,
-            positions=None, batches=None, nb_out: int = 0, want=("o", "tau"), threads: int = 0):
+            positions=None, batches=None, nb_out: int = 0, want=("o", "tau"), threads: int = 0,
+            q_bar=None):
     """Causal (or non-causal) prefill: q [B, H, N, d], k/v [B, Hkv, N, d].
 
     Computes the rows (b, i) for b in ``batches`` (default all) and i in
@@ -166,7 +179,7 @@ def prefill(q, k, v, w_s, *, bs: int, alpha: float, gamma: float, causal: bool =
     nblocks = N // bs
     sub_k = np.asarray(k, dtype=np.float32)[batches]
     sub_v = np.asarray(v, dtype=np.float32)[batches]
-    summ = summaries(sub_k, w_s, bs, nblocks)
+    summ = summaries(sub_k, w_s, bs, nblocks, q_bar)
     rb = np.repeat(np.arange(len(batches)), len(positions))
     rp = np.tile(positions, len(batches))
     q_rows = np.ascontiguousarray(np.asarray(q)[batches][:, :, positions, :].transpose(0, 2, 1, 3)
@@ -179,7 +192,7 @@ def prefill(q, k, v, w_s, *, bs: int, alpha: float, gamma: float, causal: bool =
 
 
 def decode(q, k_cache, v_cache, cache_len, w_s, *, bs: int, alpha: float, gamma: float,
-           batches=None, nb_out: int = 0, want=("o", "tau"), threads: int = 0):
+           batches=None, nb_out: int = 0, want=("o", "tau"), threads: int = 0, q_bar=None):
     """One decode step: q [B, H, d] is the query at position cache_len[b] - 1
     whose key/value are already in the caches [B, Hkv, max_len, d].  Also
     returns the summary of the block this token completes (None otherwise)."""
@@ -190,7 +203,7 @@ def decode(q, k_cache, v_cache, cache_len, w_s, *, bs: int, alpha: float, gamma:
     sub_k = np.asarray(k_cache, dtype=np.float32)[batches]
     sub_v = np.asarray(v_cache, dtype=np.float32)[batches]
     nblocks = int(lens.max()) // bs
-    summ = summaries(sub_k, w_s, bs, nblocks)
+    summ = summaries(sub_k, w_s, bs, nblocks, q_bar)
     res = forward_rows(q[batches], np.arange(len(batches)), lens - 1, sub_k, sub_v, summ,
                        n_heads=H, bs=bs, alpha=alpha, gamma=gamma, causal=True,
                        nb_out=nb_out, want=want, threads=threads)

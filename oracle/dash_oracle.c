@@ -33,6 +33,10 @@
  *       (after entmax); every head of the group uses the average pbar.
  *   R6  prior-induced softmax: logit q.k/sqrt(d) + log pbar(block) on routed
  *       blocks (pbar > 0); blocks with pbar = 0 are masked.
+ *   R3b with a summary query qbar (one d-vector per KV head), the block is
+ *       pooled by scaled dot-product attention of qbar over the block's keys,
+ *       the keys serving as values: m = sum_t softmax_t(qbar . k_t / sqrt(d)) k_t,
+ *       then s_j = m . W_s as in R3.  qbar = 0 gives R3's uniform mean.
  */
 #include <math.h>
 #include <stdint.h>
@@ -134,18 +138,40 @@ double oracle_entmax(const double* x, int n, double alpha, int method, double* p
 /* ------------------------------------------------------------------------ */
 
 /* k: [B, Hkv, kv_stride, d] float32; blocks [0, nblocks) must be complete.
- * out: [B, Hkv, nblocks, d] double.  s_j = (1/bs sum_{t in j} k_t) . W_s. */
+ * q_bar: NULL (uniform pooling, R3) or [Hkv, d] float32 summary queries (R3b).
+ * out: [B, Hkv, nblocks, d] double.
+ *   weights  e_t = 1                                           (q_bar NULL)
+ *            e_t = exp(z_t - max_u z_u), z_t = qbar_h . k_t / sqrt(d)
+ *   pooled   m = sum_{t in j} e_t k_t / sum_{t in j} e_t
+ *   summary  s_j = m . W_s */
 void oracle_summaries(const float* k, int B, int Hkv, int64_t kv_stride, int d, int bs,
-                      int64_t nblocks, const float* w_s, double* out) {
+                      int64_t nblocks, const float* w_s, const float* q_bar, double* out) {
   int64_t units = (int64_t)B * Hkv * nblocks;
 #pragma omp parallel for schedule(static)
   for (int64_t u = 0; u < units; ++u) {
     int64_t j = u % nblocks, bh = u / nblocks;
+    int h = (int)(bh % Hkv);
     const float* kb = k + (bh * kv_stride + j * bs) * d;
+    double* e = (double*)malloc(sizeof(double) * bs);
+    double esum = 0.0;
+    if (q_bar == NULL) {
+      for (int t = 0; t < bs; ++t) e[t] = 1.0;
+    } else {
+      const float* qb = q_bar + (int64_t)h * d;
+      double zmax = -INFINITY;
+      for (int t = 0; t < bs; ++t) {
+        double z = 0.0;
+        for (int c = 0; c < d; ++c) z += (double)qb[c] * (double)kb[(int64_t)t * d + c];
+        e[t] = z / sqrt((double)d);
+        if (e[t] > zmax) zmax = e[t];
+      }
+      for (int t = 0; t < bs; ++t) e[t] = exp(e[t] - zmax);
+    }
+    for (int t = 0; t < bs; ++t) esum += e[t];
     double* m = (double*)calloc(d, sizeof(double));
     for (int t = 0; t < bs; ++t)
-      for (int c = 0; c < d; ++c) m[c] += (double)kb[(int64_t)t * d + c];
-    for (int c = 0; c < d; ++c) m[c] /= bs;
+      for (int c = 0; c < d; ++c) m[c] += e[t] * (double)kb[(int64_t)t * d + c];
+    for (int c = 0; c < d; ++c) m[c] /= esum;
     double* s = out + u * d;
     for (int c = 0; c < d; ++c) {
       double acc = 0.0;
@@ -153,6 +179,7 @@ void oracle_summaries(const float* k, int B, int Hkv, int64_t kv_stride, int d, 
       s[c] = acc;
     }
     free(m);
+    free(e);
   }
 }
 
