@@ -120,6 +120,11 @@ def prefill_bench(args, torch, dash, W):
     rb = dash.RouteBuffers(sizes, dev)
     t_sum = events_time(lambda: dash.dash_summarize(p, k, N, 0, nb, ws_mat, summ, nb),
                         args.steps, 2, torch)
+    # Stage 0 pooled by seeded summary queries (same keys, same output size)
+    qb = torch.from_numpy(W.summary_query(w.replace(summary_query=1.0))).to(dev)
+    summ_q = torch.empty_like(summ)
+    t_sum_q = events_time(lambda: dash.dash_summarize(p, k, N, 0, nb, ws_mat, summ_q, nb,
+                                                      q_bar=qb), args.steps, 2, torch)
     t_route = events_time(lambda: dash.dash_route(p, q, N, summ, nb, rb), args.steps, 2, torch)
     o2 = torch.empty_like(q)
     t_att = events_time(lambda: dash.dash_attend(p, q, k, v, N, rb, o2), args.steps, 2, torch)
@@ -139,7 +144,8 @@ def prefill_bench(args, torch, dash, W):
     traffic = traffic_for_attend(w.name)
     res = {
         "workload": w, "ms_step": ms_step, "tok_s": B * N / (ms_step * 1e-3),
-        "stages_ms": {"summarize": t_sum, "route": t_route, "attend": t_att},
+        "stages_ms": {"summarize": t_sum, "route": t_route, "attend": t_att,
+                      "summarize_qbar": t_sum_q},
         "attend_flops": att_flops, "attend_tflops": achieved,
         "tile_union_density": tile_union_density,
         "selected_chunk_fraction": float(chunks) / dense_chunks,

@@ -138,17 +138,23 @@ dash_status dash_route_sizes_decode(const dash_params* p, int64_t max_len, dash_
 dash_status dash_prefill_workspace_bytes(const dash_params* p, int64_t n, size_t* bytes);
 dash_status dash_decode_workspace_bytes(const dash_params* p, int64_t max_len, size_t* bytes);
 
-/* Stage 0 ("local chunk summarization"; summaries are computed once a chunk
- * is complete and then cached).  For every sequence b, KV head g and block
- * j in [blk_begin, blk_end): summ[b, g, j, :] = mean(k[b, g, j*bs:(j+1)*bs, :]) . w_s,
- * accumulated in float32.
+/* Stage 0 ("local chunk summarization", DashAttention explainer, Technical
+ * summary; summaries are computed once a chunk is complete and then cached).
+ * For every sequence b, KV head g and block j in [blk_begin, blk_end), with
+ * K = k[b, g, j*bs:(j+1)*bs, :]:
+ *   q_bar NULL    summ[b, g, j, :] = mean_t(K[t]) . w_s
+ *   q_bar given   summ[b, g, j, :] = (sum_t a_t K[t]) . w_s,
+ *                 a = softmax_t(q_bar[g] . K[t] / sqrt(d))
+ * (the learned summary query attending to the chunk's keys by local scaled
+ * dot-product attention; a zero query is the mean), accumulated in float32.
  *   k      [B, Hkv, kv_len, d] dtype; (blk_end * bs) <= kv_len
  *   w_s    [d, d] float32
+ *   q_bar  NULL or [Hkv, d] float32 summary queries
  *   summ   [B, Hkv, summ_blocks, d] float32, blk_end <= summ_blocks
  * Blocks outside [blk_begin, blk_end) are left untouched. */
 dash_status dash_summarize(const dash_params* p, const void* k, int64_t kv_len, int64_t blk_begin,
-                           int64_t blk_end, const float* w_s, float* summ, int64_t summ_blocks,
-                           void* stream);
+                           int64_t blk_end, const float* w_s, const float* q_bar, float* summ,
+                           int64_t summ_blocks, void* stream);
 
 /* Stage 1 for causal prefill of positions 0..n-1: coarse scores, alpha-entmax
  * per (query, head), GQA average, per-tile union and compaction.
@@ -168,24 +174,27 @@ dash_status dash_route(const dash_params* p, const void* q, int64_t n, const flo
 dash_status dash_attend(const dash_params* p, const void* q, const void* k, const void* v,
                         int64_t n, const dash_route_buf* route, void* o, void* stream);
 
-/* Fused causal prefill: dash_summarize of blocks [0, floor(n/bs)) into summ,
- * dash_route into the workspace, dash_attend into o.
+/* Fused causal prefill: dash_summarize of blocks [0, floor(n/bs)) into summ
+ * (with the summary queries q_bar, NULL = mean pooling), dash_route into the
+ * workspace, dash_attend into o.
  *   summ   [B, Hkv, summ_blocks, d] float32, summ_blocks >= floor(n/bs)
+ *   q_bar  NULL or [Hkv, d] float32 summary queries
  *   ws     >= dash_prefill_workspace_bytes(p, n) bytes, 256-byte aligned
  * Same size limit as dash_attend. */
 dash_status dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
-                         int64_t n, const float* w_s, float* summ, int64_t summ_blocks, void* o,
-                         void* ws, size_t ws_bytes, void* stream);
+                         int64_t n, const float* w_s, const float* q_bar, float* summ,
+                         int64_t summ_blocks, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* One incremental decoding step for every sequence b: the query q[b] sits at
  * position L = cache_len[b] - 1 and its key/value are already in the caches.
  * Routes over the cached summaries of blocks j < floor(L / bs), attends to the
  * selected blocks plus keys [floor(L/bs)*bs, L] of the own block, and, when
  * cache_len[b] % bs == 0 (the step completes a block), writes the summary of
- * block cache_len[b]/bs - 1 into summ.
+ * block cache_len[b]/bs - 1 into summ (as dash_summarize with q_bar).
  *   q, o            [B, H, d] dtype
  *   k_cache, v_cache [B, Hkv, max_len, d] dtype
  *   cache_len       [B] int32 DEVICE array, 1 <= cache_len[b] <= max_len
+ *   q_bar           NULL or [Hkv, d] float32 summary queries
  *   summ            [B, Hkv, summ_blocks, d] float32, summ_blocks >= ceil(max_len/bs),
  *                   read for blocks < floor((cache_len-1)/bs), written as above
  *   route           optional (NULL = use the workspace): where the routing
@@ -196,8 +205,9 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
  * B * Hkv > 65535, or for bf16 when B * Hkv > 8192. */
 dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* cache_len, int64_t max_len,
-                        const float* w_s, float* summ, int64_t summ_blocks, void* o,
-                        const dash_route_buf* route, void* ws, size_t ws_bytes, void* stream);
+                        const float* w_s, const float* q_bar, float* summ, int64_t summ_blocks,
+                        void* o, const dash_route_buf* route, void* ws, size_t ws_bytes,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -69,15 +69,16 @@ for _name in ("dash_prefill_workspace_bytes", "dash_decode_workspace_bytes"):
     getattr(_lib, _name).restype = ctypes.c_int
     getattr(_lib, _name).argtypes = [_P, _I, ctypes.POINTER(ctypes.c_size_t)]
 _lib.dash_summarize.restype = ctypes.c_int
-_lib.dash_summarize.argtypes = [_P, _V, _I, _I, _I, _V, _V, _I, _V]
+_lib.dash_summarize.argtypes = [_P, _V, _I, _I, _I, _V, _V, _V, _I, _V]
 _lib.dash_route.restype = ctypes.c_int
 _lib.dash_route.argtypes = [_P, _V, _I, _V, _I, _R, _V]
 _lib.dash_attend.restype = ctypes.c_int
 _lib.dash_attend.argtypes = [_P, _V, _V, _V, _I, _R, _V, _V]
 _lib.dash_prefill.restype = ctypes.c_int
-_lib.dash_prefill.argtypes = [_P, _V, _V, _V, _I, _V, _V, _I, _V, _V, ctypes.c_size_t, _V]
+_lib.dash_prefill.argtypes = [_P, _V, _V, _V, _I, _V, _V, _V, _I, _V, _V, ctypes.c_size_t, _V]
 _lib.dash_decode.restype = ctypes.c_int
-_lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _I, _V, _R, _V, ctypes.c_size_t, _V]
+_lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _V, _I, _V, _R, _V, ctypes.c_size_t,
+                             _V]
 
 EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
             "dash_route_sizes_decode", "dash_prefill_workspace_bytes",
@@ -123,6 +124,11 @@ def _dev(t, name, numel, dtype=None):
     if t.numel() < numel:
         raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
     return t.data_ptr()
+
+
+def _opt_dev(t, name, numel, dtype=None):
+    """As _dev, or a null pointer for None."""
+    return None if t is None else _dev(t, name, numel, dtype)
 
 
 def _stream(stream):
@@ -204,11 +210,13 @@ def workspace(nbytes, device="cuda"):
 # entry points
 # ---------------------------------------------------------------------------------------
 
-def dash_summarize(p, k, kv_len, blk_begin, blk_end, w_s, summ, summ_blocks, stream=None):
+def dash_summarize(p, k, kv_len, blk_begin, blk_end, w_s, summ, summ_blocks, stream=None,
+                   q_bar=None):
     B, Hkv, d = p.batch, p.n_kv_heads, p.head_dim
     _check("dash_summarize", _lib.dash_summarize(
         ctypes.byref(p), _dev(k, "k", B * Hkv * kv_len * d, torch_dtype(p)), kv_len, blk_begin,
         blk_end, _dev(w_s, "w_s", d * d, torch.float32),
+        _opt_dev(q_bar, "q_bar", Hkv * d, torch.float32),
         _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
         _stream(stream)))
 
@@ -236,19 +244,20 @@ def dash_attend(p, q, k, v, n, route: RouteBuffers, o, stream=None):
         _stream(stream)))
 
 
-def dash_prefill(p, q, k, v, n, w_s, summ, summ_blocks, o, ws, stream=None):
+def dash_prefill(p, q, k, v, n, w_s, summ, summ_blocks, o, ws, stream=None, q_bar=None):
     B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
     dt = torch_dtype(p)
     _check("dash_prefill", _lib.dash_prefill(
         ctypes.byref(p), _dev(q, "q", B * H * n * d, dt), _dev(k, "k", B * Hkv * n * d, dt),
         _dev(v, "v", B * Hkv * n * d, dt), n, _dev(w_s, "w_s", d * d, torch.float32),
+        _opt_dev(q_bar, "q_bar", Hkv * d, torch.float32),
         _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
         _dev(o, "o", B * H * n * d, dt), _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
         _stream(stream)))
 
 
 def dash_decode(p, q, k_cache, v_cache, cache_len, max_len, w_s, summ, summ_blocks, o,
-                ws, route: RouteBuffers | None = None, stream=None):
+                ws, route: RouteBuffers | None = None, stream=None, q_bar=None):
     B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
     dt = torch_dtype(p)
     rb = None
@@ -263,6 +272,7 @@ def dash_decode(p, q, k_cache, v_cache, cache_len, max_len, w_s, summ, summ_bloc
         _dev(v_cache, "v_cache", B * Hkv * max_len * d, dt),
         _dev(cache_len, "cache_len", B, torch.int32), max_len,
         _dev(w_s, "w_s", d * d, torch.float32),
+        _opt_dev(q_bar, "q_bar", Hkv * d, torch.float32),
         _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
         _dev(o, "o", B * H * d, dt), rb, _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
         _stream(stream)))

@@ -162,8 +162,8 @@ dash_status dash_decode_workspace_bytes(const dash_params* p, int64_t max_len, s
 }
 
 dash_status dash_summarize(const dash_params* p, const void* k, int64_t kv_len, int64_t blk_begin,
-                           int64_t blk_end, const float* w_s, float* summ, int64_t summ_blocks,
-                           void* stream) {
+                           int64_t blk_end, const float* w_s, const float* q_bar, float* summ,
+                           int64_t summ_blocks, void* stream) {
   Shape s;
   dash_status st = check_params(p, &s);
   if (st != DASH_OK) return st;
@@ -171,7 +171,7 @@ dash_status dash_summarize(const dash_params* p, const void* k, int64_t kv_len, 
   if (blk_begin < 0 || blk_end < blk_begin || kv_len < blk_end * s.bs || summ_blocks < blk_end)
     return DASH_ERR_INVALID_ARG;
   if (!grid_ok((blk_end - blk_begin) * s.B * s.Hkv)) return DASH_ERR_UNSUPPORTED;
-  return hip_status(dash::launch_summarize(s, k, kv_len, blk_begin, blk_end, w_s, summ,
+  return hip_status(dash::launch_summarize(s, k, kv_len, blk_begin, blk_end, w_s, q_bar, summ,
                                            summ_blocks, (hipStream_t)stream));
 }
 
@@ -205,8 +205,8 @@ dash_status dash_attend(const dash_params* p, const void* q, const void* k, cons
 }
 
 dash_status dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
-                         int64_t n, const float* w_s, float* summ, int64_t summ_blocks, void* o,
-                         void* ws, size_t ws_bytes, void* stream) {
+                         int64_t n, const float* w_s, const float* q_bar, float* summ,
+                         int64_t summ_blocks, void* o, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   dash_status st = check_params(p, &s);
   if (st != DASH_OK) return st;
@@ -227,7 +227,7 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
   rb.sel_logp = (float*)(base + L.off_logp);
   rb.support_bits = nullptr;
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = dash::launch_summarize(s, k, n, 0, n / s.bs, w_s, summ, summ_blocks, hs);
+  hipError_t e = dash::launch_summarize(s, k, n, 0, n / s.bs, w_s, q_bar, summ, summ_blocks, hs);
   if (e == hipSuccess) e = dash::launch_route_prefill(s, q, n, summ, summ_blocks, rb, hs);
   if (e == hipSuccess) e = dash::launch_attend_prefill(s, q, k, v, n, rb, o, hs);
   return hip_status(e);
@@ -235,8 +235,9 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
 
 dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* cache_len, int64_t max_len,
-                        const float* w_s, float* summ, int64_t summ_blocks, void* o,
-                        const dash_route_buf* route, void* ws, size_t ws_bytes, void* stream) {
+                        const float* w_s, const float* q_bar, float* summ, int64_t summ_blocks,
+                        void* o, const dash_route_buf* route, void* ws, size_t ws_bytes,
+                        void* stream) {
   Shape s;
   dash_status st = check_params(p, &s);
   if (st != DASH_OK) return st;
@@ -254,8 +255,9 @@ dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache
     return DASH_ERR_UNSUPPORTED;
   dash_route_buf rb = {nullptr, nullptr, nullptr, nullptr, nullptr};
   if (route) rb = *route;
-  return hip_status(dash::launch_decode(s, q, k_cache, v_cache, cache_len, max_len, w_s, summ,
-                                        summ_blocks, o, rb, L, (char*)ws, (hipStream_t)stream));
+  return hip_status(dash::launch_decode(s, q, k_cache, v_cache, cache_len, max_len, w_s, q_bar,
+                                        summ, summ_blocks, o, rb, L, (char*)ws,
+                                        (hipStream_t)stream));
 }
 
 }  // extern "C"

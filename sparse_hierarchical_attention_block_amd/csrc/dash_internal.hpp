@@ -16,10 +16,11 @@ struct Shape {
   int dtype;  // dash_dtype
 };
 
-// Stage 0: summaries of blocks [blk_begin, blk_end) for every (b, kv head).
+// Stage 0: summaries of blocks [blk_begin, blk_end) for every (b, kv head);
+// q_bar is nullptr (mean pooling) or [Hkv, d] summary queries.
 hipError_t launch_summarize(const Shape& s, const void* k, int64_t kv_len, int64_t blk_begin,
-                            int64_t blk_end, const float* w_s, float* summ, int64_t summ_blocks,
-                            hipStream_t st);
+                            int64_t blk_end, const float* w_s, const float* q_bar, float* summ,
+                            int64_t summ_blocks, hipStream_t st);
 
 // Stage 1, causal prefill of positions 0..n-1.
 hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const float* summ,
@@ -52,8 +53,9 @@ constexpr int kMaxDevices = 64;    // per-device launch-shape caches
 
 // One decode step (route, attend, combine, summary update).
 hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const void* vc,
-                         const int32_t* cache_len, int64_t max_len, const float* w_s, float* summ,
-                         int64_t summ_blocks, void* o, const dash_route_buf& rb,
+                         const int32_t* cache_len, int64_t max_len, const float* w_s,
+                         const float* q_bar, float* summ, int64_t summ_blocks, void* o,
+                         const dash_route_buf& rb,
                          const DecodeLayout& L, char* ws, hipStream_t st);
 
 }  // namespace dash

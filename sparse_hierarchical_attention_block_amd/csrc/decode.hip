@@ -51,6 +51,7 @@ struct DecodeArgs {
   float* part;       // [B, Hkv, n_split, G, D + 2]
   float* summ_w;     // the summary cache, written for a block this step completes
   const float* w_s;
+  const float* q_bar;  // [Hkv, D] summary queries, or null (mean pooling)
   int64_t nb;
   int64_t n_split;
   int nwords;
@@ -686,6 +687,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     if ((len & (a.bs - 1)) == 0) {
       const int64_t j = (len >> a.bs_log) - 1;
       summarize_blocks<T, D, 1>((const T*)a.kc + (bg * a.max_len + j * a.bs) * D, 1, a.bs, a.w_s,
+                                a.q_bar ? a.q_bar + g * D : nullptr,
                                 a.summ_w + (bg * a.summ_blocks + j) * D);
     }
     return;
@@ -781,9 +783,10 @@ DecodeLayout decode_layout(const Shape& s, int64_t max_len) {
 }
 
 hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const void* vc,
-                         const int32_t* cache_len, int64_t max_len, const float* w_s, float* summ,
-                         int64_t summ_blocks, void* o, const dash_route_buf& rb,
-                         const DecodeLayout& L, char* ws, hipStream_t st) {
+                         const int32_t* cache_len, int64_t max_len, const float* w_s,
+                         const float* q_bar, float* summ, int64_t summ_blocks, void* o,
+                         const dash_route_buf& rb, const DecodeLayout& L, char* ws,
+                         hipStream_t st) {
   DecodeArgs a;
   a.xpitch = 0;
   a.q = q;
@@ -803,6 +806,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   a.part = (float*)(ws + L.off_part);
   a.summ_w = summ;
   a.w_s = w_s;
+  a.q_bar = q_bar;
   a.nb = L.nb;
   a.n_split = L.n_split;
   a.nwords = (int)((L.nb + 31) / 32);

@@ -27,6 +27,12 @@ def to_dev(a, dtype):
     return t.to(dev(), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
 
 
+def qbar_dev(inp):
+    """The summary queries of ``inp`` on the GPU, or None."""
+    qb = inp.get("q_bar")
+    return None if qb is None else torch.from_numpy(np.ascontiguousarray(qb, np.float32)).to(dev())
+
+
 def params(w, **over):
     kw = dict(batch=w.batch, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
               block_size=w.block_size, alpha=w.alpha, gamma=w.gamma, dtype=w.dtype)
@@ -51,7 +57,7 @@ def run_prefill(w, inp, bits=True):
     nbf = N // bs
     summ_blocks = max(nbf, 1)
     summ = torch.zeros(B * Hkv * summ_blocks * d, dtype=torch.float32, device=dev())
-    dash.dash_summarize(p, k, N, 0, nbf, ws, summ, summ_blocks)
+    dash.dash_summarize(p, k, N, 0, nbf, ws, summ, summ_blocks, q_bar=qbar_dev(inp))
     sizes = dash.dash_route_sizes_prefill(p, N)
     rb = dash.RouteBuffers(sizes, dev(), bits=bits)
     dash.dash_route(p, q, N, summ, summ_blocks, rb)
@@ -81,7 +87,7 @@ def run_prefill_fused(w, inp):
     summ = torch.zeros(B * Hkv * summ_blocks * d, dtype=torch.float32, device=dev())
     o = torch.empty_like(q)
     ws = dash.workspace(dash.dash_prefill_workspace_bytes(p, N), dev())
-    dash.dash_prefill(p, q, k, v, N, ws_mat, summ, summ_blocks, o, ws)
+    dash.dash_prefill(p, q, k, v, N, ws_mat, summ, summ_blocks, o, ws, q_bar=qbar_dev(inp))
     torch.cuda.synchronize()
     return o.float().cpu().numpy()
 
@@ -104,13 +110,15 @@ def run_decode(w, inp, summ_np=None, route=True):
             np.ascontiguousarray(summ_np, np.float32)).to(dev())
     elif Lmax // bs > 0:
         # blocks complete before each sequence's new token
-        dash.dash_summarize(p, kc, Lmax, 0, Lmax // bs, ws_mat, summ, summ_blocks)
+        dash.dash_summarize(p, kc, Lmax, 0, Lmax // bs, ws_mat, summ, summ_blocks,
+                            q_bar=qbar_dev(inp))
     summ_before = summ.clone()
     o = torch.empty_like(q)
     ws = dash.workspace(dash.dash_decode_workspace_bytes(p, Lmax), dev())
     rb = dash.RouteBuffers(dash.dash_route_sizes_decode(p, Lmax), dev(), bits=True) if route \
         else None
-    dash.dash_decode(p, q, kc, vc, lens, Lmax, ws_mat, summ, summ_blocks, o, ws, route=rb)
+    dash.dash_decode(p, q, kc, vc, lens, Lmax, ws_mat, summ, summ_blocks, o, ws, route=rb,
+                     q_bar=qbar_dev(inp))
     torch.cuda.synchronize()
     nb = summ_blocks
     out = {"o": o.float().cpu().numpy(),

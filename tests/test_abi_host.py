@@ -74,33 +74,33 @@ def test_bad_params(kw, code):
     out = ctypes.c_size_t()
     p = P(**kw)
     assert L._lib.dash_prefill_workspace_bytes(ctypes.byref(p), 1024, ctypes.byref(out)) == code
-    assert L._lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, 16, FAKE,
+    assert L._lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, None, FAKE, 16, FAKE,
                                FAKE, 1 << 40, None) == code
 
 
 def test_null_pointers_and_sizes():
     p = P()
     lib = L._lib
-    assert lib.dash_prefill(ctypes.byref(p), None, FAKE, FAKE, 1024, FAKE, FAKE, 16, FAKE, FAKE,
-                            1 << 30, None) == L.DASH_ERR_INVALID_ARG
-    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, -1, FAKE, FAKE, 16, FAKE, FAKE,
-                            1 << 30, None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_prefill(ctypes.byref(p), None, FAKE, FAKE, 1024, FAKE, None, FAKE, 16, FAKE,
+                            FAKE, 1 << 30, None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, -1, FAKE, None, FAKE, 16, FAKE,
+                            FAKE, 1 << 30, None) == L.DASH_ERR_INVALID_ARG
     # summary capacity below floor(n / bs)
-    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, 15, FAKE, FAKE,
-                            1 << 30, None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, None, FAKE, 15, FAKE,
+                            FAKE, 1 << 30, None) == L.DASH_ERR_INVALID_ARG
     # workspace too small / misaligned
     need = dash.dash_prefill_workspace_bytes(p, 1024)
-    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, 16, FAKE, FAKE,
-                            need - 1, None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
-    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, 16, FAKE,
+    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, None, FAKE, 16, FAKE,
+                            FAKE, need - 1, None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, None, FAKE, 16, FAKE,
                             FAKE + 8, need, None) == L.DASH_ERR_INVALID_ARG
     # empty problem: nothing to do
-    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, FAKE, FAKE,
-                            0, None) == L.DASH_OK
+    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, 0, FAKE,
+                            FAKE, 0, None) == L.DASH_OK
     # summarize past the keys / past the summary capacity
-    assert lib.dash_summarize(ctypes.byref(p), FAKE, 1000, 0, 16, FAKE, FAKE, 16,
+    assert lib.dash_summarize(ctypes.byref(p), FAKE, 1000, 0, 16, FAKE, None, FAKE, 16,
                               None) == L.DASH_ERR_INVALID_ARG
-    assert lib.dash_summarize(ctypes.byref(p), FAKE, 1024, 0, 16, FAKE, FAKE, 15,
+    assert lib.dash_summarize(ctypes.byref(p), FAKE, 1024, 0, 16, FAKE, None, FAKE, 15,
                               None) == L.DASH_ERR_INVALID_ARG
     # route without buffers
     rb = L.dash_route_buf(FAKE, FAKE, None, FAKE, None)
@@ -108,12 +108,12 @@ def test_null_pointers_and_sizes():
                           None) == L.DASH_ERR_INVALID_ARG
     # decode: bad max_len, small summary cache, small workspace
     dneed = dash.dash_decode_workspace_bytes(p, 4096)
-    assert lib.dash_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 64, FAKE, None,
-                           FAKE, dneed, None) == L.DASH_ERR_INVALID_ARG
-    assert lib.dash_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, 63, FAKE,
+    assert lib.dash_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, 64, FAKE,
                            None, FAKE, dneed, None) == L.DASH_ERR_INVALID_ARG
-    assert lib.dash_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, 64, FAKE,
-                           None, FAKE, dneed - 1, None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    assert lib.dash_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 4096, FAKE, None, FAKE,
+                           63, FAKE, None, FAKE, dneed, None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 4096, FAKE, None, FAKE,
+                           64, FAKE, None, FAKE, dneed - 1, None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_binding_rejects_host_tensors():

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import sparse_hierarchical_attention_block_amd as dash
 import workloads as W
 from gpu_helpers import (TOL, check_list, check_supports, check_tau, dev, params, run_decode,
                          run_prefill, run_prefill_fused, tile_union_ref, to_dev)
@@ -36,12 +37,18 @@ PREFILL_CASES = {
                                                         alpha=1.25, gamma=4.0),
     "batch3_ragged_f32": tiny(batch=3, seq_len=700, n_heads=4, n_kv_heads=1, gamma=5.0),
     "alpha175_general": tiny(seq_len=640, dtype="bf16", alpha=1.75, gamma=6.0),
+    # Stage 0 pooled by per-KV-head summary queries
+    "qbar_tiny_f32": tiny(gamma=8.0, summary_query=1.0),
+    "qbar_gqa4_d128_bf16": W.get("prefill_8k").replace(seq_len=2048, summary_query=1.0),
+    "qbar_sharp_bs128_d64": tiny(batch=2, n_heads=8, n_kv_heads=4, seq_len=1100,
+                                 block_size=128, dtype="bf16", gamma=6.0, summary_query=4.0),
 }
 
 
 def oracle_prefill(w, inp, nb):
     r = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["w_s"], bs=w.block_size, alpha=w.alpha,
-                       gamma=w.gamma, nb_out=nb, want=("o", "tau", "x", "pbar"))
+                       gamma=w.gamma, nb_out=nb, want=("o", "tau", "x", "pbar"),
+                       q_bar=inp.get("q_bar"))
     B, N, H, Hkv = w.batch, w.seq_len, w.n_heads, w.n_kv_heads
     return {"o": r["o"].reshape(B, N, H, -1).transpose(0, 2, 1, 3),
             "tau": r["tau"].reshape(B, N, H), "x": r["x"].reshape(B, N, H, nb),
@@ -181,6 +188,36 @@ def test_deterministic():
 # decode
 # ----------------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,bs", [(64, 64), (128, 64), (64, 128), (128, 128)])
+@pytest.mark.parametrize("scale", [0.0, 1.0, 6.0])
+def test_summarize_with_query(dtype, d, bs, scale):
+    """dash_summarize with summary queries against the oracle; blocks [2, 7) of
+    a 3-sequence, 3-KV-head cache (7 workgroups per head, odd split)."""
+    print(f"[summarize q_bar] {dtype} d={d} bs={bs} scale={scale}", flush=True)
+    w = tiny(batch=3, n_heads=3, n_kv_heads=3, head_dim=d, block_size=bs, seq_len=7 * bs + 5,
+             dtype=dtype, summary_query=max(scale, 1.0))
+    inp = W.make_prefill(w)
+    qb = inp["q_bar"] * (scale / max(scale, 1.0))
+    p = params(w)
+    N, B, Hkv = w.seq_len, w.batch, w.n_kv_heads
+    k = to_dev(inp["k"], dtype)
+    ws = torch.from_numpy(inp["w_s"]).to(dev())
+    summ = torch.full((B * Hkv * 8 * d,), 7.0, dtype=torch.float32, device=dev())
+    qbt = torch.from_numpy(np.ascontiguousarray(qb)).to(dev())
+    dash.dash_summarize(p, k, N, 2, 7, ws, summ, 8, q_bar=qbt)
+    g = summ.cpu().numpy().reshape(B, Hkv, 8, d)
+    ref = oracle.summaries(inp["k"], inp["w_s"], bs, 7, qb)
+    np.testing.assert_allclose(g[:, :, 2:7], ref[:, :, 2:7], rtol=1e-5, atol=2e-5)
+    assert (g[:, :, :2] == 7.0).all() and (g[:, :, 7] == 7.0).all()
+    if scale == 0.0:
+        # a zero query pools like the mean-pooling path
+        summ0 = torch.zeros_like(summ)
+        dash.dash_summarize(p, k, N, 2, 7, ws, summ0, 8)
+        g0 = summ0.cpu().numpy().reshape(B, Hkv, 8, d)
+        np.testing.assert_allclose(g[:, :, 2:7], g0[:, :, 2:7], rtol=1e-6, atol=1e-6)
+
+
 DECODE_CASES = {
     "tiny_f32_ragged": (tiny(batch=7, gamma=8.0, kind="decode"),
                         [1, 63, 64, 65, 300, 1000, 1024]),
@@ -208,6 +245,12 @@ DECODE_CASES = {
                        [1500 - 37 * i for i in range(32)]),
     "fused_gqa8": (W.get("decode_128k").replace(batch=16, seq_len=2000, count_hi=24),
                    [2000 - 61 * i for i in range(16)]),
+    # Stage 0 pooled by summary queries: routed summaries and the completed block's
+    "qbar_f32_ragged": (tiny(batch=5, gamma=8.0, kind="decode", summary_query=1.0),
+                        [64, 65, 640, 1000, 1024]),
+    "qbar_fused_bf16": (W.get("decode_32k").replace(batch=16, seq_len=2048, count_lo=2,
+                                                    count_hi=20, summary_query=2.0),
+                        [2048 - 64 * i for i in range(16)]),
     # more than 2048 candidates: scores and routing as two kernels, the row in memory
     "long_row_in_memory": (W.get("decode_32k").replace(batch=1, n_heads=4, n_kv_heads=1,
                                                        seq_len=139264),
@@ -225,12 +268,13 @@ def test_decode_parity(case):
     nb = -(-Lmax // bs)
     lens = np.asarray(lens)
     # summary cache holds exactly the blocks complete before each new token
-    summ = oracle.summaries(inp["k_cache"], inp["w_s"], bs, Lmax // bs)
+    summ = oracle.summaries(inp["k_cache"], inp["w_s"], bs, Lmax // bs, inp.get("q_bar"))
     for b in range(B):
         summ[b, :, (lens[b] - 1) // bs:] = 0.0
     g = run_decode(w, inp, summ_np=summ)
     ref = oracle.decode(inp["q"], inp["k_cache"], inp["v_cache"], lens, inp["w_s"], bs=bs,
-                        alpha=w.alpha, gamma=w.gamma, nb_out=nb, want=("o", "tau", "x", "pbar"))
+                        alpha=w.alpha, gamma=w.gamma, nb_out=nb, want=("o", "tau", "x", "pbar"),
+                        q_bar=inp.get("q_bar"))
     check_tau(g["tau"], ref["tau"])
     ncand = (lens - 1) // bs
     check_supports(g["bits"], ref["x"], ref["tau"], ncand)

@@ -32,7 +32,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
 # tensor ids for the seed sequences
-_T_Q, _T_K, _T_V, _T_WS, _T_PLANT, _T_EPS = 1, 2, 3, 4, 5, 6
+_T_Q, _T_K, _T_V, _T_WS, _T_PLANT, _T_EPS, _T_QBAR = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -55,6 +55,7 @@ class Workload:
     log_uniform: bool = False   # ... or log-uniform in [count_lo, count_hi]
     plant_per_head: bool = False
     max_len: int = 0      # decode cache capacity (0 = seq_len)
+    summary_query: float = 0.0  # > 0: Stage 0 summary queries q_bar ~ this * N(0, 1)
 
     @property
     def group(self) -> int:
@@ -139,6 +140,15 @@ def w_s(w: Workload) -> np.ndarray:
             + 0.01 * _rng(w.seed, _T_WS).standard_normal((d, d), dtype=np.float32))
 
 
+def summary_query(w: Workload):
+    """Summary queries q_bar [Hkv, d] float32, drawn as summary_query * N(0, 1)
+    (a stand-in for a learned query), or None when the workload has none."""
+    if w.summary_query <= 0:
+        return None
+    return (w.summary_query * _rng(w.seed, _T_QBAR).standard_normal(
+        (w.n_kv_heads, w.head_dim), dtype=np.float32)).astype(np.float32)
+
+
 def _unit(rng: np.random.Generator, d: int) -> np.ndarray:
     u = rng.standard_normal(d).astype(np.float64)
     return (u / np.linalg.norm(u)).astype(np.float32)
@@ -174,7 +184,8 @@ def _pool_map(fn, items):
 
 
 def make_prefill(w: Workload, batches=None):
-    """q [B', H, N, d], k, v [B', Hkv, N, d], w_s [d, d] as float32 arrays."""
+    """q [B', H, N, d], k, v [B', Hkv, N, d], w_s [d, d] as float32 arrays, and
+    q_bar [Hkv, d] or None."""
     B, H, Hkv, N, d, bs, G = w.batch, w.n_heads, w.n_kv_heads, w.seq_len, w.head_dim, \
         w.block_size, w.group
     batches = list(range(B)) if batches is None else list(batches)
@@ -203,7 +214,7 @@ def make_prefill(w: Workload, batches=None):
             q[bi, h] = _cast(w, qq)
 
     _pool_map(unit, [(bi, b, g) for bi, b in enumerate(batches) for g in range(Hkv)])
-    return {"q": q, "k": k, "v": v, "w_s": w_s(w)}
+    return {"q": q, "k": k, "v": v, "w_s": w_s(w), "q_bar": summary_query(w)}
 
 
 def decode_plan(w: Workload, b: int, g: int):
@@ -223,7 +234,8 @@ def decode_plan(w: Workload, b: int, g: int):
 
 def make_decode(w: Workload, batches=None, cache_len=None):
     """q [B', H, d]; k_cache, v_cache [B', Hkv, max_len, d]; cache_len [B'] int32;
-    w_s.  The new token's key/value (position cache_len - 1) are in the caches."""
+    w_s; q_bar or None.  The new token's key/value (position cache_len - 1) are in
+    the caches."""
     B, H, Hkv, d, bs, G = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, w.group
     Lmax = w.cache_len
     batches = list(range(B)) if batches is None else list(batches)
@@ -256,4 +268,5 @@ def make_decode(w: Workload, batches=None, cache_len=None):
                 q[bi, h] = _cast(w, eps)
 
     _pool_map(unit, [(bi, b, g) for bi, b in enumerate(batches) for g in range(Hkv)])
-    return {"q": q, "k_cache": kc, "v_cache": vc, "cache_len": lens, "w_s": w_s(w)}
+    return {"q": q, "k_cache": kc, "v_cache": vc, "cache_len": lens, "w_s": w_s(w),
+            "q_bar": summary_query(w)}
