@@ -63,7 +63,8 @@ def _load():
         lib.oracle_forward_rows.argtypes = [
             fp, ip, ip, ctypes.c_int64, fp, fp, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            ctypes.c_double, ctypes.c_double, ctypes.c_int, dp, ctypes.c_int64,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int, dp,
+            ctypes.c_int64,
             ctypes.c_int64, dp, dp, dp, dp, dp, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -123,7 +124,8 @@ def summaries(k, w_s, bs: int, nblocks: int, q_bar=None):
 
 def forward_rows(q_rows, row_b, row_pos, k, v, summ, *, n_heads: int, bs: int, alpha: float,
                  gamma: float, causal: bool = True, n_kv: int | None = None,
-                 nb_out: int = 0, want=("o", "tau"), threads: int = 0):
+                 nb_out: int = 0, want=("o", "tau"), threads: int = 0, sigma: float = 1.0,
+                 window: int = 1):
     """Stages 1-2 for the given query rows.
 
     q_rows [nrows, H, d]; row_b / row_pos [nrows]; k, v [B, Hkv, L, d];
@@ -155,7 +157,8 @@ def forward_rows(q_rows, row_b, row_pos, k, v, summ, *, n_heads: int, bs: int, a
     rc = _load().oracle_forward_rows(
         _ptr(q_rows, ctypes.c_float), _ptr(row_b, ctypes.c_int64), _ptr(row_pos, ctypes.c_int64),
         nrows, _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), L, n_kv, B, H, Hkv, d, bs,
-        float(alpha), float(gamma), 1 if causal else 0, _ptr(summ, ctypes.c_double),
+        float(alpha), float(gamma), float(sigma), int(window), 1 if causal else 0,
+        _ptr(summ, ctypes.c_double),
         summ.shape[2], nb_out, _ptr(out["o"], ctypes.c_double),
         _ptr(out.get("tau"), ctypes.c_double), _ptr(out.get("x"), ctypes.c_double),
         _ptr(out.get("p"), ctypes.c_double), _ptr(out.get("pbar"), ctypes.c_double), threads)
@@ -166,7 +169,7 @@ def forward_rows(q_rows, row_b, row_pos, k, v, summ, *, n_heads: int, bs: int, a
 
 def prefill(q, k, v, w_s, *, bs: int, alpha: float, gamma: float, causal: bool = True,
             positions=None, batches=None, nb_out: int = 0, want=("o", "tau"), threads: int = 0,
-            q_bar=None):
+            q_bar=None, sigma: float = 1.0, window: int = 1):
     """Causal (or non-causal) prefill: q [B, H, N, d], k/v [B, Hkv, N, d].
 
     Computes the rows (b, i) for b in ``batches`` (default all) and i in
@@ -186,13 +189,14 @@ def prefill(q, k, v, w_s, *, bs: int, alpha: float, gamma: float, causal: bool =
                                   .reshape(len(batches) * len(positions), H, d))
     res = forward_rows(q_rows, rb, rp, sub_k, sub_v, summ, n_heads=H, bs=bs, alpha=alpha,
                        gamma=gamma, causal=causal, n_kv=N, nb_out=nb_out, want=want,
-                       threads=threads)
+                       threads=threads, sigma=sigma, window=window)
     res["summ"] = summ
     return res
 
 
 def decode(q, k_cache, v_cache, cache_len, w_s, *, bs: int, alpha: float, gamma: float,
-           batches=None, nb_out: int = 0, want=("o", "tau"), threads: int = 0, q_bar=None):
+           batches=None, nb_out: int = 0, want=("o", "tau"), threads: int = 0, q_bar=None,
+           sigma: float = 1.0, window: int = 1):
     """One decode step: q [B, H, d] is the query at position cache_len[b] - 1
     whose key/value are already in the caches [B, Hkv, max_len, d].  Also
     returns the summary of the block this token completes (None otherwise)."""
@@ -206,7 +210,7 @@ def decode(q, k_cache, v_cache, cache_len, w_s, *, bs: int, alpha: float, gamma:
     summ = summaries(sub_k, w_s, bs, nblocks, q_bar)
     res = forward_rows(q[batches], np.arange(len(batches)), lens - 1, sub_k, sub_v, summ,
                        n_heads=H, bs=bs, alpha=alpha, gamma=gamma, causal=True,
-                       nb_out=nb_out, want=want, threads=threads)
+                       nb_out=nb_out, want=want, threads=threads, sigma=sigma, window=window)
     res["new_summary"] = [summ[r, :, lens[r] // bs - 1] if lens[r] % bs == 0 else None
                           for r in range(len(batches))]
     return res

@@ -33,6 +33,13 @@
  *       (after entmax); every head of the group uses the average pbar.
  *   R6  prior-induced softmax: logit q.k/sqrt(d) + log pbar(block) on routed
  *       blocks (pbar > 0); blocks with pbar = 0 are masked.
+ *   R8  prior strength sigma >= 0: the routed-block bias is sigma * log pbar,
+ *       i.e. the reference distribution is g proportional to pbar^sigma on the
+ *       support (sigma = 1: the routing distribution; sigma = 0: uniform over
+ *       the support, the routing then acts as a mask only).
+ *   R9  near-diagonal window W >= 1: the query's own block and the W - 1 blocks
+ *       before it form the separate branch (bias 0, token-causal, never routed);
+ *       routing candidates are the complete blocks j < own - (W - 1).
  *   R3b with a summary query qbar (one d-vector per KV head), the block is
  *       pooled by scaled dot-product attention of qbar over the block's keys,
  *       the keys serving as values: m = sum_t softmax_t(qbar . k_t / sqrt(d)) k_t,
@@ -194,8 +201,10 @@ void oracle_summaries(const float* k, int B, int Hkv, int64_t kv_stride, int d, 
  *   k, v   : [B, Hkv, kv_stride, d] float32
  *   n_kv   : valid keys per sequence (non-causal only; causal uses i + 1)
  *   summ   : [B, Hkv, summ_stride, d] double, summaries of complete blocks
- *   causal : 1 = rules R4; 0 = every block of the n_kv keys is a candidate
- *            (n_kv % bs == 0 required) and there is no own block.
+ *   causal : 1 = rules R4 and R9; 0 = every block of the n_kv keys is a
+ *            candidate (n_kv % bs == 0 required) and there is no own block.
+ *   sigma  : prior strength (R8), >= 0
+ *   window : near-diagonal window in blocks (R9), >= 1
  * Outputs (each may be NULL except o):
  *   o      : [nrows, H, d]
  *   tau    : [nrows, H]                 NaN when the row has no candidate
@@ -207,10 +216,11 @@ void oracle_summaries(const float* k, int B, int Hkv, int64_t kv_stride, int d, 
 int oracle_forward_rows(const float* q_rows, const int64_t* row_b, const int64_t* row_pos,
                         int64_t nrows, const float* k, const float* v, int64_t kv_stride,
                         int64_t n_kv, int B, int H, int Hkv, int d, int bs, double alpha,
-                        double gamma, int causal, const double* summ, int64_t summ_stride,
-                        int64_t nb_out, double* o, double* tau, double* x_out, double* p_out,
-                        double* pbar, int nthreads) {
+                        double gamma, double sigma, int window, int causal, const double* summ,
+                        int64_t summ_stride, int64_t nb_out, double* o, double* tau,
+                        double* x_out, double* p_out, double* pbar, int nthreads) {
   if (H % Hkv != 0 || alpha <= 1.0 || alpha > 2.0 || bs <= 0 || d <= 0) return -1;
+  if (!(sigma >= 0.0) || window < 1) return -1;
   if (!causal && n_kv % bs != 0) return -1;
   const int G = H / Hkv;
   const double inv_sqrt_d = 1.0 / sqrt((double)d);
@@ -230,7 +240,9 @@ int oracle_forward_rows(const float* q_rows, const int64_t* row_b, const int64_t
       continue;
     }
     const int64_t own = i / bs;
-    const int64_t ncand = causal ? own : n_kv / bs;
+    /* first block of the near-diagonal branch; candidates are the blocks before it */
+    const int64_t win0 = own - (window - 1) > 0 ? own - (window - 1) : 0;
+    const int64_t ncand = causal ? win0 : n_kv / bs;
     if (ncand > summ_stride || (nb_out > 0 && ncand > nb_out)) {
 #pragma omp atomic write
       err = 1;
@@ -271,9 +283,9 @@ int oracle_forward_rows(const float* q_rows, const int64_t* row_b, const int64_t
             pbar[((int64_t)r * Hkv + g) * nb_out + j] = j < ncand ? pb[g * ncand + j] : 0.0;
     }
 
-    /* Stage 2: softmax over the keys of routed blocks (bias log pbar) and the
-     * causal part of the own block (bias 0). */
-    const int64_t nkeys_max = (ncand + 1) * (int64_t)bs;
+    /* Stage 2: softmax over the keys of routed blocks (bias sigma log pbar)
+     * and the near-diagonal branch: keys win0 * bs .. i (bias 0). */
+    const int64_t nkeys_max = (ncand + (causal ? window : 0)) * (int64_t)bs;
     double* logit = (double*)malloc(sizeof(double) * nkeys_max);
     int64_t* key = (int64_t*)malloc(sizeof(int64_t) * nkeys_max);
     for (int h = 0; h < H; ++h) {
@@ -287,11 +299,11 @@ int oracle_forward_rows(const float* q_rows, const int64_t* row_b, const int64_t
         if (!(pj > 0.0)) continue;
         for (int64_t t = j * bs; t < (j + 1) * bs; ++t) {
           key[nk] = t;
-          logit[nk++] = log(pj);
+          logit[nk++] = sigma * log(pj);
         }
       }
       if (causal)
-        for (int64_t t = own * bs; t <= i; ++t) {
+        for (int64_t t = win0 * bs; t <= i; ++t) {
           key[nk] = t;
           logit[nk++] = 0.0;
         }
