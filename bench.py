@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--workload", default="prefill_8k")
     ap.add_argument("--decode-workload", default="decode_32k")
     ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--sigma", type=float, default=None,
+                    help="prior strength (default: the workload's, 1)")
+    ap.add_argument("--window", type=int, default=None,
+                    help="near-diagonal branch in blocks (default: the workload's, 1)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--dense", action="store_true",
@@ -94,15 +98,24 @@ def traffic_for_attend(workload):
         return None
 
 
-def prefill_bench(args, torch, dash, W):
-    w = W.get(args.workload)
-    if args.alpha is not None:
+def with_overrides(w, args, alpha=True):
+    """The workload with the command line's alpha / sigma / window applied."""
+    if alpha and args.alpha is not None:
         w = w.replace(alpha=args.alpha)
+    if args.sigma is not None:
+        w = w.replace(sigma=args.sigma)
+    if args.window is not None:
+        w = w.replace(window=args.window)
+    return w
+
+
+def prefill_bench(args, torch, dash, W):
+    w = with_overrides(W.get(args.workload), args)
     dev = torch.device("cuda:0")
     inp = W.make_prefill(w)
     B, H, Hkv, N, d, bs, G = w.batch, w.n_heads, w.n_kv_heads, w.seq_len, w.head_dim, \
         w.block_size, w.group
-    p = dash.make_params(B, H, Hkv, d, bs, w.alpha, w.gamma, w.dtype)
+    p = dash.make_params(B, H, Hkv, d, bs, w.alpha, w.gamma, w.dtype, w.sigma, w.window)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v = (torch.from_numpy(inp[x]).to(dev, tdt) for x in ("q", "k", "v"))
     ws_mat = torch.from_numpy(inp["w_s"]).to(dev)
@@ -132,14 +145,16 @@ def prefill_bench(args, torch, dash, W):
     count = rb.sel_count.view(B, Hkv, -1).cpu().numpy().astype(np.int64)
     n_qt = count.shape[2]
     qt = np.arange(n_qt)
-    cand = (qt * QT) // bs                                 # routing candidates per tile
+    own_blk = (qt * QT) // bs
+    cand = np.maximum(own_blk - (w.window - 1), 0)         # routing candidates per tile
+    n_branch = own_blk - cand + 1                           # near-diagonal branch blocks
     cpb = bs // 64
-    own_chunks = qt - (qt * QT // bs) * cpb + 1            # own-block 64-key chunks walked
+    own_chunks = qt - cand * cpb + 1                       # branch 64-key chunks walked
     chunks = (count * cpb + own_chunks[None, None, :]).sum()
     flops_per_chunk = 4.0 * G * QT * 64 * d                # QK^T + PV for G*64 rows x 64 keys
     att_flops = float(chunks) * flops_per_chunk
     dense_chunks = float(B * Hkv) * (cand * cpb + own_chunks).sum()
-    tile_union_density = float((count + 1).sum() / (B * Hkv * (cand + 1).sum()))
+    tile_union_density = float((count + n_branch).sum() / (B * Hkv * (cand + n_branch).sum()))
     achieved = att_flops / (t_att * 1e-3) / 1e12
     traffic = traffic_for_attend(w.name)
     res = {
@@ -169,10 +184,10 @@ def prefill_bench(args, torch, dash, W):
 
 
 def decode_bench(args, torch, dash, W):
-    w = W.get(args.decode_workload)
+    w = with_overrides(W.get(args.decode_workload), args, alpha=False)
     dev = torch.device("cuda:0")
     B, H, Hkv, d, bs, L = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.block_size, w.seq_len
-    p = dash.make_params(B, H, Hkv, d, bs, w.alpha, w.gamma, w.dtype)
+    p = dash.make_params(B, H, Hkv, d, bs, w.alpha, w.gamma, w.dtype, w.sigma, w.window)
     kc = torch.empty((B, Hkv, L, d), dtype=torch.bfloat16, device=dev)
     vc = torch.empty_like(kc)
     q = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
@@ -196,9 +211,12 @@ def decode_bench(args, torch, dash, W):
     ms = events_time(step, args.steps, args.warmup, torch)
     count = rb.sel_count.cpu().numpy().astype(np.int64)
     own_len = (L - 1) % bs + 1
-    sel_bytes = float(((count * bs + own_len) * d * 2 * 2).sum())
-    ncand = (L - 1) // bs
-    density = float((count + 1).sum() / (B * Hkv * (ncand + 1)))
+    own = (L - 1) // bs
+    ncand = max(own - (w.window - 1), 0)
+    n_branch = own - ncand + 1
+    branch_keys = own_len + (n_branch - 1) * bs
+    sel_bytes = float(((count * bs + branch_keys) * d * 2 * 2).sum())
+    density = float((count + n_branch).sum() / (B * Hkv * (ncand + n_branch)))
     summ_bytes = float(B * Hkv * ncand * d * 4)
     gbs = sel_bytes / (ms * 1e-3) / 1e9
     return {"workload": w, "us_per_step": ms * 1e3, "selected_kv_bytes": sel_bytes,
@@ -214,15 +232,13 @@ def cpu_baseline(args, W, min_seconds=10.0):
     repeated until at least `min_seconds` of CPU work; tokens/s = positions
     processed / seconds (input generation excluded)."""
     import oracle
-    w = W.get(args.workload)
-    if args.alpha is not None:
-        w = w.replace(alpha=args.alpha)
+    w = with_overrides(W.get(args.workload), args)
     inp = W.make_prefill(w)
     threads = oracle.max_threads()
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.prefill(inp["q"], inp["k"], inp["v"], inp["w_s"], bs=w.block_size,
-                       alpha=w.alpha, gamma=w.gamma)
+                       alpha=w.alpha, gamma=w.gamma, sigma=w.sigma, window=w.window)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= 100:
@@ -271,7 +287,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: causal prefill B={w.batch} N={w.seq_len} "
                                f"H={w.n_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
-                               f"block={w.block_size} alpha={w.alpha} gamma={w.gamma}",
+                               f"block={w.block_size} alpha={w.alpha} gamma={w.gamma}"
+                               + (f" sigma={w.sigma} window={w.window}"
+                                  if (w.sigma, w.window) != (1.0, 1) else ""),
                    "global_batch": w.batch, "seq_len": w.seq_len,
                    "tile_union_block_density": round(pre["tile_union_density"], 4),
                    "parallelism": "single GPU"},
@@ -286,7 +304,9 @@ def main():
     if dec is not None:
         dw = dec["workload"]
         line["decode"] = {"workload": f"{dw.name}: batch {dw.batch} x {dw.seq_len} context, "
-                                      f"H={dw.n_heads} Hkv={dw.n_kv_heads} block={dw.block_size}",
+                                      f"H={dw.n_heads} Hkv={dw.n_kv_heads} block={dw.block_size}"
+                                      + (f" sigma={dw.sigma} window={dw.window}"
+                                         if (dw.sigma, dw.window) != (1.0, 1) else ""),
                           "us_per_step": round(dec["us_per_step"], 2),
                           "block_density": round(dec["block_density"], 4),
                           "selected_kv_gb": round(dec["selected_kv_bytes"] / 1e9, 4),

@@ -74,7 +74,16 @@ typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
  *   alpha       entmax exponent, 1 < alpha <= 2
  *   gamma       routing scale, finite and > 0
  *   dtype       element type of q, k, v and o (DASH_F32 or DASH_BF16); the
- *               summaries and W_s are always float32 */
+ *               summaries and W_s are always float32
+ *   sigma       prior strength (Stage 2, "prior-induced sparse softmax"): the
+ *               bias of a routed block is sigma * log pbar, i.e. the reference
+ *               distribution is proportional to pbar^sigma on the support;
+ *               finite and >= 0; 1 = the routing distribution itself, 0 = only
+ *               its support (a mask)
+ *   window      near-diagonal branch in blocks, >= 1: the query's own block and
+ *               the window - 1 blocks before it are attended token-causally
+ *               with bias 0 and are never routed; routing candidates are the
+ *               complete blocks j < own - (window - 1) */
 typedef struct {
   int32_t batch;
   int32_t n_heads;
@@ -84,12 +93,14 @@ typedef struct {
   float alpha;
   float gamma;
   int32_t dtype;
+  float sigma;
+  int32_t window;
 } dash_params;
 
 /* Query tile of the prefill path: 64 consecutive positions of one sequence
  * and one KV head (all G query heads of the group).  The routing result is
  * stored per tile: the union of the tile's selected blocks and, for each
- * selected block, the log prior of every position of the tile. */
+ * selected block, the prior bias of every position of the tile. */
 #define DASH_QUERY_TILE 64
 
 /* Storage of the routing result (Stage 1 -> Stage 2 hand-over), caller-owned.
@@ -101,8 +112,9 @@ typedef struct {
  *   sel_count    [B, Hkv, n_qt]       int32; number of selected blocks
  *   sel_idx      [B, Hkv, n_qt, nb]   int32; ascending selected block ids,
  *                                     the first sel_count entries are valid
- *   sel_logp     [B, Hkv, n_qt, nb, QT] float; log pbar(block, query) indexed
- *                                     by BLOCK ID, -inf where pbar = 0; valid for
+ *   sel_logp     [B, Hkv, n_qt, nb, QT] float; the Stage 2 bias
+ *                                     sigma * log pbar(block, query) indexed by
+ *                                     BLOCK ID, -inf where pbar = 0; valid for
  *                                     the candidate blocks of the tile
  *   support_bits [B, H, n, ceil(nb/32)] uint32, optional (NULL = not written);
  *                                     bit j set iff block j is in that head's own

@@ -35,7 +35,8 @@ class dash_params(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("alpha", ctypes.c_float),
-                ("gamma", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("gamma", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("sigma", ctypes.c_float), ("window", ctypes.c_int32)]
 
 
 class dash_route_buf(ctypes.Structure):
@@ -90,8 +91,10 @@ EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
 # helpers
 # ---------------------------------------------------------------------------------------
 
-def make_params(batch, n_heads, n_kv_heads, head_dim, block_size, alpha, gamma, dtype):
-    """dtype: "bf16"/"f32", torch dtype, or DASH_* code."""
+def make_params(batch, n_heads, n_kv_heads, head_dim, block_size, alpha, gamma, dtype,
+                sigma=1.0, window=1):
+    """dtype: "bf16"/"f32", torch dtype, or DASH_* code; sigma: prior strength;
+    window: near-diagonal branch in blocks."""
     if dtype in ("bf16", torch.bfloat16):
         code = DASH_BF16
     elif dtype in ("f32", torch.float32):
@@ -99,7 +102,8 @@ def make_params(batch, n_heads, n_kv_heads, head_dim, block_size, alpha, gamma, 
     else:
         code = int(dtype)
     return dash_params(int(batch), int(n_heads), int(n_kv_heads), int(head_dim),
-                       int(block_size), float(alpha), float(gamma), code)
+                       int(block_size), float(alpha), float(gamma), code, float(sigma),
+                       int(window))
 
 
 def torch_dtype(p: dash_params):

@@ -24,6 +24,8 @@ dash_status check_params(const dash_params* p, Shape* s) {
   if (p->dtype != DASH_F32 && p->dtype != DASH_BF16) return DASH_ERR_INVALID_ARG;
   if (!std::isfinite(p->alpha) || !(p->alpha > 1.0f) || p->alpha > 2.0f) return DASH_ERR_INVALID_ARG;
   if (!std::isfinite(p->gamma) || !(p->gamma > 0.0f)) return DASH_ERR_INVALID_ARG;
+  if (!std::isfinite(p->sigma) || !(p->sigma >= 0.0f)) return DASH_ERR_INVALID_ARG;
+  if (p->window < 1) return DASH_ERR_INVALID_ARG;
   if (p->head_dim < 1 || p->block_size < 1) return DASH_ERR_INVALID_ARG;
   const int G = p->n_heads / p->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return DASH_ERR_UNSUPPORTED;
@@ -39,6 +41,8 @@ dash_status check_params(const dash_params* p, Shape* s) {
   s->alpha = p->alpha;
   s->gamma = p->gamma;
   s->dtype = p->dtype;
+  s->sigma = p->sigma;
+  s->window = p->window;
   return DASH_OK;
 }
 

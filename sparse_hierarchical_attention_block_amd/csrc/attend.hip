@@ -1,16 +1,17 @@
 // attend.hip -- Stage 2 of DashAttention for causal prefill ("prior-induced
 // sparse softmax", DashAttention explainer, Technical summary): attention of
 // each query restricted to the blocks its 64-position tile selected, with the
-// routing probability as a prior (logit q.k/sqrt(d) + log pbar), blocks of
-// probability 0 masked (-inf), and the query's own block attended causally
-// with bias 0 (the near-diagonal branch).  The pages' kernel is a modified
+// routing probability as a prior (logit q.k/sqrt(d) + sigma log pbar, the
+// bias Stage 1 stored), blocks of probability 0 masked (-inf), and the
+// near-diagonal branch -- the query's own block and the window - 1 blocks
+// before it -- attended causally with bias 0.  The pages' kernel is a modified
 // FlashAttention that walks the active chunks and adds the routing bias before
 // the softmax; this is a gfx950 design of that idea.
 //
 // bf16 kernel: one workgroup per (sequence, KV head, query tile) -- up to 8
 // waves; each wave owns 32 queries of one head of the group, so every K/V
 // chunk staged in LDS serves all G heads.  The walk goes over 64-key chunks:
-// own-block chunks first (so every running max is finite), then the selected
+// branch chunks first (so every running max is finite), then the selected
 // blocks.  Per chunk and wave:
 //   S^T (64 keys x 32 queries) = K Q^T     2 x 8 MFMA 32x32x16 (d = 128)
 //   online softmax in the exp2 domain, bias added per (query, block)
@@ -41,7 +42,14 @@ struct AttendArgs {
   int H, Hkv, G, bs, B;
   float scale_log2;   // log2(e) / sqrt(d)
   int wg_per_tile;
+  int window;         // near-diagonal branch: own block + window - 1 blocks before it
 };
+
+// first block of the tile's near-diagonal branch (own block - (window - 1), >= 0)
+__device__ __forceinline__ int64_t branch_block0(int64_t p_begin, int bs, int window) {
+  const int64_t j = p_begin / bs - (window - 1);
+  return j > 0 ? j : 0;
+}
 
 // chunk c of the tile's walk -> first key and bias source
 struct ChunkRef {
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   }
 
   const int cpb_log = a.bs == 2 * kChunk ? 1 : 0;   // chunks per block: 1 or 2
-  const int64_t own_c0 = (p_begin / a.bs) << cpb_log;
+  const int64_t own_c0 = branch_block0(p_begin, a.bs, a.window) << cpb_log;
   const int n_own = (int)(qt - own_c0 + 1);
   const int count = a.sel_count[tile];
   const int n_chunks = n_own + (count << cpb_log);
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
     ov[c] = 0.f;
   }
   const int cpb = a.bs / kChunk;
-  const int64_t own_c0 = (p_begin / a.bs) * cpb;
+  const int64_t own_c0 = branch_block0(p_begin, a.bs, a.window) * cpb;
   const int n_own = (int)(qt - own_c0 + 1);
   const int count = a.sel_count[tile];
   const int32_t* idx = a.sel_idx + tile * a.nb;
@@ -462,6 +470,7 @@ hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, c
   a.G = s.G;
   a.bs = s.bs;
   a.B = s.B;
+  a.window = s.window;
   a.scale_log2 = kLog2e / sqrtf((float)s.d);
   const int64_t tiles = a.n_qt * s.B * s.Hkv;
   if (s.dtype == DASH_BF16) {

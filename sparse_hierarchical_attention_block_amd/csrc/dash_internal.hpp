@@ -14,6 +14,8 @@ struct Shape {
   int B, H, Hkv, G, d, bs;
   float alpha, gamma;
   int dtype;  // dash_dtype
+  float sigma;   // prior strength: routed-block bias sigma * log pbar
+  int window;    // near-diagonal branch: own block + window - 1 blocks before it
 };
 
 // Stage 0: summaries of blocks [blk_begin, blk_end) for every (b, kv head);

@@ -5,15 +5,17 @@
 //
 // Per sequence b the new query sits at position L = cache_len[b] - 1:
 //   1. scores          x[b,h,j] = (alpha-1) gamma q_h . s_j / sqrt(d) for the
-//                      cached summaries j < floor(L / bs): a coalesced scan of
-//                      the float32 summary cache with MFMA 4x4x1 f32
+//                      cached summaries j < floor(L / bs) - (window - 1) (the
+//                      blocks before the near-diagonal branch): a coalesced
+//                      scan of the float32 summary cache with MFMA 4x4x1 f32
 //   2. route           one wave per query head finds tau; the G heads of a KV
 //                      head average p; the union is compacted into an
-//                      ascending list with log pbar per listed block
+//                      ascending list with the bias sigma log pbar per block
 //      (1 and 2 run as one kernel, decode_select, when there are enough
 //      (sequence, KV head) pairs to fill the GPU with one workgroup each;
 //      otherwise as decode_scores + decode_route)
-//   3. decode_attend   split-K over the list [own block, selected blocks...],
+//   3. decode_attend   split-K over the list [branch blocks, selected blocks...]
+//                      (branch: the own block and the window - 1 before it),
 //                      32 entries per work item, a persistent grid walking
 //                      the items, 4 waves; MFMA 16x16x32 with the G query
 //                      heads as MFMA rows (padded to 16); K and V stream from
@@ -60,6 +62,8 @@ struct DecodeArgs {
   int xpitch;        // fused score/route kernel: LDS row pitch of the scores
   int mode;
   float e, scale, scale_log2;
+  float sigma;       // prior strength: logp = sigma * log pbar
+  int window;        // near-diagonal branch in blocks
 };
 
 __host__ __device__ inline int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
@@ -67,6 +71,17 @@ __host__ __device__ inline int64_t min64(int64_t x, int64_t y) { return x < y ? 
 __device__ __forceinline__ int64_t clamp_len(int32_t v, int64_t max_len) {
   int64_t l = v;
   return l < 1 ? 1 : (l > max_len ? max_len : l);
+}
+
+// Routing candidates of a query at position len - 1: the complete blocks
+// before its near-diagonal branch (own block and the window - 1 before it).
+__device__ __forceinline__ int decode_ncand(const DecodeArgs& a, int64_t len) {
+  return max(0, (int)((len - 1) >> a.bs_log) - (a.window - 1));
+}
+// Blocks of that branch: min(window, own + 1); the list of a (sequence, KV
+// head) is [own, own - 1, ..., own - n_branch + 1, selected blocks...].
+__device__ __forceinline__ int decode_nbranch(const DecodeArgs& a, int64_t len) {
+  return min(a.window, (int)((len - 1) >> a.bs_log) + 1);
 }
 
 // ---- 1. coarse scores ------------------------------------------------------------------------
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(kScoreThreads) void decode_scores_kernel(DecodeArgs
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int ncand = (int)((len - 1) >> a.bs_log);
+  const int ncand = decode_ncand(a, len);
   const int gb = blockIdx.x * (kScoreRows / 16);
   const int ge = min((ncand + 15) >> 4, gb + kScoreRows / 16);
   if (gb >= ge) return;
@@ -240,7 +255,7 @@ __device__ __forceinline__ void route_union(const DecodeArgs& a, int64_t bg, int
     if (j < je) {
       for (int h = 0; h < a.G; ++h) pb += Ps[h * pitch + j];
       pb *= invG;
-      a.logp[bg * a.nb + j] = pb > 0.f ? __logf(pb) : -INFINITY;
+      a.logp[bg * a.nb + j] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
       Ps[j] = pb;   // column j is only touched by this lane
     }
     cnt += __popcll(__ballot(pb > 0.f));
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
   const int64_t bg = blockIdx.x;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
-  const int ncand = (int)((len - 1) >> a.bs_log);
+  const int ncand = decode_ncand(a, len);
   const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
   const int64_t row = (int64_t)b * a.H + g * a.G + hh;
   const float* xr = a.x + row * a.nb;
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(DecodeArg
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int G = a.G;
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
-  const int ncand = (int)((len - 1) >> a.bs_log);
+  const int ncand = decode_ncand(a, len);
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t row0 = (int64_t)b * a.H + g * G;
@@ -361,7 +376,8 @@ __global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(DecodeArg
 
 // ---- 3. split-K attend (bf16, MFMA) ----------------------------------------------------------
 // One work item: split s of the list of (sequence, KV head) bgi, i.e. entries
-// [s * kDecodeSplit, (s + 1) * kDecodeSplit) of [own block, selected blocks...].
+// [s * kDecodeSplit, (s + 1) * kDecodeSplit) of [branch blocks (own block
+// first), selected blocks...].
 // All 256 threads call; ms / ls / os are the workgroup's merge buffers.
 template <int D>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
@@ -381,7 +397,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   int32_t meta;
   {
-    const int64_t slot = min64(max(s * kDecodeSplit + wv + 4 * lane - 1, 0), a.nb - 1);
+    // entry e >= n_branch is selected block e - n_branch; when a sequence
+    // has selected blocks its branch is full (n_branch = window)
+    const int64_t slot =
+        min64(max(s * kDecodeSplit + wv + 4 * lane - a.window, 0), a.nb - 1);
     const int32_t* src = lane < kPerWave    ? a.idx + bg * a.nb + slot
                          : lane == kPerWave ? a.count + bg
                                             : a.cache_len + b;
@@ -393,7 +412,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
   const int count = __builtin_amdgcn_readlane(meta, kPerWave);
   const int64_t len = clamp_len(__builtin_amdgcn_readlane(meta, kPerWave + 1), a.max_len);
   const int64_t own = (len - 1) >> a.bs_log;
-  const int n_entries = 1 + count;
+  const int n_branch = decode_nbranch(a, len);
+  const int n_entries = n_branch + count;
 
   // K/V of this (sequence, KV head) through buffer resources sized to the
   // current length: keys >= len read as zeros (and are masked below)
@@ -421,7 +441,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
   for (int ei = 0; ei < kPerWave; ++ei) {
     const int e = s * kDecodeSplit + wv + 4 * ei;
     if (e >= e_end) break;
-    const int64_t j = e == 0 ? own : (int64_t)jraw[ei];
+    const int64_t j = e < n_branch ? own - e : (int64_t)jraw[ei];
     for (int c64 = 0; c64 < (a.bs >> 6); ++c64) {
       const int64_t key0 = (j << a.bs_log) + 64 * c64;
       if (key0 >= len) break;
@@ -451,7 +471,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
             vin[ks][ep][0] = t.x; vin[ks][ep][1] = t.y;
           }
         }
-      const float bias2 = e == 0 ? 0.f : a.logp[bg * a.nb + j] * kLog2e;
+      const float bias2 = e < n_branch ? 0.f : a.logp[bg * a.nb + j] * kLog2e;
       // keep every load of the chunk ahead of the first use: one HBM latency
       // per chunk instead of one per dependent group of loads
       __builtin_amdgcn_sched_barrier(0);
@@ -557,7 +577,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
 
 // Persistent grid (as many workgroups as fit on the GPU at once): every
 // workgroup derives the work items from the list lengths -- item ranges
-// pre[bg] .. pre[bg+1] with ceil((1 + count[bg]) / kDecodeSplit) items per
+// pre[bg] .. pre[bg+1] with ceil((n_branch + count[bg]) / kDecodeSplit) items per
 // (sequence, KV head) -- and takes items blockIdx.x, + gridDim.x, ...  No
 // workgroup is launched for a split past its list, so none holds a slot
 // waiting only to find it has nothing to do.
@@ -575,7 +595,9 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
   const int i0 = min(nbg, (int)threadIdx.x * per), i1 = min(nbg, i0 + per);
   int tot = 0;
   for (int i = i0; i < i1; ++i) {
-    const int ns = (a.count[i] + kDecodeSplit) / kDecodeSplit;   // ceil((1 + count) / split)
+    const int nbr = a.window == 1 ? 1
+                                  : decode_nbranch(a, clamp_len(a.cache_len[i / a.Hkv], a.max_len));
+    const int ns = (a.count[i] + nbr + kDecodeSplit - 1) / kDecodeSplit;
     pre[i] = ns;
     tot += ns;
   }
@@ -618,7 +640,8 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
   const int64_t own = (len - 1) / a.bs;
   const int count = a.count[bg];
-  const int n_entries = 1 + count;
+  const int n_branch = decode_nbranch(a, len);
+  const int n_entries = n_branch + count;
   if (s * kDecodeSplit >= n_entries) return;
   const float* kb = (const float*)a.kc + bg * a.max_len * D;
   const float* vb = (const float*)a.vc + bg * a.max_len * D;
@@ -629,8 +652,8 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
   for (int c = 0; c < D / 32; ++c) ov[c] = 0.f;
   const int e_end = min(n_entries, (s + 1) * kDecodeSplit);
   for (int e = s * kDecodeSplit; e < e_end; ++e) {
-    const int64_t j = e == 0 ? own : (int64_t)a.idx[bg * a.nb + e - 1];
-    const float bias2 = e == 0 ? 0.f : a.logp[bg * a.nb + j] * kLog2e;
+    const int64_t j = e < n_branch ? own - e : (int64_t)a.idx[bg * a.nb + e - n_branch];
+    const float bias2 = e < n_branch ? 0.f : a.logp[bg * a.nb + j] * kLog2e;
     for (int64_t key0 = j * a.bs; key0 < (j + 1) * a.bs && key0 < len; key0 += 64) {
       __syncthreads();
       for (int p = threadIdx.x; p < a.G * 64; p += 256) {
@@ -692,7 +715,8 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     }
     return;
   }
-  const int n_entries = 1 + a.count[bg];
+  const int n_entries =
+      decode_nbranch(a, clamp_len(a.cache_len[b], a.max_len)) + a.count[bg];
   const int ns = (n_entries + kDecodeSplit - 1) / kDecodeSplit;
   const int G = a.G;
   const int q0 = blockIdx.x * HPW;                 // first head of this workgroup
@@ -768,8 +792,10 @@ static int persistent_grid(size_t lds) {
 DecodeLayout decode_layout(const Shape& s, int64_t max_len) {
   DecodeLayout L;
   L.nb = (max_len + s.bs - 1) / s.bs;
-  L.ncand_max = (max_len - 1) / s.bs;
-  L.n_split = (L.ncand_max + 1 + kDecodeSplit - 1) / kDecodeSplit;
+  // list entries per (sequence, KV head): branch blocks + candidates <= own + 1
+  const int64_t own_max = (max_len - 1) / s.bs;
+  L.ncand_max = own_max - (s.window - 1) > 0 ? own_max - (s.window - 1) : 0;
+  L.n_split = (own_max + 1 + kDecodeSplit - 1) / kDecodeSplit;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 0;
   L.off_x = off;     off = al(off + sizeof(float) * s.B * s.H * L.nb);
@@ -820,6 +846,8 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   a.e = 1.0f / (s.alpha - 1.0f);
   a.scale = (s.alpha - 1.0f) * s.gamma / sqrtf((float)s.d);
   a.scale_log2 = kLog2e / sqrtf((float)s.d);
+  a.sigma = s.sigma;
+  a.window = s.window;
   const bool bf16 = s.dtype == DASH_BF16;
   const unsigned nbg = (unsigned)(s.B * s.Hkv);
 

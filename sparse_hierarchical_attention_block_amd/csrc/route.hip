@@ -7,7 +7,8 @@
 //
 // One workgroup per (sequence, KV head, query tile of 64 positions), heaviest
 // tiles (most candidate blocks) first.  Candidates of tile qt are the complete
-// blocks j < floor(64 qt / bs).  Rows are (position, head of the group)
+// blocks before its near-diagonal branch, j < floor(64 qt / bs) - (window - 1).
+// Rows are (position, head of the group)
 // pairs; for tiles with more than 128 candidates (or float32 queries) they are
 // processed in passes of PP positions, PP as large as an 80 KB LDS score
 // buffer allows:
@@ -17,8 +18,8 @@
 //      plain FMAs;
 //   2. tau per row (entmax_device.hpp), lanes-per-row = threads / rows;
 //   3. pbar per (position, block) = mean over the group's heads of
-//      [x - tau]_+^e, written as log pbar (-inf for 0) into sel_logp, and the
-//      tile-union flags.
+//      [x - tau]_+^e, written as the Stage 2 bias sigma log pbar (-inf for 0)
+//      into sel_logp, and the tile-union flags.
 // Finally wave 0 compacts the flags into sel_idx / sel_count.
 #include "dash_internal.hpp"
 #include "device_common.hpp"
@@ -46,6 +47,8 @@ struct RouteArgs {
   int H, Hkv, G, bs, B;
   int mode;
   float e, scale;
+  float sigma;  // prior strength: sel_logp = sigma * log pbar
+  int window;   // near-diagonal branch in blocks
   int PP;      // positions per pass
   int pitch;   // X row pitch in floats (multiple of 4)
 };
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t p_begin = qt * kQT;
   const int npos = (int)min((int64_t)kQT, a.n - p_begin);
-  const int t = (int)(p_begin / a.bs);
+  const int t = max(0, (int)(p_begin / a.bs) - (a.window - 1));   // candidates
   const int64_t tile = bg * a.n_qt + qt;
 
   if (t == 0) {
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
           const int j = sub + lpr * (s2 | h);
           if (j < t) {
             const float pb = pv[s2] * invG;
-            a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? __logf(pb) : -INFINITY;
+            a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
             if (pb > 0.f) uflag[j] = 1;
           }
         }
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
           if (y > 0.f) pb += entmax_pow(y, a.mode, a.e);
         }
         pb *= invG;
-        a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? __logf(pb) : -INFINITY;
+        a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
         if (pb > 0.f) uflag[j] = 1;
       }
     }
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
   const int64_t bg = blockIdx.x % nbg;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t p_begin = qt * kQT;
-  const int t = (int)(p_begin / a.bs);
+  const int t = max(0, (int)(p_begin / a.bs) - (a.window - 1));   // candidates
   const int64_t tile = bg * a.n_qt + qt;
   const int G = a.G;
 
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
         const int j = 16 * (slot >> 2) + 4 * lg + (slot & 3);
         if (j < t) {
           const float pb = xv[s2] * invG;
-          lp[j * kQT] = pb > 0.f ? __logf(pb) : -INFINITY;
+          lp[j * kQT] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
           if (pb > 0.f) uflag[j] = 1;
         }
       }
@@ -585,7 +588,9 @@ hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const 
   a.mode = entmax_mode(s.alpha);
   a.e = 1.0f / (s.alpha - 1.0f);
   a.scale = (s.alpha - 1.0f) * s.gamma / sqrtf((float)s.d);
-  const int t_max = (int)(((a.n_qt - 1) * kQT) / s.bs);
+  a.sigma = s.sigma;
+  a.window = s.window;
+  const int t_max = max(0, (int)(((a.n_qt - 1) * kQT) / s.bs) - (s.window - 1));
   if (s.dtype == DASH_BF16 && t_max <= 16 * kTileMaxCT) {
     // tile-resident path: one wave per 64 rows of the tile
     a.pitch = round_up16(t_max > 0 ? t_max : 1);

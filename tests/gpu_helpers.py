@@ -35,7 +35,8 @@ def qbar_dev(inp):
 
 def params(w, **over):
     kw = dict(batch=w.batch, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
-              block_size=w.block_size, alpha=w.alpha, gamma=w.gamma, dtype=w.dtype)
+              block_size=w.block_size, alpha=w.alpha, gamma=w.gamma, dtype=w.dtype,
+              sigma=w.sigma, window=w.window)
     kw.update(over)
     return dash.make_params(**kw)
 
@@ -132,6 +133,20 @@ def run_decode(w, inp, summ_np=None, route=True):
             "logp": rb.sel_logp.cpu().numpy().reshape(B, Hkv, nb),
             "bits": unpack_bits(rb.support_bits.cpu().numpy().reshape(B, H, -1), nb)})
     return out
+
+
+def check_bias(logp, pbar, sigma):
+    """Stage 2 bias sigma * log pbar written by Stage 1, against the oracle's
+    pbar: in probability units for sigma > 0; for sigma = 0 the bias is 0 on
+    the support and -inf off it (entries within 2e-5 of 0 may go either way)."""
+    if sigma > 0:
+        with np.errstate(over="ignore"):
+            np.testing.assert_allclose(np.exp(logp / sigma), pbar, atol=2e-5)
+        return
+    off = np.isneginf(logp)
+    assert np.all(logp[~off] == 0.0)
+    bad = (off != (pbar == 0)) & (pbar > 2e-5)
+    assert not bad.any(), f"{int(bad.sum())} support entries differ"
 
 
 def check_supports(gpu_bits, x, tau, ncand):

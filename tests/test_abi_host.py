@@ -44,6 +44,14 @@ def P(**kw):
     return dash.make_params(**base)
 
 
+def test_params_layout_matches_header():
+    # dash_params in include/dash.h: 8 four-byte fields, then sigma and window
+    assert ctypes.sizeof(L.dash_params) == 40
+    assert L.dash_params.sigma.offset == 32 and L.dash_params.window.offset == 36
+    p = P()
+    assert p.sigma == 1.0 and p.window == 1
+
+
 def test_route_sizes():
     s = dash.dash_route_sizes_prefill(P(), 8192)
     assert s["n_qt"] == 128 and s["nb"] == 128 and s["qt"] == 64
@@ -69,6 +77,9 @@ def test_route_sizes():
     (dict(head_dim=96), L.DASH_ERR_UNSUPPORTED),
     (dict(block_size=32), L.DASH_ERR_UNSUPPORTED),
     (dict(n_heads=48, n_kv_heads=4), L.DASH_ERR_UNSUPPORTED),   # G = 12
+    (dict(sigma=-0.5), L.DASH_ERR_INVALID_ARG),
+    (dict(sigma=float("nan")), L.DASH_ERR_INVALID_ARG),
+    (dict(window=0), L.DASH_ERR_INVALID_ARG),
 ])
 def test_bad_params(kw, code):
     out = ctypes.c_size_t()

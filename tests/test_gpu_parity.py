@@ -13,7 +13,8 @@ import torch
 import oracle
 import sparse_hierarchical_attention_block_amd as dash
 import workloads as W
-from gpu_helpers import (TOL, check_list, check_supports, check_tau, dev, params, run_decode,
+from gpu_helpers import (TOL, check_bias, check_list, check_supports, check_tau, dev, params,
+                         run_decode,
                          run_prefill, run_prefill_fused, tile_union_ref, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -42,13 +43,19 @@ PREFILL_CASES = {
     "qbar_gqa4_d128_bf16": W.get("prefill_8k").replace(seq_len=2048, summary_query=1.0),
     "qbar_sharp_bs128_d64": tiny(batch=2, n_heads=8, n_kv_heads=4, seq_len=1100,
                                  block_size=128, dtype="bf16", gamma=6.0, summary_query=4.0),
+    # prior strength and near-diagonal window
+    "sigma05_window2_gqa4": W.get("prefill_8k").replace(seq_len=2048, sigma=0.5, window=2),
+    "sigma0_window3_f32": tiny(batch=2, seq_len=900, gamma=8.0, sigma=0.0, window=3),
+    "sigma2_window4_bs128": W.get("prefill_64k").replace(seq_len=2048, gamma=2.0, sigma=2.0,
+                                                         window=4),
+    "window_covers_all_bf16": tiny(seq_len=700, dtype="bf16", gamma=8.0, window=11),
 }
 
 
 def oracle_prefill(w, inp, nb):
     r = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["w_s"], bs=w.block_size, alpha=w.alpha,
                        gamma=w.gamma, nb_out=nb, want=("o", "tau", "x", "pbar"),
-                       q_bar=inp.get("q_bar"))
+                       q_bar=inp.get("q_bar"), sigma=w.sigma, window=w.window)
     B, N, H, Hkv = w.batch, w.seq_len, w.n_heads, w.n_kv_heads
     return {"o": r["o"].reshape(B, N, H, -1).transpose(0, 2, 1, 3),
             "tau": r["tau"].reshape(B, N, H), "x": r["x"].reshape(B, N, H, nb),
@@ -64,7 +71,7 @@ def compare_prefill(w, g, ref):
     # Stage 1: thresholds and per-head supports
     check_tau(g["tau"].transpose(0, 2, 1), ref["tau"])
     pos = np.arange(N)
-    ncand = np.tile(pos // bs, B)
+    ncand = np.tile(np.maximum(pos // bs - (w.window - 1), 0), B)
     bits = g["bits"].transpose(0, 2, 1, 3).reshape(B * N, H, nb)
     check_supports(bits, ref["x"].reshape(B * N, H, nb), ref["tau"].reshape(B * N, H), ncand)
     # tile lists and log priors
@@ -73,7 +80,7 @@ def compare_prefill(w, g, ref):
         for gg in range(Hkv):
             for qt in range(n_qt):
                 p0, p1 = qt * QT, min(N, qt * QT + QT)
-                t = p0 // bs
+                t = max(p0 // bs - (w.window - 1), 0)
                 hs = slice(gg * G, gg * G + G)
                 union, solid, near = tile_union_ref(ref["pbar"][b, p0:p1, gg, :t],
                                                     ref["x"][b, p0:p1, hs, :t],
@@ -81,9 +88,8 @@ def compare_prefill(w, g, ref):
                 cnt = g["count"][b, gg, qt]
                 check_list(cnt, g["idx"][b, gg, qt], union, solid, near)
                 lst = g["idx"][b, gg, qt, :cnt]
-                with np.errstate(over="ignore"):
-                    pg = np.exp(g["logp"][b, gg, qt, lst, : p1 - p0]).T      # [P, listed]
-                np.testing.assert_allclose(pg, ref["pbar"][b, p0:p1, gg][:, lst], atol=2e-5)
+                check_bias(g["logp"][b, gg, qt, lst, : p1 - p0].T,           # [P, listed]
+                           ref["pbar"][b, p0:p1, gg][:, lst], w.sigma)
     # Stage 2 output
     err = np.abs(g["o"] - ref["o"]).max()
     assert err <= tol, f"output max-abs error {err:.3e} > {tol}"
@@ -251,6 +257,17 @@ DECODE_CASES = {
     "qbar_fused_bf16": (W.get("decode_32k").replace(batch=16, seq_len=2048, count_lo=2,
                                                     count_hi=20, summary_query=2.0),
                         [2048 - 64 * i for i in range(16)]),
+    # prior strength and near-diagonal window: two-kernel f32, fused bf16 (lists
+    # that start past the first split), and windows longer than short sequences
+    "sigma05_window2_f32": (tiny(batch=6, gamma=8.0, kind="decode", sigma=0.5, window=2),
+                            [1, 64, 65, 129, 700, 1024]),
+    "sigma0_window3_fused": (W.get("decode_32k").replace(batch=16, seq_len=3000, count_lo=4,
+                                                         count_hi=30, sigma=0.0, window=3),
+                             [1, 63, 64, 128, 129, 192, 193, 500, 1000, 1024, 2047, 2048,
+                              2049, 2500, 2999, 3000]),
+    "sigma2_window40_gqa8": (W.get("decode_128k").replace(batch=2, seq_len=8192, count_hi=64,
+                                                          sigma=2.0, window=40),
+                             [8192, 2600]),
     # more than 2048 candidates: scores and routing as two kernels, the row in memory
     "long_row_in_memory": (W.get("decode_32k").replace(batch=1, n_heads=4, n_kv_heads=1,
                                                        seq_len=139264),
@@ -270,13 +287,13 @@ def test_decode_parity(case):
     # summary cache holds exactly the blocks complete before each new token
     summ = oracle.summaries(inp["k_cache"], inp["w_s"], bs, Lmax // bs, inp.get("q_bar"))
     for b in range(B):
-        summ[b, :, (lens[b] - 1) // bs:] = 0.0
+        summ[b, :, max((lens[b] - 1) // bs - (w.window - 1), 0):] = 0.0
     g = run_decode(w, inp, summ_np=summ)
     ref = oracle.decode(inp["q"], inp["k_cache"], inp["v_cache"], lens, inp["w_s"], bs=bs,
                         alpha=w.alpha, gamma=w.gamma, nb_out=nb, want=("o", "tau", "x", "pbar"),
-                        q_bar=inp.get("q_bar"))
+                        q_bar=inp.get("q_bar"), sigma=w.sigma, window=w.window)
     check_tau(g["tau"], ref["tau"])
-    ncand = (lens - 1) // bs
+    ncand = np.maximum((lens - 1) // bs - (w.window - 1), 0)
     check_supports(g["bits"], ref["x"], ref["tau"], ncand)
     for b in range(B):
         for gg in range(Hkv):
@@ -287,8 +304,7 @@ def test_decode_parity(case):
             cnt = g["count"][b, gg]
             check_list(cnt, g["idx"][b, gg], union, solid, near)
             lst = g["idx"][b, gg, :cnt]
-            np.testing.assert_allclose(np.exp(g["logp"][b, gg, lst]), ref["pbar"][b, gg, lst],
-                                       atol=2e-5)
+            check_bias(g["logp"][b, gg, lst], ref["pbar"][b, gg, lst], w.sigma)
     err = np.abs(g["o"] - ref["o"]).max()
     assert err <= TOL[w.dtype], f"decode max-abs err {err:.3e}"
     # summary written exactly when the step completes a block

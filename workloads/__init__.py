@@ -56,6 +56,8 @@ class Workload:
     plant_per_head: bool = False
     max_len: int = 0      # decode cache capacity (0 = seq_len)
     summary_query: float = 0.0  # > 0: Stage 0 summary queries q_bar ~ this * N(0, 1)
+    sigma: float = 1.0    # prior strength (Stage 2 bias sigma * log pbar)
+    window: int = 1       # near-diagonal branch in blocks
 
     @property
     def group(self) -> int:
