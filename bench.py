@@ -139,6 +139,12 @@ def prefill_bench(args, torch, dash, W):
     t_sum_q = events_time(lambda: dash.dash_summarize(p, k, N, 0, nb, ws_mat, summ_q, nb,
                                                       q_bar=qb), args.steps, 2, torch)
     t_route = events_time(lambda: dash.dash_route(p, q, N, summ, nb, rb), args.steps, 2, torch)
+    # the bit-packed mask hand-over: routing that also writes the tile masks,
+    # and the lists rebuilt from those masks
+    rbm = dash.RouteBuffers(sizes, dev, tile_bits=True)
+    t_route_m = events_time(lambda: dash.dash_route(p, q, N, summ, nb, rbm), args.steps, 2,
+                            torch)
+    t_m2l = events_time(lambda: dash.dash_mask_to_list(p, N, rbm), args.steps, 2, torch)
     o2 = torch.empty_like(q)
     t_att = events_time(lambda: dash.dash_attend(p, q, k, v, N, rb, o2), args.steps, 2, torch)
 
@@ -160,7 +166,8 @@ def prefill_bench(args, torch, dash, W):
     res = {
         "workload": w, "ms_step": ms_step, "tok_s": B * N / (ms_step * 1e-3),
         "stages_ms": {"summarize": t_sum, "route": t_route, "attend": t_att,
-                      "summarize_qbar": t_sum_q},
+                      "summarize_qbar": t_sum_q, "route_with_tile_masks": t_route_m,
+                      "mask_to_list": t_m2l},
         "attend_flops": att_flops, "attend_tflops": achieved,
         "tile_union_density": tile_union_density,
         "selected_chunk_fraction": float(chunks) / dense_chunks,

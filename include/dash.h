@@ -119,19 +119,25 @@ typedef struct {
  *   support_bits [B, H, n, ceil(nb/32)] uint32, optional (NULL = not written);
  *                                     bit j set iff block j is in that head's own
  *                                     entmax support (x_j > tau), before the GQA
- *                                     average */
+ *                                     average
+ *   tile_bits    [B, Hkv, n_qt, ceil(nb/32)] uint32, optional (NULL = not
+ *                                     written); the bit-packed mask of active
+ *                                     chunks handed to Stage 2: bit j (word j/32,
+ *                                     bit j%32) set iff block j is in the tile's
+ *                                     list, every other bit 0 */
 typedef struct {
   float* tau;
   int32_t* sel_count;
   int32_t* sel_idx;
   float* sel_logp;
   uint32_t* support_bits;
+  uint32_t* tile_bits;
 } dash_route_buf;
 
 /* Element counts of each dash_route_buf array (not bytes). */
 typedef struct {
   int64_t n_qt, nb, qt;
-  int64_t tau, sel_count, sel_idx, sel_logp, support_bits;
+  int64_t tau, sel_count, sel_idx, sel_logp, support_bits, tile_bits;
 } dash_route_sizes;
 
 const char* dash_status_string(dash_status s);
@@ -185,6 +191,19 @@ dash_status dash_route(const dash_params* p, const void* q, int64_t n, const flo
  * ((n + 64) * d * element size >= 2^31). */
 dash_status dash_attend(const dash_params* p, const void* q, const void* k, const void* v,
                         int64_t n, const dash_route_buf* route, void* o, void* stream);
+
+/* Bit-packed mask -> Stage 2 lists, for prefill (the DashAttention explainer,
+ * Technical summary, Stage 2: the attention kernel walks the active chunks
+ * that a bit-packed mask defines).  For every tile, the set bits of
+ * route->tile_bits that fall on the tile's routing candidates (blocks
+ * j < floor(64 qt / bs) - (window - 1)) become sel_idx (ascending) and
+ * sel_count; bits on any other block are ignored.  dash_attend then runs on
+ * route, with sel_logp (the bias of each listed block, -inf to mask a
+ * position) supplied by the caller.
+ *   route  tile_bits (read), sel_count and sel_idx (written); sized by
+ *          dash_route_sizes_prefill(p, n) */
+dash_status dash_mask_to_list(const dash_params* p, int64_t n, const dash_route_buf* route,
+                              void* stream);
 
 /* Fused causal prefill: dash_summarize of blocks [0, floor(n/bs)) into summ
  * (with the summary queries q_bar, NULL = mean pooling), dash_route into the

@@ -42,12 +42,13 @@ class dash_params(ctypes.Structure):
 class dash_route_buf(ctypes.Structure):
     _fields_ = [("tau", ctypes.c_void_p), ("sel_count", ctypes.c_void_p),
                 ("sel_idx", ctypes.c_void_p), ("sel_logp", ctypes.c_void_p),
-                ("support_bits", ctypes.c_void_p)]
+                ("support_bits", ctypes.c_void_p), ("tile_bits", ctypes.c_void_p)]
 
 
 class dash_route_sizes(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in
-                ("n_qt", "nb", "qt", "tau", "sel_count", "sel_idx", "sel_logp", "support_bits")]
+                ("n_qt", "nb", "qt", "tau", "sel_count", "sel_idx", "sel_logp", "support_bits",
+                 "tile_bits")]
 
 
 if not os.path.exists(LIB_PATH):
@@ -75,6 +76,8 @@ _lib.dash_route.restype = ctypes.c_int
 _lib.dash_route.argtypes = [_P, _V, _I, _V, _I, _R, _V]
 _lib.dash_attend.restype = ctypes.c_int
 _lib.dash_attend.argtypes = [_P, _V, _V, _V, _I, _R, _V, _V]
+_lib.dash_mask_to_list.restype = ctypes.c_int
+_lib.dash_mask_to_list.argtypes = [_P, _I, _R, _V]
 _lib.dash_prefill.restype = ctypes.c_int
 _lib.dash_prefill.argtypes = [_P, _V, _V, _V, _I, _V, _V, _V, _I, _V, _V, ctypes.c_size_t, _V]
 _lib.dash_decode.restype = ctypes.c_int
@@ -84,7 +87,7 @@ _lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _V, _I, _V, _R, _V,
 EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
             "dash_route_sizes_decode", "dash_prefill_workspace_bytes",
             "dash_decode_workspace_bytes", "dash_summarize", "dash_route", "dash_attend",
-            "dash_prefill", "dash_decode")
+            "dash_mask_to_list", "dash_prefill", "dash_decode")
 
 
 # ---------------------------------------------------------------------------------------
@@ -182,7 +185,7 @@ def dash_decode_workspace_bytes(p, max_len) -> int:
 class RouteBuffers:
     """Device tensors of a dash_route_buf (torch supplies the memory)."""
 
-    def __init__(self, sizes, device="cuda", bits=False):
+    def __init__(self, sizes, device="cuda", bits=False, tile_bits=False):
         self.sizes = sizes
         self.tau = torch.empty(sizes["tau"], dtype=torch.float32, device=device)
         self.sel_count = torch.empty(sizes["sel_count"], dtype=torch.int32, device=device)
@@ -190,6 +193,8 @@ class RouteBuffers:
         self.sel_logp = torch.empty(sizes["sel_logp"], dtype=torch.float32, device=device)
         self.support_bits = (torch.empty(sizes["support_bits"], dtype=torch.int32, device=device)
                              if bits else None)
+        self.tile_bits = (torch.empty(sizes["tile_bits"], dtype=torch.int32, device=device)
+                          if tile_bits else None)
 
     def struct(self):
         s = self.sizes
@@ -199,7 +204,9 @@ class RouteBuffers:
             _dev(self.sel_idx, "sel_idx", s["sel_idx"], torch.int32),
             _dev(self.sel_logp, "sel_logp", s["sel_logp"], torch.float32),
             None if self.support_bits is None else
-            _dev(self.support_bits, "support_bits", s["support_bits"], torch.int32))
+            _dev(self.support_bits, "support_bits", s["support_bits"], torch.int32),
+            None if self.tile_bits is None else
+            _dev(self.tile_bits, "tile_bits", s["tile_bits"], torch.int32))
 
 
 def workspace(nbytes, device="cuda"):
@@ -246,6 +253,17 @@ def dash_attend(p, q, k, v, n, route: RouteBuffers, o, stream=None):
         ctypes.byref(p), _dev(q, "q", B * H * n * d, dt), _dev(k, "k", B * Hkv * n * d, dt),
         _dev(v, "v", B * Hkv * n * d, dt), n, ctypes.byref(rb), _dev(o, "o", B * H * n * d, dt),
         _stream(stream)))
+
+
+def dash_mask_to_list(p, n, route: RouteBuffers, stream=None):
+    """route.tile_bits -> route.sel_idx / sel_count (prefill layout)."""
+    if route.sizes != dash_route_sizes_prefill(p, n):
+        raise ValueError("route buffers were sized for another problem")
+    if route.tile_bits is None:
+        raise ValueError("route buffers hold no tile_bits")
+    rb = route.struct()
+    _check("dash_mask_to_list", _lib.dash_mask_to_list(ctypes.byref(p), n, ctypes.byref(rb),
+                                                       _stream(stream)))
 
 
 def dash_prefill(p, q, k, v, n, w_s, summ, summ_blocks, o, ws, stream=None, q_bar=None):

@@ -67,6 +67,7 @@ void prefill_sizes(const Shape& s, int64_t n, dash_route_sizes* r) {
   r->sel_idx = r->sel_count * r->nb;
   r->sel_logp = r->sel_idx * kQT;
   r->support_bits = (int64_t)s.B * s.H * n * ((r->nb + 31) / 32);
+  r->tile_bits = r->sel_count * ((r->nb + 31) / 32);
 }
 
 // LDS needed by the prefill routing kernel (must match route.hip)
@@ -144,6 +145,7 @@ dash_status dash_route_sizes_decode(const dash_params* p, int64_t max_len, dash_
   out->sel_idx = out->sel_count * out->nb;
   out->sel_logp = out->sel_idx;
   out->support_bits = (int64_t)s.B * s.H * ((out->nb + 31) / 32);
+  out->tile_bits = out->sel_count * ((out->nb + 31) / 32);
   return DASH_OK;
 }
 
@@ -208,6 +210,18 @@ dash_status dash_attend(const dash_params* p, const void* q, const void* k, cons
   return hip_status(dash::launch_attend_prefill(s, q, k, v, n, *route, o, (hipStream_t)stream));
 }
 
+dash_status dash_mask_to_list(const dash_params* p, int64_t n, const dash_route_buf* route,
+                              void* stream) {
+  Shape s;
+  dash_status st = check_params(p, &s);
+  if (st != DASH_OK) return st;
+  if (n < 0 || !route || !route->tile_bits || !route->sel_count || !route->sel_idx)
+    return DASH_ERR_INVALID_ARG;
+  if (n == 0) return DASH_OK;
+  if (!grid_ok(((n + kQT - 1) / kQT) * s.B * s.Hkv)) return DASH_ERR_UNSUPPORTED;
+  return hip_status(dash::launch_mask_to_list(s, n, *route, (hipStream_t)stream));
+}
+
 dash_status dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
                          int64_t n, const float* w_s, const float* q_bar, float* summ,
                          int64_t summ_blocks, void* o, void* ws, size_t ws_bytes, void* stream) {
@@ -230,6 +244,7 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
   rb.sel_idx = (int32_t*)(base + L.off_idx);
   rb.sel_logp = (float*)(base + L.off_logp);
   rb.support_bits = nullptr;
+  rb.tile_bits = nullptr;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = dash::launch_summarize(s, k, n, 0, n / s.bs, w_s, q_bar, summ, summ_blocks, hs);
   if (e == hipSuccess) e = dash::launch_route_prefill(s, q, n, summ, summ_blocks, rb, hs);
@@ -257,7 +272,7 @@ dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache
   if (!grid_ok(L.n_split) || (int64_t)s.B * s.Hkv > 65535) return DASH_ERR_UNSUPPORTED;
   if (s.dtype == DASH_BF16 && (int64_t)s.B * s.Hkv > dash::kDecodeMaxBg)
     return DASH_ERR_UNSUPPORTED;
-  dash_route_buf rb = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  dash_route_buf rb = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   if (route) rb = *route;
   return hip_status(dash::launch_decode(s, q, k_cache, v_cache, cache_len, max_len, w_s, q_bar,
                                         summ, summ_blocks, o, rb, L, (char*)ws,

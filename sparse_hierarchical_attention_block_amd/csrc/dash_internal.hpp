@@ -28,6 +28,10 @@ hipError_t launch_summarize(const Shape& s, const void* k, int64_t kv_len, int64
 hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const float* summ,
                                 int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st);
 
+// Bit-packed tile masks -> ascending lists (prefill layout).
+hipError_t launch_mask_to_list(const Shape& s, int64_t n, const dash_route_buf& rb,
+                               hipStream_t st);
+
 // Stage 2, causal prefill.
 hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                  int64_t n, const dash_route_buf& rb, void* o, hipStream_t st);

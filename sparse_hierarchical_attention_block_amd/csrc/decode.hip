@@ -50,6 +50,7 @@ struct DecodeArgs {
   int32_t* idx;      // [B, Hkv, nb]
   float* logp;       // [B, Hkv, nb]  by block id
   uint32_t* bits;    // [B, H, nwords] or null
+  uint32_t* tile_bits;  // [B, Hkv, nwords] bit-packed union, or null
   float* part;       // [B, Hkv, n_split, G, D + 2]
   float* summ_w;     // the summary cache, written for a block this step completes
   const float* w_s;
@@ -268,14 +269,29 @@ __device__ __forceinline__ void route_union(const DecodeArgs& a, int64_t bg, int
     base += w < wave ? c : 0;
     total += c;
   }
+  uint32_t* tb = a.tile_bits ? a.tile_bits + bg * a.nwords : nullptr;
   for (int j0 = jb; j0 < je; j0 += kWave) {
     const int j = j0 + lane;
     const bool f = j < je && Ps[j] > 0.f;
     const uint64_t mask = __ballot(f);
     if (f) a.idx[bg * a.nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
     base += __popcll(mask);
+    // the bit-packed union: j0 is a multiple of 64, so this chunk is two words
+    if (tb && lane < 2 && j0 / 32 + lane < a.nwords)
+      tb[j0 / 32 + lane] = (uint32_t)(mask >> (32 * lane));
   }
+  if (tb)
+    for (int w = 2 * ((ncand + kWave - 1) / kWave) + (int)threadIdx.x; w < a.nwords;
+         w += blockDim.x)
+      tb[w] = 0u;
   if (threadIdx.x == 0) a.count[bg] = total;
+}
+
+// The routing result of a (sequence, KV head) without candidates.
+__device__ __forceinline__ void route_pair_empty(const DecodeArgs& a, int64_t bg) {
+  if (threadIdx.x == 0) a.count[bg] = 0;
+  if (a.tile_bits)
+    for (int w = threadIdx.x; w < a.nwords; w += blockDim.x) a.tile_bits[bg * a.nwords + w] = 0u;
 }
 
 // One workgroup per (sequence, KV head), one wave per query head.  With VPL > 0
@@ -294,7 +310,7 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
   const float* xr = a.x + row * a.nb;
   if (ncand == 0) {
     route_row_empty(a, row);
-    if (threadIdx.x == 0) a.count[bg] = 0;
+    route_pair_empty(a, bg);
     return;
   }
   if constexpr (VPL > 0) {
@@ -354,7 +370,7 @@ __global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(DecodeArg
   const int64_t row0 = (int64_t)b * a.H + g * G;
   if (ncand == 0) {
     if (wave < G) route_row_empty(a, row0 + wave);
-    if (threadIdx.x == 0) a.count[bg] = 0;
+    route_pair_empty(a, bg);
     return;
   }
   score_groups<__bf16, D, kSelectGroups>(a, bg, row0, ncand, wave, kSelectWaves,
@@ -829,6 +845,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   a.idx = rb.sel_idx ? rb.sel_idx : (int32_t*)(ws + L.off_idx);
   a.logp = rb.sel_logp ? rb.sel_logp : (float*)(ws + L.off_logp);
   a.bits = rb.support_bits;
+  a.tile_bits = rb.tile_bits;
   a.part = (float*)(ws + L.off_part);
   a.summ_w = summ;
   a.w_s = w_s;

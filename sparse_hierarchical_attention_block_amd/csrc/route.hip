@@ -42,6 +42,7 @@ struct RouteArgs {
   int32_t* sel_idx;
   float* sel_logp;
   uint32_t* bits;
+  uint32_t* tile_bits;   // optional bit-packed union per tile
   int64_t n_qt, nb;
   int nwords;
   int H, Hkv, G, bs, B;
@@ -54,6 +55,27 @@ struct RouteArgs {
 };
 
 __host__ __device__ inline int round_up16(int x) { return (x + 15) & ~15; }
+
+// Compaction of the tile's union flags (blocks j < t) into the ascending list
+// sel_idx / sel_count, and the same set as the tile's bit-packed mask when
+// asked for (words past the candidates are zero).  One wave calls.
+__device__ void compact_union(const RouteArgs& a, const int* uflag, int t, int64_t tile) {
+  const int lane = threadIdx.x % kWave;
+  uint32_t* tb = a.tile_bits ? a.tile_bits + tile * a.nwords : nullptr;
+  int base = 0;
+  for (int j0 = 0; j0 < t; j0 += kWave) {
+    const int j = j0 + lane;
+    const bool f = j < t && uflag[j] != 0;
+    const uint64_t mask = __ballot(f);
+    if (f) a.sel_idx[tile * a.nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
+    base += __popcll(mask);
+    if (tb && lane < 2 && j0 / 32 + lane < a.nwords)
+      tb[j0 / 32 + lane] = (uint32_t)(mask >> (32 * lane));
+  }
+  if (tb)
+    for (int w = 2 * ((t + kWave - 1) / kWave) + lane; w < a.nwords; w += kWave) tb[w] = 0u;
+  if (lane == 0) a.sel_count[tile] = base;
+}
 
 // ---- step 1, bf16: MFMA with a 3-way bf16 split of the summaries ----------------
 // Wave w computes candidate tiles w, w + NT/64, ... against every row tile of
@@ -175,6 +197,8 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
         for (int w = 0; w < a.nwords; ++w) a.bits[r * a.nwords + w] = 0u;
     }
     if (threadIdx.x == 0) a.sel_count[tile] = 0;
+    if (a.tile_bits)
+      for (int w = threadIdx.x; w < a.nwords; w += blockDim.x) a.tile_bits[tile * a.nwords + w] = 0u;
     return;
   }
 
@@ -304,19 +328,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
   __syncthreads();
 
   // step 4: compaction (ascending block ids)
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    int base = 0;
-    for (int j0 = 0; j0 < t; j0 += kWave) {
-      const int j = j0 + lane;
-      const bool f = j < t && uflag[j] != 0;
-      const uint64_t mask = __ballot(f);
-      const int before = __popcll(mask & ((1ull << lane) - 1ull));
-      if (f) a.sel_idx[tile * a.nb + base + before] = j;
-      base += __popcll(mask);
-    }
-    if (lane == 0) a.sel_count[tile] = base;
-  }
+  if (threadIdx.x < kWave) compact_union(a, uflag, t, tile);
 }
 
 
@@ -364,6 +376,8 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
         for (int w = 0; w < a.nwords; ++w) a.bits[r * a.nwords + w] = 0u;
     }
     if (threadIdx.x == 0) a.sel_count[tile] = 0;
+    if (a.tile_bits)
+      for (int w = threadIdx.x; w < a.nwords; w += blockDim.x) a.tile_bits[tile * a.nwords + w] = 0u;
     return;
   }
   const int CT = (t + 15) / 16;
@@ -541,17 +555,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
   __syncthreads();
 
   // ---- compaction (ascending block ids) ----
-  if (threadIdx.x < kWave) {
-    int base = 0;
-    for (int j0 = 0; j0 < t; j0 += kWave) {
-      const int j = j0 + lane;
-      const bool f = j < t && uflag[j] != 0;
-      const uint64_t mask = __ballot(f);
-      if (f) a.sel_idx[tile * a.nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
-      base += __popcll(mask);
-    }
-    if (lane == 0) a.sel_count[tile] = base;
-  }
+  if (threadIdx.x < kWave) compact_union(a, uflag, t, tile);
 }
 
 // positions per pass: largest power of two in [16/G, 64] whose score buffer
@@ -562,6 +566,37 @@ static int route_pp(int G, int pitch, size_t budget) {
   while (pp * G < 16) pp <<= 1;
   while (pp * G > 16 * kRouteMaxRowTiles) pp >>= 1;
   return pp;
+}
+
+// Bit-packed tile masks -> ascending lists: one wave per tile; only bits on
+// the tile's routing candidates count.
+__global__ __launch_bounds__(kWave) void mask_to_list_kernel(
+    const uint32_t* __restrict__ tile_bits, int32_t* __restrict__ sel_count,
+    int32_t* __restrict__ sel_idx, int64_t n_qt, int64_t nb, int nwords, int bs, int window) {
+  const int64_t tile = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t qt = tile % n_qt;
+  const int t = max(0, (int)((qt * kQT) / bs) - (window - 1));
+  const uint32_t* tb = tile_bits + tile * nwords;
+  int base = 0;
+  for (int j0 = 0; j0 < t; j0 += kWave) {
+    const int j = j0 + lane;
+    const bool f = j < t && ((tb[j >> 5] >> (j & 31)) & 1u) != 0u;
+    const uint64_t mask = __ballot(f);
+    if (f) sel_idx[tile * nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
+    base += __popcll(mask);
+  }
+  if (lane == 0) sel_count[tile] = base;
+}
+
+hipError_t launch_mask_to_list(const Shape& s, int64_t n, const dash_route_buf& rb,
+                               hipStream_t st) {
+  const int64_t n_qt = (n + kQT - 1) / kQT;
+  const int64_t nb = (n + s.bs - 1) / s.bs;
+  hipLaunchKernelGGL(mask_to_list_kernel, dim3((unsigned)(n_qt * s.B * s.Hkv)), dim3(kWave), 0,
+                     st, (const uint32_t*)rb.tile_bits, rb.sel_count, rb.sel_idx, n_qt, nb,
+                     (int)((nb + 31) / 32), s.bs, s.window);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const float* summ,
@@ -577,6 +612,7 @@ hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const 
   a.sel_idx = rb.sel_idx;
   a.sel_logp = rb.sel_logp;
   a.bits = rb.support_bits;
+  a.tile_bits = rb.tile_bits;
   a.n_qt = (n + kQT - 1) / kQT;
   a.nb = (n + s.bs - 1) / s.bs;
   a.nwords = (int)((a.nb + 31) / 32);

@@ -60,7 +60,7 @@ def run_prefill(w, inp, bits=True):
     summ = torch.zeros(B * Hkv * summ_blocks * d, dtype=torch.float32, device=dev())
     dash.dash_summarize(p, k, N, 0, nbf, ws, summ, summ_blocks, q_bar=qbar_dev(inp))
     sizes = dash.dash_route_sizes_prefill(p, N)
-    rb = dash.RouteBuffers(sizes, dev(), bits=bits)
+    rb = dash.RouteBuffers(sizes, dev(), bits=bits, tile_bits=True)
     dash.dash_route(p, q, N, summ, summ_blocks, rb)
     o = torch.empty_like(q)
     dash.dash_attend(p, q, k, v, N, rb, o)
@@ -73,6 +73,8 @@ def run_prefill(w, inp, bits=True):
         "count": rb.sel_count.cpu().numpy().reshape(B, Hkv, n_qt),
         "idx": rb.sel_idx.cpu().numpy().reshape(B, Hkv, n_qt, nb),
         "logp": rb.sel_logp.cpu().numpy().reshape(B, Hkv, n_qt, nb, dash.QUERY_TILE),
+        "tile_bits": unpack_bits(rb.tile_bits.cpu().numpy().reshape(B, Hkv, n_qt, -1), nb),
+        "tile_words": rb.tile_bits.cpu().numpy().reshape(B, Hkv, n_qt, -1),
     }
     if bits:
         out["bits"] = unpack_bits(rb.support_bits.cpu().numpy().reshape(B, H, N, -1), nb)
@@ -116,8 +118,8 @@ def run_decode(w, inp, summ_np=None, route=True):
     summ_before = summ.clone()
     o = torch.empty_like(q)
     ws = dash.workspace(dash.dash_decode_workspace_bytes(p, Lmax), dev())
-    rb = dash.RouteBuffers(dash.dash_route_sizes_decode(p, Lmax), dev(), bits=True) if route \
-        else None
+    rb = dash.RouteBuffers(dash.dash_route_sizes_decode(p, Lmax), dev(), bits=True,
+                           tile_bits=True) if route else None
     dash.dash_decode(p, q, kc, vc, lens, Lmax, ws_mat, summ, summ_blocks, o, ws, route=rb,
                      q_bar=qbar_dev(inp))
     torch.cuda.synchronize()
@@ -131,7 +133,9 @@ def run_decode(w, inp, summ_np=None, route=True):
             "count": rb.sel_count.cpu().numpy().reshape(B, Hkv),
             "idx": rb.sel_idx.cpu().numpy().reshape(B, Hkv, nb),
             "logp": rb.sel_logp.cpu().numpy().reshape(B, Hkv, nb),
-            "bits": unpack_bits(rb.support_bits.cpu().numpy().reshape(B, H, -1), nb)})
+            "bits": unpack_bits(rb.support_bits.cpu().numpy().reshape(B, H, -1), nb),
+            "tile_bits": unpack_bits(rb.tile_bits.cpu().numpy().reshape(B, Hkv, -1), nb),
+            "tile_words": rb.tile_bits.cpu().numpy().reshape(B, Hkv, -1)})
     return out
 
 
@@ -147,6 +151,20 @@ def check_bias(logp, pbar, sigma):
     assert np.all(logp[~off] == 0.0)
     bad = (off != (pbar == 0)) & (pbar > 2e-5)
     assert not bad.any(), f"{int(bad.sum())} support entries differ"
+
+
+def check_tile_mask(words, bits, count, idx):
+    """The bit-packed mask holds exactly the listed blocks: bits [..., nb] and
+    words [..., nwords] against sel_count / sel_idx (bit-exact), padding bits 0."""
+    nb = bits.shape[-1]
+    flat_bits = bits.reshape(-1, nb)
+    flat_words = words.reshape(flat_bits.shape[0], -1)
+    cnt, lst = count.reshape(-1), idx.reshape(flat_bits.shape[0], -1)
+    for r in range(flat_bits.shape[0]):
+        np.testing.assert_array_equal(np.flatnonzero(flat_bits[r]), lst[r, :cnt[r]])
+    pad = flat_words.shape[1] * 32 - nb
+    if pad:
+        assert not np.any(flat_words[:, -1].astype(np.uint32) >> np.uint32(32 - pad))
 
 
 def check_supports(gpu_bits, x, tau, ncand):

@@ -114,7 +114,7 @@ def test_null_pointers_and_sizes():
     assert lib.dash_summarize(ctypes.byref(p), FAKE, 1024, 0, 16, FAKE, None, FAKE, 15,
                               None) == L.DASH_ERR_INVALID_ARG
     # route without buffers
-    rb = L.dash_route_buf(FAKE, FAKE, None, FAKE, None)
+    rb = L.dash_route_buf(FAKE, FAKE, None, FAKE, None, None)
     assert lib.dash_route(ctypes.byref(p), FAKE, 1024, FAKE, 16, ctypes.byref(rb),
                           None) == L.DASH_ERR_INVALID_ARG
     # decode: bad max_len, small summary cache, small workspace
@@ -125,6 +125,27 @@ def test_null_pointers_and_sizes():
                            63, FAKE, None, FAKE, dneed, None) == L.DASH_ERR_INVALID_ARG
     assert lib.dash_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 4096, FAKE, None, FAKE,
                            64, FAKE, None, FAKE, dneed - 1, None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_mask_to_list_argument_checks():
+    p = P()
+    lib = L._lib
+    full = L.dash_route_buf(FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    no_bits = L.dash_route_buf(FAKE, FAKE, FAKE, FAKE, None, None)
+    no_idx = L.dash_route_buf(FAKE, FAKE, None, FAKE, None, FAKE)
+    assert lib.dash_mask_to_list(ctypes.byref(p), 1024, ctypes.byref(no_bits),
+                                 None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_mask_to_list(ctypes.byref(p), 1024, ctypes.byref(no_idx),
+                                 None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_mask_to_list(ctypes.byref(p), -1, ctypes.byref(full),
+                                 None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_mask_to_list(ctypes.byref(p), 1024, None, None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_mask_to_list(ctypes.byref(p), 0, ctypes.byref(full), None) == L.DASH_OK
+    assert lib.dash_mask_to_list(ctypes.byref(P(window=0)), 1024, ctypes.byref(full),
+                                 None) == L.DASH_ERR_INVALID_ARG
+    s = dash.dash_route_sizes_prefill(p, 8192)
+    assert s["tile_bits"] == 8 * 128 * 4
+    assert dash.dash_route_sizes_decode(P(batch=32), 32768)["tile_bits"] == 32 * 8 * 16
 
 
 def test_binding_rejects_host_tensors():

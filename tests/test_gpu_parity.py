@@ -12,9 +12,10 @@ import torch
 
 import oracle
 import sparse_hierarchical_attention_block_amd as dash
+from brute import dense_attention
 import workloads as W
-from gpu_helpers import (TOL, check_bias, check_list, check_supports, check_tau, dev, params,
-                         run_decode,
+from gpu_helpers import (TOL, check_bias, check_list, check_supports, check_tau,
+                         check_tile_mask, dev, params, run_decode,
                          run_prefill, run_prefill_fused, tile_union_ref, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -90,6 +91,8 @@ def compare_prefill(w, g, ref):
                 lst = g["idx"][b, gg, qt, :cnt]
                 check_bias(g["logp"][b, gg, qt, lst, : p1 - p0].T,           # [P, listed]
                            ref["pbar"][b, p0:p1, gg][:, lst], w.sigma)
+    # the bit-packed mask of each tile holds exactly its list
+    check_tile_mask(g["tile_words"], g["tile_bits"], g["count"], g["idx"])
     # Stage 2 output
     err = np.abs(g["o"] - ref["o"]).max()
     assert err <= tol, f"output max-abs error {err:.3e} > {tol}"
@@ -158,6 +161,72 @@ def test_attend_given_oracle_route():
     torch.cuda.synchronize()
     err = np.abs(o.float().cpu().numpy() - ref["o"]).max()
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("dtype,window", [("f32", 1), ("bf16", 1), ("bf16", 3), ("f32", 2)])
+def test_external_mask_drives_stage2(dtype, window):
+    """Stage 2 from a bit-packed mask made outside the library: seeded random
+    tile masks (with bits set on blocks outside the candidates, which must be
+    ignored) and random biases; dash_mask_to_list builds the lists, dash_attend
+    runs on them; checked against brute-force dense attention with that mask
+    and bias.  Also: the lists round-trip through the mask dash_route writes."""
+    w = tiny(batch=2, n_heads=4, n_kv_heads=2, seq_len=700, dtype=dtype, gamma=8.0,
+             window=window)
+    print(f"[external mask] {dtype} window={window}", flush=True)
+    inp = W.make_prefill(w)
+    B, H, Hkv, N, d, bs, G = w.batch, w.n_heads, w.n_kv_heads, w.seq_len, w.head_dim, \
+        w.block_size, w.group
+    p = params(w)
+    sizes = dash.dash_route_sizes_prefill(p, N)
+    n_qt, nb = sizes["n_qt"], sizes["nb"]
+    nwords = (nb + 31) // 32
+    rng = np.random.default_rng(1234 + window)
+    bits = rng.random((B, Hkv, n_qt, nwords * 32)) < 0.4
+    weights = np.uint64(1) << np.arange(32, dtype=np.uint64)          # bit j % 32 of word j // 32
+    words = (bits.reshape(B, Hkv, n_qt, nwords, 32) * weights).sum(-1).astype(np.uint32)
+    logp = np.log(rng.uniform(0.05, 1.0, (B, Hkv, n_qt, nb, QT))).astype(np.float32)
+    logp[rng.random(logp.shape) < 0.1] = -np.inf
+    rb = dash.RouteBuffers(sizes, dev(), tile_bits=True)
+    rb.tile_bits.copy_(torch.from_numpy(words.view(np.int32).ravel()))
+    rb.sel_logp.copy_(torch.from_numpy(logp.ravel()))
+    dash.dash_mask_to_list(p, N, rb)
+    q, k, v = (to_dev(inp[x], dtype) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    dash.dash_attend(p, q, k, v, N, rb, o)
+    torch.cuda.synchronize()
+    count = rb.sel_count.cpu().numpy().reshape(B, Hkv, n_qt)
+    idx = rb.sel_idx.cpu().numpy().reshape(B, Hkv, n_qt, nb)
+    got = o.float().cpu().numpy()
+    t = np.arange(N)
+    for b in range(B):
+        for g in range(Hkv):
+            bias = np.full((N, N), -np.inf)
+            for qt in range(n_qt):
+                p0, p1 = qt * QT, min(N, qt * QT + QT)
+                ncand = max(p0 // bs - (window - 1), 0)
+                want = np.flatnonzero(bits[b, g, qt, :ncand])
+                np.testing.assert_array_equal(idx[b, g, qt, :count[b, g, qt]], want)
+                for j in want:
+                    bias[p0:p1, j * bs:(j + 1) * bs] = logp[b, g, qt, j, :p1 - p0, None]
+                for i in range(p0, p1):
+                    bias[i, ncand * bs:i + 1] = 0.0
+            mask = np.isfinite(bias)
+            for hh in range(G):
+                h = g * G + hh
+                ref = dense_attention(inp["q"][b, h], inp["k"][b, g], inp["v"][b, g],
+                                      bias=np.where(mask, bias, 0.0), mask=mask)
+                err = np.abs(got[b, h] - ref).max()
+                assert err <= TOL[dtype], f"b={b} h={h}: {err:.3e}"
+    # round trip: the mask dash_route writes rebuilds its own lists
+    g1 = run_prefill(w, inp, bits=False)
+    rb2 = dash.RouteBuffers(sizes, dev(), tile_bits=True)
+    rb2.tile_bits.copy_(torch.from_numpy(g1["tile_words"].ravel()))
+    dash.dash_mask_to_list(p, N, rb2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(rb2.sel_count.cpu().numpy().reshape(B, Hkv, n_qt), g1["count"])
+    idx2 = rb2.sel_idx.cpu().numpy().reshape(B, Hkv, n_qt, nb)
+    for (b, g, qt), c in np.ndenumerate(g1["count"]):
+        np.testing.assert_array_equal(idx2[b, g, qt, :c], g1["idx"][b, g, qt, :c])
 
 
 def test_unselected_values_do_not_matter():
@@ -305,6 +374,7 @@ def test_decode_parity(case):
             check_list(cnt, g["idx"][b, gg], union, solid, near)
             lst = g["idx"][b, gg, :cnt]
             check_bias(g["logp"][b, gg, lst], ref["pbar"][b, gg, lst], w.sigma)
+    check_tile_mask(g["tile_words"], g["tile_bits"], g["count"], g["idx"])
     err = np.abs(g["o"] - ref["o"]).max()
     assert err <= TOL[w.dtype], f"decode max-abs err {err:.3e}"
     # summary written exactly when the step completes a block
