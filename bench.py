@@ -216,6 +216,24 @@ def decode_bench(args, torch, dash, W):
     step = lambda: dash.dash_decode(p, q, kc, vc, lens, L, ws_mat, summ, nb, o, ws,  # noqa
                                     route=rb)
     ms = events_time(step, args.steps, args.warmup, torch)
+    # the same step over a paged cache: every block in its own page, pages in a
+    # seeded random order
+    nblk = (L + bs - 1) // bs
+    gen = torch.Generator(device="cpu").manual_seed(1234)
+    perm = torch.randperm(B * nblk, generator=gen).to(dev)
+    kp = torch.empty((B * nblk, Hkv, bs, d), dtype=kc.dtype, device=dev)
+    vp = torch.empty_like(kp)
+    kp[perm] = kc.view(B, Hkv, nblk, bs, d).transpose(1, 2).reshape(B * nblk, Hkv, bs, d)
+    vp[perm] = vc.view(B, Hkv, nblk, bs, d).transpose(1, 2).reshape(B * nblk, Hkv, bs, d)
+    table = perm.view(B, nblk).to(torch.int32).contiguous()
+    op = torch.empty_like(q)
+    rbp = dash.RouteBuffers(dash.dash_route_sizes_decode(p, L), dev)
+    step_p = lambda: dash.dash_decode_paged(p, q, kp, vp, table, lens, L, ws_mat, summ, nb,  # noqa
+                                            op, ws, route=rbp)
+    ms_paged = events_time(step_p, args.steps, args.warmup, torch)
+    paged_same = bool(torch.equal(op, o))
+    del kp, vp
+
     count = rb.sel_count.cpu().numpy().astype(np.int64)
     own_len = (L - 1) % bs + 1
     own = (L - 1) // bs
@@ -226,7 +244,10 @@ def decode_bench(args, torch, dash, W):
     density = float((count + n_branch).sum() / (B * Hkv * (ncand + n_branch)))
     summ_bytes = float(B * Hkv * ncand * d * 4)
     gbs = sel_bytes / (ms * 1e-3) / 1e9
+    gbs_p = sel_bytes / (ms_paged * 1e-3) / 1e9
     return {"workload": w, "us_per_step": ms * 1e3, "selected_kv_bytes": sel_bytes,
+            "paged": {"us_per_step": round(ms_paged * 1e3, 2), "same_output": paged_same,
+                      "roofline_frac": round(gbs_p / PEAK_HBM_GBS, 4)},
             "block_density": density,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -318,7 +339,8 @@ def main():
                           "block_density": round(dec["block_density"], 4),
                           "selected_kv_gb": round(dec["selected_kv_bytes"] / 1e9, 4),
                           "roofline": dec["roofline"],
-                          "all_bytes_gbs": dec["all_bytes_gbs"]}
+                          "all_bytes_gbs": dec["all_bytes_gbs"],
+                          "paged_kv": dec["paged"]}
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 

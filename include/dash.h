@@ -240,6 +240,25 @@ dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache
                         void* o, const dash_route_buf* route, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* dash_decode over a paged KV cache (serving layout; DashAttention explainer,
+ * Contributions: the kernels support incremental decoding).  One page holds
+ * one block of bs keys of every KV head:
+ *   k_pages, v_pages [num_pages, Hkv, bs, d] dtype
+ *   block_table      [B, max_blocks] int32 DEVICE array: block j of sequence b
+ *                    (j < ceil(cache_len[b] / bs)) is in page block_table[b, j];
+ *                    max_blocks >= ceil(max_len / bs)
+ * Every other argument, the result and the summary written for a completed
+ * block are as in dash_decode (the summaries stay per sequence,
+ * [B, Hkv, summ_blocks, d]).  Page ids outside [0, num_pages) are clamped into
+ * that range: a bad table gives wrong results but no access outside the
+ * pages.  No 2 GiB limit on the cache. */
+dash_status dash_decode_paged(const dash_params* p, const void* q, const void* k_pages,
+                              const void* v_pages, int64_t num_pages, const int32_t* block_table,
+                              int64_t max_blocks, const int32_t* cache_len, int64_t max_len,
+                              const float* w_s, const float* q_bar, float* summ,
+                              int64_t summ_blocks, void* o, const dash_route_buf* route,
+                              void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

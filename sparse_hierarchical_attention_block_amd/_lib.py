@@ -80,6 +80,9 @@ _lib.dash_mask_to_list.restype = ctypes.c_int
 _lib.dash_mask_to_list.argtypes = [_P, _I, _R, _V]
 _lib.dash_prefill.restype = ctypes.c_int
 _lib.dash_prefill.argtypes = [_P, _V, _V, _V, _I, _V, _V, _V, _I, _V, _V, ctypes.c_size_t, _V]
+_lib.dash_decode_paged.restype = ctypes.c_int
+_lib.dash_decode_paged.argtypes = [_P, _V, _V, _V, _I, _V, _I, _V, _I, _V, _V, _V, _I, _V, _R, _V,
+                                   ctypes.c_size_t, _V]
 _lib.dash_decode.restype = ctypes.c_int
 _lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _V, _I, _V, _R, _V, ctypes.c_size_t,
                              _V]
@@ -87,7 +90,7 @@ _lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _V, _I, _V, _R, _V,
 EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
             "dash_route_sizes_decode", "dash_prefill_workspace_bytes",
             "dash_decode_workspace_bytes", "dash_summarize", "dash_route", "dash_attend",
-            "dash_mask_to_list", "dash_prefill", "dash_decode")
+            "dash_mask_to_list", "dash_prefill", "dash_decode", "dash_decode_paged")
 
 
 # ---------------------------------------------------------------------------------------
@@ -292,6 +295,39 @@ def dash_decode(p, q, k_cache, v_cache, cache_len, max_len, w_s, summ, summ_bloc
         ctypes.byref(p), _dev(q, "q", B * H * d, dt),
         _dev(k_cache, "k_cache", B * Hkv * max_len * d, dt),
         _dev(v_cache, "v_cache", B * Hkv * max_len * d, dt),
+        _dev(cache_len, "cache_len", B, torch.int32), max_len,
+        _dev(w_s, "w_s", d * d, torch.float32),
+        _opt_dev(q_bar, "q_bar", Hkv * d, torch.float32),
+        _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
+        _dev(o, "o", B * H * d, dt), rb, _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def dash_decode_paged(p, q, k_pages, v_pages, block_table, cache_len, max_len, w_s, summ,
+                      summ_blocks, o, ws, route: RouteBuffers | None = None, stream=None,
+                      q_bar=None):
+    """dash_decode over paged caches k_pages / v_pages [num_pages, Hkv, bs, d] and
+    block_table [B, max_blocks] int32 (block j of sequence b in page block_table[b, j])."""
+    B, H, Hkv, d, bs = p.batch, p.n_heads, p.n_kv_heads, p.head_dim, p.block_size
+    dt = torch_dtype(p)
+    if k_pages.dim() != 4 or tuple(k_pages.shape[1:]) != (Hkv, bs, d):
+        raise ValueError("k_pages must be [num_pages, Hkv, bs, d]")
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("v_pages must match k_pages")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    num_pages, max_blocks = k_pages.shape[0], block_table.shape[1]
+    rb = None
+    if route is not None:
+        if route.sizes != dash_route_sizes_decode(p, max_len):
+            raise ValueError("route buffers were sized for another problem")
+        rb_struct = route.struct()
+        rb = ctypes.byref(rb_struct)
+    _check("dash_decode_paged", _lib.dash_decode_paged(
+        ctypes.byref(p), _dev(q, "q", B * H * d, dt),
+        _dev(k_pages, "k_pages", num_pages * Hkv * bs * d, dt),
+        _dev(v_pages, "v_pages", num_pages * Hkv * bs * d, dt), num_pages,
+        _dev(block_table, "block_table", B * max_blocks, torch.int32), max_blocks,
         _dev(cache_len, "cache_len", B, torch.int32), max_len,
         _dev(w_s, "w_s", d * d, torch.float32),
         _opt_dev(q_bar, "q_bar", Hkv * d, torch.float32),

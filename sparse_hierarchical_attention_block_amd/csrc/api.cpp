@@ -252,11 +252,14 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
   return hip_status(e);
 }
 
-dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache,
+// Shared checks and launch of dash_decode / dash_decode_paged (block_table
+// null: contiguous caches).
+static dash_status decode_impl(const dash_params* p, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* cache_len, int64_t max_len,
                         const float* w_s, const float* q_bar, float* summ, int64_t summ_blocks,
                         void* o, const dash_route_buf* route, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        void* stream, const int32_t* block_table, int64_t max_blocks,
+                        int64_t num_pages) {
   Shape s;
   dash_status st = check_params(p, &s);
   if (st != DASH_OK) return st;
@@ -267,7 +270,8 @@ dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache
   const dash::DecodeLayout L = dash::decode_layout(s, max_len);
   if (!ws || ((uintptr_t)ws % kAlign) != 0) return DASH_ERR_INVALID_ARG;
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE_TOO_SMALL;
-  if ((int64_t)s.G * L.nb * 4 > 160 * 1024 || !seq_bytes_ok(s, max_len))
+  // contiguous caches address one (sequence, KV head) through a 31-bit range
+  if ((int64_t)s.G * L.nb * 4 > 160 * 1024 || (!block_table && !seq_bytes_ok(s, max_len)))
     return DASH_ERR_UNSUPPORTED;
   if (!grid_ok(L.n_split) || (int64_t)s.B * s.Hkv > 65535) return DASH_ERR_UNSUPPORTED;
   if (s.dtype == DASH_BF16 && (int64_t)s.B * s.Hkv > dash::kDecodeMaxBg)
@@ -276,7 +280,30 @@ dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache
   if (route) rb = *route;
   return hip_status(dash::launch_decode(s, q, k_cache, v_cache, cache_len, max_len, w_s, q_bar,
                                         summ, summ_blocks, o, rb, L, (char*)ws,
-                                        (hipStream_t)stream));
+                                        (hipStream_t)stream, block_table, max_blocks,
+                                        num_pages));
+}
+
+dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* cache_len, int64_t max_len,
+                        const float* w_s, const float* q_bar, float* summ, int64_t summ_blocks,
+                        void* o, const dash_route_buf* route, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return decode_impl(p, q, k_cache, v_cache, cache_len, max_len, w_s, q_bar, summ, summ_blocks,
+                     o, route, ws, ws_bytes, stream, nullptr, 0, 0);
+}
+
+dash_status dash_decode_paged(const dash_params* p, const void* q, const void* k_pages,
+                              const void* v_pages, int64_t num_pages, const int32_t* block_table,
+                              int64_t max_blocks, const int32_t* cache_len, int64_t max_len,
+                              const float* w_s, const float* q_bar, float* summ,
+                              int64_t summ_blocks, void* o, const dash_route_buf* route,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (!p || !block_table || num_pages < 1 || max_len < 1 || p->block_size < 1)
+    return DASH_ERR_INVALID_ARG;
+  if (max_blocks < (max_len + p->block_size - 1) / p->block_size) return DASH_ERR_INVALID_ARG;
+  return decode_impl(p, q, k_pages, v_pages, cache_len, max_len, w_s, q_bar, summ, summ_blocks,
+                     o, route, ws, ws_bytes, stream, block_table, max_blocks, num_pages);
 }
 
 }  // extern "C"

@@ -57,11 +57,16 @@ constexpr int kDecodeSplit = 32;   // list entries (blocks) per split (8 per wav
 constexpr int kDecodeMaxBg = 8192; // sequences x KV heads of one bf16 decode call
 constexpr int kMaxDevices = 64;    // per-device launch-shape caches
 
-// One decode step (route, attend, combine, summary update).
+// One decode step (route, attend, combine, summary update).  block_table
+// null: contiguous caches [B, Hkv, max_len, d]; otherwise paged caches
+// [num_pages, Hkv, bs, d] with block j of sequence b in page
+// block_table[b * max_blocks + j].
 hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const void* vc,
                          const int32_t* cache_len, int64_t max_len, const float* w_s,
                          const float* q_bar, float* summ, int64_t summ_blocks, void* o,
                          const dash_route_buf& rb,
-                         const DecodeLayout& L, char* ws, hipStream_t st);
+                         const DecodeLayout& L, char* ws, hipStream_t st,
+                         const int32_t* block_table = nullptr, int64_t max_blocks = 0,
+                         int64_t num_pages = 0);
 
 }  // namespace dash

@@ -55,6 +55,12 @@ struct DecodeArgs {
   float* summ_w;     // the summary cache, written for a block this step completes
   const float* w_s;
   const float* q_bar;  // [Hkv, D] summary queries, or null (mean pooling)
+  // paged caches: kc / vc are [num_pages, Hkv, bs, D] and block j of sequence
+  // b lives in page block_table[b * max_blocks + j]; null = contiguous caches
+  // [B, Hkv, max_len, D]
+  const int32_t* block_table;
+  int64_t max_blocks;
+  int64_t num_pages;
   int64_t nb;
   int64_t n_split;
   int nwords;
@@ -68,6 +74,21 @@ struct DecodeArgs {
 };
 
 __host__ __device__ inline int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
+
+// Element offset of the first key of block j of (sequence b, KV head g) in
+// the K or V cache.  Paged: the table entry, with j and the page id clamped
+// into range (a bad table gives wrong keys, never an access outside the
+// pages).
+__device__ __forceinline__ int64_t page_of(const DecodeArgs& a, int b, int64_t j) {
+  const int64_t jc = j < 0 ? 0 : (j >= a.max_blocks ? a.max_blocks - 1 : j);
+  const int64_t pg = a.block_table[(int64_t)b * a.max_blocks + jc];
+  return pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+}
+template <int D>
+__device__ __forceinline__ int64_t block_offset(const DecodeArgs& a, int b, int g, int64_t j) {
+  if (a.block_table) return (page_of(a, b, j) * a.Hkv + g) * a.bs * D;
+  return (((int64_t)b * a.Hkv + g) * a.max_len + j * a.bs) * D;
+}
 
 __device__ __forceinline__ int64_t clamp_len(int32_t v, int64_t max_len) {
   int64_t l = v;
@@ -395,7 +416,7 @@ __global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(DecodeArg
 // [s * kDecodeSplit, (s + 1) * kDecodeSplit) of [branch blocks (own block
 // first), selected blocks...].
 // All 256 threads call; ms / ls / os are the workgroup's merge buffers.
-template <int D>
+template <int D, bool PAGED>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
                                             float (&ms)[4][16], float (&ls)[4][16],
                                             float (&os)[4][8][D]) {
@@ -431,11 +452,25 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
   const int n_branch = decode_nbranch(a, len);
   const int n_entries = n_branch + count;
 
-  // K/V of this (sequence, KV head) through buffer resources sized to the
-  // current length: keys >= len read as zeros (and are masked below)
-  const uint32_t len_bytes = (uint32_t)(len * (D * 2));
-  const buf_rsrc rk = make_rsrc((const __bf16*)a.kc + bg * a.max_len * D, len_bytes);
-  const buf_rsrc rv = make_rsrc((const __bf16*)a.vc + bg * a.max_len * D, len_bytes);
+  // Contiguous caches: K/V of this (sequence, KV head) through buffer
+  // resources sized to the current length (keys >= len read as zeros and are
+  // masked below).  Paged caches: one more vector load fetches the page of
+  // each of this wave's entries; each block gets its own resource.
+  buf_rsrc rk, rv;
+  int32_t pages[kPerWave];
+  if constexpr (PAGED) {
+    int32_t pg = 0;
+    if (lane < kPerWave) {
+      const int e = s * kDecodeSplit + wv + 4 * lane;
+      pg = (int32_t)page_of(a, b, e < n_branch ? own - e : (int64_t)meta);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) pages[i] = __builtin_amdgcn_readlane(pg, i);
+  } else {
+    const uint32_t len_bytes = (uint32_t)(len * (D * 2));
+    rk = make_rsrc((const __bf16*)a.kc + bg * a.max_len * D, len_bytes);
+    rv = make_rsrc((const __bf16*)a.vc + bg * a.max_len * D, len_bytes);
+  }
 
   // Q^T operand: column = query head l16 (< G), k = d in [32 s' + 8 lg, +8);
   // columns l16 >= G fall outside the resource and read as zeros
@@ -458,12 +493,19 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
     const int e = s * kDecodeSplit + wv + 4 * ei;
     if (e >= e_end) break;
     const int64_t j = e < n_branch ? own - e : (int64_t)jraw[ei];
+    if constexpr (PAGED) {
+      // the block's page, limited to the keys below len
+      const int64_t off = ((int64_t)pages[ei] * a.Hkv + g) * a.bs * D;
+      const uint32_t nbytes = (uint32_t)(min64(a.bs, len - (j << a.bs_log)) * (D * 2));
+      rk = make_rsrc((const __bf16*)a.kc + off, nbytes);
+      rv = make_rsrc((const __bf16*)a.vc + off, nbytes);
+    }
     for (int c64 = 0; c64 < (a.bs >> 6); ++c64) {
       const int64_t key0 = (j << a.bs_log) + 64 * c64;
       if (key0 >= len) break;
       // Issue every load of the chunk before any use (32-bit byte offsets
-      // from the chunk's first key).
-      const uint32_t c0 = (uint32_t)(key0 * (D * 2));
+      // from the chunk's first key, within the block when paged).
+      const uint32_t c0 = PAGED ? (uint32_t)(64 * c64 * (D * 2)) : (uint32_t)(key0 * (D * 2));
       u32x4 kw[4][D / 32];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -597,7 +639,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
 // (sequence, KV head) -- and takes items blockIdx.x, + gridDim.x, ...  No
 // workgroup is launched for a split past its list, so none holds a slot
 // waiting only to find it has nothing to do.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
   __shared__ float ms[4][16], ls[4][16];
   __shared__ float os[4][8][D];
@@ -641,7 +683,7 @@ __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
       const int mid = (lo + hi) >> 1;
       if (pre[mid] <= it) lo = mid; else hi = mid;
     }
-    decode_item<D>(a, lo, it - pre[lo], ms, ls, os);
+    decode_item<D, PAGED>(a, lo, it - pre[lo], ms, ls, os);
   }
 }
 
@@ -659,8 +701,6 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
   const int n_branch = decode_nbranch(a, len);
   const int n_entries = n_branch + count;
   if (s * kDecodeSplit >= n_entries) return;
-  const float* kb = (const float*)a.kc + bg * a.max_len * D;
-  const float* vb = (const float*)a.vc + bg * a.max_len * D;
   const float* qb = (const float*)a.q + ((int64_t)b * a.H + g * a.G) * D;
   for (int e = threadIdx.x; e < a.G * D; e += 256) qs[e / D][e % D] = qb[e];
   const int qr = threadIdx.x / 32, dl = threadIdx.x % 32;   // 8 heads x 32 lanes
@@ -670,6 +710,10 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
   for (int e = s * kDecodeSplit; e < e_end; ++e) {
     const int64_t j = e < n_branch ? own - e : (int64_t)a.idx[bg * a.nb + e - n_branch];
     const float bias2 = e < n_branch ? 0.f : a.logp[bg * a.nb + j] * kLog2e;
+    // keys and values of block j, indexed by key - j * bs
+    const int64_t boff = block_offset<D>(a, b, g, j), kfirst = j * a.bs;
+    const float* kb = (const float*)a.kc + boff;
+    const float* vb = (const float*)a.vc + boff;
     for (int64_t key0 = j * a.bs; key0 < (j + 1) * a.bs && key0 < len; key0 += 64) {
       __syncthreads();
       for (int p = threadIdx.x; p < a.G * 64; p += 256) {
@@ -678,7 +722,7 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
         float sv = -INFINITY;
         if (key < len) {
           float acc = 0.f;
-          for (int c = 0; c < D; ++c) acc = fmaf(qs[h][c], kb[key * D + c], acc);
+          for (int c = 0; c < D; ++c) acc = fmaf(qs[h][c], kb[(key - kfirst) * D + c], acc);
           sv = fmaf(acc, a.scale_log2, bias2);
         }
         sc[h][kk] = sv;
@@ -691,7 +735,8 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
           const float m_new = fmaxf(m_run, sv);
           const float corr = fast_exp2(m_run - m_new), p = fast_exp2(sv - m_new);
           l_run = l_run * corr + p;
-          for (int c = 0; c < D / 32; ++c) ov[c] = fmaf(p, vb[(key0 + kk) * D + dl + 32 * c], ov[c] * corr);
+          for (int c = 0; c < D / 32; ++c)
+            ov[c] = fmaf(p, vb[(key0 + kk - kfirst) * D + dl + 32 * c], ov[c] * corr);
           m_run = m_new;
         }
       }
@@ -725,7 +770,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     const int64_t len = clamp_len(a.cache_len[b], a.max_len);
     if ((len & (a.bs - 1)) == 0) {
       const int64_t j = (len >> a.bs_log) - 1;
-      summarize_blocks<T, D, 1>((const T*)a.kc + (bg * a.max_len + j * a.bs) * D, 1, a.bs, a.w_s,
+      summarize_blocks<T, D, 1>((const T*)a.kc + block_offset<D>(a, b, g, j), 1, a.bs, a.w_s,
                                 a.q_bar ? a.q_bar + g * D : nullptr,
                                 a.summ_w + (bg * a.summ_blocks + j) * D);
     }
@@ -784,7 +829,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
 // Workgroups of decode_attend_bf16_kernel<D> resident on the current device at
 // once with `lds` bytes of dynamic LDS (cached per device and 4 KB step of lds).
 constexpr int kLdsSteps = (kDecodeMaxBg + 1) * 4 / 4096 + 1;
-template <int D>
+template <int D, bool PAGED>
 static int persistent_grid(size_t lds) {
   static std::atomic<int> cache[kMaxDevices][kLdsSteps];
   int dev = 0;
@@ -795,7 +840,7 @@ static int persistent_grid(size_t lds) {
   if (g == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, (const void*)decode_attend_bf16_kernel<D>, 256, lds) != hipSuccess)
+            &per_cu, (const void*)decode_attend_bf16_kernel<D, PAGED>, 256, lds) != hipSuccess)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
@@ -828,9 +873,13 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
                          const int32_t* cache_len, int64_t max_len, const float* w_s,
                          const float* q_bar, float* summ, int64_t summ_blocks, void* o,
                          const dash_route_buf& rb, const DecodeLayout& L, char* ws,
-                         hipStream_t st) {
+                         hipStream_t st, const int32_t* block_table, int64_t max_blocks,
+                         int64_t num_pages) {
   DecodeArgs a;
   a.xpitch = 0;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
   a.q = q;
   a.kc = kc;
   a.vc = vc;
@@ -928,14 +977,13 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   if (bf16) {
     const int64_t items_max = (int64_t)nbg * L.n_split;
     const size_t lds_pre = sizeof(int) * ((size_t)nbg + 1);   // the item prefix
-    if (s.d == 64)
-      hipLaunchKernelGGL(decode_attend_bf16_kernel<64>,
-                         dim3((unsigned)min64(items_max, persistent_grid<64>(lds_pre))), dim3(256),
-                         lds_pre, st, a);
-    else
-      hipLaunchKernelGGL(decode_attend_bf16_kernel<128>,
-                         dim3((unsigned)min64(items_max, persistent_grid<128>(lds_pre))), dim3(256),
-                         lds_pre, st, a);
+#define DASH_DA(D, PG)                                                                     \
+  hipLaunchKernelGGL((decode_attend_bf16_kernel<D, PG>),                                   \
+                     dim3((unsigned)min64(items_max, persistent_grid<D, PG>(lds_pre))),    \
+                     dim3(256), lds_pre, st, a)
+    if (s.d == 64) { if (a.block_table) DASH_DA(64, true); else DASH_DA(64, false); }
+    else { if (a.block_table) DASH_DA(128, true); else DASH_DA(128, false); }
+#undef DASH_DA
   } else {
     if (s.d == 64) hipLaunchKernelGGL(decode_attend_f32_kernel<64>, g3, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(decode_attend_f32_kernel<128>, g3, dim3(256), 0, st, a);

@@ -148,6 +148,25 @@ def test_mask_to_list_argument_checks():
     assert dash.dash_route_sizes_decode(P(batch=32), 32768)["tile_bits"] == 32 * 8 * 16
 
 
+def test_decode_paged_argument_checks():
+    p = P()
+    lib = L._lib
+    need = dash.dash_decode_workspace_bytes(p, 4096)
+    # no block table / no pages / table narrower than ceil(max_len / bs)
+    assert lib.dash_decode_paged(ctypes.byref(p), FAKE, FAKE, FAKE, 64, None, 64, FAKE, 4096, FAKE,
+                                 None, FAKE, 64, FAKE, None, FAKE, need,
+                                 None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_decode_paged(ctypes.byref(p), FAKE, FAKE, FAKE, 0, FAKE, 64, FAKE, 4096, FAKE,
+                                 None, FAKE, 64, FAKE, None, FAKE, need,
+                                 None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_decode_paged(ctypes.byref(p), FAKE, FAKE, FAKE, 64, FAKE, 63, FAKE, 4096, FAKE,
+                                 None, FAKE, 64, FAKE, None, FAKE, need,
+                                 None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_decode_paged(ctypes.byref(p), FAKE, FAKE, FAKE, 64, FAKE, 64, FAKE, 4096, FAKE,
+                                 None, FAKE, 64, FAKE, None, FAKE, need - 1,
+                                 None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_binding_rejects_host_tensors():
     p = P(n_heads=2, n_kv_heads=2, head_dim=64)
     t = torch.zeros(2 * 64 * 64)
