@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--window", type=int, default=None,
                     help="near-diagonal branch in blocks (default: the workload's, 1)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the ragged-batch prefill leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--dense", action="store_true",
                     help="also time the in-house dense causal attention (all blocks, zero prior)")
@@ -190,6 +192,49 @@ def prefill_bench(args, torch, dash, W):
     return res
 
 
+VARLEN_LENS = (8192, 6144, 3000, 1000)   # a ragged batch of prefill_8k-shaped sequences
+
+
+def varlen_bench(args, torch, dash, W):
+    """dash_prefill_varlen on a ragged batch (sequences of prefill_8k's shape,
+    lengths VARLEN_LENS, padded to 8192) against the same sequences run one
+    dash_prefill call after another."""
+    w = with_overrides(W.get(args.workload), args).replace(batch=len(VARLEN_LENS))
+    dev = torch.device("cuda:0")
+    inp = W.make_prefill(w)
+    B, H, Hkv, N, d, bs = w.batch, w.n_heads, w.n_kv_heads, w.seq_len, w.head_dim, w.block_size
+    p = dash.make_params(B, H, Hkv, d, bs, w.alpha, w.gamma, w.dtype, w.sigma, w.window)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(inp[x]).to(dev, tdt) for x in ("q", "k", "v"))
+    ws_mat = torch.from_numpy(inp["w_s"]).to(dev)
+    del inp
+    nb = N // bs
+    summ = torch.zeros(B * Hkv * nb * d, dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    ws = dash.workspace(dash.dash_prefill_workspace_bytes(p, N), dev)
+    lens = torch.tensor(VARLEN_LENS, dtype=torch.int32, device=dev)
+    ms = events_time(lambda: dash.dash_prefill_varlen(p, q, k, v, N, lens, ws_mat, summ, nb, o,
+                                                      ws), args.steps, args.warmup, torch)
+    # one call per sequence, back to back on the same stream
+    p1 = dash.make_params(1, H, Hkv, d, bs, w.alpha, w.gamma, w.dtype, w.sigma, w.window)
+    parts = []
+    for b, n in enumerate(VARLEN_LENS):
+        qs, ks, vs = (t[b:b + 1, :, :n].contiguous() for t in (q, k, v))
+        parts.append((n, qs, ks, vs, torch.empty_like(qs),
+                      torch.zeros(Hkv * max(n // bs, 1) * d, dtype=torch.float32, device=dev),
+                      dash.workspace(dash.dash_prefill_workspace_bytes(p1, n), dev)))
+
+    def one_by_one():
+        for n, qs, ks, vs, os_, ss, wss in parts:
+            dash.dash_prefill(p1, qs, ks, vs, n, ws_mat, ss, max(n // bs, 1), os_, wss)
+    ms_seq = events_time(one_by_one, args.steps, args.warmup, torch)
+    tokens = sum(VARLEN_LENS)
+    return {"workload": f"ragged batch of {w.name} sequences, lengths {list(VARLEN_LENS)} "
+                        f"padded to {N}",
+            "ms_per_step": round(ms, 4), "tok_s": round(tokens / (ms * 1e-3), 1),
+            "one_call_per_sequence_ms": round(ms_seq, 4)}
+
+
 def decode_bench(args, torch, dash, W):
     w = with_overrides(W.get(args.decode_workload), args, alpha=False)
     dev = torch.device("cuda:0")
@@ -298,6 +343,7 @@ def main():
 
     pre = prefill_bench(args, torch, dash, W)
     dec = None if args.no_decode else decode_bench(args, torch, dash, W)
+    var = None if args.no_varlen else varlen_bench(args, torch, dash, W)
     cpu = None if args.no_cpu else cpu_baseline(args, W)
     w = pre["workload"]
     line = {
@@ -341,6 +387,8 @@ def main():
                           "roofline": dec["roofline"],
                           "all_bytes_gbs": dec["all_bytes_gbs"],
                           "paged_kv": dec["paged"]}
+    if var is not None:
+        line["varlen_prefill"] = var
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 

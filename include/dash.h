@@ -216,6 +216,22 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
                          int64_t n, const float* w_s, const float* q_bar, float* summ,
                          int64_t summ_blocks, void* o, void* ws, size_t ws_bytes, void* stream);
 
+/* dash_prefill for a batch of sequences of different lengths (a ragged
+ * batch): sequence b has seq_lens[b] positions, stored in the first rows of
+ * its n_max-row slices,
+ *   q, o   [B, H, n_max, d] dtype;  k, v [B, Hkv, n_max, d] dtype
+ *   seq_lens [B] int32 DEVICE array, values clamped into [0, n_max]
+ * Every sequence is computed exactly as dash_prefill would compute it alone
+ * (its complete blocks summarised into summ, routing and attention over its
+ * own positions); rows at or past seq_lens[b] of o and summaries of blocks
+ * past its last complete block are not written.  Query tiles past a
+ * sequence's end exit at once, so the work follows the real lengths.
+ * Workspace and limits as dash_prefill with n = n_max. */
+dash_status dash_prefill_varlen(const dash_params* p, const void* q, const void* k, const void* v,
+                                int64_t n_max, const int32_t* seq_lens, const float* w_s,
+                                const float* q_bar, float* summ, int64_t summ_blocks, void* o,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* One incremental decoding step for every sequence b: the query q[b] sits at
  * position L = cache_len[b] - 1 and its key/value are already in the caches.
  * Routes over the cached summaries of blocks j < floor(L / bs), attends to the

@@ -80,6 +80,9 @@ _lib.dash_mask_to_list.restype = ctypes.c_int
 _lib.dash_mask_to_list.argtypes = [_P, _I, _R, _V]
 _lib.dash_prefill.restype = ctypes.c_int
 _lib.dash_prefill.argtypes = [_P, _V, _V, _V, _I, _V, _V, _V, _I, _V, _V, ctypes.c_size_t, _V]
+_lib.dash_prefill_varlen.restype = ctypes.c_int
+_lib.dash_prefill_varlen.argtypes = [_P, _V, _V, _V, _I, _V, _V, _V, _V, _I, _V, _V,
+                                     ctypes.c_size_t, _V]
 _lib.dash_decode_paged.restype = ctypes.c_int
 _lib.dash_decode_paged.argtypes = [_P, _V, _V, _V, _I, _V, _I, _V, _I, _V, _V, _V, _I, _V, _R, _V,
                                    ctypes.c_size_t, _V]
@@ -90,7 +93,8 @@ _lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _V, _I, _V, _R, _V,
 EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
             "dash_route_sizes_decode", "dash_prefill_workspace_bytes",
             "dash_decode_workspace_bytes", "dash_summarize", "dash_route", "dash_attend",
-            "dash_mask_to_list", "dash_prefill", "dash_decode", "dash_decode_paged")
+            "dash_mask_to_list", "dash_prefill", "dash_prefill_varlen", "dash_decode",
+            "dash_decode_paged")
 
 
 # ---------------------------------------------------------------------------------------
@@ -278,6 +282,22 @@ def dash_prefill(p, q, k, v, n, w_s, summ, summ_blocks, o, ws, stream=None, q_ba
         _opt_dev(q_bar, "q_bar", Hkv * d, torch.float32),
         _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
         _dev(o, "o", B * H * n * d, dt), _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def dash_prefill_varlen(p, q, k, v, n_max, seq_lens, w_s, summ, summ_blocks, o, ws, stream=None,
+                        q_bar=None):
+    """dash_prefill over a ragged batch: sequence b has seq_lens[b] (int32, on
+    the GPU) of the n_max positions of its slices."""
+    B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
+    dt = torch_dtype(p)
+    _check("dash_prefill_varlen", _lib.dash_prefill_varlen(
+        ctypes.byref(p), _dev(q, "q", B * H * n_max * d, dt),
+        _dev(k, "k", B * Hkv * n_max * d, dt), _dev(v, "v", B * Hkv * n_max * d, dt), n_max,
+        _dev(seq_lens, "seq_lens", B, torch.int32), _dev(w_s, "w_s", d * d, torch.float32),
+        _opt_dev(q_bar, "q_bar", Hkv * d, torch.float32),
+        _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
+        _dev(o, "o", B * H * n_max * d, dt), _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
         _stream(stream)))
 
 

@@ -222,9 +222,12 @@ dash_status dash_mask_to_list(const dash_params* p, int64_t n, const dash_route_
   return hip_status(dash::launch_mask_to_list(s, n, *route, (hipStream_t)stream));
 }
 
-dash_status dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
-                         int64_t n, const float* w_s, const float* q_bar, float* summ,
-                         int64_t summ_blocks, void* o, void* ws, size_t ws_bytes, void* stream) {
+// Shared checks and launches of dash_prefill / dash_prefill_varlen (seq_len
+// null: every sequence has n positions).
+static dash_status prefill_impl(const dash_params* p, const void* q, const void* k, const void* v,
+                                int64_t n, const int32_t* seq_len, const float* w_s,
+                                const float* q_bar, float* summ, int64_t summ_blocks, void* o,
+                                void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   dash_status st = check_params(p, &s);
   if (st != DASH_OK) return st;
@@ -246,10 +249,27 @@ dash_status dash_prefill(const dash_params* p, const void* q, const void* k, con
   rb.support_bits = nullptr;
   rb.tile_bits = nullptr;
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = dash::launch_summarize(s, k, n, 0, n / s.bs, w_s, q_bar, summ, summ_blocks, hs);
-  if (e == hipSuccess) e = dash::launch_route_prefill(s, q, n, summ, summ_blocks, rb, hs);
-  if (e == hipSuccess) e = dash::launch_attend_prefill(s, q, k, v, n, rb, o, hs);
+  hipError_t e =
+      dash::launch_summarize(s, k, n, 0, n / s.bs, w_s, q_bar, summ, summ_blocks, hs, seq_len);
+  if (e == hipSuccess) e = dash::launch_route_prefill(s, q, n, summ, summ_blocks, rb, hs, seq_len);
+  if (e == hipSuccess) e = dash::launch_attend_prefill(s, q, k, v, n, rb, o, hs, seq_len);
   return hip_status(e);
+}
+
+dash_status dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
+                         int64_t n, const float* w_s, const float* q_bar, float* summ,
+                         int64_t summ_blocks, void* o, void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl(p, q, k, v, n, nullptr, w_s, q_bar, summ, summ_blocks, o, ws, ws_bytes,
+                      stream);
+}
+
+dash_status dash_prefill_varlen(const dash_params* p, const void* q, const void* k, const void* v,
+                                int64_t n_max, const int32_t* seq_lens, const float* w_s,
+                                const float* q_bar, float* summ, int64_t summ_blocks, void* o,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (!seq_lens) return DASH_ERR_INVALID_ARG;
+  return prefill_impl(p, q, k, v, n_max, seq_lens, w_s, q_bar, summ, summ_blocks, o, ws,
+                      ws_bytes, stream);
 }
 
 // Shared checks and launch of dash_decode / dash_decode_paged (block_table

@@ -27,6 +27,7 @@
 namespace dash {
 
 constexpr int kQTa = DASH_QUERY_TILE;
+constexpr int kXcds = 8;   // accelerator complex dies of the part, one L2 each
 constexpr int kChunk = 64;
 
 struct AttendArgs {
@@ -43,7 +44,15 @@ struct AttendArgs {
   float scale_log2;   // log2(e) / sqrt(d)
   int wg_per_tile;
   int window;         // near-diagonal branch: own block + window - 1 blocks before it
+  const int32_t* seq_len;   // [B] valid positions per sequence, or null (all n)
 };
+
+// Valid positions of sequence b: seq_len[b] clamped into [0, n], or n.
+__device__ __forceinline__ int64_t attend_valid_len(const AttendArgs& a, int b) {
+  if (!a.seq_len) return a.n;
+  const int64_t l = a.seq_len[b];
+  return l < 0 ? 0 : (l > a.n ? a.n : l);
+}
 
 // first block of the tile's near-diagonal branch (own block - (window - 1), >= 0)
 __device__ __forceinline__ int64_t branch_block0(int64_t p_begin, int bs, int window) {
@@ -179,13 +188,33 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   const int l32 = lane % 32, lh = lane / 32;
 
   const int64_t nbg = (int64_t)a.B * a.Hkv;
-  const int64_t tile_rank = blockIdx.x / a.wg_per_tile;
-  const int wi = blockIdx.x % a.wg_per_tile;
-  const int64_t qt = a.n_qt - 1 - tile_rank / nbg;   // heaviest tiles first
-  const int64_t bg = tile_rank % nbg;
+  int64_t qt, bg;
+  int wi;
+  if (nbg > kXcds && nbg % kXcds == 0) {
+    // Workgroups go to the XCDs round-robin (workgroup w to XCD w % 8), each
+    // XCD with its own L2: give every (sequence, KV head) to one XCD and let
+    // that XCD walk its pairs one after another, each pair's tiles heaviest
+    // first, so one L2 holds one pair's K/V at a time.
+    const int64_t x = blockIdx.x % kXcds, r = blockIdx.x / kXcds;
+    const int64_t per_pair = a.n_qt * a.wg_per_tile;
+    const int64_t rem = r % per_pair;
+    bg = x + kXcds * (r / per_pair);
+    qt = a.n_qt - 1 - rem / a.wg_per_tile;
+    wi = (int)(rem % a.wg_per_tile);
+  } else {
+    // at most one pair per XCD (or a count that does not divide evenly): all
+    // tiles heaviest first, the pairs of one tile rank side by side
+    const int64_t tile_rank = blockIdx.x / a.wg_per_tile;
+    wi = blockIdx.x % a.wg_per_tile;
+    qt = a.n_qt - 1 - tile_rank / nbg;
+    bg = tile_rank % nbg;
+  }
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t p_begin = qt * kQTa;
   const int64_t tile = bg * a.n_qt + qt;
+  // positions of this sequence (rows are a.n apart); a tile past its end has nothing to do
+  const int64_t nv = attend_valid_len(a, b);
+  if (p_begin >= nv) return;
 
   const int gw = wi * (NT / kWave) + wave;   // wave index within the tile
   const int h = g * a.G + gw / 2;            // query head
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   const int64_t qpos = p_begin + qloc;
 
   const __bf16* qp = (const __bf16*)a.q + (((int64_t)b * a.H + h) * a.n) * D;
-  const uint32_t seq_bytes = (uint32_t)(a.n * (D * 2));
+  const uint32_t seq_bytes = (uint32_t)(nv * (D * 2));
   const buf_rsrc rk = make_rsrc((const __bf16*)a.k + (bg * a.n) * D, seq_bytes);
   const buf_rsrc rv = make_rsrc((const __bf16*)a.v + (bg * a.n) * D, seq_bytes);
   const buf_rsrc rb = make_rsrc(a.sel_logp + tile * a.nb * kQTa, (uint32_t)(a.nb * kQTa * 4));
@@ -204,7 +233,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (qpos < a.n) w = *(const u32x4*)(qp + qpos * D + 16 * s + 8 * lh);
+    if (qpos < nv) w = *(const u32x4*)(qp + qpos * D + 16 * s + 8 * lh);
     qf[s] = as_bf16x8(w);
   }
 
@@ -367,7 +396,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   }
 
   // ---- normalise and store: acc[dt][i] = O[query l32][32 dt + 8 (i/4) + 4 lh + i%4] ----
-  if (qpos < a.n) {
+  if (qpos < nv) {
     const float inv = 1.0f / l_run;
     __bf16* op = (__bf16*)a.o + (((int64_t)b * a.H + h) * a.n + qpos) * D;
 #pragma unroll
@@ -397,6 +426,8 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
   const int h = g * a.G + hh;
   const int64_t p_begin = qt * kQTa;
   const int64_t tile = bg * a.n_qt + qt;
+  const int64_t nv = attend_valid_len(a, b);
+  if (p_begin >= nv) return;
   const int qloc = threadIdx.x;
   const int64_t qpos = p_begin + qloc;
   const float* kp = (const float*)a.k + (bg * a.n) * D;
@@ -406,7 +437,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
   const float* qrow = (const float*)a.q + (((int64_t)b * a.H + h) * a.n + qpos) * D;
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    qv[c] = qpos < a.n ? qrow[c] : 0.f;
+    qv[c] = qpos < nv ? qrow[c] : 0.f;
     ov[c] = 0.f;
   }
   const int cpb = a.bs / kChunk;
@@ -423,8 +454,8 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
     __syncthreads();
     for (int e = threadIdx.x; e < kChunk * D; e += 64) {
       const int64_t kpos = cr.key0 + e / D;
-      Ks[e] = kpos < a.n ? kp[cr.key0 * D + e] : 0.f;
-      Vs[e] = kpos < a.n ? vp[cr.key0 * D + e] : 0.f;
+      Ks[e] = kpos < nv ? kp[cr.key0 * D + e] : 0.f;
+      Vs[e] = kpos < nv ? vp[cr.key0 * D + e] : 0.f;
     }
     __syncthreads();
     const float bias2 =
@@ -444,7 +475,7 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
       m_run = m_new;
     }
   }
-  if (qpos < a.n) {
+  if (qpos < nv) {
     float* orow = (float*)a.o + (((int64_t)b * a.H + h) * a.n + qpos) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) orow[c] = ov[c] / l_run;
@@ -452,9 +483,11 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
 }
 
 hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
-                                 int64_t n, const dash_route_buf& rb, void* o, hipStream_t st) {
+                                 int64_t n, const dash_route_buf& rb, void* o, hipStream_t st,
+                                 const int32_t* seq_len) {
   if (n <= 0) return hipSuccess;
   AttendArgs a;
+  a.seq_len = seq_len;
   a.q = q;
   a.k = k;
   a.v = v;

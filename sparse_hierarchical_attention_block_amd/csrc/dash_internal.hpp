@@ -20,13 +20,17 @@ struct Shape {
 
 // Stage 0: summaries of blocks [blk_begin, blk_end) for every (b, kv head);
 // q_bar is nullptr (mean pooling) or [Hkv, d] summary queries.
+// seq_len: null, or [B] valid positions per sequence (only its complete
+// blocks are summarised); the same for the two prefill launches below.
 hipError_t launch_summarize(const Shape& s, const void* k, int64_t kv_len, int64_t blk_begin,
                             int64_t blk_end, const float* w_s, const float* q_bar, float* summ,
-                            int64_t summ_blocks, hipStream_t st);
+                            int64_t summ_blocks, hipStream_t st,
+                            const int32_t* seq_len = nullptr);
 
 // Stage 1, causal prefill of positions 0..n-1.
 hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const float* summ,
-                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st);
+                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st,
+                                const int32_t* seq_len = nullptr);
 
 // Bit-packed tile masks -> ascending lists (prefill layout).
 hipError_t launch_mask_to_list(const Shape& s, int64_t n, const dash_route_buf& rb,
@@ -34,7 +38,8 @@ hipError_t launch_mask_to_list(const Shape& s, int64_t n, const dash_route_buf& 
 
 // Stage 2, causal prefill.
 hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
-                                 int64_t n, const dash_route_buf& rb, void* o, hipStream_t st);
+                                 int64_t n, const dash_route_buf& rb, void* o, hipStream_t st,
+                                 const int32_t* seq_len = nullptr);
 
 // Decode workspace layout (byte offsets from the workspace base).
 struct DecodeLayout {

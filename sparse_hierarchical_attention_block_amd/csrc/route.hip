@@ -34,7 +34,9 @@ constexpr int kRouteMaxRowTiles = 4;   // rows per pass <= 64
 
 struct RouteArgs {
   const void* q;
-  int64_t n;
+  int64_t n;            // positions per sequence in memory (the row stride)
+  const int32_t* seq_len;  // [B] valid positions per sequence, or null (all n)
+  int64_t nv;           // valid positions of the workgroup's sequence
   const float* summ;
   int64_t summ_blocks;
   float* tau;
@@ -55,6 +57,20 @@ struct RouteArgs {
 };
 
 __host__ __device__ inline int round_up16(int x) { return (x + 15) & ~15; }
+
+// Valid positions of sequence b: seq_len[b] clamped into [0, n], or n.
+__device__ __forceinline__ int64_t valid_len(const int32_t* seq_len, int b, int64_t n) {
+  if (!seq_len) return n;
+  const int64_t l = seq_len[b];
+  return l < 0 ? 0 : (l > n ? n : l);
+}
+
+// A tile at or past its sequence's end: an empty list (its rows are not written).
+__device__ __forceinline__ void route_tile_past_end(const RouteArgs& a, int64_t tile) {
+  if (threadIdx.x == 0) a.sel_count[tile] = 0;
+  if (a.tile_bits)
+    for (int w = threadIdx.x; w < a.nwords; w += blockDim.x) a.tile_bits[tile * a.nwords + w] = 0u;
+}
 
 // Compaction of the tile's union flags (blocks j < t) into the ascending list
 // sel_idx / sel_count, and the same set as the tile's bit-packed mask when
@@ -102,7 +118,7 @@ __device__ void route_scores_bf16(const RouteArgs& a, float* X, int t, int64_t b
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 qv = {0u, 0u, 0u, 0u};
-      if (rt < RT && pos < a.n) qv = *(const u32x4*)(qrow + 32 * s + 8 * lg);
+      if (rt < RT && pos < a.nv) qv = *(const u32x4*)(qrow + 32 * s + 8 * lg);
       qf[rt][s] = as_bf16x8(qv);
     }
   }
@@ -162,7 +178,7 @@ __device__ void route_scores_f32(const RouteArgs& a, float* X, int t, int64_t bg
     const int m = row / a.G, h = row % a.G;
     const int64_t pos = pos0 + m;
     float acc = 0.f;
-    if (pos < a.n) {
+    if (pos < a.nv) {
       const float* qrow = q + (((int64_t)b * a.H + g * a.G + h) * a.n + pos) * D;
       const float* srow = a.summ + (bg * a.summ_blocks + j) * D;
       for (int c = 0; c < D; ++c) acc = fmaf(qrow[c], srow[c], acc);
@@ -184,9 +200,14 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
   const int64_t bg = blockIdx.x % nbg;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t p_begin = qt * kQT;
-  const int npos = (int)min((int64_t)kQT, a.n - p_begin);
-  const int t = max(0, (int)(p_begin / a.bs) - (a.window - 1));   // candidates
   const int64_t tile = bg * a.n_qt + qt;
+  a.nv = valid_len(a.seq_len, b, a.n);
+  if (p_begin >= a.nv) {
+    route_tile_past_end(a, tile);
+    return;
+  }
+  const int npos = (int)min((int64_t)kQT, a.nv - p_begin);
+  const int t = max(0, (int)(p_begin / a.bs) - (a.window - 1));   // candidates
 
   if (t == 0) {
     for (int idx = threadIdx.x; idx < npos * a.G; idx += NT) {
@@ -235,7 +256,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
       else tau = entmax_tau_reg<VPL, MODE>(xv, GroupReduce{lpr}, a.e, nact4);
       const int m = row / a.G, h = row % a.G;
       const int64_t pos = pos0 + m;
-      if (pos < a.n) {
+      if (pos < a.nv) {
         const int64_t r = ((int64_t)b * a.H + g * a.G + h) * a.n + pos;
         if (sub == 0) a.tau[r] = tau;
         if (a.bits)
@@ -295,7 +316,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
         const int m = row / a.G, h = row % a.G;
         const int64_t pos = pos0 + m;
         if (sub == 0) tau_s[row] = tau;
-        if (pos < a.n) {
+        if (pos < a.nv) {
           const int64_t r = ((int64_t)b * a.H + g * a.G + h) * a.n + pos;
           if (sub == 0) a.tau[r] = tau;
           if (a.bits)
@@ -365,9 +386,14 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
   const int t = max(0, (int)(p_begin / a.bs) - (a.window - 1));   // candidates
   const int64_t tile = bg * a.n_qt + qt;
   const int G = a.G;
+  a.nv = valid_len(a.seq_len, b, a.n);
+  if (p_begin >= a.nv) {
+    route_tile_past_end(a, tile);
+    return;
+  }
 
   if (t == 0) {
-    const int npos = (int)min((int64_t)kQT, a.n - p_begin);
+    const int npos = (int)min((int64_t)kQT, a.nv - p_begin);
     for (int idx = threadIdx.x; idx < npos * G; idx += nthreads) {
       const int m = idx / G, h = idx % G;
       const int64_t r = ((int64_t)b * a.H + g * G + h) * a.n + p_begin + m;
@@ -441,7 +467,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 qv = {0u, 0u, 0u, 0u};
-      if (rpos[rt] < a.n) qv = *(const u32x4*)(qrow + 32 * s + 8 * lg);
+      if (rpos[rt] < a.nv) qv = *(const u32x4*)(qrow + 32 * s + 8 * lg);
       qf[rt][s] = as_bf16x8(qv);
     }
   }
@@ -498,7 +524,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
             chunk[ct] |= (uint32_t)((mk >> (16 * l2 + l16)) & 1ull) << (4 * l2 + i);
         }
       }
-      if (lg == 0 && pos < a.n)
+      if (lg == 0 && pos < a.nv)
         for (int w = 0; w < a.nwords; ++w) {
           uint32_t word = 0u;
 #pragma unroll
@@ -507,7 +533,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
           a.bits[rglob * a.nwords + w] = word;
         }
     }
-    if (lg == 0 && pos < a.n) a.tau[rglob] = tau;
+    if (lg == 0 && pos < a.nv) a.tau[rglob] = tau;
     // p of this row's slots (slot s = 4 ct + i <-> candidate 16 ct + 4 lg + i)
 #pragma unroll
     for (int ct = 0; ct < kTileMaxCT; ++ct) {
@@ -536,7 +562,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
         }
       }
     }
-    if (pos < a.n) {
+    if (pos < a.nv) {
       const int mloc = (int)(pos - p_begin);
       float* lp = a.sel_logp + tile * a.nb * kQT + mloc;
 #pragma unroll
@@ -600,11 +626,14 @@ hipError_t launch_mask_to_list(const Shape& s, int64_t n, const dash_route_buf& 
 }
 
 hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const float* summ,
-                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st) {
+                                int64_t summ_blocks, const dash_route_buf& rb, hipStream_t st,
+                                const int32_t* seq_len) {
   if (n <= 0) return hipSuccess;
   RouteArgs a;
   a.q = q;
   a.n = n;
+  a.seq_len = seq_len;
+  a.nv = n;
   a.summ = summ;
   a.summ_blocks = summ_blocks;
   a.tau = rb.tau;

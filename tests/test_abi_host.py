@@ -167,6 +167,19 @@ def test_decode_paged_argument_checks():
                                  None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_prefill_varlen_argument_checks():
+    p = P()
+    lib = L._lib
+    need = dash.dash_prefill_workspace_bytes(p, 1024)
+    assert lib.dash_prefill_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, None, FAKE, None,
+                                   FAKE, 16, FAKE, FAKE, need, None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_prefill_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, None,
+                                   FAKE, 15, FAKE, FAKE, need, None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_prefill_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE, None,
+                                   FAKE, 16, FAKE, FAKE, need - 1,
+                                   None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_binding_rejects_host_tensors():
     p = P(n_heads=2, n_kv_heads=2, head_dim=64)
     t = torch.zeros(2 * 64 * 64)
