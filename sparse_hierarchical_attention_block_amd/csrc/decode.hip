@@ -634,56 +634,83 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
 }
 
 // Persistent grid (as many workgroups as fit on the GPU at once): every
-// workgroup derives the work items from the list lengths -- item ranges
-// pre[bg] .. pre[bg+1] with ceil((n_branch + count[bg]) / kDecodeSplit) items per
-// (sequence, KV head) -- and takes items blockIdx.x, + gridDim.x, ...  No
-// workgroup is launched for a split past its list, so none holds a slot
-// waiting only to find it has nothing to do.
+// workgroup derives the work items from the list lengths -- each list of
+// n_branch + count[bg] entries splits into full items of kDecodeSplit
+// entries and at most one shorter last item -- and takes items blockIdx.x,
+// + gridDim.x, ...  No workgroup is launched for a split past its list, so
+// none holds a slot waiting only to find it has nothing to do.
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_attend_bf16_kernel(DecodeArgs a) {
   __shared__ float ms[4][16], ls[4][16];
   __shared__ float os[4][8][D];
-  extern __shared__ int pre[];   // [B Hkv + 1], sized at launch
-  __shared__ int wsum[4];
+  // Items: first every full split (kDecodeSplit entries) of every list, then
+  // the partial last splits, so the workgroups that take a second item in
+  // the tail mostly get short ones.  Exclusive prefixes over the pairs of the
+  // full-split counts (preF) and of the partial-split flags (preP).
+  extern __shared__ int pre[];   // [2][B Hkv + 1], sized at launch
+  __shared__ int wsum[2][4];
   const int nbg = a.B * a.Hkv;
+  int* preF = pre;
+  int* preP = pre + nbg + 1;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  // exclusive prefix of the item counts: 256 contiguous ranges, then a scan
-  // of the range totals
+  // 256 contiguous ranges of pairs, then a scan of the range totals
   const int per = (nbg + 255) / 256;
   const int i0 = min(nbg, (int)threadIdx.x * per), i1 = min(nbg, i0 + per);
-  int tot = 0;
+  int totF = 0, totP = 0;
   for (int i = i0; i < i1; ++i) {
     const int nbr = a.window == 1 ? 1
                                   : decode_nbranch(a, clamp_len(a.cache_len[i / a.Hkv], a.max_len));
-    const int ns = (a.count[i] + nbr + kDecodeSplit - 1) / kDecodeSplit;
-    pre[i] = ns;
-    tot += ns;
+    const int n = a.count[i] + nbr;
+    preF[i] = n / kDecodeSplit;
+    preP[i] = n % kDecodeSplit != 0;
+    totF += preF[i];
+    totP += preP[i];
   }
-  int incl = tot;
+  int inclF = totF, inclP = totP;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
+    const int yf = __shfl_up(inclF, o, kWave), yp = __shfl_up(inclP, o, kWave);
+    if (lane >= o) {
+      inclF += yf;
+      inclP += yp;
+    }
   }
-  if (lane == kWave - 1) wsum[wave] = incl;
+  if (lane == kWave - 1) {
+    wsum[0][wave] = inclF;
+    wsum[1][wave] = inclP;
+  }
   __syncthreads();
-  int run = incl - tot;
-  for (int w = 0; w < wave; ++w) run += wsum[w];
+  int runF = inclF - totF, runP = inclP - totP;
+  for (int w = 0; w < wave; ++w) {
+    runF += wsum[0][w];
+    runP += wsum[1][w];
+  }
   for (int i = i0; i < i1; ++i) {
-    const int ns = pre[i];
-    pre[i] = run;
-    run += ns;
+    const int f = preF[i], pp = preP[i];
+    preF[i] = runF;
+    preP[i] = runP;
+    runF += f;
+    runP += pp;
   }
-  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  if (threadIdx.x == 0) pre[nbg] = total;
+  const int totalF = wsum[0][0] + wsum[0][1] + wsum[0][2] + wsum[0][3];
+  const int totalP = wsum[1][0] + wsum[1][1] + wsum[1][2] + wsum[1][3];
+  if (threadIdx.x == 0) {
+    preF[nbg] = totalF;
+    preP[nbg] = totalP;
+  }
   __syncthreads();
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    int lo = 0, hi = nbg;   // pre[lo] <= it < pre[hi]
+  for (int it = blockIdx.x; it < totalF + totalP; it += gridDim.x) {
+    const bool full = it < totalF;
+    const int* pr = full ? preF : preP;
+    const int key = full ? it : it - totalF;
+    int lo = 0, hi = nbg;   // pr[lo] <= key < pr[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= it) lo = mid; else hi = mid;
+      if (pr[mid] <= key) lo = mid; else hi = mid;
     }
-    decode_item<D, PAGED>(a, lo, it - pre[lo], ms, ls, os);
+    // a partial split comes after the pair's full ones
+    const int split = full ? key - preF[lo] : preF[lo + 1] - preF[lo];
+    decode_item<D, PAGED>(a, lo, split, ms, ls, os);
   }
 }
 
@@ -828,7 +855,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
 
 // Workgroups of decode_attend_bf16_kernel<D> resident on the current device at
 // once with `lds` bytes of dynamic LDS (cached per device and 4 KB step of lds).
-constexpr int kLdsSteps = (kDecodeMaxBg + 1) * 4 / 4096 + 1;
+constexpr int kLdsSteps = 2 * (kDecodeMaxBg + 1) * 4 / 4096 + 1;
 template <int D, bool PAGED>
 static int persistent_grid(size_t lds) {
   static std::atomic<int> cache[kMaxDevices][kLdsSteps];
@@ -976,7 +1003,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   dim3 g3((unsigned)L.n_split, nbg);
   if (bf16) {
     const int64_t items_max = (int64_t)nbg * L.n_split;
-    const size_t lds_pre = sizeof(int) * ((size_t)nbg + 1);   // the item prefix
+    const size_t lds_pre = 2 * sizeof(int) * ((size_t)nbg + 1);   // the item prefixes
 #define DASH_DA(D, PG)                                                                     \
   hipLaunchKernelGGL((decode_attend_bf16_kernel<D, PG>),                                   \
                      dim3((unsigned)min64(items_max, persistent_grid<D, PG>(lds_pre))),    \
