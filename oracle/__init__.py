@@ -10,7 +10,8 @@ arXiv 2605.18753), "Technical summary": Stage 0 (local chunk summarization),
 Stage 1 (entmax chunk routing, w = alpha-entmax(gamma * zbar)) and Stage 2
 (prior-induced sparse softmax).  Stage 0 pools a block uniformly, or, given
 a summary query q_bar per KV head, by scaled dot-product attention of q_bar
-over the block's keys.  This module only marshals numpy arrays.
+over the block's keys.  This module only marshals numpy arrays; the backward
+pass of the prefill is written out in ``oracle/backward.py``.
 
 Parity pins (all in ``tests/test_oracle_*.py``): closed-form sparsemax and
 1.5-entmax values, an independent SLSQP solve of the Tsallis-entmax problem,
