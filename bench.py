@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "prefill tok/s + decode step µs at ~75% block sparsity; % HBM/MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3      # vector float32 FMA peak
 QT = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_prefill_8k_traffic.txt")
 ATTEND_SRC = os.path.join(ROOT, "sparse_hierarchical_attention_block_amd", "csrc", "attend.hip")
@@ -56,6 +57,8 @@ def parse():
     ap.add_argument("--window", type=int, default=None,
                     help="near-diagonal branch in blocks (default: the workload's, 1)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward of the prefill step")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the ragged-batch prefill leg")
     ap.add_argument("--no-cpu", action="store_true")
@@ -150,6 +153,20 @@ def prefill_bench(args, torch, dash, W):
     o2 = torch.empty_like(q)
     t_att = events_time(lambda: dash.dash_attend(p, q, k, v, N, rb, o2), args.steps, 2, torch)
 
+    # backward of the same step (mean-pooled summaries), from the forward's
+    # summaries, routing and output
+    t_bwd = None
+    if not args.no_backward:
+        d_o = torch.randn(q.shape, generator=torch.Generator(device="cpu").manual_seed(7)).to(
+            dev, q.dtype)
+        grads = [torch.empty(x.shape, dtype=torch.float32, device=dev) for x in (q, k, v)]
+        dws = torch.empty((d, d), dtype=torch.float32, device=dev)
+        wsb = dash.workspace(dash.dash_prefill_backward_workspace_bytes(p, N), dev)
+        t_bwd = events_time(lambda: dash.dash_prefill_backward(p, q, k, v, o2, d_o, N, ws_mat,
+                                                               summ, nb, rb, *grads, dws, wsb),
+                            max(1, args.steps // 10), 2, torch)
+        del grads, wsb
+
     count = rb.sel_count.view(B, Hkv, -1).cpu().numpy().astype(np.int64)
     n_qt = count.shape[2]
     qt = np.arange(n_qt)
@@ -177,6 +194,16 @@ def prefill_bench(args, torch, dash, W):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if t_bwd is not None:
+        # algorithmic work of the attention backward: the five products S, dP,
+        # dQ, dK, dV over the walked chunks = 2.5 x the forward's two
+        bwd_flops = 2.5 * att_flops
+        bt = bwd_flops / (t_bwd * 1e-3) / 1e12
+        res["backward"] = {"ms": round(t_bwd, 4), "attention_gflop": round(bwd_flops / 1e9, 2),
+                           "roofline": {"bound": "alu", "achieved": round(bt, 2),
+                                        "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(bt / PEAK_FP32_TFLOPS, 4),
+                                        "scope": "float32 FMA kernels, attention products only"}}
     if args.dense:
         rbd = dash.RouteBuffers(sizes, dev)
         rbd.sel_count.copy_(torch.from_numpy(np.broadcast_to(cand, (B * Hkv, n_qt)).astype(
@@ -387,6 +414,8 @@ def main():
                           "roofline": dec["roofline"],
                           "all_bytes_gbs": dec["all_bytes_gbs"],
                           "paged_kv": dec["paged"]}
+    if "backward" in pre:
+        line["prefill_backward"] = pre["backward"]
     if var is not None:
         line["varlen_prefill"] = var
     line["cpu_baseline"] = cpu

@@ -232,6 +232,29 @@ dash_status dash_prefill_varlen(const dash_params* p, const void* q, const void*
                                 const float* q_bar, float* summ, int64_t summ_blocks, void* o,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* Backward pass of the causal prefill (the pages stress that alpha-entmax
+ * keeps the hierarchy differentiable: gradients flow from the attention
+ * output back through the routing into the chunk summaries).  For mean-pooled
+ * summaries (no summary query), given the forward's inputs, its output o, its
+ * summaries and routing result, and dO = dL/do:
+ *   q, o, d_o  [B, H, n, d] dtype;  k, v [B, Hkv, n, d] dtype
+ *   summ       [B, Hkv, summ_blocks, d] float32 as dash_summarize wrote it
+ *   route      as dash_route wrote it for these inputs (tau, sel_count,
+ *              sel_idx, sel_logp)
+ *   dq         [B, H, n, d] float32;  dk, dv [B, Hkv, n, d] float32;
+ *   dw_s       [d, d] float32 -- all written (not accumulated)
+ *   ws         >= dash_prefill_backward_workspace_bytes(p, n), 256-byte aligned
+ * The gradient reaches q through both the fine attention and the coarse
+ * scores, k through the attention and the block means, and W_s through the
+ * summaries.  Blocks with pbar = 0 take no gradient.  float32 arithmetic. */
+dash_status dash_prefill_backward_workspace_bytes(const dash_params* p, int64_t n,
+                                                  size_t* bytes);
+dash_status dash_prefill_backward(const dash_params* p, const void* q, const void* k,
+                                  const void* v, const void* o, const void* d_o, int64_t n,
+                                  const float* w_s, const float* summ, int64_t summ_blocks,
+                                  const dash_route_buf* route, float* dq, float* dk, float* dv,
+                                  float* dw_s, void* ws, size_t ws_bytes, void* stream);
+
 /* One incremental decoding step for every sequence b: the query q[b] sits at
  * position L = cache_len[b] - 1 and its key/value are already in the caches.
  * Routes over the cached summaries of blocks j < floor(L / bs), attends to the

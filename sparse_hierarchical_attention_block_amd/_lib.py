@@ -80,6 +80,11 @@ _lib.dash_mask_to_list.restype = ctypes.c_int
 _lib.dash_mask_to_list.argtypes = [_P, _I, _R, _V]
 _lib.dash_prefill.restype = ctypes.c_int
 _lib.dash_prefill.argtypes = [_P, _V, _V, _V, _I, _V, _V, _V, _I, _V, _V, ctypes.c_size_t, _V]
+_lib.dash_prefill_backward_workspace_bytes.restype = ctypes.c_int
+_lib.dash_prefill_backward_workspace_bytes.argtypes = [_P, _I, ctypes.POINTER(ctypes.c_size_t)]
+_lib.dash_prefill_backward.restype = ctypes.c_int
+_lib.dash_prefill_backward.argtypes = [_P, _V, _V, _V, _V, _V, _I, _V, _V, _I, _R, _V, _V, _V, _V,
+                                       _V, ctypes.c_size_t, _V]
 _lib.dash_prefill_varlen.restype = ctypes.c_int
 _lib.dash_prefill_varlen.argtypes = [_P, _V, _V, _V, _I, _V, _V, _V, _V, _I, _V, _V,
                                      ctypes.c_size_t, _V]
@@ -94,7 +99,8 @@ EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
             "dash_route_sizes_decode", "dash_prefill_workspace_bytes",
             "dash_decode_workspace_bytes", "dash_summarize", "dash_route", "dash_attend",
             "dash_mask_to_list", "dash_prefill", "dash_prefill_varlen", "dash_decode",
-            "dash_decode_paged")
+            "dash_decode_paged", "dash_prefill_backward_workspace_bytes",
+            "dash_prefill_backward")
 
 
 # ---------------------------------------------------------------------------------------
@@ -354,3 +360,30 @@ def dash_decode_paged(p, q, k_pages, v_pages, block_table, cache_len, max_len, w
         _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
         _dev(o, "o", B * H * d, dt), rb, _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def dash_prefill_backward_workspace_bytes(p, n) -> int:
+    out = ctypes.c_size_t()
+    _check("dash_prefill_backward_workspace_bytes",
+           _lib.dash_prefill_backward_workspace_bytes(ctypes.byref(p), n, ctypes.byref(out)))
+    return out.value
+
+
+def dash_prefill_backward(p, q, k, v, o, d_o, n, w_s, summ, summ_blocks, route: RouteBuffers,
+                          dq, dk, dv, dw_s, ws, stream=None):
+    """Gradients of the causal prefill (mean-pooled summaries) into float32 dq, dk,
+    dv, dw_s, from the forward's inputs, output, summaries and routing."""
+    B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
+    dt = torch_dtype(p)
+    if route.sizes != dash_route_sizes_prefill(p, n):
+        raise ValueError("route buffers were sized for another problem")
+    rb = route.struct()
+    f32 = torch.float32
+    _check("dash_prefill_backward", _lib.dash_prefill_backward(
+        ctypes.byref(p), _dev(q, "q", B * H * n * d, dt), _dev(k, "k", B * Hkv * n * d, dt),
+        _dev(v, "v", B * Hkv * n * d, dt), _dev(o, "o", B * H * n * d, dt),
+        _dev(d_o, "d_o", B * H * n * d, dt), n, _dev(w_s, "w_s", d * d, f32),
+        _dev(summ, "summ", B * Hkv * summ_blocks * d, f32), summ_blocks, ctypes.byref(rb),
+        _dev(dq, "dq", B * H * n * d, f32), _dev(dk, "dk", B * Hkv * n * d, f32),
+        _dev(dv, "dv", B * Hkv * n * d, f32), _dev(dw_s, "dw_s", d * d, f32),
+        _dev(ws, "ws", 0), ws.numel() * ws.element_size(), _stream(stream)))

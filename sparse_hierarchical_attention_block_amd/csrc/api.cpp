@@ -272,6 +272,39 @@ dash_status dash_prefill_varlen(const dash_params* p, const void* q, const void*
                       ws_bytes, stream);
 }
 
+dash_status dash_prefill_backward_workspace_bytes(const dash_params* p, int64_t n,
+                                                  size_t* bytes) {
+  Shape s;
+  dash_status st = check_params(p, &s);
+  if (st != DASH_OK) return st;
+  if (n < 0 || !bytes) return DASH_ERR_INVALID_ARG;
+  *bytes = dash::bwd_layout(s, n).total;
+  return DASH_OK;
+}
+
+dash_status dash_prefill_backward(const dash_params* p, const void* q, const void* k,
+                                  const void* v, const void* o, const void* d_o, int64_t n,
+                                  const float* w_s, const float* summ, int64_t summ_blocks,
+                                  const dash_route_buf* route, float* dq, float* dk, float* dv,
+                                  float* dw_s, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  dash_status st = check_params(p, &s);
+  if (st != DASH_OK) return st;
+  if (n < 0 || !q || !k || !v || !o || !d_o || !w_s || !summ || !dq || !dk || !dv || !dw_s)
+    return DASH_ERR_INVALID_ARG;
+  if ((st = check_route_buf(route)) != DASH_OK) return st;
+  if (summ_blocks < n / s.bs) return DASH_ERR_INVALID_ARG;
+  if (n == 0) return DASH_OK;
+  const dash::BwdLayout L = dash::bwd_layout(s, n);
+  if (!ws || ((uintptr_t)ws % kAlign) != 0) return DASH_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return DASH_ERR_WORKSPACE_TOO_SMALL;
+  if (!grid_ok(n * s.B * s.Hkv) || !grid_ok(((n + kQT - 1) / kQT) * s.B * s.H))
+    return DASH_ERR_UNSUPPORTED;
+  return hip_status(dash::launch_prefill_backward(s, q, k, v, o, d_o, n, w_s, summ, summ_blocks,
+                                                  *route, dq, dk, dv, dw_s, L, (char*)ws,
+                                                  (hipStream_t)stream));
+}
+
 // Shared checks and launch of dash_decode / dash_decode_paged (block_table
 // null: contiguous caches).
 static dash_status decode_impl(const dash_params* p, const void* q, const void* k_cache,

@@ -1,0 +1,516 @@
+// backward.hip -- gradients of the causal DashAttention prefill (the pages'
+// point that alpha-entmax keeps the hierarchy differentiable, so gradients
+// reach the chunk summaries through the routing: DashAttention explainer,
+// Technical summary and Contributions).
+//
+// Given the forward inputs and output, its routing result and dO, the
+// kernels below produce dq, dk, dv and dW_s (float32) for mean-pooled
+// summaries:
+//   rows    per (query tile, head): log-sum-exp and delta = dO.o by a first
+//           pass over the tile's chunks, then dl_t = P_t (dO.v_t - delta),
+//           dq = sum dl_t k_t / sqrt(d), and the bias gradient of every
+//           routed block, sigma * sum_{t in block} dl_t, added over the
+//           group's heads into dlogp[tile, block, row]
+//   keys    per 64-key chunk of a (sequence, KV head): every later tile that
+//           attends the chunk (branch or list), every head and row of it:
+//           dk_t = sum dl_t q / sqrt(d), dv_t = sum P_t dO
+//   route   per (position, KV head): dpbar = dlogp / pbar, dp_h = dpbar / G,
+//           the entmax Jacobian with u = (x - tau)_+^((2-alpha)/(alpha-1)):
+//           dzbar = gamma (u dp - u (u.dp) / sum u); dq += dzbar . s / sqrt(d)
+//   summ    ds_j = sum over later rows and heads of dzbar_j q / sqrt(d)
+//   means   dk of block j += (ds_j W_s^T) / bs; block means m_j
+//   w_s     dW_s = sum_j m_j^T ds_j
+// Every product is plain float32 FMAs (no MFMA); a row or key is spread over
+// 4 lanes of D/4 columns each, dot products reduced over those lanes.
+#include "dash_internal.hpp"
+#include "device_common.hpp"
+
+namespace dash {
+
+constexpr int kBwdTile = DASH_QUERY_TILE;   // 64 query rows per tile
+constexpr int kBwdChunk = 64;               // keys per chunk
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* w_s;
+  const float* summ;
+  int64_t summ_blocks;
+  const float* tau;         // [B, H, n]
+  const int32_t* sel_count; // [B, Hkv, n_qt]
+  const int32_t* sel_idx;   // [B, Hkv, n_qt, nb]
+  const float* sel_logp;    // [B, Hkv, n_qt, nb, 64]
+  float* dq;                // [B, H, n, D]
+  float* dk;                // [B, Hkv, n, D]
+  float* dv;
+  float* dw_s;              // [D, D]
+  float* lse2;              // [B, H, n] log2-sum-exp2 of the scaled logits
+  float* delta;             // [B, H, n] dO . o
+  float* dlogp;             // [B, Hkv, n_qt, nb, 64]
+  float* dz;                // [B, H, n, nb]
+  float* ds;                // [B, Hkv, nb, D]
+  float* mean;              // [B, Hkv, nb, D]
+  int64_t n, n_qt, nb;
+  int B, H, Hkv, G, bs, window;
+  float scale_log2;         // log2(e) / sqrt(d)
+  float rs;                 // 1 / sqrt(d)
+  float xscale;             // (alpha - 1) gamma / sqrt(d)
+  float gamma, sigma, ue;   // ue = (2 - alpha) / (alpha - 1)
+};
+
+template <typename T>
+__device__ __forceinline__ float ld(const void* p, int64_t i) {
+  return to_f32(((const T*)p)[i]);
+}
+
+// sum over the 4 lanes of a row (lanes 4r .. 4r+3)
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x;
+}
+
+// The tile's walk: branch chunks first (bias 0; the last one is the diagonal
+// chunk), then the chunks of the listed blocks.
+struct BwdWalk {
+  int64_t own_c0;   // first branch chunk
+  int n_own, count, cpb;
+};
+__device__ __forceinline__ BwdWalk bwd_walk(const BwdArgs& a, int64_t tile, int64_t qt) {
+  BwdWalk w;
+  w.cpb = a.bs / kBwdChunk;
+  const int64_t own = (qt * kBwdTile) / a.bs;
+  const int64_t b0 = own - (a.window - 1) > 0 ? own - (a.window - 1) : 0;
+  w.own_c0 = b0 * w.cpb;
+  w.n_own = (int)(qt - w.own_c0 + 1);
+  w.count = a.sel_count[tile];
+  return w;
+}
+
+// ---- rows: lse, delta, dq (fine part), bias gradients ---------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
+  constexpr int S = D / 4;   // columns per lane
+  extern __shared__ float lds_rows[];   // K and V of the chunk, [64][D] each
+  float(*Kc)[D] = (float(*)[D])lds_rows;
+  float(*Vc)[D] = (float(*)[D])(lds_rows + kBwdChunk * D);
+  const int64_t qt = blockIdx.x % a.n_qt;
+  const int64_t bh = blockIdx.x / a.n_qt;   // b * H + h
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H), g = h / a.G;
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  const int64_t tile = bg * a.n_qt + qt;
+  const int row = threadIdx.x / 4, sl = threadIdx.x % 4;
+  const int64_t qpos = qt * kBwdTile + row;
+  const bool valid = qpos < a.n;
+  const int64_t rbase = (bh * a.n + (valid ? qpos : 0)) * D + sl * S;
+  float qv[S], dov[S], acc[S];
+  float dlt = 0.f;
+#pragma unroll
+  for (int c = 0; c < S; ++c) {
+    qv[c] = valid ? ld<T>(a.q, rbase + c) : 0.f;
+    dov[c] = valid ? ld<T>(a.dO, rbase + c) : 0.f;
+    dlt = fmaf(dov[c], valid ? ld<T>(a.o, rbase + c) : 0.f, dlt);
+    acc[c] = 0.f;
+  }
+  dlt = quad_sum(dlt);
+  const BwdWalk w = bwd_walk(a, tile, qt);
+  const int n_chunks = w.n_own + w.count * w.cpb;
+  const T* kb = (const T*)a.k + bg * a.n * D;
+  const T* vb = (const T*)a.v + bg * a.n * D;
+
+  // chunk c -> first key, block (-1 for branch chunks)
+  auto chunk = [&](int c, int64_t& key0, int64_t& blk) {
+    if (c < w.n_own) {
+      key0 = (w.own_c0 + c) * kBwdChunk;
+      blk = -1;
+    } else {
+      const int e = (c - w.n_own) / w.cpb;
+      blk = a.sel_idx[tile * a.nb + e];
+      key0 = blk * a.bs + ((c - w.n_own) % w.cpb) * kBwdChunk;
+    }
+  };
+  auto stage = [&](int64_t key0, bool with_v) {
+    for (int e = threadIdx.x; e < kBwdChunk * D; e += 256) {
+      const int kk = e / D, c = e % D;
+      const bool in = key0 + kk < a.n;
+      Kc[kk][c] = in ? to_f32(kb[(key0 + kk) * D + c]) : 0.f;
+      if (with_v) Vc[kk][c] = in ? to_f32(vb[(key0 + kk) * D + c]) : 0.f;
+    }
+  };
+  // scaled logit (log2 units) of key kk of the chunk, -inf when masked
+  auto logit = [&](int kk, int64_t key0, int64_t blk, float bias2) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < S; ++c) s = fmaf(qv[c], Kc[kk][sl * S + c], s);
+    s = quad_sum(s);
+    const int64_t key = key0 + kk;
+    if (blk < 0 && key > qpos) return -INFINITY;
+    return fmaf(s, a.scale_log2, bias2);
+  };
+
+  // pass 1: log-sum-exp
+  float m = -INFINITY, l = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    int64_t key0, blk;
+    chunk(c, key0, blk);
+    const float bias2 =
+        blk < 0 ? 0.f : a.sel_logp[(tile * a.nb + blk) * kBwdTile + row] * kLog2e;
+    __syncthreads();
+    stage(key0, false);
+    __syncthreads();
+    if (bias2 == -INFINITY) continue;
+    for (int kk = 0; kk < kBwdChunk; ++kk) {
+      const float s = logit(kk, key0, blk, bias2);
+      if (s == -INFINITY) continue;
+      const float mn = fmaxf(m, s);
+      l = l * exp2f(m - mn) + exp2f(s - mn);
+      m = mn;
+    }
+  }
+  const float lse = m + log2f(l);
+  if (valid && sl == 0) {
+    a.lse2[bh * a.n + qpos] = lse;
+    a.delta[bh * a.n + qpos] = dlt;
+  }
+
+  // pass 2: dl, dq, bias gradients
+  float bacc = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    int64_t key0, blk;
+    chunk(c, key0, blk);
+    const float bias2 =
+        blk < 0 ? 0.f : a.sel_logp[(tile * a.nb + blk) * kBwdTile + row] * kLog2e;
+    __syncthreads();
+    stage(key0, true);
+    __syncthreads();
+    if (bias2 != -INFINITY) {
+      for (int kk = 0; kk < kBwdChunk; ++kk) {
+        const float s = logit(kk, key0, blk, bias2);
+        const float p = s == -INFINITY ? 0.f : exp2f(s - lse);
+        float dp = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < S; ++cc) dp = fmaf(dov[cc], Vc[kk][sl * S + cc], dp);
+        dp = quad_sum(dp);
+        const float dl = p * (dp - dlt);
+        if (blk >= 0) bacc += dl;
+#pragma unroll
+        for (int cc = 0; cc < S; ++cc) acc[cc] = fmaf(dl * a.rs, Kc[kk][sl * S + cc], acc[cc]);
+      }
+    }
+    // end of a listed block: its bias gradient, added over the group's heads
+    if (blk >= 0 && (c - w.n_own) % w.cpb == w.cpb - 1) {
+      if (valid && sl == 0 && bias2 != -INFINITY)
+        atomicAdd(&a.dlogp[(tile * a.nb + blk) * kBwdTile + row], a.sigma * bacc);
+      bacc = 0.f;
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int c = 0; c < S; ++c) a.dq[rbase + c] = acc[c];
+  }
+}
+
+// ---- keys: dk (fine part), dv --------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
+  constexpr int S = D / 4;
+  extern __shared__ float lds_keys[];   // q and dO rows of a tile, [64][D] each, then row data
+  float(*Qs)[D] = (float(*)[D])lds_keys;
+  float(*Os)[D] = (float(*)[D])(lds_keys + kBwdTile * D);
+  float* rowl = lds_keys + 2 * kBwdTile * D;
+  float* rowd = rowl + kBwdTile;
+  float* rowb = rowd + kBwdTile;
+  const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
+  const int64_t ch = blockIdx.x % nch;
+  const int64_t bg = blockIdx.x / nch;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int key = threadIdx.x / 4, sl = threadIdx.x % 4;
+  const int64_t kpos = ch * kBwdChunk + key;
+  const bool valid = kpos < a.n;
+  const int64_t kbase = (bg * a.n + (valid ? kpos : 0)) * D + sl * S;
+  float kv[S], vv[S], dkv[S], dvv[S];
+#pragma unroll
+  for (int c = 0; c < S; ++c) {
+    kv[c] = valid ? ld<T>(a.k, kbase + c) : 0.f;
+    vv[c] = valid ? ld<T>(a.v, kbase + c) : 0.f;
+    dkv[c] = 0.f;
+    dvv[c] = 0.f;
+  }
+  const int64_t blk = (ch * kBwdChunk) / a.bs;
+  for (int64_t qt = ch; qt < a.n_qt; ++qt) {
+    const int64_t tile = bg * a.n_qt + qt;
+    const int64_t own = (qt * kBwdTile) / a.bs;
+    const int64_t b0 = own - (a.window - 1) > 0 ? own - (a.window - 1) : 0;
+    bool branch = blk >= b0 && blk <= own;
+    bool listed = false;
+    if (!branch) {
+      // the tile's ascending list: binary search for blk
+      const int cnt = a.sel_count[tile];
+      const int32_t* lst = a.sel_idx + tile * a.nb;
+      int lo = 0, hi = cnt;
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (lst[mid] < blk) lo = mid + 1; else hi = mid;
+      }
+      listed = lo < cnt && lst[lo] == blk;
+    }
+    if (!branch && !listed) continue;
+    for (int hh = 0; hh < a.G; ++hh) {
+      const int h = g * a.G + hh;
+      const int64_t bh = (int64_t)b * a.H + h;
+      __syncthreads();
+      for (int e = threadIdx.x; e < kBwdTile * D; e += 256) {
+        const int r = e / D, c = e % D;
+        const int64_t pos = qt * kBwdTile + r;
+        const bool in = pos < a.n;
+        Qs[r][c] = in ? ld<T>(a.q, (bh * a.n + pos) * D + c) : 0.f;
+        Os[r][c] = in ? ld<T>(a.dO, (bh * a.n + pos) * D + c) : 0.f;
+      }
+      for (int r = threadIdx.x; r < kBwdTile; r += 256) {
+        const int64_t pos = qt * kBwdTile + r;
+        const bool in = pos < a.n;
+        rowl[r] = in ? a.lse2[bh * a.n + pos] : 0.f;
+        rowd[r] = in ? a.delta[bh * a.n + pos] : 0.f;
+        rowb[r] = !in ? -INFINITY
+                      : (branch ? 0.f : a.sel_logp[(tile * a.nb + blk) * kBwdTile + r] * kLog2e);
+      }
+      __syncthreads();
+      for (int r = 0; r < kBwdTile; ++r) {
+        const int64_t pos = qt * kBwdTile + r;
+        if (rowb[r] == -INFINITY) continue;
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int c = 0; c < S; ++c) {
+          s = fmaf(Qs[r][sl * S + c], kv[c], s);
+          dp = fmaf(Os[r][sl * S + c], vv[c], dp);
+        }
+        s = quad_sum(s);
+        dp = quad_sum(dp);
+        float p = exp2f(fmaf(s, a.scale_log2, rowb[r]) - rowl[r]);
+        if (!valid || (branch && kpos > pos)) p = 0.f;
+        const float dl = p * (dp - rowd[r]);
+#pragma unroll
+        for (int c = 0; c < S; ++c) {
+          dkv[c] = fmaf(dl * a.rs, Qs[r][sl * S + c], dkv[c]);
+          dvv[c] = fmaf(p, Os[r][sl * S + c], dvv[c]);
+        }
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      a.dk[kbase + c] = dkv[c];
+      a.dv[kbase + c] = dvv[c];
+    }
+  }
+}
+
+// ---- route: dzbar and the coarse part of dq (one wave per position and KV head) ------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_route_kernel(BwdArgs a) {
+  extern __shared__ float dzs[];   // [nb]
+  const int64_t pos = blockIdx.x % a.n;
+  const int64_t bg = blockIdx.x / a.n;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int lane = threadIdx.x;
+  const int64_t own = pos / a.bs;
+  const int ncand = (int)(own - (a.window - 1) > 0 ? own - (a.window - 1) : 0);
+  if (ncand == 0) return;
+  const int64_t qt = pos / kBwdTile, tile = bg * a.n_qt + qt;
+  const int r = (int)(pos % kBwdTile);
+  const float* srow = a.summ + bg * a.summ_blocks * D;
+  for (int hh = 0; hh < a.G; ++hh) {
+    const int h = g * a.G + hh;
+    const int64_t bh = (int64_t)b * a.H + h;
+    const float tau = a.tau[bh * a.n + pos];
+    const T* qrow = (const T*)a.q + (bh * a.n + pos) * D;
+    float su = 0.f, sud = 0.f;
+    for (int j = lane; j < ncand; j += kWave) {
+      float x = 0.f;
+      for (int c = 0; c < D; ++c) x = fmaf(to_f32(qrow[c]), srow[j * D + c], x);
+      x *= a.xscale;
+      const float y = x - tau;
+      const float u = y > 0.f ? (a.ue == 0.f ? 1.f : powf(y, a.ue)) : 0.f;
+      const int64_t li = (tile * a.nb + j) * kBwdTile + r;
+      const float lp = a.sel_logp[li];
+      float dp = 0.f;
+      if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)a.G;
+      su += u;
+      sud = fmaf(u, dp, sud);
+      dzs[j] = u;           // u for now, dz below
+      a.dz[(bh * a.n + pos) * a.nb + j] = dp;
+    }
+    su = wave_sum(su);
+    sud = wave_sum(sud);
+    const float corr = su > 0.f ? sud / su : 0.f;
+    for (int j = lane; j < ncand; j += kWave) {
+      float* dzp = a.dz + (bh * a.n + pos) * a.nb + j;
+      const float u = dzs[j];
+      const float dz = a.gamma * u * (*dzp - corr);
+      *dzp = dz;
+      dzs[j] = dz;
+    }
+    __syncthreads();
+    for (int c = lane; c < D; c += kWave) {
+      float acc = 0.f;
+      for (int j = 0; j < ncand; ++j) acc = fmaf(dzs[j], srow[j * D + c], acc);
+      a.dq[(bh * a.n + pos) * D + c] += acc * a.rs;
+    }
+    __syncthreads();
+  }
+}
+
+// ---- summaries: ds_j = sum over later rows and heads of dzbar_j q / sqrt(d) -----------------
+template <typename T, int D>
+__global__ __launch_bounds__(D) void bwd_summ_kernel(BwdArgs a) {
+  const int64_t j = blockIdx.x % a.nb;
+  const int64_t bg = blockIdx.x / a.nb;
+  const int c = threadIdx.x;
+  if (j >= a.n / a.bs) {   // no summary for an incomplete block
+    a.ds[(bg * a.nb + j) * D + c] = 0.f;
+    return;
+  }
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  float acc = 0.f;
+  for (int64_t pos = (j + a.window) * a.bs; pos < a.n; ++pos)
+    for (int hh = 0; hh < a.G; ++hh) {
+      const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
+      acc = fmaf(a.dz[(bh * a.n + pos) * a.nb + j], ld<T>(a.q, (bh * a.n + pos) * D + c), acc);
+    }
+  a.ds[(bg * a.nb + j) * D + c] = acc * a.rs;
+}
+
+// ---- block means, and dk += (ds_j W_s^T) / bs over the block ---------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
+  const int64_t j = blockIdx.x % a.nb;
+  const int64_t bg = blockIdx.x / a.nb;
+  const int r = threadIdx.x;
+  float* mrow = a.mean + (bg * a.nb + j) * D;
+  if (j >= a.n / a.bs) {   // incomplete block: no summary, no gradient
+    mrow[r] = 0.f;
+    return;
+  }
+  const int64_t k0 = bg * a.n + j * a.bs;
+  float m = 0.f;
+  for (int t = 0; t < a.bs; ++t) m += ld<T>(a.k, (k0 + t) * D + r);
+  mrow[r] = m / (float)a.bs;
+  const float* dsr = a.ds + (bg * a.nb + j) * D;
+  float dm = 0.f;
+  for (int c = 0; c < D; ++c) dm = fmaf(dsr[c], a.w_s[r * D + c], dm);
+  dm /= (float)a.bs;
+  for (int t = 0; t < a.bs; ++t) a.dk[(k0 + t) * D + r] += dm;
+}
+
+// ---- dW_s = sum_j m_j^T ds_j ---------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_ws_kernel(BwdArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)D * D) return;
+  const int r = (int)(idx / D), c = (int)(idx % D);
+  const int64_t nblk = (int64_t)a.B * a.Hkv * a.nb;
+  float acc = 0.f;
+  for (int64_t u = 0; u < nblk; ++u) acc = fmaf(a.mean[u * D + r], a.ds[u * D + c], acc);
+  a.dw_s[idx] = acc;
+}
+
+__global__ void bwd_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+BwdLayout bwd_layout(const Shape& s, int64_t n) {
+  BwdLayout L;
+  const int64_t n_qt = (n + kBwdTile - 1) / kBwdTile, nb = (n + s.bs - 1) / s.bs;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 0;
+  L.off_lse = off;   off = al(off + sizeof(float) * s.B * s.H * n);
+  L.off_delta = off; off = al(off + sizeof(float) * s.B * s.H * n);
+  L.off_dlogp = off; off = al(off + sizeof(float) * s.B * s.Hkv * n_qt * nb * kBwdTile);
+  L.off_dz = off;    off = al(off + sizeof(float) * s.B * s.H * n * nb);
+  L.off_ds = off;    off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
+  L.off_mean = off;  off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
+  L.total = off;
+  return L;
+}
+
+template <typename T, int D>
+static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
+  const int64_t nzero = nbg * a.n_qt * a.nb * kBwdTile;
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, st, a.dlogp, nzero);
+  const size_t lds_r = sizeof(float) * 2 * kBwdChunk * D;
+  const size_t lds_k = sizeof(float) * (2 * kBwdTile * D + 3 * kBwdTile);
+  (void)hipFuncSetAttribute((const void*)bwd_rows_kernel<T, D>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
+  (void)hipFuncSetAttribute((const void*)bwd_keys_kernel<T, D>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_k);
+  hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3((unsigned)(a.n_qt * a.B * a.H)), dim3(256),
+                     lds_r, st, a);
+  const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
+  hipLaunchKernelGGL((bwd_keys_kernel<T, D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_k, st,
+                     a);
+  hipLaunchKernelGGL((bwd_route_kernel<T, D>), dim3((unsigned)(a.n * nbg)), dim3(kWave),
+                     sizeof(float) * a.nb, st, a);
+  hipLaunchKernelGGL((bwd_summ_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
+  hipLaunchKernelGGL((bwd_means_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
+  hipLaunchKernelGGL((bwd_ws_kernel<D>), dim3((unsigned)((D * D + 255) / 256)), dim3(256), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_backward(const Shape& s, const void* q, const void* k, const void* v,
+                                   const void* o, const void* dO, int64_t n, const float* w_s,
+                                   const float* summ, int64_t summ_blocks,
+                                   const dash_route_buf& rb, float* dq, float* dk, float* dv,
+                                   float* dw_s, const BwdLayout& L, char* ws, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dO = dO;
+  a.w_s = w_s;
+  a.summ = summ;
+  a.summ_blocks = summ_blocks;
+  a.tau = rb.tau;
+  a.sel_count = rb.sel_count;
+  a.sel_idx = rb.sel_idx;
+  a.sel_logp = rb.sel_logp;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dw_s = dw_s;
+  a.lse2 = (float*)(ws + L.off_lse);
+  a.delta = (float*)(ws + L.off_delta);
+  a.dlogp = (float*)(ws + L.off_dlogp);
+  a.dz = (float*)(ws + L.off_dz);
+  a.ds = (float*)(ws + L.off_ds);
+  a.mean = (float*)(ws + L.off_mean);
+  a.n = n;
+  a.n_qt = (n + kBwdTile - 1) / kBwdTile;
+  a.nb = (n + s.bs - 1) / s.bs;
+  a.B = s.B;
+  a.H = s.H;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.bs = s.bs;
+  a.window = s.window;
+  a.scale_log2 = kLog2e / sqrtf((float)s.d);
+  a.rs = 1.0f / sqrtf((float)s.d);
+  a.xscale = (s.alpha - 1.0f) * s.gamma / sqrtf((float)s.d);
+  a.gamma = s.gamma;
+  a.sigma = s.sigma;
+  a.ue = (2.0f - s.alpha) / (s.alpha - 1.0f);
+  if (s.dtype == DASH_BF16)
+    return s.d == 64 ? bwd_t<__bf16, 64>(a, st) : bwd_t<__bf16, 128>(a, st);
+  return s.d == 64 ? bwd_t<float, 64>(a, st) : bwd_t<float, 128>(a, st);
+}
+
+}  // namespace dash

@@ -74,4 +74,16 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
                          const int32_t* block_table = nullptr, int64_t max_blocks = 0,
                          int64_t num_pages = 0);
 
+// Backward pass of the causal prefill (mean-pooled summaries): workspace
+// layout and launch.
+struct BwdLayout {
+  size_t off_lse, off_delta, off_dlogp, off_dz, off_ds, off_mean, total;
+};
+BwdLayout bwd_layout(const Shape& s, int64_t n);
+hipError_t launch_prefill_backward(const Shape& s, const void* q, const void* k, const void* v,
+                                   const void* o, const void* dO, int64_t n, const float* w_s,
+                                   const float* summ, int64_t summ_blocks,
+                                   const dash_route_buf& rb, float* dq, float* dk, float* dv,
+                                   float* dw_s, const BwdLayout& L, char* ws, hipStream_t st);
+
 }  // namespace dash
