@@ -17,7 +17,8 @@
 //   route   per (position, KV head): dpbar = dlogp / pbar, dp_h = dpbar / G,
 //           the entmax Jacobian with u = (x - tau)_+^((2-alpha)/(alpha-1)):
 //           dzbar = gamma (u dp - u (u.dp) / sum u); dq += dzbar . s / sqrt(d)
-//   summ    ds_j = sum over later rows and heads of dzbar_j q / sqrt(d)
+//   summ    ds_j = sum over later rows and heads of dzbar_j q / sqrt(d),
+//           eight blocks at a time over slices of the rows
 //   means   dk of block j += (ds_j W_s^T) / bs; block means m_j
 //   w_s     dW_s = sum_j m_j^T ds_j
 // Every product is plain float32 FMAs (no MFMA); a row or key is spread over
@@ -94,9 +95,11 @@ __device__ __forceinline__ BwdWalk bwd_walk(const BwdArgs& a, int64_t tile, int6
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
   constexpr int S = D / 4;   // columns per lane
-  extern __shared__ float lds_rows[];   // K and V of the chunk, [64][D] each
-  float(*Kc)[D] = (float(*)[D])lds_rows;
-  float(*Vc)[D] = (float(*)[D])(lds_rows + kBwdChunk * D);
+  // K and V of the chunk, [64][D] each, in the input type (bf16 halves the
+  // LDS and doubles the workgroups per CU)
+  extern __shared__ __attribute__((aligned(16))) char lds_rows[];
+  T(*Kc)[D] = (T(*)[D])lds_rows;
+  T(*Vc)[D] = (T(*)[D])(lds_rows + sizeof(T) * kBwdChunk * D);
   const int64_t qt = blockIdx.x % a.n_qt;
   const int64_t bh = blockIdx.x / a.n_qt;   // b * H + h
   const int b = (int)(bh / a.H), h = (int)(bh % a.H), g = h / a.G;
@@ -136,15 +139,15 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
     for (int e = threadIdx.x; e < kBwdChunk * D; e += 256) {
       const int kk = e / D, c = e % D;
       const bool in = key0 + kk < a.n;
-      Kc[kk][c] = in ? to_f32(kb[(key0 + kk) * D + c]) : 0.f;
-      if (with_v) Vc[kk][c] = in ? to_f32(vb[(key0 + kk) * D + c]) : 0.f;
+      Kc[kk][c] = in ? kb[(key0 + kk) * D + c] : (T)0.f;
+      if (with_v) Vc[kk][c] = in ? vb[(key0 + kk) * D + c] : (T)0.f;
     }
   };
   // scaled logit (log2 units) of key kk of the chunk, -inf when masked
   auto logit = [&](int kk, int64_t key0, int64_t blk, float bias2) {
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < S; ++c) s = fmaf(qv[c], Kc[kk][sl * S + c], s);
+    for (int c = 0; c < S; ++c) s = fmaf(qv[c], to_f32(Kc[kk][sl * S + c]), s);
     s = quad_sum(s);
     const int64_t key = key0 + kk;
     if (blk < 0 && key > qpos) return -INFINITY;
@@ -192,12 +195,13 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
         const float p = s == -INFINITY ? 0.f : exp2f(s - lse);
         float dp = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < S; ++cc) dp = fmaf(dov[cc], Vc[kk][sl * S + cc], dp);
+        for (int cc = 0; cc < S; ++cc) dp = fmaf(dov[cc], to_f32(Vc[kk][sl * S + cc]), dp);
         dp = quad_sum(dp);
         const float dl = p * (dp - dlt);
         if (blk >= 0) bacc += dl;
 #pragma unroll
-        for (int cc = 0; cc < S; ++cc) acc[cc] = fmaf(dl * a.rs, Kc[kk][sl * S + cc], acc[cc]);
+        for (int cc = 0; cc < S; ++cc)
+          acc[cc] = fmaf(dl * a.rs, to_f32(Kc[kk][sl * S + cc]), acc[cc]);
       }
     }
     // end of a listed block: its bias gradient, added over the group's heads
@@ -217,10 +221,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
   constexpr int S = D / 4;
-  extern __shared__ float lds_keys[];   // q and dO rows of a tile, [64][D] each, then row data
-  float(*Qs)[D] = (float(*)[D])lds_keys;
-  float(*Os)[D] = (float(*)[D])(lds_keys + kBwdTile * D);
-  float* rowl = lds_keys + 2 * kBwdTile * D;
+  // q and dO rows of a tile, [64][D] each in the input type, then row data
+  extern __shared__ __attribute__((aligned(16))) char lds_keys[];
+  T(*Qs)[D] = (T(*)[D])lds_keys;
+  T(*Os)[D] = (T(*)[D])(lds_keys + sizeof(T) * kBwdTile * D);
+  float* rowl = (float*)(lds_keys + sizeof(T) * 2 * kBwdTile * D);
   float* rowd = rowl + kBwdTile;
   float* rowb = rowd + kBwdTile;
   const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
@@ -266,8 +271,8 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
         const int r = e / D, c = e % D;
         const int64_t pos = qt * kBwdTile + r;
         const bool in = pos < a.n;
-        Qs[r][c] = in ? ld<T>(a.q, (bh * a.n + pos) * D + c) : 0.f;
-        Os[r][c] = in ? ld<T>(a.dO, (bh * a.n + pos) * D + c) : 0.f;
+        Qs[r][c] = in ? ((const T*)a.q)[(bh * a.n + pos) * D + c] : (T)0.f;
+        Os[r][c] = in ? ((const T*)a.dO)[(bh * a.n + pos) * D + c] : (T)0.f;
       }
       for (int r = threadIdx.x; r < kBwdTile; r += 256) {
         const int64_t pos = qt * kBwdTile + r;
@@ -284,8 +289,8 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
         float s = 0.f, dp = 0.f;
 #pragma unroll
         for (int c = 0; c < S; ++c) {
-          s = fmaf(Qs[r][sl * S + c], kv[c], s);
-          dp = fmaf(Os[r][sl * S + c], vv[c], dp);
+          s = fmaf(to_f32(Qs[r][sl * S + c]), kv[c], s);
+          dp = fmaf(to_f32(Os[r][sl * S + c]), vv[c], dp);
         }
         s = quad_sum(s);
         dp = quad_sum(dp);
@@ -294,8 +299,8 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
         const float dl = p * (dp - rowd[r]);
 #pragma unroll
         for (int c = 0; c < S; ++c) {
-          dkv[c] = fmaf(dl * a.rs, Qs[r][sl * S + c], dkv[c]);
-          dvv[c] = fmaf(p, Os[r][sl * S + c], dvv[c]);
+          dkv[c] = fmaf(dl * a.rs, to_f32(Qs[r][sl * S + c]), dkv[c]);
+          dvv[c] = fmaf(p, to_f32(Os[r][sl * S + c]), dvv[c]);
         }
       }
     }
@@ -365,23 +370,47 @@ __global__ __launch_bounds__(64) void bwd_route_kernel(BwdArgs a) {
 }
 
 // ---- summaries: ds_j = sum over later rows and heads of dzbar_j q / sqrt(d) -----------------
+// One workgroup per (sequence, KV head, group of kSummJ blocks, slice of the
+// rows); thread c accumulates column c of the group's kSummJ summaries (each
+// q element read once feeds kSummJ FMAs) and adds them into ds, which starts
+// at zero.
+constexpr int kSummJ = 8;
+constexpr int kSummSlices = 16;
 template <typename T, int D>
 __global__ __launch_bounds__(D) void bwd_summ_kernel(BwdArgs a) {
-  const int64_t j = blockIdx.x % a.nb;
-  const int64_t bg = blockIdx.x / a.nb;
-  const int c = threadIdx.x;
-  if (j >= a.n / a.bs) {   // no summary for an incomplete block
-    a.ds[(bg * a.nb + j) * D + c] = 0.f;
-    return;
-  }
+  const int64_t njg = (a.nb + kSummJ - 1) / kSummJ;
+  const int slice = blockIdx.x % kSummSlices;
+  const int64_t jg = (blockIdx.x / kSummSlices) % njg;
+  const int64_t bg = blockIdx.x / kSummSlices / njg;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
-  float acc = 0.f;
-  for (int64_t pos = (j + a.window) * a.bs; pos < a.n; ++pos)
-    for (int hh = 0; hh < a.G; ++hh) {
-      const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
-      acc = fmaf(a.dz[(bh * a.n + pos) * a.nb + j], ld<T>(a.q, (bh * a.n + pos) * D + c), acc);
+  const int c = threadIdx.x;
+  const int64_t nfull = a.n / a.bs;            // blocks with a summary
+  const int64_t j0 = jg * kSummJ;
+  if (j0 >= nfull) return;
+  // rows that route over block j0 (the group's first, so the most rows)
+  const int64_t r0 = (j0 + a.window) * a.bs;
+  if (r0 >= a.n) return;
+  const int64_t span = (a.n - r0 + kSummSlices - 1) / kSummSlices;
+  const int64_t p0 = r0 + slice * span, p1 = min(a.n, p0 + span);
+  float acc[kSummJ];
+#pragma unroll
+  for (int jj = 0; jj < kSummJ; ++jj) acc[jj] = 0.f;
+  for (int hh = 0; hh < a.G; ++hh) {
+    const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
+    for (int64_t pos = p0; pos < p1; ++pos) {
+      const float qc = ld<T>(a.q, (bh * a.n + pos) * D + c);
+      const float* dzr = a.dz + (bh * a.n + pos) * a.nb + j0;
+      // block j0 + jj is a candidate of row pos when pos >= (j0 + jj + window) bs;
+      // dz is not written past a row's candidates
+      const int64_t ncand = pos / a.bs - (a.window - 1);
+#pragma unroll
+      for (int jj = 0; jj < kSummJ; ++jj)
+        if (j0 + jj < ncand) acc[jj] = fmaf(dzr[jj], qc, acc[jj]);
     }
-  a.ds[(bg * a.nb + j) * D + c] = acc * a.rs;
+  }
+#pragma unroll
+  for (int jj = 0; jj < kSummJ; ++jj)
+    if (j0 + jj < nfull) atomicAdd(&a.ds[(bg * a.nb + j0 + jj) * D + c], acc[jj] * a.rs);
 }
 
 // ---- block means, and dk += (ds_j W_s^T) / bs over the block ---------------------------------
@@ -444,8 +473,9 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
   const int64_t nbg = (int64_t)a.B * a.Hkv;
   const int64_t nzero = nbg * a.n_qt * a.nb * kBwdTile;
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, st, a.dlogp, nzero);
-  const size_t lds_r = sizeof(float) * 2 * kBwdChunk * D;
-  const size_t lds_k = sizeof(float) * (2 * kBwdTile * D + 3 * kBwdTile);
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3(256), dim3(256), 0, st, a.ds, nbg * a.nb * D);
+  const size_t lds_r = sizeof(T) * 2 * kBwdChunk * D;
+  const size_t lds_k = sizeof(T) * 2 * kBwdTile * D + sizeof(float) * 3 * kBwdTile;
   (void)hipFuncSetAttribute((const void*)bwd_rows_kernel<T, D>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
   (void)hipFuncSetAttribute((const void*)bwd_keys_kernel<T, D>,
@@ -457,7 +487,9 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
                      a);
   hipLaunchKernelGGL((bwd_route_kernel<T, D>), dim3((unsigned)(a.n * nbg)), dim3(kWave),
                      sizeof(float) * a.nb, st, a);
-  hipLaunchKernelGGL((bwd_summ_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
+  const int64_t njg = (a.nb + kSummJ - 1) / kSummJ;
+  hipLaunchKernelGGL((bwd_summ_kernel<T, D>), dim3((unsigned)(njg * kSummSlices * nbg)), dim3(D),
+                     0, st, a);
   hipLaunchKernelGGL((bwd_means_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
   hipLaunchKernelGGL((bwd_ws_kernel<D>), dim3((unsigned)((D * D + 255) / 256)), dim3(256), 0, st,
                      a);
