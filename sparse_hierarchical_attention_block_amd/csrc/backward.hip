@@ -217,6 +217,219 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
   }
 }
 
+// ---- rows, bf16 with MFMA: the forward's layout, three products per chunk -------------------
+// One workgroup per (sequence, KV head, query tile), 2 G waves of 32 queries
+// of one head each, so a staged K/V chunk serves the whole group.  Per chunk
+// and wave (keys are the MFMA rows, as in the forward kernel):
+//   S^T  (64 keys x 32 queries) = K Q^T          P^T = exp2(S^T scale + bias - lse)
+//   dP^T (64 keys x 32 queries) = V dO^T          dS^T = P^T (dP^T - delta)
+//   dQ^T (d x 32 queries)      += K^T dS^T        (dS^T rounded to bf16 as the B operand)
+// K and V are staged row-major, and K once more transposed with the keys of
+// each 16 permuted as the accumulator order of dS^T needs (key 16m+8a+4b+r
+// at column 16m+8b+4a+r).  A first pass over the chunks (S^T only) gives lse.
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void bwd_rows_mfma_kernel(BwdArgs a) {
+  constexpr int KP = D + 8;            // row pitch of K and V (bf16)
+  constexpr int VP = kBwdChunk + 8;    // row pitch of K^T
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBwdChunk * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[kBwdChunk * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 Kt[D * VP];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int l32 = lane % 32, lh = lane / 32;
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
+  const int wpt = (2 * a.G + NT / kWave - 1) / (NT / kWave);   // workgroups per tile
+  const int64_t rank = blockIdx.x / wpt;
+  const int gw = (int)(blockIdx.x % wpt) * (NT / kWave) + wave;   // wave within the tile
+  const int64_t qt = a.n_qt - 1 - rank / nbg;   // heaviest tiles first
+  const int64_t bg = rank % nbg;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int64_t tile = bg * a.n_qt + qt;
+  const int h = g * a.G + gw / 2;
+  const int qloc = 32 * (gw % 2) + l32;
+  const int64_t qpos = qt * kBwdTile + qloc;
+  const bool valid = qpos < a.n;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const __bf16* qrow = (const __bf16*)a.q + (bh * a.n + (valid ? qpos : 0)) * D;
+  const __bf16* dorow = (const __bf16*)a.dO + (bh * a.n + (valid ? qpos : 0)) * D;
+  const __bf16* orow = (const __bf16*)a.o + (bh * a.n + (valid ? qpos : 0)) * D;
+  // Q^T and dO^T operand fragments: column = query l32, k = d in [16 s + 8 lh, +8)
+  bf16x8 qf[D / 16], df[D / 16];
+  float dlt = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < D / 16; ++s2) {
+    u32x4 wq = {0u, 0u, 0u, 0u}, wd = {0u, 0u, 0u, 0u}, wo = {0u, 0u, 0u, 0u};
+    if (valid) {
+      wq = *(const u32x4*)(qrow + 16 * s2 + 8 * lh);
+      wd = *(const u32x4*)(dorow + 16 * s2 + 8 * lh);
+      wo = *(const u32x4*)(orow + 16 * s2 + 8 * lh);
+    }
+    qf[s2] = as_bf16x8(wq);
+    df[s2] = as_bf16x8(wd);
+    const uint32_t dw[4] = {wd.x, wd.y, wd.z, wd.w}, ow[4] = {wo.x, wo.y, wo.z, wo.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dlt += bf16_lo(dw[e]) * bf16_lo(ow[e]) + bf16_hi(dw[e]) * bf16_hi(ow[e]);
+  }
+  dlt = xor_reduce<32>(dlt, DppAdd{});   // the two halves of d
+
+  const BwdWalk w = bwd_walk(a, tile, qt);
+  const int n_chunks = w.n_own + w.count * w.cpb;
+  const uint32_t seq_bytes = (uint32_t)(a.n * (D * 2));
+  const buf_rsrc rk = make_rsrc((const __bf16*)a.k + bg * a.n * D, seq_bytes);
+  const buf_rsrc rv = make_rsrc((const __bf16*)a.v + bg * a.n * D, seq_bytes);
+  auto chunk = [&](int c, int64_t& key0, int64_t& blk) {
+    if (c < w.n_own) {
+      key0 = (w.own_c0 + c) * kBwdChunk;
+      blk = -1;
+    } else {
+      const int e = (c - w.n_own) / w.cpb;
+      blk = a.sel_idx[tile * a.nb + e];
+      key0 = blk * a.bs + ((c - w.n_own) % w.cpb) * kBwdChunk;
+    }
+  };
+  auto stage = [&](int64_t key0, bool full) {
+    for (int e = threadIdx.x; e < kBwdChunk * (D / 8); e += NT) {
+      const int key = e / (D / 8), seg = e % (D / 8);
+      const uint32_t off = (uint32_t)((key0 + key) * (D * 2) + seg * 16);
+      const u32x4 kw = buf_load16(rk, off);
+      *(u32x4*)(Ks + key * KP + seg * 8) = kw;
+      if (full) {
+        *(u32x4*)(Vs + key * KP + seg * 8) = buf_load16(rv, off);
+        const int col = 16 * (key / 16) + 8 * ((key / 4) % 2) + 4 * ((key / 8) % 2) + key % 4;
+        const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const uint32_t lo = kk[e2] & 0xffffu, hi = kk[e2] >> 16;
+          Kt[(seg * 8 + 2 * e2) * VP + col] = __builtin_bit_cast(__bf16, (uint16_t)lo);
+          Kt[(seg * 8 + 2 * e2 + 1) * VP + col] = __builtin_bit_cast(__bf16, (uint16_t)hi);
+        }
+      }
+    }
+  };
+  // S^T of the staged chunk, masked, in log2 units with the bias: st[kt][i]
+  // is query l32, key 32 kt + 8 (i / 4) + 4 lh + i % 4
+  auto scores = [&](int c, float bias2, f32x16 (&st)[2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2)
+        st[kt] = mfma32(as_bf16x8(*(const u32x4*)(Ks + (32 * kt + l32) * KP + 16 * s2 + 8 * lh)),
+                        qf[s2], st[kt]);
+    }
+    const bool diag = c == w.n_own - 1;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * kt + 8 * (i / 4) + 4 * lh + (i % 4);
+        st[kt][i] = (diag && key > qloc) ? -INFINITY : fmaf(st[kt][i], a.scale_log2, bias2);
+      }
+  };
+
+  // pass 1: log2-sum-exp2 per query
+  float m = -INFINITY, l = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    int64_t key0, blk;
+    chunk(c, key0, blk);
+    const float bias2 =
+        blk < 0 ? 0.f : a.sel_logp[(tile * a.nb + blk) * kBwdTile + qloc] * kLog2e;
+    __syncthreads();
+    stage(key0, false);
+    __syncthreads();
+    f32x16 st[2];
+    scores(c, bias2, st);
+    float cm = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cm = fmaxf(cm, st[kt][i]);
+    cm = xor_reduce<32>(cm, DppMax{});
+    if (cm == -INFINITY) continue;
+    const float mn = fmaxf(m, cm);
+    float cs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cs += exp2f(st[kt][i] - mn);
+    cs = xor_reduce<32>(cs, DppAdd{});
+    l = l * exp2f(m - mn) + cs;
+    m = mn;
+  }
+  const float lse = m + log2f(l);
+  if (valid && lh == 0) {
+    a.lse2[bh * a.n + qpos] = lse;
+    a.delta[bh * a.n + qpos] = dlt;
+  }
+
+  // pass 2
+  f32x16 dqa[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqa[dt][i] = 0.f;
+  float bacc = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    int64_t key0, blk;
+    chunk(c, key0, blk);
+    const float bias2 =
+        blk < 0 ? 0.f : a.sel_logp[(tile * a.nb + blk) * kBwdTile + qloc] * kLog2e;
+    __syncthreads();
+    stage(key0, true);
+    __syncthreads();
+    f32x16 st[2], dp[2];
+    scores(c, bias2, st);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp[kt][i] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2)
+        dp[kt] = mfma32(as_bf16x8(*(const u32x4*)(Vs + (32 * kt + l32) * KP + 16 * s2 + 8 * lh)),
+                        df[s2], dp[kt]);
+    }
+    // dS^T, its column sums (the bias gradient), and the bf16 B operands
+    float csum = 0.f;
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = ks / 2, i0 = 8 * (ks % 2);
+      float dv8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = exp2f(st[kt][i0 + e] - lse);   // 0 where masked
+        dv8[e] = pv * (dp[kt][i0 + e] - dlt);
+        csum += dv8[e];
+      }
+      const u32x4 pw = {pack_bf16(dv8[0], dv8[1]), pack_bf16(dv8[2], dv8[3]),
+                        pack_bf16(dv8[4], dv8[5]), pack_bf16(dv8[6], dv8[7])};
+      dsf[ks] = as_bf16x8(pw);
+    }
+    csum = xor_reduce<32>(csum, DppAdd{});
+    if (blk >= 0) bacc += csum;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        dqa[dt] = mfma32(as_bf16x8(*(const u32x4*)(Kt + (32 * dt + l32) * VP + 16 * ks + 8 * lh)),
+                         dsf[ks], dqa[dt]);
+    if (blk >= 0 && (c - w.n_own) % w.cpb == w.cpb - 1) {
+      if (valid && lh == 0 && bias2 != -INFINITY)
+        atomicAdd(&a.dlogp[(tile * a.nb + blk) * kBwdTile + qloc], a.sigma * bacc);
+      bacc = 0.f;
+    }
+  }
+  // dqa[dt][i] = dQ[query l32][32 dt + 8 (i / 4) + 4 lh + i % 4]
+  if (valid) {
+    float* dqr = a.dq + (bh * a.n + qpos) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dqr[32 * dt + 8 * (i / 4) + 4 * lh + (i % 4)] = dqa[dt][i] * a.rs;
+  }
+}
+
 // ---- keys: dk (fine part), dv --------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
@@ -480,8 +693,18 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
   (void)hipFuncSetAttribute((const void*)bwd_keys_kernel<T, D>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_k);
-  hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3((unsigned)(a.n_qt * a.B * a.H)), dim3(256),
-                     lds_r, st, a);
+  if constexpr (sizeof(T) == 2) {
+    // 2 G waves of 32 queries per tile, at most 8 per workgroup
+    const int waves = 2 * a.G, wpt = (waves + 7) / 8;
+    const dim3 grid((unsigned)(a.n_qt * nbg * wpt));
+    if (waves == 2) hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 128>), grid, dim3(128), 0, st, a);
+    else if (waves == 4)
+      hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 256>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 512>), grid, dim3(512), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3((unsigned)(a.n_qt * a.B * a.H)), dim3(256),
+                       lds_r, st, a);
+  }
   const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
   hipLaunchKernelGGL((bwd_keys_kernel<T, D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_k, st,
                      a);
