@@ -199,11 +199,13 @@ def prefill_bench(args, torch, dash, W):
         # dQ, dK, dV over the walked chunks = 2.5 x the forward's two
         bwd_flops = 2.5 * att_flops
         bt = bwd_flops / (t_bwd * 1e-3) / 1e12
+        # bf16 inputs: the attention products run on bf16 MFMA; float32: vector FMAs
+        bound, peak = ("mfma", PEAK_BF16_TFLOPS) if w.dtype == "bf16" else \
+            ("alu", PEAK_FP32_TFLOPS)
         res["backward"] = {"ms": round(t_bwd, 4), "attention_gflop": round(bwd_flops / 1e9, 2),
-                           "roofline": {"bound": "alu", "achieved": round(bt, 2),
-                                        "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                                        "frac": round(bt / PEAK_FP32_TFLOPS, 4),
-                                        "scope": "float32 FMA kernels, attention products only"}}
+                           "roofline": {"bound": bound, "achieved": round(bt, 2), "peak": peak,
+                                        "unit": "TFLOP/s", "frac": round(bt / peak, 4),
+                                        "scope": "whole backward, attention products counted"}}
     if args.dense:
         rbd = dash.RouteBuffers(sizes, dev)
         rbd.sel_count.copy_(torch.from_numpy(np.broadcast_to(cand, (B * Hkv, n_qt)).astype(

@@ -527,10 +527,179 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
   }
 }
 
+// ---- keys, bf16 with MFMA ------------------------------------------------------------------
+// One workgroup of 4 waves per 64-key chunk of a (sequence, KV head); wave w
+// owns keys 32 (w / 2) .. +32 and half (w % 2) of the d columns of dK and dV.
+// For every (tile, head) that attends the chunk, q and dO of the tile are
+// staged row-major and transposed (queries of each 16 permuted as the
+// accumulator order of P and dS needs), then per 32-query half:
+//   S  (32 queries x 32 keys) = Q K^T,  dP = dO V^T      (queries are MFMA rows)
+//   P = exp2(S scale + bias - lse),  dS = P (dP - delta)
+//   dV^T (d x keys) += dO^T P,  dK^T += Q^T dS            (P, dS as bf16 B operands)
+// The wave's K and V fragments stay in registers for the whole walk.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
+  constexpr int RP = D + 8;            // row pitch of the staged q / dO rows
+  constexpr int TP = kBwdTile + 8;     // row pitch of the transposed ones
+  constexpr int NDT = D / 64;          // d tiles of 32 per wave
+  extern __shared__ __attribute__((aligned(16))) char lds_km[];
+  __bf16* Qr = (__bf16*)lds_km;
+  __bf16* Or = Qr + kBwdTile * RP;
+  __bf16* Qt = Or + kBwdTile * RP;
+  __bf16* Ot = Qt + D * TP;
+  float* rowl = (float*)(Ot + D * TP);
+  float* rowd = rowl + kBwdTile;
+  float* rowb = rowd + kBwdTile;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int l32 = lane % 32, lh = lane / 32;
+  const int kt = wave / 2, dh = wave % 2;
+  const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
+  const int64_t ch = blockIdx.x % nch;
+  const int64_t bg = blockIdx.x / nch;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int64_t kpos = ch * kBwdChunk + 32 * kt + l32;   // this lane's key
+  const bool kvalid = kpos < a.n;
+  // K^T / V^T operand fragments of the lane's key: k = d in [16 s + 8 lh, +8)
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const __bf16* kr = (const __bf16*)a.k + (bg * a.n + (kvalid ? kpos : 0)) * D;
+    const __bf16* vr = (const __bf16*)a.v + (bg * a.n + (kvalid ? kpos : 0)) * D;
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
+      u32x4 wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
+      if (kvalid) {
+        wk = *(const u32x4*)(kr + 16 * s2 + 8 * lh);
+        wv = *(const u32x4*)(vr + 16 * s2 + 8 * lh);
+      }
+      kf[s2] = as_bf16x8(wk);
+      vf[s2] = as_bf16x8(wv);
+    }
+  }
+  f32x16 dka[NDT], dva[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dka[t][i] = dva[t][i] = 0.f;
+
+  const int64_t blk = (ch * kBwdChunk) / a.bs;
+  for (int64_t qt = ch; qt < a.n_qt; ++qt) {
+    const int64_t tile = bg * a.n_qt + qt;
+    const int64_t own = (qt * kBwdTile) / a.bs;
+    const int64_t b0 = own - (a.window - 1) > 0 ? own - (a.window - 1) : 0;
+    const bool branch = blk >= b0 && blk <= own;
+    bool listed = false;
+    if (!branch) {
+      const int cnt = a.sel_count[tile];
+      const int32_t* lst = a.sel_idx + tile * a.nb;
+      int lo = 0, hi = cnt;
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (lst[mid] < blk) lo = mid + 1; else hi = mid;
+      }
+      listed = lo < cnt && lst[lo] == blk;
+    }
+    if (!branch && !listed) continue;
+    for (int hh = 0; hh < a.G; ++hh) {
+      const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
+      const __bf16* qb = (const __bf16*)a.q + (bh * a.n + qt * kBwdTile) * D;
+      const __bf16* ob = (const __bf16*)a.dO + (bh * a.n + qt * kBwdTile) * D;
+      __syncthreads();
+      for (int e = threadIdx.x; e < kBwdTile * (D / 8); e += 256) {
+        const int r = e / (D / 8), seg = e % (D / 8);
+        const bool in = qt * kBwdTile + r < a.n;
+        u32x4 wq = {0u, 0u, 0u, 0u}, wo = {0u, 0u, 0u, 0u};
+        if (in) {
+          wq = *(const u32x4*)(qb + r * D + seg * 8);
+          wo = *(const u32x4*)(ob + r * D + seg * 8);
+        }
+        *(u32x4*)(Qr + r * RP + seg * 8) = wq;
+        *(u32x4*)(Or + r * RP + seg * 8) = wo;
+        const int col = 16 * (r / 16) + 8 * ((r / 4) % 2) + 4 * ((r / 8) % 2) + r % 4;
+        const uint32_t qq[4] = {wq.x, wq.y, wq.z, wq.w}, oo[4] = {wo.x, wo.y, wo.z, wo.w};
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          Qt[(seg * 8 + 2 * e2) * TP + col] = __builtin_bit_cast(__bf16, (uint16_t)(qq[e2] & 0xffffu));
+          Qt[(seg * 8 + 2 * e2 + 1) * TP + col] = __builtin_bit_cast(__bf16, (uint16_t)(qq[e2] >> 16));
+          Ot[(seg * 8 + 2 * e2) * TP + col] = __builtin_bit_cast(__bf16, (uint16_t)(oo[e2] & 0xffffu));
+          Ot[(seg * 8 + 2 * e2 + 1) * TP + col] = __builtin_bit_cast(__bf16, (uint16_t)(oo[e2] >> 16));
+        }
+      }
+      for (int r = threadIdx.x; r < kBwdTile; r += 256) {
+        const int64_t pos = qt * kBwdTile + r;
+        const bool in = pos < a.n;
+        rowl[r] = in ? a.lse2[bh * a.n + pos] : 0.f;
+        rowd[r] = in ? a.delta[bh * a.n + pos] : 0.f;
+        rowb[r] = !in ? -INFINITY
+                      : (branch ? 0.f : a.sel_logp[(tile * a.nb + blk) * kBwdTile + r] * kLog2e);
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int qh = 0; qh < 2; ++qh) {
+        // S and dP: queries 32 qh + row, keys of this wave's tile (lane l32)
+        f32x16 sv, dpv;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[i] = dpv[i] = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < D / 16; ++s2) {
+          const int roff = (32 * qh + l32) * RP + 16 * s2 + 8 * lh;
+          sv = mfma32(as_bf16x8(*(const u32x4*)(Qr + roff)), kf[s2], sv);
+          dpv = mfma32(as_bf16x8(*(const u32x4*)(Or + roff)), vf[s2], dpv);
+        }
+        // element i: query 32 qh + 8 (i / 4) + 4 lh + i % 4, key kpos
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          float pv[8], dv8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = 8 * k2 + e;
+            const int r = 32 * qh + 8 * (i / 4) + 4 * lh + (i % 4);
+            const int64_t pos = qt * kBwdTile + r;
+            float p = exp2f(fmaf(sv[i], a.scale_log2, rowb[r]) - rowl[r]);
+            if (!kvalid || (branch && kpos > pos)) p = 0.f;
+            pv[e] = p;
+            dv8[e] = p * (dpv[i] - rowd[r]);
+          }
+          pf[k2] = as_bf16x8((u32x4){pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
+                                     pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])});
+          dsf[k2] = as_bf16x8((u32x4){pack_bf16(dv8[0], dv8[1]), pack_bf16(dv8[2], dv8[3]),
+                                      pack_bf16(dv8[4], dv8[5]), pack_bf16(dv8[6], dv8[7])});
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS over the two 16-query k-steps
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) {
+            const int dt = NDT * dh + t;
+            const int toff = (32 * dt + l32) * TP + 16 * (2 * qh + k2) + 8 * lh;
+            dva[t] = mfma32(as_bf16x8(*(const u32x4*)(Ot + toff)), pf[k2], dva[t]);
+            dka[t] = mfma32(as_bf16x8(*(const u32x4*)(Qt + toff)), dsf[k2], dka[t]);
+          }
+      }
+    }
+  }
+  // dka[t][i] = dK^T[d = 32 dt + 8 (i / 4) + 4 lh + i % 4][key kpos]
+  if (kvalid) {
+    float* dkr = a.dk + (bg * a.n + kpos) * D;
+    float* dvr = a.dv + (bg * a.n + kpos) * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int dcol = 32 * (NDT * dh + t) + 8 * (i / 4) + 4 * lh + (i % 4);
+        dkr[dcol] = dka[t][i] * a.rs;
+        dvr[dcol] = dva[t][i];
+      }
+  }
+}
+
 // ---- route: dzbar and the coarse part of dq (one wave per position and KV head) ------------
+// The group's G query rows sit in LDS; each lane takes candidates j, lane + 64,
+// ... and reads summary row j once for all G heads (x, then dzbar), and the
+// coarse dq reads every summary column once for all G heads.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void bwd_route_kernel(BwdArgs a) {
-  extern __shared__ float dzs[];   // [nb]
+  extern __shared__ float route_lds[];   // q rows [G][D], then u / dzbar [G][nb]
   const int64_t pos = blockIdx.x % a.n;
   const int64_t bg = blockIdx.x / a.n;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
@@ -538,47 +707,75 @@ __global__ __launch_bounds__(64) void bwd_route_kernel(BwdArgs a) {
   const int64_t own = pos / a.bs;
   const int ncand = (int)(own - (a.window - 1) > 0 ? own - (a.window - 1) : 0);
   if (ncand == 0) return;
+  const int G = a.G;
+  float* qs = route_lds;
+  float* us = route_lds + G * D;
   const int64_t qt = pos / kBwdTile, tile = bg * a.n_qt + qt;
   const int r = (int)(pos % kBwdTile);
+  const int64_t bh0 = (int64_t)b * a.H + g * G;
+  for (int e = lane; e < G * D; e += kWave)
+    qs[e] = ld<T>(a.q, ((bh0 + e / D) * a.n + pos) * D + e % D);
+  __syncthreads();
   const float* srow = a.summ + bg * a.summ_blocks * D;
-  for (int hh = 0; hh < a.G; ++hh) {
-    const int h = g * a.G + hh;
-    const int64_t bh = (int64_t)b * a.H + h;
-    const float tau = a.tau[bh * a.n + pos];
-    const T* qrow = (const T*)a.q + (bh * a.n + pos) * D;
-    float su = 0.f, sud = 0.f;
-    for (int j = lane; j < ncand; j += kWave) {
-      float x = 0.f;
-      for (int c = 0; c < D; ++c) x = fmaf(to_f32(qrow[c]), srow[j * D + c], x);
-      x *= a.xscale;
-      const float y = x - tau;
+  float su[8], sud[8];
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh) su[hh] = sud[hh] = 0.f;
+  for (int j = lane; j < ncand; j += kWave) {
+    float x[8];
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) x[hh] = 0.f;
+    for (int c = 0; c < D; ++c) {
+      const float sc = srow[j * D + c];
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh)
+        if (hh < G) x[hh] = fmaf(qs[hh * D + c], sc, x[hh]);
+    }
+    const int64_t li = (tile * a.nb + j) * kBwdTile + r;
+    const float lp = a.sel_logp[li];
+    float dp = 0.f;
+    if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)G;
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+      if (hh >= G) break;
+      const float y = x[hh] * a.xscale - a.tau[(bh0 + hh) * a.n + pos];
       const float u = y > 0.f ? (a.ue == 0.f ? 1.f : powf(y, a.ue)) : 0.f;
-      const int64_t li = (tile * a.nb + j) * kBwdTile + r;
-      const float lp = a.sel_logp[li];
-      float dp = 0.f;
-      if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)a.G;
-      su += u;
-      sud = fmaf(u, dp, sud);
-      dzs[j] = u;           // u for now, dz below
-      a.dz[(bh * a.n + pos) * a.nb + j] = dp;
+      su[hh] += u;
+      sud[hh] = fmaf(u, dp, sud[hh]);
+      us[hh * a.nb + j] = u;
     }
-    su = wave_sum(su);
-    sud = wave_sum(sud);
-    const float corr = su > 0.f ? sud / su : 0.f;
-    for (int j = lane; j < ncand; j += kWave) {
-      float* dzp = a.dz + (bh * a.n + pos) * a.nb + j;
-      const float u = dzs[j];
-      const float dz = a.gamma * u * (*dzp - corr);
-      *dzp = dz;
-      dzs[j] = dz;
+    a.dz[((bh0) * a.n + pos) * a.nb + j] = dp;   // dp for now, shared by the heads
+  }
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh) {
+    if (hh >= G) break;
+    su[hh] = wave_sum(su[hh]);
+    sud[hh] = wave_sum(sud[hh]);
+  }
+  for (int j = lane; j < ncand; j += kWave) {
+    const float dp = a.dz[((bh0) * a.n + pos) * a.nb + j];
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+      if (hh >= G) break;
+      const float corr = su[hh] > 0.f ? sud[hh] / su[hh] : 0.f;
+      const float dz = a.gamma * us[hh * a.nb + j] * (dp - corr);
+      us[hh * a.nb + j] = dz;
+      a.dz[((bh0 + hh) * a.n + pos) * a.nb + j] = dz;
     }
-    __syncthreads();
-    for (int c = lane; c < D; c += kWave) {
-      float acc = 0.f;
-      for (int j = 0; j < ncand; ++j) acc = fmaf(dzs[j], srow[j * D + c], acc);
-      a.dq[(bh * a.n + pos) * D + c] += acc * a.rs;
+  }
+  __syncthreads();
+  for (int c = lane; c < D; c += kWave) {
+    float acc[8];
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) acc[hh] = 0.f;
+    for (int j = 0; j < ncand; ++j) {
+      const float sc = srow[j * D + c];
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh)
+        if (hh < G) acc[hh] = fmaf(us[hh * a.nb + j], sc, acc[hh]);
     }
-    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh)
+      if (hh < G) a.dq[((bh0 + hh) * a.n + pos) * D + c] += acc[hh] * a.rs;
   }
 }
 
@@ -610,6 +807,7 @@ __global__ __launch_bounds__(D) void bwd_summ_kernel(BwdArgs a) {
   for (int jj = 0; jj < kSummJ; ++jj) acc[jj] = 0.f;
   for (int hh = 0; hh < a.G; ++hh) {
     const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
+#pragma unroll 4
     for (int64_t pos = p0; pos < p1; ++pos) {
       const float qc = ld<T>(a.q, (bh * a.n + pos) * D + c);
       const float* dzr = a.dz + (bh * a.n + pos) * a.nb + j0;
@@ -706,10 +904,23 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
                        lds_r, st, a);
   }
   const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
-  hipLaunchKernelGGL((bwd_keys_kernel<T, D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_k, st,
-                     a);
-  hipLaunchKernelGGL((bwd_route_kernel<T, D>), dim3((unsigned)(a.n * nbg)), dim3(kWave),
-                     sizeof(float) * a.nb, st, a);
+  if constexpr (sizeof(T) == 2) {
+    const size_t lds_km = sizeof(__bf16) * (2 * kBwdTile * (D + 8) + 2 * D * (kBwdTile + 8)) +
+                          sizeof(float) * 3 * kBwdTile;
+    (void)hipFuncSetAttribute((const void*)bwd_keys_mfma_kernel<D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_km);
+    hipLaunchKernelGGL((bwd_keys_mfma_kernel<D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_km,
+                       st, a);
+  } else {
+    hipLaunchKernelGGL((bwd_keys_kernel<T, D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_k,
+                       st, a);
+  }
+  const size_t lds_rt = sizeof(float) * a.G * (D + a.nb);
+  if (lds_rt > 64 * 1024)
+    (void)hipFuncSetAttribute((const void*)bwd_route_kernel<T, D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_rt);
+  hipLaunchKernelGGL((bwd_route_kernel<T, D>), dim3((unsigned)(a.n * nbg)), dim3(kWave), lds_rt,
+                     st, a);
   const int64_t njg = (a.nb + kSummJ - 1) / kSummJ;
   hipLaunchKernelGGL((bwd_summ_kernel<T, D>), dim3((unsigned)(njg * kSummSlices * nbg)), dim3(D),
                      0, st, a);
