@@ -18,7 +18,7 @@
 //           the entmax Jacobian with u = (x - tau)_+^((2-alpha)/(alpha-1)):
 //           dzbar = gamma (u dp - u (u.dp) / sum u); dq += dzbar . s / sqrt(d)
 //   summ    ds_j = sum over later rows and heads of dzbar_j q / sqrt(d),
-//           eight blocks at a time over slices of the rows
+//           32 blocks at a time over slices of the rows
 //   means   dk of block j += (ds_j W_s^T) / bs; block means m_j
 //   w_s     dW_s = sum_j m_j^T ds_j
 // Every product is plain float32 FMAs (no MFMA); a row or key is spread over
@@ -784,8 +784,8 @@ __global__ __launch_bounds__(64) void bwd_route_kernel(BwdArgs a) {
 // rows); thread c accumulates column c of the group's kSummJ summaries (each
 // q element read once feeds kSummJ FMAs) and adds them into ds, which starts
 // at zero.
-constexpr int kSummJ = 8;
-constexpr int kSummSlices = 16;
+constexpr int kSummJ = 32;
+constexpr int kSummSlices = 64;
 template <typename T, int D>
 __global__ __launch_bounds__(D) void bwd_summ_kernel(BwdArgs a) {
   const int64_t njg = (a.nb + kSummJ - 1) / kSummJ;
