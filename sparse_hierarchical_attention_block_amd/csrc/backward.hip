@@ -91,6 +91,28 @@ __device__ __forceinline__ BwdWalk bwd_walk(const BwdArgs& a, int64_t tile, int6
   return w;
 }
 
+// Does tile qt of pair bg attend block blk?  0: no, 1: through its
+// near-diagonal branch, 2: through its list (binary search in the ascending
+// list).
+__device__ __forceinline__ int tile_attends(const BwdArgs& a, int64_t bg, int64_t qt,
+                                            int64_t blk) {
+  const int64_t tile = bg * a.n_qt + qt;
+  const int64_t own = (qt * kBwdTile) / a.bs;
+  const int64_t b0 = own - (a.window - 1) > 0 ? own - (a.window - 1) : 0;
+  if (blk >= b0 && blk <= own) return 1;
+  const int cnt = a.sel_count[tile];
+  const int32_t* lst = a.sel_idx + tile * a.nb;
+  int lo = 0, hi = cnt;
+  while (lo < hi) {
+    const int mid = (lo + hi) / 2;
+    if (lst[mid] < blk) lo = mid + 1; else hi = mid;
+  }
+  return lo < cnt && lst[lo] == blk ? 2 : 0;
+}
+// The tiles that attend a chunk are found 256 at a time, one per thread (the
+// binary searches run side by side), into an LDS flag array.
+constexpr int kFlagTiles = 256;
+
 // ---- rows: lse, delta, dq (fine part), bias gradients ---------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
@@ -458,24 +480,19 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
     dvv[c] = 0.f;
   }
   const int64_t blk = (ch * kBwdChunk) / a.bs;
-  for (int64_t qt = ch; qt < a.n_qt; ++qt) {
+  __shared__ int8_t flags[kFlagTiles];
+  for (int64_t q0 = ch; q0 < a.n_qt; q0 += kFlagTiles) {
+  __syncthreads();
+  if (threadIdx.x < kFlagTiles)
+    flags[threadIdx.x] =
+        q0 + threadIdx.x < a.n_qt ? (int8_t)tile_attends(a, bg, q0 + threadIdx.x, blk) : 0;
+  __syncthreads();
+  const int nq = (int)min((int64_t)kFlagTiles, a.n_qt - q0);
+  for (int tq = 0; tq < nq; ++tq) {
+    if (!flags[tq]) continue;
+    const int64_t qt = q0 + tq;
     const int64_t tile = bg * a.n_qt + qt;
-    const int64_t own = (qt * kBwdTile) / a.bs;
-    const int64_t b0 = own - (a.window - 1) > 0 ? own - (a.window - 1) : 0;
-    bool branch = blk >= b0 && blk <= own;
-    bool listed = false;
-    if (!branch) {
-      // the tile's ascending list: binary search for blk
-      const int cnt = a.sel_count[tile];
-      const int32_t* lst = a.sel_idx + tile * a.nb;
-      int lo = 0, hi = cnt;
-      while (lo < hi) {
-        const int mid = (lo + hi) / 2;
-        if (lst[mid] < blk) lo = mid + 1; else hi = mid;
-      }
-      listed = lo < cnt && lst[lo] == blk;
-    }
-    if (!branch && !listed) continue;
+    const bool branch = flags[tq] == 1;
     for (int hh = 0; hh < a.G; ++hh) {
       const int h = g * a.G + hh;
       const int64_t bh = (int64_t)b * a.H + h;
@@ -517,6 +534,7 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
         }
       }
     }
+  }
   }
   if (valid) {
 #pragma unroll
@@ -582,23 +600,19 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) dka[t][i] = dva[t][i] = 0.f;
 
   const int64_t blk = (ch * kBwdChunk) / a.bs;
-  for (int64_t qt = ch; qt < a.n_qt; ++qt) {
+  __shared__ int8_t flags[kFlagTiles];
+  for (int64_t q0 = ch; q0 < a.n_qt; q0 += kFlagTiles) {
+  __syncthreads();
+  if (threadIdx.x < kFlagTiles)
+    flags[threadIdx.x] =
+        q0 + threadIdx.x < a.n_qt ? (int8_t)tile_attends(a, bg, q0 + threadIdx.x, blk) : 0;
+  __syncthreads();
+  const int nq = (int)min((int64_t)kFlagTiles, a.n_qt - q0);
+  for (int tq = 0; tq < nq; ++tq) {
+    if (!flags[tq]) continue;
+    const int64_t qt = q0 + tq;
     const int64_t tile = bg * a.n_qt + qt;
-    const int64_t own = (qt * kBwdTile) / a.bs;
-    const int64_t b0 = own - (a.window - 1) > 0 ? own - (a.window - 1) : 0;
-    const bool branch = blk >= b0 && blk <= own;
-    bool listed = false;
-    if (!branch) {
-      const int cnt = a.sel_count[tile];
-      const int32_t* lst = a.sel_idx + tile * a.nb;
-      int lo = 0, hi = cnt;
-      while (lo < hi) {
-        const int mid = (lo + hi) / 2;
-        if (lst[mid] < blk) lo = mid + 1; else hi = mid;
-      }
-      listed = lo < cnt && lst[lo] == blk;
-    }
-    if (!branch && !listed) continue;
+    const bool branch = flags[tq] == 1;
     for (int hh = 0; hh < a.G; ++hh) {
       const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
       const __bf16* qb = (const __bf16*)a.q + (bh * a.n + qt * kBwdTile) * D;
@@ -678,6 +692,7 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
       }
     }
   }
+  }
   // dka[t][i] = dK^T[d = 32 dt + 8 (i / 4) + 4 lh + i % 4][key kpos]
   if (kvalid) {
     float* dkr = a.dk + (bg * a.n + kpos) * D;
@@ -724,6 +739,7 @@ __global__ __launch_bounds__(64) void bwd_route_kernel(BwdArgs a) {
     float x[8];
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) x[hh] = 0.f;
+#pragma unroll 8
     for (int c = 0; c < D; ++c) {
       const float sc = srow[j * D + c];
 #pragma unroll
@@ -767,6 +783,7 @@ __global__ __launch_bounds__(64) void bwd_route_kernel(BwdArgs a) {
     float acc[8];
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) acc[hh] = 0.f;
+#pragma unroll 8
     for (int j = 0; j < ncand; ++j) {
       const float sc = srow[j * D + c];
 #pragma unroll
