@@ -50,6 +50,8 @@ PREFILL_CASES = {
     "sigma2_window4_bs128": W.get("prefill_64k").replace(seq_len=2048, gamma=2.0, sigma=2.0,
                                                          window=4),
     "window_covers_all_bf16": tiny(seq_len=700, dtype="bf16", gamma=8.0, window=11),
+    # 64 < candidates <= 128 in the last tiles, full oracle parity
+    "cand74_gqa4": W.get("prefill_8k").replace(seq_len=4800, n_heads=8, n_kv_heads=2),
 }
 
 
