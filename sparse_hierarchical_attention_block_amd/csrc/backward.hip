@@ -313,19 +313,28 @@ __global__ __launch_bounds__(NT) void bwd_rows_mfma_kernel(BwdArgs a) {
     for (int e = threadIdx.x; e < kBwdChunk * (D / 8); e += NT) {
       const int key = e / (D / 8), seg = e % (D / 8);
       const uint32_t off = (uint32_t)((key0 + key) * (D * 2) + seg * 16);
-      const u32x4 kw = buf_load16(rk, off);
-      *(u32x4*)(Ks + key * KP + seg * 8) = kw;
-      if (full) {
-        *(u32x4*)(Vs + key * KP + seg * 8) = buf_load16(rv, off);
-        const int col = 16 * (key / 16) + 8 * ((key / 4) % 2) + 4 * ((key / 8) % 2) + key % 4;
-        const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+      *(u32x4*)(Ks + key * KP + seg * 8) = buf_load16(rk, off);
+      if (full) *(u32x4*)(Vs + key * KP + seg * 8) = buf_load16(rv, off);
+    }
+    if (!full) return;
+    // K^T in 4 x 4 blocks (4 keys x 4 d): four 8-byte loads, register
+    // transposes, four 8-byte stores; keys 16 m + 8 a + 4 b + [0, 4) go to
+    // columns 16 m + 8 b + 4 a + [0, 4)
+    for (int e = threadIdx.x; e < (kBwdChunk / 4) * (D / 4); e += NT) {
+      const int db = e % (D / 4), kb4 = e / (D / 4);
+      u32x2 in[4];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const uint32_t lo = kk[e2] & 0xffffu, hi = kk[e2] >> 16;
-          Kt[(seg * 8 + 2 * e2) * VP + col] = __builtin_bit_cast(__bf16, (uint16_t)lo);
-          Kt[(seg * 8 + 2 * e2 + 1) * VP + col] = __builtin_bit_cast(__bf16, (uint16_t)hi);
-        }
-      }
+      for (int rr = 0; rr < 4; ++rr)
+        in[rr] = buf_load8(rk, (uint32_t)((key0 + 4 * kb4 + rr) * (D * 2) + db * 8));
+      const int col = 16 * (kb4 / 4) + 8 * (kb4 % 2) + 4 * ((kb4 / 2) % 2);
+      *(u32x2*)(Kt + (4 * db + 0) * VP + col) = (u32x2){pack_lo(in[0].x, in[1].x),
+                                                        pack_lo(in[2].x, in[3].x)};
+      *(u32x2*)(Kt + (4 * db + 1) * VP + col) = (u32x2){pack_hi(in[0].x, in[1].x),
+                                                        pack_hi(in[2].x, in[3].x)};
+      *(u32x2*)(Kt + (4 * db + 2) * VP + col) = (u32x2){pack_lo(in[0].y, in[1].y),
+                                                        pack_lo(in[2].y, in[3].y)};
+      *(u32x2*)(Kt + (4 * db + 3) * VP + col) = (u32x2){pack_hi(in[0].y, in[1].y),
+                                                        pack_hi(in[2].y, in[3].y)};
     }
   };
   // S^T of the staged chunk, masked, in log2 units with the bias: st[kt][i]
@@ -628,15 +637,32 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
         }
         *(u32x4*)(Qr + r * RP + seg * 8) = wq;
         *(u32x4*)(Or + r * RP + seg * 8) = wo;
-        const int col = 16 * (r / 16) + 8 * ((r / 4) % 2) + 4 * ((r / 8) % 2) + r % 4;
-        const uint32_t qq[4] = {wq.x, wq.y, wq.z, wq.w}, oo[4] = {wo.x, wo.y, wo.z, wo.w};
+      }
+      // transposed copies in 4 x 4 blocks (4 queries x 4 d): four 8-byte
+      // loads, register transposes, four 8-byte stores; queries 16 m + 8 a +
+      // 4 b + [0, 4) go to columns 16 m + 8 b + 4 a + [0, 4)
+      for (int e = threadIdx.x; e < 2 * (kBwdTile / 4) * (D / 4); e += 256) {
+        const int which = e / ((kBwdTile / 4) * (D / 4));
+        const int e1 = e % ((kBwdTile / 4) * (D / 4));
+        const int db = e1 % (D / 4), qb4 = e1 / (D / 4);
+        const __bf16* src = which ? ob : qb;
+        __bf16* dst = which ? Ot : Qt;
+        u32x2 in[4];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          Qt[(seg * 8 + 2 * e2) * TP + col] = __builtin_bit_cast(__bf16, (uint16_t)(qq[e2] & 0xffffu));
-          Qt[(seg * 8 + 2 * e2 + 1) * TP + col] = __builtin_bit_cast(__bf16, (uint16_t)(qq[e2] >> 16));
-          Ot[(seg * 8 + 2 * e2) * TP + col] = __builtin_bit_cast(__bf16, (uint16_t)(oo[e2] & 0xffffu));
-          Ot[(seg * 8 + 2 * e2 + 1) * TP + col] = __builtin_bit_cast(__bf16, (uint16_t)(oo[e2] >> 16));
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 4 * qb4 + rr;
+          in[rr] = qt * kBwdTile + r < a.n ? *(const u32x2*)(src + r * D + 4 * db)
+                                           : (u32x2){0u, 0u};
         }
+        const int col = 16 * (qb4 / 4) + 8 * (qb4 % 2) + 4 * ((qb4 / 2) % 2);
+        *(u32x2*)(dst + (4 * db + 0) * TP + col) = (u32x2){pack_lo(in[0].x, in[1].x),
+                                                           pack_lo(in[2].x, in[3].x)};
+        *(u32x2*)(dst + (4 * db + 1) * TP + col) = (u32x2){pack_hi(in[0].x, in[1].x),
+                                                           pack_hi(in[2].x, in[3].x)};
+        *(u32x2*)(dst + (4 * db + 2) * TP + col) = (u32x2){pack_lo(in[0].y, in[1].y),
+                                                           pack_lo(in[2].y, in[3].y)};
+        *(u32x2*)(dst + (4 * db + 3) * TP + col) = (u32x2){pack_hi(in[0].y, in[1].y),
+                                                           pack_hi(in[2].y, in[3].y)};
       }
       for (int r = threadIdx.x; r < kBwdTile; r += 256) {
         const int64_t pos = qt * kBwdTile + r;
