@@ -848,6 +848,8 @@ __global__ __launch_bounds__(D) void bwd_summ_kernel(BwdArgs a) {
   float acc[kSummJ];
 #pragma unroll
   for (int jj = 0; jj < kSummJ; ++jj) acc[jj] = 0.f;
+  // 16-byte loads of the dz rows when the group lies inside every row
+  const bool vec = a.nb % 4 == 0 && j0 + kSummJ <= a.nb;
   for (int hh = 0; hh < a.G; ++hh) {
     const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
 #pragma unroll 4
@@ -857,9 +859,24 @@ __global__ __launch_bounds__(D) void bwd_summ_kernel(BwdArgs a) {
       // block j0 + jj is a candidate of row pos when pos >= (j0 + jj + window) bs;
       // dz is not written past a row's candidates
       const int64_t ncand = pos / a.bs - (a.window - 1);
+      if (vec) {
+        // eight 16-byte loads; entries past the row's candidates were never
+        // written and are dropped by the select
 #pragma unroll
-      for (int jj = 0; jj < kSummJ; ++jj)
-        if (j0 + jj < ncand) acc[jj] = fmaf(dzr[jj], qc, acc[jj]);
+        for (int k4 = 0; k4 < kSummJ / 4; ++k4) {
+          const float4 v = ((const float4*)dzr)[k4];
+          const float ve[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jj = 4 * k4 + e;
+            acc[jj] = fmaf(j0 + jj < ncand ? ve[e] : 0.f, qc, acc[jj]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < kSummJ; ++jj)
+          if (j0 + jj < ncand) acc[jj] = fmaf(dzr[jj], qc, acc[jj]);
+      }
     }
   }
 #pragma unroll
