@@ -945,12 +945,6 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
   const int64_t nzero = nbg * a.n_qt * a.nb * kBwdTile;
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, st, a.dlogp, nzero);
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(256), dim3(256), 0, st, a.ds, nbg * a.nb * D);
-  const size_t lds_r = sizeof(T) * 2 * kBwdChunk * D;
-  const size_t lds_k = sizeof(T) * 2 * kBwdTile * D + sizeof(float) * 3 * kBwdTile;
-  (void)hipFuncSetAttribute((const void*)bwd_rows_kernel<T, D>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
-  (void)hipFuncSetAttribute((const void*)bwd_keys_kernel<T, D>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_k);
   if constexpr (sizeof(T) == 2) {
     // 2 G waves of 32 queries per tile, at most 8 per workgroup
     const int waves = 2 * a.G, wpt = (waves + 7) / 8;
@@ -960,6 +954,9 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 256>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 512>), grid, dim3(512), 0, st, a);
   } else {
+    const size_t lds_r = sizeof(T) * 2 * kBwdChunk * D;
+    (void)hipFuncSetAttribute((const void*)bwd_rows_kernel<T, D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
     hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3((unsigned)(a.n_qt * a.B * a.H)), dim3(256),
                        lds_r, st, a);
   }
@@ -972,6 +969,9 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_keys_mfma_kernel<D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_km,
                        st, a);
   } else {
+    const size_t lds_k = sizeof(T) * 2 * kBwdTile * D + sizeof(float) * 3 * kBwdTile;
+    (void)hipFuncSetAttribute((const void*)bwd_keys_kernel<T, D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_k);
     hipLaunchKernelGGL((bwd_keys_kernel<T, D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_k,
                        st, a);
   }
