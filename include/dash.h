@@ -247,8 +247,7 @@ dash_status dash_prefill_varlen(const dash_params* p, const void* q, const void*
  * The gradient reaches q through both the fine attention and the coarse
  * scores, k through the attention and the block means, and W_s through the
  * summaries.  Blocks with pbar = 0 take no gradient.  Accumulation in float32
- * (bf16 inputs: the attention products on bf16 MFMA).  DASH_ERR_UNSUPPORTED
- * when G * (d + ceil(n / bs)) * 4 bytes exceed 160 KB. */
+ * (bf16 inputs: the attention products on bf16 MFMA). */
 dash_status dash_prefill_backward_workspace_bytes(const dash_params* p, int64_t n,
                                                   size_t* bytes);
 dash_status dash_prefill_backward(const dash_params* p, const void* q, const void* k,

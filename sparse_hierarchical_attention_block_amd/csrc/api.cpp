@@ -300,9 +300,6 @@ dash_status dash_prefill_backward(const dash_params* p, const void* q, const voi
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE_TOO_SMALL;
   if (!grid_ok(n * s.B * s.Hkv) || !grid_ok(((n + kQT - 1) / kQT) * s.B * s.H))
     return DASH_ERR_UNSUPPORTED;
-  // the routing gradient keeps the group's query rows and a row of every
-  // block per head in LDS
-  if ((int64_t)s.G * (s.d + (n + s.bs - 1) / s.bs) * 4 > 160 * 1024) return DASH_ERR_UNSUPPORTED;
   return hip_status(dash::launch_prefill_backward(s, q, k, v, o, d_o, n, w_s, summ, summ_blocks,
                                                   *route, dq, dk, dv, dw_s, L, (char*)ws,
                                                   (hipStream_t)stream));

@@ -14,7 +14,7 @@
 //   keys    per 64-key chunk of a (sequence, KV head): every later tile that
 //           attends the chunk (branch or list), every head and row of it:
 //           dk_t = sum dl_t q / sqrt(d), dv_t = sum P_t dO
-//   route   per (position, KV head): dpbar = dlogp / pbar, dp_h = dpbar / G,
+//   route   per (query tile, KV head): dpbar = dlogp / pbar, dp_h = dpbar / G,
 //           the entmax Jacobian with u = (x - tau)_+^((2-alpha)/(alpha-1)):
 //           dzbar = gamma (u dp - u (u.dp) / sum u); dq += dzbar . s / sqrt(d)
 //   summ    ds_j = sum over later rows and heads of dzbar_j q / sqrt(d),
@@ -734,91 +734,149 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
   }
 }
 
-// ---- route: dzbar and the coarse part of dq (one wave per position and KV head) ------------
-// The group's G query rows sit in LDS; each lane takes candidates j, lane + 64,
-// ... and reads summary row j once for all G heads (x, then dzbar), and the
-// coarse dq reads every summary column once for all G heads.
+// ---- route, tiled: one workgroup per (query tile, KV head) -----------------------------------
+// All 64 positions of a tile share their candidates (j < t), so per head the
+// coarse scores X = Q S^T (64 x t), the entmax Jacobian and the coarse dq =
+// dZ S (64 x d) are small dense products: summary rows come through LDS 32
+// at a time, each thread owns a 2 x 4 block of X and a 4 x (D / 16) block of dq.
+constexpr int kRtJ = 32;   // summary rows per LDS chunk
 template <typename T, int D>
-__global__ __launch_bounds__(64) void bwd_route_kernel(BwdArgs a) {
-  extern __shared__ float route_lds[];   // q rows [G][D], then u / dzbar [G][nb]
-  const int64_t pos = blockIdx.x % a.n;
-  const int64_t bg = blockIdx.x / a.n;
+__global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
+  constexpr int CK = D / 16;   // dq columns per thread: 16 column groups cover D
+  __shared__ float Qh[kBwdTile][D + 1];
+  __shared__ float Sc[kRtJ][D + 1];
+  __shared__ float Zc[kBwdTile][kRtJ + 1];
+  __shared__ float red[2][8][kBwdTile];
+  const int64_t qt = blockIdx.x % a.n_qt;
+  const int64_t bg = blockIdx.x / a.n_qt;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
-  const int lane = threadIdx.x;
-  const int64_t own = pos / a.bs;
-  const int ncand = (int)(own - (a.window - 1) > 0 ? own - (a.window - 1) : 0);
-  if (ncand == 0) return;
-  const int G = a.G;
-  float* qs = route_lds;
-  float* us = route_lds + G * D;
-  const int64_t qt = pos / kBwdTile, tile = bg * a.n_qt + qt;
-  const int r = (int)(pos % kBwdTile);
-  const int64_t bh0 = (int64_t)b * a.H + g * G;
-  for (int e = lane; e < G * D; e += kWave)
-    qs[e] = ld<T>(a.q, ((bh0 + e / D) * a.n + pos) * D + e % D);
-  __syncthreads();
+  const int64_t p0 = qt * kBwdTile;
+  const int t = (int)max((int64_t)0, p0 / a.bs - (a.window - 1));   // candidates
+  if (t == 0) return;
+  const int64_t tile = bg * a.n_qt + qt;
+  const int tid = threadIdx.x;
   const float* srow = a.summ + bg * a.summ_blocks * D;
-  float su[8], sud[8];
-#pragma unroll
-  for (int hh = 0; hh < 8; ++hh) su[hh] = sud[hh] = 0.f;
-  for (int j = lane; j < ncand; j += kWave) {
-    float x[8];
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) x[hh] = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) {
-      const float sc = srow[j * D + c];
-#pragma unroll
-      for (int hh = 0; hh < 8; ++hh)
-        if (hh < G) x[hh] = fmaf(qs[hh * D + c], sc, x[hh]);
+  const int rg = tid % 32, jg = tid / 32;      // phase A: rows 2 rg, 2 rg + 1; cands 4 jg + k
+  const int rq = tid % 16, cq = tid / 16;      // phase C: rows 4 rq + i; columns CK cq + k
+  for (int hh = 0; hh < a.G; ++hh) {
+    const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
+    __syncthreads();
+    for (int e = tid; e < kBwdTile * D; e += 256) {
+      const int r = e / D, c = e % D;
+      Qh[r][c] = p0 + r < a.n ? ld<T>(a.q, (bh * a.n + p0 + r) * D + c) : 0.f;
     }
-    const int64_t li = (tile * a.nb + j) * kBwdTile + r;
-    const float lp = a.sel_logp[li];
-    float dp = 0.f;
-    if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)G;
+    float tau2[2];
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-      if (hh >= G) break;
-      const float y = x[hh] * a.xscale - a.tau[(bh0 + hh) * a.n + pos];
-      const float u = y > 0.f ? (a.ue == 0.f ? 1.f : powf(y, a.ue)) : 0.f;
-      su[hh] += u;
-      sud[hh] = fmaf(u, dp, sud[hh]);
-      us[hh * a.nb + j] = u;
+    for (int i = 0; i < 2; ++i) {
+      const int64_t pos = p0 + 2 * rg + i;
+      tau2[i] = pos < a.n ? a.tau[bh * a.n + pos] : 0.f;
     }
-    a.dz[((bh0) * a.n + pos) * a.nb + j] = dp;   // dp for now, shared by the heads
-  }
+    // phase A: u and the row sums of u and u dp
+    float su[2] = {0.f, 0.f}, sud[2] = {0.f, 0.f};
+    for (int j0 = 0; j0 < t; j0 += kRtJ) {
+      __syncthreads();
+      for (int e = tid; e < kRtJ * D; e += 256) {
+        const int jr = e / D, c = e % D;
+        Sc[jr][c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
+      }
+      __syncthreads();
+      float x[2][4];
 #pragma unroll
-  for (int hh = 0; hh < 8; ++hh) {
-    if (hh >= G) break;
-    su[hh] = wave_sum(su[hh]);
-    sud[hh] = wave_sum(sud[hh]);
-  }
-  for (int j = lane; j < ncand; j += kWave) {
-    const float dp = a.dz[((bh0) * a.n + pos) * a.nb + j];
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-      if (hh >= G) break;
-      const float corr = su[hh] > 0.f ? sud[hh] / su[hh] : 0.f;
-      const float dz = a.gamma * us[hh * a.nb + j] * (dp - corr);
-      us[hh * a.nb + j] = dz;
-      a.dz[((bh0 + hh) * a.n + pos) * a.nb + j] = dz;
+        for (int k = 0; k < 4; ++k) x[i][k] = 0.f;
+      for (int c = 0; c < D; ++c) {
+        const float q0 = Qh[2 * rg][c], q1 = Qh[2 * rg + 1][c];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float sv = Sc[4 * jg + k][c];
+          x[0][k] = fmaf(q0, sv, x[0][k]);
+          x[1][k] = fmaf(q1, sv, x[1][k]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 2 * rg + i;
+        const int64_t pos = p0 + r;
+        if (pos >= a.n) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = j0 + 4 * jg + k;
+          if (j >= t) continue;
+          const float y = x[i][k] * a.xscale - tau2[i];
+          const float u = y > 0.f ? (a.ue == 0.f ? 1.f : powf(y, a.ue)) : 0.f;
+          const int64_t li = (tile * a.nb + j) * kBwdTile + r;
+          const float lp = a.sel_logp[li];
+          float dp = 0.f;
+          if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)a.G;
+          su[i] += u;
+          sud[i] = fmaf(u, dp, sud[i]);
+          a.dz[(bh * a.n + pos) * a.nb + j] = u;   // u for now
+        }
+      }
     }
-  }
-  __syncthreads();
-  for (int c = lane; c < D; c += kWave) {
-    float acc[8];
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh) acc[hh] = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < ncand; ++j) {
-      const float sc = srow[j * D + c];
+    for (int i = 0; i < 2; ++i) {
+      red[0][jg][2 * rg + i] = su[i];
+      red[1][jg][2 * rg + i] = sud[i];
+    }
+    __syncthreads();
+    // phase B + C: dz = gamma u (dp - corr); dq += dz S / sqrt(d)
+    float dqa[4][CK];
 #pragma unroll
-      for (int hh = 0; hh < 8; ++hh)
-        if (hh < G) acc[hh] = fmaf(us[hh * a.nb + j], sc, acc[hh]);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < CK; ++k) dqa[i][k] = 0.f;
+    for (int j0 = 0; j0 < t; j0 += kRtJ) {
+      __syncthreads();
+      for (int e = tid; e < kRtJ * D; e += 256) {
+        const int jr = e / D, c = e % D;
+        Sc[jr][c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
+      }
+      for (int e = tid; e < kBwdTile * kRtJ; e += 256) {
+        const int r = e / kRtJ, jr = e % kRtJ, j = j0 + jr;
+        const int64_t pos = p0 + r;
+        float dz = 0.f;
+        if (j < t && pos < a.n) {
+          float s_u = 0.f, s_ud = 0.f;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            s_u += red[0][w][r];
+            s_ud += red[1][w][r];
+          }
+          const float corr = s_u > 0.f ? s_ud / s_u : 0.f;
+          const int64_t li = (tile * a.nb + j) * kBwdTile + r;
+          const float lp = a.sel_logp[li];
+          float dp = 0.f;
+          if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)a.G;
+          float* zp = a.dz + (bh * a.n + pos) * a.nb + j;
+          dz = a.gamma * *zp * (dp - corr);
+          *zp = dz;
+        }
+        Zc[r][jr] = dz;
+      }
+      __syncthreads();
+      const int jn = min(kRtJ, t - j0);
+      for (int jr = 0; jr < jn; ++jr) {
+        float zv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zv[i] = Zc[4 * rq + i][jr];
+#pragma unroll
+        for (int k = 0; k < CK; ++k) {
+          const float sv = Sc[jr][CK * cq + k];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dqa[i][k] = fmaf(zv[i], sv, dqa[i][k]);
+        }
+      }
     }
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh)
-      if (hh < G) a.dq[((bh0 + hh) * a.n + pos) * D + c] += acc[hh] * a.rs;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t pos = p0 + 4 * rq + i;
+      if (pos >= a.n) continue;
+      float* dqr = a.dq + (bh * a.n + pos) * D + CK * cq;
+#pragma unroll
+      for (int k = 0; k < CK; ++k) dqr[k] += dqa[i][k] * a.rs;
+    }
   }
 }
 
@@ -975,11 +1033,7 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_keys_kernel<T, D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_k,
                        st, a);
   }
-  const size_t lds_rt = sizeof(float) * a.G * (D + a.nb);
-  if (lds_rt > 64 * 1024)
-    (void)hipFuncSetAttribute((const void*)bwd_route_kernel<T, D>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_rt);
-  hipLaunchKernelGGL((bwd_route_kernel<T, D>), dim3((unsigned)(a.n * nbg)), dim3(kWave), lds_rt,
+  hipLaunchKernelGGL((bwd_route_tile_kernel<T, D>), dim3((unsigned)(a.n_qt * nbg)), dim3(256), 0,
                      st, a);
   const int64_t njg = (a.nb + kSummJ - 1) / kSummJ;
   hipLaunchKernelGGL((bwd_summ_kernel<T, D>), dim3((unsigned)(njg * kSummSlices * nbg)), dim3(D),
