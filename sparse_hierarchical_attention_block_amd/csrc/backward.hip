@@ -17,8 +17,8 @@
 //   route   per (query tile, KV head): dpbar = dlogp / pbar, dp_h = dpbar / G,
 //           the entmax Jacobian with u = (x - tau)_+^((2-alpha)/(alpha-1)):
 //           dzbar = gamma (u dp - u (u.dp) / sum u); dq += dzbar . s / sqrt(d)
-//   summ    ds_j = sum over later rows and heads of dzbar_j q / sqrt(d),
-//           32 blocks at a time over slices of the rows
+//           and the summaries' gradient ds_j = sum over the rows and heads of
+//           dzbar_j q / sqrt(d) (atomics across tiles)
 //   means   dk of block j += (ds_j W_s^T) / bs; block means m_j
 //   w_s     dW_s = sum_j m_j^T ds_j
 // Every product is plain float32 FMAs (no MFMA); a row or key is spread over
@@ -736,9 +736,11 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
 
 // ---- route, tiled: one workgroup per (query tile, KV head) -----------------------------------
 // All 64 positions of a tile share their candidates (j < t), so per head the
-// coarse scores X = Q S^T (64 x t), the entmax Jacobian and the coarse dq =
-// dZ S (64 x d) are small dense products: summary rows come through LDS 32
-// at a time, each thread owns a 2 x 4 block of X and a 4 x (D / 16) block of dq.
+// coarse scores X = Q S^T (64 x t), the entmax Jacobian, the coarse dq =
+// dZ S (64 x d) and the tile's share of the summary gradient dZ^T Q (t x d)
+// are small dense products: summary rows come through LDS 32 at a time, each
+// thread owns a 2 x 4 block of X, a 4 x (D / 16) block of dq and a 2 x (D / 16)
+// block of the summary gradient, which is added into ds with atomics.
 constexpr int kRtJ = 32;   // summary rows per LDS chunk
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
@@ -868,6 +870,33 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
           for (int i = 0; i < 4; ++i) dqa[i][k] = fmaf(zv[i], sv, dqa[i][k]);
         }
       }
+      // the summaries' share: ds_j += sum over the tile's rows of dz_j q / sqrt(d),
+      // thread (jq, cc) owns rows j0 + 2 jq + {0, 1} and columns CK cc + k
+      {
+        const int jq = tid / 16, cc = tid % 16;
+        float dsa[2][CK];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int k = 0; k < CK; ++k) dsa[jj][k] = 0.f;
+        for (int r = 0; r < kBwdTile; ++r) {
+          const float z0 = Zc[r][2 * jq], z1 = Zc[r][2 * jq + 1];
+#pragma unroll
+          for (int k = 0; k < CK; ++k) {
+            const float qv = Qh[r][CK * cc + k];
+            dsa[0][k] = fmaf(z0, qv, dsa[0][k]);
+            dsa[1][k] = fmaf(z1, qv, dsa[1][k]);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = j0 + 2 * jq + jj;
+          if (j < t)
+#pragma unroll
+            for (int k = 0; k < CK; ++k)
+              atomicAdd(&a.ds[(bg * a.nb + j) * D + CK * cc + k], dsa[jj][k] * a.rs);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -878,68 +907,6 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
       for (int k = 0; k < CK; ++k) dqr[k] += dqa[i][k] * a.rs;
     }
   }
-}
-
-// ---- summaries: ds_j = sum over later rows and heads of dzbar_j q / sqrt(d) -----------------
-// One workgroup per (sequence, KV head, group of kSummJ blocks, slice of the
-// rows); thread c accumulates column c of the group's kSummJ summaries (each
-// q element read once feeds kSummJ FMAs) and adds them into ds, which starts
-// at zero.
-constexpr int kSummJ = 32;
-constexpr int kSummSlices = 64;
-template <typename T, int D>
-__global__ __launch_bounds__(D) void bwd_summ_kernel(BwdArgs a) {
-  const int64_t njg = (a.nb + kSummJ - 1) / kSummJ;
-  const int slice = blockIdx.x % kSummSlices;
-  const int64_t jg = (blockIdx.x / kSummSlices) % njg;
-  const int64_t bg = blockIdx.x / kSummSlices / njg;
-  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
-  const int c = threadIdx.x;
-  const int64_t nfull = a.n / a.bs;            // blocks with a summary
-  const int64_t j0 = jg * kSummJ;
-  if (j0 >= nfull) return;
-  // rows that route over block j0 (the group's first, so the most rows)
-  const int64_t r0 = (j0 + a.window) * a.bs;
-  if (r0 >= a.n) return;
-  const int64_t span = (a.n - r0 + kSummSlices - 1) / kSummSlices;
-  const int64_t p0 = r0 + slice * span, p1 = min(a.n, p0 + span);
-  float acc[kSummJ];
-#pragma unroll
-  for (int jj = 0; jj < kSummJ; ++jj) acc[jj] = 0.f;
-  // 16-byte loads of the dz rows when the group lies inside every row
-  const bool vec = a.nb % 4 == 0 && j0 + kSummJ <= a.nb;
-  for (int hh = 0; hh < a.G; ++hh) {
-    const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
-#pragma unroll 4
-    for (int64_t pos = p0; pos < p1; ++pos) {
-      const float qc = ld<T>(a.q, (bh * a.n + pos) * D + c);
-      const float* dzr = a.dz + (bh * a.n + pos) * a.nb + j0;
-      // block j0 + jj is a candidate of row pos when pos >= (j0 + jj + window) bs;
-      // dz is not written past a row's candidates
-      const int64_t ncand = pos / a.bs - (a.window - 1);
-      if (vec) {
-        // eight 16-byte loads; entries past the row's candidates were never
-        // written and are dropped by the select
-#pragma unroll
-        for (int k4 = 0; k4 < kSummJ / 4; ++k4) {
-          const float4 v = ((const float4*)dzr)[k4];
-          const float ve[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int jj = 4 * k4 + e;
-            acc[jj] = fmaf(j0 + jj < ncand ? ve[e] : 0.f, qc, acc[jj]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < kSummJ; ++jj)
-          if (j0 + jj < ncand) acc[jj] = fmaf(dzr[jj], qc, acc[jj]);
-      }
-    }
-  }
-#pragma unroll
-  for (int jj = 0; jj < kSummJ; ++jj)
-    if (j0 + jj < nfull) atomicAdd(&a.ds[(bg * a.nb + j0 + jj) * D + c], acc[jj] * a.rs);
 }
 
 // ---- block means, and dk += (ds_j W_s^T) / bs over the block ---------------------------------
@@ -1035,9 +1002,7 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   hipLaunchKernelGGL((bwd_route_tile_kernel<T, D>), dim3((unsigned)(a.n_qt * nbg)), dim3(256), 0,
                      st, a);
-  const int64_t njg = (a.nb + kSummJ - 1) / kSummJ;
-  hipLaunchKernelGGL((bwd_summ_kernel<T, D>), dim3((unsigned)(njg * kSummSlices * nbg)), dim3(D),
-                     0, st, a);
+
   hipLaunchKernelGGL((bwd_means_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
   hipLaunchKernelGGL((bwd_ws_kernel<D>), dim3((unsigned)((D * D + 255) / 256)), dim3(256), 0, st,
                      a);
