@@ -51,7 +51,7 @@ struct BwdArgs {
   float* lse2;              // [B, H, n] log2-sum-exp2 of the scaled logits
   float* delta;             // [B, H, n] dO . o
   float* dlogp;             // [B, Hkv, n_qt, nb, 64]
-  float* dz;                // [B, H, n, nb]
+  float* ucoarse;           // [B, Hkv, n_qt, G, nb, 64] entmax u of the coarse scores
   float* ds;                // [B, Hkv, nb, D]
   float* mean;              // [B, Hkv, nb, D]
   int64_t n, n_qt, nb;
@@ -473,8 +473,9 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
   float* rowd = rowl + kBwdTile;
   float* rowb = rowd + kBwdTile;
   const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
-  const int64_t ch = blockIdx.x % nch;
-  const int64_t bg = blockIdx.x / nch;
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
+  const int64_t ch = blockIdx.x / nbg;   // early chunks, attended by the most tiles, first
+  const int64_t bg = blockIdx.x % nbg;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int key = threadIdx.x / 4, sl = threadIdx.x % 4;
   const int64_t kpos = ch * kBwdChunk + key;
@@ -581,8 +582,9 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
   const int l32 = lane % 32, lh = lane / 32;
   const int kt = wave / 2, dh = wave % 2;
   const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
-  const int64_t ch = blockIdx.x % nch;
-  const int64_t bg = blockIdx.x / nch;
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
+  const int64_t ch = blockIdx.x / nbg;   // early chunks, attended by the most tiles, first
+  const int64_t bg = blockIdx.x % nbg;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t kpos = ch * kBwdChunk + 32 * kt + l32;   // this lane's key
   const bool kvalid = kpos < a.n;
@@ -749,8 +751,10 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
   __shared__ float Sc[kRtJ][D + 1];
   __shared__ float Zc[kBwdTile][kRtJ + 1];
   __shared__ float red[2][8][kBwdTile];
-  const int64_t qt = blockIdx.x % a.n_qt;
-  const int64_t bg = blockIdx.x / a.n_qt;
+  __shared__ float corr_s[kBwdTile];
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
+  const int64_t qt = a.n_qt - 1 - blockIdx.x / nbg;   // most candidates first
+  const int64_t bg = blockIdx.x % nbg;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t p0 = qt * kBwdTile;
   const int t = (int)max((int64_t)0, p0 / a.bs - (a.window - 1));   // candidates
@@ -813,7 +817,7 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
           if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)a.G;
           su[i] += u;
           sud[i] = fmaf(u, dp, sud[i]);
-          a.dz[(bh * a.n + pos) * a.nb + j] = u;   // u for now
+          a.ucoarse[((tile * a.G + hh) * a.nb + j) * kBwdTile + r] = u;
         }
       }
     }
@@ -823,6 +827,15 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
       red[1][jg][2 * rg + i] = sud[i];
     }
     __syncthreads();
+    if (tid < kBwdTile) {   // the row's correction (u . dp) / sum u
+      float s_u = 0.f, s_ud = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        s_u += red[0][w][tid];
+        s_ud += red[1][w][tid];
+      }
+      corr_s[tid] = s_u > 0.f ? s_ud / s_u : 0.f;
+    }
     // phase B + C: dz = gamma u (dp - corr); dq += dz S / sqrt(d)
     float dqa[4][CK];
 #pragma unroll
@@ -836,24 +849,16 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
         Sc[jr][c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
       }
       for (int e = tid; e < kBwdTile * kRtJ; e += 256) {
-        const int r = e / kRtJ, jr = e % kRtJ, j = j0 + jr;
+        const int r = e % kBwdTile, jr = e / kBwdTile, j = j0 + jr;
         const int64_t pos = p0 + r;
         float dz = 0.f;
         if (j < t && pos < a.n) {
-          float s_u = 0.f, s_ud = 0.f;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            s_u += red[0][w][r];
-            s_ud += red[1][w][r];
-          }
-          const float corr = s_u > 0.f ? s_ud / s_u : 0.f;
           const int64_t li = (tile * a.nb + j) * kBwdTile + r;
           const float lp = a.sel_logp[li];
           float dp = 0.f;
           if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)a.G;
-          float* zp = a.dz + (bh * a.n + pos) * a.nb + j;
-          dz = a.gamma * *zp * (dp - corr);
-          *zp = dz;
+          const float u = a.ucoarse[((tile * a.G + hh) * a.nb + j) * kBwdTile + r];
+          dz = a.gamma * u * (dp - corr_s[r]);
         }
         Zc[r][jr] = dz;
       }
@@ -932,15 +937,23 @@ __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
 }
 
 // ---- dW_s = sum_j m_j^T ds_j ---------------------------------------------------------------
+// The sum over all blocks of all (sequence, KV head) pairs is cut into
+// kWsSplit slices (blockIdx.y); each adds its partial sum into the zeroed
+// dW_s with one atomic per entry.
+constexpr int kWsSplit = 32;
 template <int D>
 __global__ __launch_bounds__(256) void bwd_ws_kernel(BwdArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)D * D) return;
   const int r = (int)(idx / D), c = (int)(idx % D);
   const int64_t nblk = (int64_t)a.B * a.Hkv * a.nb;
+  const int64_t per = (nblk + kWsSplit - 1) / kWsSplit;
+  const int64_t u0 = blockIdx.y * per, u1 = min(nblk, u0 + per);
+  if (u0 >= u1) return;
   float acc = 0.f;
-  for (int64_t u = 0; u < nblk; ++u) acc = fmaf(a.mean[u * D + r], a.ds[u * D + c], acc);
-  a.dw_s[idx] = acc;
+#pragma unroll 4
+  for (int64_t u = u0; u < u1; ++u) acc = fmaf(a.mean[u * D + r], a.ds[u * D + c], acc);
+  atomicAdd(a.dw_s + idx, acc);
 }
 
 __global__ void bwd_zero_kernel(float* p, int64_t n) {
@@ -957,7 +970,7 @@ BwdLayout bwd_layout(const Shape& s, int64_t n) {
   L.off_lse = off;   off = al(off + sizeof(float) * s.B * s.H * n);
   L.off_delta = off; off = al(off + sizeof(float) * s.B * s.H * n);
   L.off_dlogp = off; off = al(off + sizeof(float) * s.B * s.Hkv * n_qt * nb * kBwdTile);
-  L.off_dz = off;    off = al(off + sizeof(float) * s.B * s.H * n * nb);
+  L.off_u = off;    off = al(off + sizeof(float) * s.B * s.H * n_qt * kBwdTile * nb);
   L.off_ds = off;    off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
   L.off_mean = off;  off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
   L.total = off;
@@ -970,6 +983,7 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
   const int64_t nzero = nbg * a.n_qt * a.nb * kBwdTile;
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, st, a.dlogp, nzero);
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(256), dim3(256), 0, st, a.ds, nbg * a.nb * D);
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3(64), dim3(256), 0, st, a.dw_s, (int64_t)D * D);
   if constexpr (sizeof(T) == 2) {
     // 2 G waves of 32 queries per tile, at most 8 per workgroup
     const int waves = 2 * a.G, wpt = (waves + 7) / 8;
@@ -1004,8 +1018,8 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
                      st, a);
 
   hipLaunchKernelGGL((bwd_means_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
-  hipLaunchKernelGGL((bwd_ws_kernel<D>), dim3((unsigned)((D * D + 255) / 256)), dim3(256), 0, st,
-                     a);
+  hipLaunchKernelGGL((bwd_ws_kernel<D>), dim3((unsigned)((D * D + 255) / 256), kWsSplit),
+                     dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1035,7 +1049,7 @@ hipError_t launch_prefill_backward(const Shape& s, const void* q, const void* k,
   a.lse2 = (float*)(ws + L.off_lse);
   a.delta = (float*)(ws + L.off_delta);
   a.dlogp = (float*)(ws + L.off_dlogp);
-  a.dz = (float*)(ws + L.off_dz);
+  a.ucoarse = (float*)(ws + L.off_u);
   a.ds = (float*)(ws + L.off_ds);
   a.mean = (float*)(ws + L.off_mean);
   a.n = n;
