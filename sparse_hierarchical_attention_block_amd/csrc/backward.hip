@@ -742,14 +742,19 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
 // dZ S (64 x d) and the tile's share of the summary gradient dZ^T Q (t x d)
 // are small dense products: summary rows come through LDS 32 at a time, each
 // thread owns a 2 x 4 block of X, a 4 x (D / 16) block of dq and a 2 x (D / 16)
-// block of the summary gradient, which is added into ds with atomics.
+// block of the summary gradient, which is added into ds with atomics.  LDS
+// rows are read 4 floats at a time; the row pitch D + 4 and the assignment of
+// rows {r, r + 32} and of column groups {4 c, 64 + 4 c} to threads keep the
+// 8 lanes of each 16-byte read on distinct banks.
 constexpr int kRtJ = 32;   // summary rows per LDS chunk
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
-  constexpr int CK = D / 16;   // dq columns per thread: 16 column groups cover D
-  __shared__ float Qh[kBwdTile][D + 1];
-  __shared__ float Sc[kRtJ][D + 1];
-  __shared__ float Zc[kBwdTile][kRtJ + 1];
+  constexpr int QP = D + 4;      // pitch of Qh and Sc rows (floats)
+  constexpr int ZP = kBwdTile + 4;
+  constexpr int NV = D / 64;     // float4 column groups per thread (64 apart)
+  __shared__ __attribute__((aligned(16))) float Qh[kBwdTile * QP];
+  __shared__ __attribute__((aligned(16))) float Sc[kRtJ * QP];
+  __shared__ __attribute__((aligned(16))) float Zt[kRtJ * ZP];   // dz, candidate-major
   __shared__ float red[2][8][kBwdTile];
   __shared__ float corr_s[kBwdTile];
   const int64_t nbg = (int64_t)a.B * a.Hkv;
@@ -762,19 +767,20 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
   const int64_t tile = bg * a.n_qt + qt;
   const int tid = threadIdx.x;
   const float* srow = a.summ + bg * a.summ_blocks * D;
-  const int rg = tid % 32, jg = tid / 32;      // phase A: rows 2 rg, 2 rg + 1; cands 4 jg + k
-  const int rq = tid % 16, cq = tid / 16;      // phase C: rows 4 rq + i; columns CK cq + k
+  const int rg = tid % 32, jg = tid / 32;   // phase A: rows rg + 32 i; candidates 4 jg + k
+  const int rq = tid % 16, cq = tid / 16;   // dq: rows 4 rq + i; columns 64 v + 4 cq + [0, 4)
+  const int jq = tid / 16, cc = tid % 16;   // ds: candidates 2 jq + {0, 1}; columns as dq's
   for (int hh = 0; hh < a.G; ++hh) {
     const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
     __syncthreads();
     for (int e = tid; e < kBwdTile * D; e += 256) {
       const int r = e / D, c = e % D;
-      Qh[r][c] = p0 + r < a.n ? ld<T>(a.q, (bh * a.n + p0 + r) * D + c) : 0.f;
+      Qh[r * QP + c] = p0 + r < a.n ? ld<T>(a.q, (bh * a.n + p0 + r) * D + c) : 0.f;
     }
     float tau2[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int64_t pos = p0 + 2 * rg + i;
+      const int64_t pos = p0 + rg + 32 * i;
       tau2[i] = pos < a.n ? a.tau[bh * a.n + pos] : 0.f;
     }
     // phase A: u and the row sums of u and u dp
@@ -783,7 +789,7 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
       __syncthreads();
       for (int e = tid; e < kRtJ * D; e += 256) {
         const int jr = e / D, c = e % D;
-        Sc[jr][c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
+        Sc[jr * QP + c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
       }
       __syncthreads();
       float x[2][4];
@@ -791,18 +797,22 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k) x[i][k] = 0.f;
-      for (int c = 0; c < D; ++c) {
-        const float q0 = Qh[2 * rg][c], q1 = Qh[2 * rg + 1][c];
+      for (int c = 0; c < D; c += 4) {
+        const f32x4 q0 = *(const f32x4*)(Qh + rg * QP + c);
+        const f32x4 q1 = *(const f32x4*)(Qh + (rg + 32) * QP + c);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float sv = Sc[4 * jg + k][c];
-          x[0][k] = fmaf(q0, sv, x[0][k]);
-          x[1][k] = fmaf(q1, sv, x[1][k]);
+          const f32x4 sv = *(const f32x4*)(Sc + (4 * jg + k) * QP + c);
+#pragma unroll
+          for (int cc4 = 0; cc4 < 4; ++cc4) {
+            x[0][k] = fmaf(q0[cc4], sv[cc4], x[0][k]);
+            x[1][k] = fmaf(q1[cc4], sv[cc4], x[1][k]);
+          }
         }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int r = 2 * rg + i;
+        const int r = rg + 32 * i;
         const int64_t pos = p0 + r;
         if (pos >= a.n) continue;
 #pragma unroll
@@ -823,8 +833,8 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      red[0][jg][2 * rg + i] = su[i];
-      red[1][jg][2 * rg + i] = sud[i];
+      red[0][jg][rg + 32 * i] = su[i];
+      red[1][jg][rg + 32 * i] = sud[i];
     }
     __syncthreads();
     if (tid < kBwdTile) {   // the row's correction (u . dp) / sum u
@@ -837,16 +847,16 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
       corr_s[tid] = s_u > 0.f ? s_ud / s_u : 0.f;
     }
     // phase B + C: dz = gamma u (dp - corr); dq += dz S / sqrt(d)
-    float dqa[4][CK];
+    f32x4 dqa[4][NV];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int k = 0; k < CK; ++k) dqa[i][k] = 0.f;
+      for (int v = 0; v < NV; ++v) dqa[i][v] = (f32x4){0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < t; j0 += kRtJ) {
       __syncthreads();
       for (int e = tid; e < kRtJ * D; e += 256) {
         const int jr = e / D, c = e % D;
-        Sc[jr][c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
+        Sc[jr * QP + c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
       }
       for (int e = tid; e < kBwdTile * kRtJ; e += 256) {
         const int r = e % kBwdTile, jr = e / kBwdTile, j = j0 + jr;
@@ -860,37 +870,38 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
           const float u = a.ucoarse[((tile * a.G + hh) * a.nb + j) * kBwdTile + r];
           dz = a.gamma * u * (dp - corr_s[r]);
         }
-        Zc[r][jr] = dz;
+        Zt[jr * ZP + r] = dz;
       }
       __syncthreads();
       const int jn = min(kRtJ, t - j0);
       for (int jr = 0; jr < jn; ++jr) {
-        float zv[4];
+        const f32x4 zv = *(const f32x4*)(Zt + jr * ZP + 4 * rq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zv[i] = Zc[4 * rq + i][jr];
+        for (int v = 0; v < NV; ++v) {
+          const f32x4 sv = *(const f32x4*)(Sc + jr * QP + 64 * v + 4 * cq);
 #pragma unroll
-        for (int k = 0; k < CK; ++k) {
-          const float sv = Sc[jr][CK * cq + k];
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dqa[i][k] = fmaf(zv[i], sv, dqa[i][k]);
+            for (int kk = 0; kk < 4; ++kk) dqa[i][v][kk] = fmaf(zv[i], sv[kk], dqa[i][v][kk]);
         }
       }
-      // the summaries' share: ds_j += sum over the tile's rows of dz_j q / sqrt(d),
-      // thread (jq, cc) owns rows j0 + 2 jq + {0, 1} and columns CK cc + k
+      // the summaries' share: ds_j += sum over the tile's rows of dz_j q / sqrt(d)
       {
-        const int jq = tid / 16, cc = tid % 16;
-        float dsa[2][CK];
+        f32x4 dsa[2][NV];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int k = 0; k < CK; ++k) dsa[jj][k] = 0.f;
+          for (int v = 0; v < NV; ++v) dsa[jj][v] = (f32x4){0.f, 0.f, 0.f, 0.f};
         for (int r = 0; r < kBwdTile; ++r) {
-          const float z0 = Zc[r][2 * jq], z1 = Zc[r][2 * jq + 1];
+          const float z0 = Zt[(2 * jq) * ZP + r], z1 = Zt[(2 * jq + 1) * ZP + r];
 #pragma unroll
-          for (int k = 0; k < CK; ++k) {
-            const float qv = Qh[r][CK * cc + k];
-            dsa[0][k] = fmaf(z0, qv, dsa[0][k]);
-            dsa[1][k] = fmaf(z1, qv, dsa[1][k]);
+          for (int v = 0; v < NV; ++v) {
+            const f32x4 qv = *(const f32x4*)(Qh + r * QP + 64 * v + 4 * cc);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              dsa[0][v][kk] = fmaf(z0, qv[kk], dsa[0][v][kk]);
+              dsa[1][v][kk] = fmaf(z1, qv[kk], dsa[1][v][kk]);
+            }
           }
         }
 #pragma unroll
@@ -898,8 +909,11 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
           const int j = j0 + 2 * jq + jj;
           if (j < t)
 #pragma unroll
-            for (int k = 0; k < CK; ++k)
-              atomicAdd(&a.ds[(bg * a.nb + j) * D + CK * cc + k], dsa[jj][k] * a.rs);
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+              for (int kk = 0; kk < 4; ++kk)
+                atomicAdd(&a.ds[(bg * a.nb + j) * D + 64 * v + 4 * cc + kk],
+                          dsa[jj][v][kk] * a.rs);
         }
       }
     }
@@ -907,9 +921,11 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int64_t pos = p0 + 4 * rq + i;
       if (pos >= a.n) continue;
-      float* dqr = a.dq + (bh * a.n + pos) * D + CK * cq;
+      float* dqr = a.dq + (bh * a.n + pos) * D;
 #pragma unroll
-      for (int k = 0; k < CK; ++k) dqr[k] += dqa[i][k] * a.rs;
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) dqr[64 * v + 4 * cq + kk] += dqa[i][v][kk] * a.rs;
     }
   }
 }
