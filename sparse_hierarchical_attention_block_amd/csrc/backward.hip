@@ -611,70 +611,90 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) dka[t][i] = dva[t][i] = 0.f;
 
   const int64_t blk = (ch * kBwdChunk) / a.bs;
+  // Staging: q and dO of a (tile, head) in blocks of 4 rows x 8 d, NBLK per
+  // thread, held in registers so that the next item's loads are in flight
+  // while the current one is computed.  Block rows 4 rb + [0, 4) land in 4
+  // adjacent columns of the transposed copies (rb runs fastest over the
+  // lanes, so those 8-byte stores hit distinct banks).
+  constexpr int NBLK = D / 64;
+  u32x4 pre[NBLK][4];
+  float pre_l = 0.f, pre_d = 0.f, pre_b = 0.f;
+  auto prefetch = [&](int64_t qt, int hh, bool branch) {
+    const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
+#pragma unroll
+    for (int m = 0; m < NBLK; ++m) {
+      const int e = threadIdx.x + 256 * m;
+      const int which = e / (2 * D), e1 = e % (2 * D);
+      const int rb = e1 % 16, cb = e1 / 16;
+      const __bf16* src = (const __bf16*)(which ? a.dO : a.q) + (bh * a.n + qt * kBwdTile) * D;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 4 * rb + rr;
+        pre[m][rr] = qt * kBwdTile + r < a.n ? *(const u32x4*)(src + r * D + 8 * cb)
+                                             : (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+    if (threadIdx.x < kBwdTile) {
+      const int r = threadIdx.x;
+      const int64_t pos = qt * kBwdTile + r;
+      const bool in = pos < a.n;
+      pre_l = in ? a.lse2[bh * a.n + pos] : 0.f;
+      pre_d = in ? a.delta[bh * a.n + pos] : 0.f;
+      pre_b = !in ? -INFINITY
+                  : (branch ? 0.f
+                            : a.sel_logp[((bg * a.n_qt + qt) * a.nb + blk) * kBwdTile + r] *
+                                  kLog2e);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int m = 0; m < NBLK; ++m) {
+      const int e = threadIdx.x + 256 * m;
+      const int which = e / (2 * D), e1 = e % (2 * D);
+      const int rb = e1 % 16, cb = e1 / 16;
+      __bf16* dr = which ? Or : Qr;
+      __bf16* dt = which ? Ot : Qt;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) *(u32x4*)(dr + (4 * rb + rr) * RP + 8 * cb) = pre[m][rr];
+      // queries 16 m' + 8 a' + 4 b' + [0, 4) go to columns 16 m' + 8 b' + 4 a' + [0, 4)
+      const int col = 16 * (rb / 4) + 8 * (rb % 2) + 4 * ((rb / 2) % 2);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        *(u32x2*)(dt + (8 * cb + 2 * w) * TP + col) =
+            (u32x2){pack_lo(pre[m][0][w], pre[m][1][w]), pack_lo(pre[m][2][w], pre[m][3][w])};
+        *(u32x2*)(dt + (8 * cb + 2 * w + 1) * TP + col) =
+            (u32x2){pack_hi(pre[m][0][w], pre[m][1][w]), pack_hi(pre[m][2][w], pre[m][3][w])};
+      }
+    }
+    if (threadIdx.x < kBwdTile) {
+      rowl[threadIdx.x] = pre_l;
+      rowd[threadIdx.x] = pre_d;
+      rowb[threadIdx.x] = pre_b;
+    }
+  };
   __shared__ int8_t flags[kFlagTiles];
   for (int64_t q0 = ch; q0 < a.n_qt; q0 += kFlagTiles) {
-  __syncthreads();
-  if (threadIdx.x < kFlagTiles)
-    flags[threadIdx.x] =
-        q0 + threadIdx.x < a.n_qt ? (int8_t)tile_attends(a, bg, q0 + threadIdx.x, blk) : 0;
-  __syncthreads();
-  const int nq = (int)min((int64_t)kFlagTiles, a.n_qt - q0);
-  for (int tq = 0; tq < nq; ++tq) {
-    if (!flags[tq]) continue;
-    const int64_t qt = q0 + tq;
-    const int64_t tile = bg * a.n_qt + qt;
-    const bool branch = flags[tq] == 1;
-    for (int hh = 0; hh < a.G; ++hh) {
-      const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
-      const __bf16* qb = (const __bf16*)a.q + (bh * a.n + qt * kBwdTile) * D;
-      const __bf16* ob = (const __bf16*)a.dO + (bh * a.n + qt * kBwdTile) * D;
+    __syncthreads();
+    if (threadIdx.x < kFlagTiles)
+      flags[threadIdx.x] =
+          q0 + threadIdx.x < a.n_qt ? (int8_t)tile_attends(a, bg, q0 + threadIdx.x, blk) : 0;
+    __syncthreads();
+    const int nq = (int)min((int64_t)kFlagTiles, a.n_qt - q0);
+    int tq = 0, hh = 0;
+    while (tq < nq && !flags[tq]) ++tq;
+    if (tq < nq) prefetch(q0 + tq, 0, flags[tq] == 1);
+    while (tq < nq) {
+      const int64_t qt = q0 + tq;
+      const bool branch = flags[tq] == 1;
+      int ntq = tq, nhh = hh + 1;
+      if (nhh == a.G) {
+        nhh = 0;
+        for (++ntq; ntq < nq && !flags[ntq];) ++ntq;
+      }
+      __syncthreads();   // the previous item is done with the staged rows
+      stage();
       __syncthreads();
-      for (int e = threadIdx.x; e < kBwdTile * (D / 8); e += 256) {
-        const int r = e / (D / 8), seg = e % (D / 8);
-        const bool in = qt * kBwdTile + r < a.n;
-        u32x4 wq = {0u, 0u, 0u, 0u}, wo = {0u, 0u, 0u, 0u};
-        if (in) {
-          wq = *(const u32x4*)(qb + r * D + seg * 8);
-          wo = *(const u32x4*)(ob + r * D + seg * 8);
-        }
-        *(u32x4*)(Qr + r * RP + seg * 8) = wq;
-        *(u32x4*)(Or + r * RP + seg * 8) = wo;
-      }
-      // transposed copies in 4 x 4 blocks (4 queries x 4 d): four 8-byte
-      // loads, register transposes, four 8-byte stores; queries 16 m + 8 a +
-      // 4 b + [0, 4) go to columns 16 m + 8 b + 4 a + [0, 4)
-      for (int e = threadIdx.x; e < 2 * (kBwdTile / 4) * (D / 4); e += 256) {
-        const int which = e / ((kBwdTile / 4) * (D / 4));
-        const int e1 = e % ((kBwdTile / 4) * (D / 4));
-        const int db = e1 % (D / 4), qb4 = e1 / (D / 4);
-        const __bf16* src = which ? ob : qb;
-        __bf16* dst = which ? Ot : Qt;
-        u32x2 in[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 4 * qb4 + rr;
-          in[rr] = qt * kBwdTile + r < a.n ? *(const u32x2*)(src + r * D + 4 * db)
-                                           : (u32x2){0u, 0u};
-        }
-        const int col = 16 * (qb4 / 4) + 8 * (qb4 % 2) + 4 * ((qb4 / 2) % 2);
-        *(u32x2*)(dst + (4 * db + 0) * TP + col) = (u32x2){pack_lo(in[0].x, in[1].x),
-                                                           pack_lo(in[2].x, in[3].x)};
-        *(u32x2*)(dst + (4 * db + 1) * TP + col) = (u32x2){pack_hi(in[0].x, in[1].x),
-                                                           pack_hi(in[2].x, in[3].x)};
-        *(u32x2*)(dst + (4 * db + 2) * TP + col) = (u32x2){pack_lo(in[0].y, in[1].y),
-                                                           pack_lo(in[2].y, in[3].y)};
-        *(u32x2*)(dst + (4 * db + 3) * TP + col) = (u32x2){pack_hi(in[0].y, in[1].y),
-                                                           pack_hi(in[2].y, in[3].y)};
-      }
-      for (int r = threadIdx.x; r < kBwdTile; r += 256) {
-        const int64_t pos = qt * kBwdTile + r;
-        const bool in = pos < a.n;
-        rowl[r] = in ? a.lse2[bh * a.n + pos] : 0.f;
-        rowd[r] = in ? a.delta[bh * a.n + pos] : 0.f;
-        rowb[r] = !in ? -INFINITY
-                      : (branch ? 0.f : a.sel_logp[(tile * a.nb + blk) * kBwdTile + r] * kLog2e);
-      }
-      __syncthreads();
+      if (ntq < nq) prefetch(q0 + ntq, nhh, flags[ntq] == 1);
 #pragma unroll 1
       for (int qh = 0; qh < 2; ++qh) {
         // S and dP: queries 32 qh + row, keys of this wave's tile (lane l32)
@@ -718,8 +738,9 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
             dka[t] = mfma32(as_bf16x8(*(const u32x4*)(Qt + toff)), dsf[k2], dka[t]);
           }
       }
+      tq = ntq;
+      hh = nhh;
     }
-  }
   }
   // dka[t][i] = dK^T[d = 32 dt + 8 (i / 4) + 4 lh + i % 4][key kpos]
   if (kvalid) {
