@@ -566,7 +566,8 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
 //   dV^T (d x keys) += dO^T P,  dK^T += Q^T dS            (P, dS as bf16 B operands)
 // The wave's K and V fragments stay in registers for the whole walk.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_keys_mfma_kernel(BwdArgs a) {
   constexpr int RP = D + 8;            // row pitch of the staged q / dO rows
   constexpr int TP = kBwdTile + 8;     // row pitch of the transposed ones
   constexpr int NDT = D / 64;          // d tiles of 32 per wave
@@ -634,19 +635,18 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
                                              : (u32x4){0u, 0u, 0u, 0u};
       }
     }
+    // loads only: any arithmetic on a loaded value here would wait for all of them
     if (threadIdx.x < kBwdTile) {
       const int r = threadIdx.x;
       const int64_t pos = qt * kBwdTile + r;
-      const bool in = pos < a.n;
-      pre_l = in ? a.lse2[bh * a.n + pos] : 0.f;
-      pre_d = in ? a.delta[bh * a.n + pos] : 0.f;
-      pre_b = !in ? -INFINITY
-                  : (branch ? 0.f
-                            : a.sel_logp[((bg * a.n_qt + qt) * a.nb + blk) * kBwdTile + r] *
-                                  kLog2e);
+      if (pos < a.n) {
+        pre_l = a.lse2[bh * a.n + pos];
+        pre_d = a.delta[bh * a.n + pos];
+        if (!branch) pre_b = a.sel_logp[((bg * a.n_qt + qt) * a.nb + blk) * kBwdTile + r];
+      }
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int64_t qt, bool branch) {
 #pragma unroll
     for (int m = 0; m < NBLK; ++m) {
       const int e = threadIdx.x + 256 * m;
@@ -667,9 +667,10 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
       }
     }
     if (threadIdx.x < kBwdTile) {
-      rowl[threadIdx.x] = pre_l;
-      rowd[threadIdx.x] = pre_d;
-      rowb[threadIdx.x] = pre_b;
+      const bool in = qt * kBwdTile + threadIdx.x < a.n;
+      rowl[threadIdx.x] = in ? pre_l : 0.f;
+      rowd[threadIdx.x] = in ? pre_d : 0.f;
+      rowb[threadIdx.x] = !in ? -INFINITY : (branch ? 0.f : pre_b * kLog2e);
     }
   };
   __shared__ int8_t flags[kFlagTiles];
@@ -692,9 +693,14 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
         for (++ntq; ntq < nq && !flags[ntq];) ++ntq;
       }
       __syncthreads();   // the previous item is done with the staged rows
-      stage();
+      stage(qt, branch);
       __syncthreads();
       if (ntq < nq) prefetch(q0 + ntq, nhh, flags[ntq] == 1);
+      const int zero_below =
+          !kvalid ? kBwdTile
+                  : (branch ? (int)min((int64_t)kBwdTile,
+                                       max((int64_t)0, kpos - qt * kBwdTile))
+                            : 0);
 #pragma unroll 1
       for (int qh = 0; qh < 2; ++qh) {
         // S and dP: queries 32 qh + row, keys of this wave's tile (lane l32)
@@ -707,20 +713,28 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(BwdArgs a) {
           sv = mfma32(as_bf16x8(*(const u32x4*)(Qr + roff)), kf[s2], sv);
           dpv = mfma32(as_bf16x8(*(const u32x4*)(Or + roff)), vf[s2], dpv);
         }
-        // element i: query 32 qh + 8 (i / 4) + 4 lh + i % 4, key kpos
+        // element i: query 32 qh + 8 (i / 4) + 4 lh + i % 4, key kpos; rows
+        // below `zero_below` get p = 0 (all rows for a key past the end; in
+        // the diagonal chunk the rows before the key)
         bf16x8 pf[2], dsf[2];
+        const int rbase = 32 * qh + 4 * lh;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           float pv[8], dv8[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = 8 * k2 + e;
-            const int r = 32 * qh + 8 * (i / 4) + 4 * lh + (i % 4);
-            const int64_t pos = qt * kBwdTile + r;
-            float p = exp2f(fmaf(sv[i], a.scale_log2, rowb[r]) - rowl[r]);
-            if (!kvalid || (branch && kpos > pos)) p = 0.f;
-            pv[e] = p;
-            dv8[e] = p * (dpv[i] - rowd[r]);
+          for (int gq = 0; gq < 2; ++gq) {
+            const int r0 = rbase + 8 * (2 * k2 + gq);
+            const f32x4 lb = *(const f32x4*)(rowb + r0);
+            const f32x4 ll = *(const f32x4*)(rowl + r0);
+            const f32x4 ld4 = *(const f32x4*)(rowd + r0);
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int i = 8 * k2 + 4 * gq + e4;
+              float p = fast_exp2(fmaf(sv[i], a.scale_log2, lb[e4]) - ll[e4]);
+              if (r0 + e4 < zero_below) p = 0.f;
+              pv[4 * gq + e4] = p;
+              dv8[4 * gq + e4] = p * (dpv[i] - ld4[e4]);
+            }
           }
           pf[k2] = as_bf16x8((u32x4){pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
                                      pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])});
