@@ -383,9 +383,9 @@ __global__ __launch_bounds__(NT) void bwd_rows_mfma_kernel(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) cs += exp2f(st[kt][i] - mn);
+      for (int i = 0; i < 16; ++i) cs += fast_exp2(st[kt][i] - mn);
     cs = xor_reduce<32>(cs, DppAdd{});
-    l = l * exp2f(m - mn) + cs;
+    l = l * fast_exp2(m - mn) + cs;
     m = mn;
   }
   const float lse = m + log2f(l);
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(NT) void bwd_rows_mfma_kernel(BwdArgs a) {
       float dv8[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pv = exp2f(st[kt][i0 + e] - lse);   // 0 where masked
+        const float pv = fast_exp2(st[kt][i0 + e] - lse);   // 0 where masked
         dv8[e] = pv * (dp[kt][i0 + e] - dlt);
         csum += dv8[e];
       }
