@@ -29,8 +29,9 @@
  *     GQA group.
  *
  * Conventions for every entry point:
- *   - All tensor pointers are DEVICE pointers unless stated; tensors are dense
- *     row-major with the shapes given.  q, o: [B, H, n, d]; k, v:
+ *   - All tensor pointers are DEVICE pointers unless stated, 16-byte aligned
+ *     (DASH_ERR_INVALID_ARG otherwise); tensors are dense row-major with the
+ *     shapes given.  q, o: [B, H, n, d]; k, v:
  *     [B, Hkv, kv_len, d] (one block of one head is a contiguous run).  Query
  *     head h reads KV head h / (H / Hkv).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null

@@ -17,6 +17,13 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
+// The kernels move tensors with 16-byte vector accesses; a null pointer
+// passes here (the null checks are separate).
+template <typename... P>
+bool aligned16(P... ptrs) {
+  return ((((uintptr_t)ptrs) % 16 == 0) && ...);
+}
+
 dash_status check_params(const dash_params* p, Shape* s) {
   if (!p) return DASH_ERR_INVALID_ARG;
   if (p->batch < 1 || p->n_heads < 1 || p->n_kv_heads < 1) return DASH_ERR_INVALID_ARG;
@@ -174,6 +181,7 @@ dash_status dash_summarize(const dash_params* p, const void* k, int64_t kv_len, 
   dash_status st = check_params(p, &s);
   if (st != DASH_OK) return st;
   if (!k || !w_s || !summ) return DASH_ERR_INVALID_ARG;
+  if (!aligned16(k, w_s, q_bar, summ)) return DASH_ERR_INVALID_ARG;
   if (blk_begin < 0 || blk_end < blk_begin || kv_len < blk_end * s.bs || summ_blocks < blk_end)
     return DASH_ERR_INVALID_ARG;
   if (!grid_ok((blk_end - blk_begin) * s.B * s.Hkv)) return DASH_ERR_UNSUPPORTED;
@@ -187,6 +195,7 @@ dash_status dash_route(const dash_params* p, const void* q, int64_t n, const flo
   dash_status st = check_params(p, &s);
   if (st != DASH_OK) return st;
   if (n < 0 || !q || !summ) return DASH_ERR_INVALID_ARG;
+  if (!aligned16(q, summ)) return DASH_ERR_INVALID_ARG;
   if ((st = check_route_buf(route)) != DASH_OK) return st;
   if (summ_blocks < n / s.bs) return DASH_ERR_INVALID_ARG;
   if (n == 0) return DASH_OK;
@@ -204,6 +213,7 @@ dash_status dash_attend(const dash_params* p, const void* q, const void* k, cons
   if (n < 0 || !q || !k || !v || !o || !route || !route->sel_count || !route->sel_idx ||
       !route->sel_logp)
     return DASH_ERR_INVALID_ARG;
+  if (!aligned16(q, k, v, o)) return DASH_ERR_INVALID_ARG;
   if (n == 0) return DASH_OK;
   if (!grid_ok(((n + kQT - 1) / kQT) * s.B * s.H) || !seq_bytes_ok(s, n))
     return DASH_ERR_UNSUPPORTED;
@@ -232,6 +242,7 @@ static dash_status prefill_impl(const dash_params* p, const void* q, const void*
   dash_status st = check_params(p, &s);
   if (st != DASH_OK) return st;
   if (n < 0 || !q || !k || !v || !w_s || !summ || !o) return DASH_ERR_INVALID_ARG;
+  if (!aligned16(q, k, v, w_s, q_bar, summ, o)) return DASH_ERR_INVALID_ARG;
   if (summ_blocks < n / s.bs) return DASH_ERR_INVALID_ARG;
   if (n == 0) return DASH_OK;
   const PrefillLayout L = prefill_layout(s, n);
@@ -292,6 +303,7 @@ dash_status dash_prefill_backward(const dash_params* p, const void* q, const voi
   if (st != DASH_OK) return st;
   if (n < 0 || !q || !k || !v || !o || !d_o || !w_s || !summ || !dq || !dk || !dv || !dw_s)
     return DASH_ERR_INVALID_ARG;
+  if (!aligned16(q, k, v, o, d_o, w_s, summ, dq, dk, dv, dw_s)) return DASH_ERR_INVALID_ARG;
   if ((st = check_route_buf(route)) != DASH_OK) return st;
   if (summ_blocks < n / s.bs) return DASH_ERR_INVALID_ARG;
   if (n == 0) return DASH_OK;
@@ -318,6 +330,7 @@ static dash_status decode_impl(const dash_params* p, const void* q, const void* 
   if (st != DASH_OK) return st;
   if (!q || !k_cache || !v_cache || !cache_len || !w_s || !summ || !o || max_len < 1)
     return DASH_ERR_INVALID_ARG;
+  if (!aligned16(q, k_cache, v_cache, w_s, q_bar, summ, o)) return DASH_ERR_INVALID_ARG;
   if (summ_blocks < (max_len + s.bs - 1) / s.bs) return DASH_ERR_INVALID_ARG;
   if (route && check_route_buf(route) != DASH_OK) return DASH_ERR_INVALID_ARG;
   const dash::DecodeLayout L = dash::decode_layout(s, max_len);

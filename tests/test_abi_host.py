@@ -105,6 +105,11 @@ def test_null_pointers_and_sizes():
                             FAKE, need - 1, None) == L.DASH_ERR_WORKSPACE_TOO_SMALL
     assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, None, FAKE, 16, FAKE,
                             FAKE + 8, need, None) == L.DASH_ERR_INVALID_ARG
+    # tensors must be 16-byte aligned
+    assert lib.dash_prefill(ctypes.byref(p), FAKE + 4, FAKE, FAKE, 1024, FAKE, None, FAKE, 16,
+                            FAKE, FAKE, need, None) == L.DASH_ERR_INVALID_ARG
+    assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1024, FAKE, FAKE + 8, FAKE, 16,
+                            FAKE, FAKE, need, None) == L.DASH_ERR_INVALID_ARG
     # empty problem: nothing to do
     assert lib.dash_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, 0, FAKE,
                             FAKE, 0, None) == L.DASH_OK
