@@ -707,11 +707,20 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
         f32x16 sv, dpv;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sv[i] = dpv[i] = 0.f;
+        // A fragments read one k-step ahead of their MFMAs
+        const int roff0 = (32 * qh + l32) * RP + 8 * lh;
+        u32x4 qa = *(const u32x4*)(Qr + roff0), oa = *(const u32x4*)(Or + roff0);
 #pragma unroll
         for (int s2 = 0; s2 < D / 16; ++s2) {
-          const int roff = (32 * qh + l32) * RP + 16 * s2 + 8 * lh;
-          sv = mfma32(as_bf16x8(*(const u32x4*)(Qr + roff)), kf[s2], sv);
-          dpv = mfma32(as_bf16x8(*(const u32x4*)(Or + roff)), vf[s2], dpv);
+          u32x4 qn = qa, on = oa;
+          if (s2 + 1 < D / 16) {
+            qn = *(const u32x4*)(Qr + roff0 + 16 * (s2 + 1));
+            on = *(const u32x4*)(Or + roff0 + 16 * (s2 + 1));
+          }
+          sv = mfma32(as_bf16x8(qa), kf[s2], sv);
+          dpv = mfma32(as_bf16x8(oa), vf[s2], dpv);
+          qa = qn;
+          oa = on;
         }
         // element i: query 32 qh + 8 (i / 4) + 4 lh + i % 4, key kpos; rows
         // below `zero_below` get p = 0 (all rows for a key past the end; in
