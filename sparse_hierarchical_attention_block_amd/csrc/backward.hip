@@ -250,7 +250,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
 // each 16 permuted as the accumulator order of dS^T needs (key 16m+8a+4b+r
 // at column 16m+8b+4a+r).  A first pass over the chunks (S^T only) gives lse.
 template <int D, int NT>
-__global__ __launch_bounds__(NT) void bwd_rows_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT >= 256 ? 2 : 1)))
+void bwd_rows_mfma_kernel(BwdArgs a) {
   constexpr int KP = D + 8;            // row pitch of K and V (bf16)
   constexpr int VP = kBwdChunk + 8;    // row pitch of K^T
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kBwdChunk * KP];
@@ -337,18 +338,34 @@ __global__ __launch_bounds__(NT) void bwd_rows_mfma_kernel(BwdArgs a) {
                                                         pack_hi(in[2].y, in[3].y)};
     }
   };
+  // acc[kt] += X[32 kt + l32, :] (row-major in LDS, pitch KP) times the
+  // register fragments fr, the two chains interleaved and each A fragment
+  // read one k-step ahead of its MFMA
+  auto two_chains = [&](const __bf16* X, const bf16x8 (&fr)[D / 16], f32x16 (&acc)[2]) {
+    const __bf16* x0 = X + l32 * KP + 8 * lh;
+    const __bf16* x1 = x0 + 32 * KP;
+    u32x4 a0 = *(const u32x4*)x0, a1 = *(const u32x4*)x1;
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
+      u32x4 n0 = a0, n1 = a1;
+      if (s2 + 1 < D / 16) {
+        n0 = *(const u32x4*)(x0 + 16 * (s2 + 1));
+        n1 = *(const u32x4*)(x1 + 16 * (s2 + 1));
+      }
+      acc[0] = mfma32(as_bf16x8(a0), fr[s2], acc[0]);
+      acc[1] = mfma32(as_bf16x8(a1), fr[s2], acc[1]);
+      a0 = n0;
+      a1 = n1;
+    }
+  };
   // S^T of the staged chunk, masked, in log2 units with the bias: st[kt][i]
   // is query l32, key 32 kt + 8 (i / 4) + 4 lh + i % 4
   auto scores = [&](int c, float bias2, f32x16 (&st)[2]) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2)
-        st[kt] = mfma32(as_bf16x8(*(const u32x4*)(Ks + (32 * kt + l32) * KP + 16 * s2 + 8 * lh)),
-                        qf[s2], st[kt]);
-    }
+    two_chains(Ks, qf, st);
     const bool diag = c == w.n_own - 1;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -412,14 +429,10 @@ __global__ __launch_bounds__(NT) void bwd_rows_mfma_kernel(BwdArgs a) {
     f32x16 st[2], dp[2];
     scores(c, bias2, st);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) dp[kt][i] = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2)
-        dp[kt] = mfma32(as_bf16x8(*(const u32x4*)(Vs + (32 * kt + l32) * KP + 16 * s2 + 8 * lh)),
-                        df[s2], dp[kt]);
-    }
+    two_chains(Vs, df, dp);
     // dS^T, its column sums (the bias gradient), and the bf16 B operands
     float csum = 0.f;
     bf16x8 dsf[4];
@@ -439,12 +452,21 @@ __global__ __launch_bounds__(NT) void bwd_rows_mfma_kernel(BwdArgs a) {
     }
     csum = xor_reduce<32>(csum, DppAdd{});
     if (blk >= 0) bacc += csum;
+    {   // dQ^T += K^T dS^T, each A fragment read one MFMA ahead
+      constexpr int NQ = 4 * (D / 32);
+      u32x4 ka = *(const u32x4*)(Kt + l32 * VP + 8 * lh);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        dqa[dt] = mfma32(as_bf16x8(*(const u32x4*)(Kt + (32 * dt + l32) * VP + 16 * ks + 8 * lh)),
-                         dsf[ks], dqa[dt]);
+      for (int x = 0; x < NQ; ++x) {
+        const int ks = x / (D / 32), dt = x % (D / 32);
+        u32x4 kn = ka;
+        if (x + 1 < NQ) {
+          const int ks1 = (x + 1) / (D / 32), dt1 = (x + 1) % (D / 32);
+          kn = *(const u32x4*)(Kt + (32 * dt1 + l32) * VP + 16 * ks1 + 8 * lh);
+        }
+        dqa[dt] = mfma32(as_bf16x8(ka), dsf[ks], dqa[dt]);
+        ka = kn;
+      }
+    }
     if (blk >= 0 && (c - w.n_own) % w.cpb == w.cpb - 1) {
       if (valid && lh == 0 && bias2 != -INFINITY)
         atomicAdd(&a.dlogp[(tile * a.nb + blk) * kBwdTile + qloc], a.sigma * bacc);
