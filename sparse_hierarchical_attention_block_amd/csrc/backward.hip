@@ -53,6 +53,7 @@ struct BwdArgs {
   float* dlogp;             // [B, Hkv, n_qt, nb, 64]
   float* ucoarse;           // [B, Hkv, n_qt, G, nb, 64] entmax u of the coarse scores
   float* ds;                // [B, Hkv, nb, D]
+  float* dspart;            // [B, Hkv, n_qt, nb, D] each tile's share of ds (its candidates)
   float* mean;              // [B, Hkv, nb, D]
   int64_t n, n_qt, nb;
   int B, H, Hkv, G, bs, window;
@@ -808,7 +809,9 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
 // dZ S (64 x d) and the tile's share of the summary gradient dZ^T Q (t x d)
 // are small dense products: summary rows come through LDS 32 at a time, each
 // thread owns a 2 x 4 block of X, a 4 x (D / 16) block of dq and a 2 x (D / 16)
-// block of the summary gradient, which is added into ds with atomics.  LDS
+// block of the summary gradient, which goes to the tile's own rows of dspart
+// (the first head stores, the others add; the block-means kernel sums the
+// tiles).  LDS
 // rows are read 4 floats at a time; the row pitch D + 4 and the assignment of
 // rows {r, r + 32} and of column groups {4 c, 64 + 4 c} to threads keep the
 // 8 lanes of each 16-byte read on distinct banks.
@@ -975,11 +978,11 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
           const int j = j0 + 2 * jq + jj;
           if (j < t)
 #pragma unroll
-            for (int v = 0; v < NV; ++v)
-#pragma unroll
-              for (int kk = 0; kk < 4; ++kk)
-                atomicAdd(&a.ds[(bg * a.nb + j) * D + 64 * v + 4 * cc + kk],
-                          dsa[jj][v][kk] * a.rs);
+            for (int v = 0; v < NV; ++v) {
+              f32x4* dst = (f32x4*)(a.dspart + (tile * a.nb + j) * D + 64 * v + 4 * cc);
+              const f32x4 val = dsa[jj][v] * a.rs;
+              *dst = hh == 0 ? val : *dst + val;
+            }
         }
       }
     }
@@ -1011,7 +1014,17 @@ __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
   float m = 0.f;
   for (int t = 0; t < a.bs; ++t) m += ld<T>(a.k, (k0 + t) * D + r);
   mrow[r] = m / (float)a.bs;
-  const float* dsr = a.ds + (bg * a.nb + j) * D;
+  // ds_j: the shares of the tiles that have block j among their candidates,
+  // floor(64 qt / bs) - (window - 1) > j
+  __shared__ float dsr[D];
+  const int64_t qt0 = ((j + a.window) * a.bs + kBwdTile - 1) / kBwdTile;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int64_t qt = qt0; qt < a.n_qt; ++qt)
+    acc += a.dspart[((bg * a.n_qt + qt) * a.nb + j) * D + r];
+  a.ds[(bg * a.nb + j) * D + r] = acc;
+  dsr[r] = acc;
+  __syncthreads();
   float dm = 0.f;
   for (int c = 0; c < D; ++c) dm = fmaf(dsr[c], a.w_s[r * D + c], dm);
   dm /= (float)a.bs;
@@ -1055,6 +1068,8 @@ BwdLayout bwd_layout(const Shape& s, int64_t n) {
   L.off_u = off;    off = al(off + sizeof(float) * s.B * s.H * n_qt * kBwdTile * nb);
   L.off_ds = off;    off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
   L.off_mean = off;  off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
+  L.off_dspart = off;
+  off = al(off + sizeof(float) * s.B * s.Hkv * n_qt * nb * s.d);
   L.total = off;
   return L;
 }
@@ -1134,6 +1149,7 @@ hipError_t launch_prefill_backward(const Shape& s, const void* q, const void* k,
   a.ucoarse = (float*)(ws + L.off_u);
   a.ds = (float*)(ws + L.off_ds);
   a.mean = (float*)(ws + L.off_mean);
+  a.dspart = (float*)(ws + L.off_dspart);
   a.n = n;
   a.n_qt = (n + kBwdTile - 1) / kBwdTile;
   a.nb = (n + s.bs - 1) / s.bs;

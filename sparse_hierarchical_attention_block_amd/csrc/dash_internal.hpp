@@ -77,7 +77,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
 // Backward pass of the causal prefill (mean-pooled summaries): workspace
 // layout and launch.
 struct BwdLayout {
-  size_t off_lse, off_delta, off_dlogp, off_u, off_ds, off_mean, total;
+  size_t off_lse, off_delta, off_dlogp, off_u, off_ds, off_mean, off_dspart, total;
 };
 BwdLayout bwd_layout(const Shape& s, int64_t n);
 hipError_t launch_prefill_backward(const Shape& s, const void* q, const void* k, const void* v,
