@@ -861,6 +861,19 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
         Sc[jr * QP + c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
       }
       __syncthreads();
+      // the routing inputs of this thread's (row, candidate) pairs, loaded
+      // before the scores so that their latency hides behind the FMAs
+      float lpv[2][4], dlv[2][4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = j0 + 4 * jg + k;
+          const bool in = j < t && p0 + rg + 32 * i < a.n;
+          const int64_t li = (tile * a.nb + j) * kBwdTile + rg + 32 * i;
+          lpv[i][k] = in ? a.sel_logp[li] : -INFINITY;
+          dlv[i][k] = in ? a.dlogp[li] : 0.f;
+        }
       float x[2][4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -890,10 +903,9 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
           if (j >= t) continue;
           const float y = x[i][k] * a.xscale - tau2[i];
           const float u = y > 0.f ? (a.ue == 0.f ? 1.f : powf(y, a.ue)) : 0.f;
-          const int64_t li = (tile * a.nb + j) * kBwdTile + r;
-          const float lp = a.sel_logp[li];
+          const float lp = lpv[i][k];
           float dp = 0.f;
-          if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)a.G;
+          if (a.sigma > 0.f && lp != -INFINITY) dp = dlv[i][k] / expf(lp / a.sigma) / (float)a.G;
           su[i] += u;
           sud[i] = fmaf(u, dp, sud[i]);
           a.ucoarse[((tile * a.G + hh) * a.nb + j) * kBwdTile + r] = u;
@@ -921,27 +933,37 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < NV; ++v) dqa[i][v] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // phase B inputs of a chunk (8 (row, candidate) pairs per thread), loaded
+    // one chunk ahead
+    constexpr int NB8 = kBwdTile * kRtJ / 256;
+    float blp[NB8], bdl[NB8], bu[NB8];
+    auto load_b = [&](int j0) {
+#pragma unroll
+      for (int m = 0; m < NB8; ++m) {
+        const int e = tid + 256 * m, r = e % kBwdTile, j = j0 + e / kBwdTile;
+        const bool in = j < t && p0 + r < a.n;
+        const int64_t li = (tile * a.nb + j) * kBwdTile + r;
+        blp[m] = in ? a.sel_logp[li] : -INFINITY;
+        bdl[m] = in ? a.dlogp[li] : 0.f;
+        bu[m] = in ? a.ucoarse[((tile * a.G + hh) * a.nb + j) * kBwdTile + r] : 0.f;
+      }
+    };
+    load_b(0);
     for (int j0 = 0; j0 < t; j0 += kRtJ) {
       __syncthreads();
       for (int e = tid; e < kRtJ * D; e += 256) {
         const int jr = e / D, c = e % D;
         Sc[jr * QP + c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
       }
-      for (int e = tid; e < kBwdTile * kRtJ; e += 256) {
-        const int r = e % kBwdTile, jr = e / kBwdTile, j = j0 + jr;
-        const int64_t pos = p0 + r;
-        float dz = 0.f;
-        if (j < t && pos < a.n) {
-          const int64_t li = (tile * a.nb + j) * kBwdTile + r;
-          const float lp = a.sel_logp[li];
-          float dp = 0.f;
-          if (a.sigma > 0.f && lp != -INFINITY) dp = a.dlogp[li] / expf(lp / a.sigma) / (float)a.G;
-          const float u = a.ucoarse[((tile * a.G + hh) * a.nb + j) * kBwdTile + r];
-          dz = a.gamma * u * (dp - corr_s[r]);
-        }
-        Zt[jr * ZP + r] = dz;
+#pragma unroll
+      for (int m = 0; m < NB8; ++m) {
+        const int e = tid + 256 * m, r = e % kBwdTile, jr = e / kBwdTile;
+        float dp = 0.f;
+        if (a.sigma > 0.f && blp[m] != -INFINITY) dp = bdl[m] / expf(blp[m] / a.sigma) / (float)a.G;
+        Zt[jr * ZP + r] = a.gamma * bu[m] * (dp - corr_s[r]);   // 0 outside (bu = 0)
       }
       __syncthreads();
+      if (j0 + kRtJ < t) load_b(j0 + kRtJ);
       const int jn = min(kRtJ, t - j0);
       for (int jr = 0; jr < jn; ++jr) {
         const f32x4 zv = *(const f32x4*)(Zt + jr * ZP + 4 * rq);
