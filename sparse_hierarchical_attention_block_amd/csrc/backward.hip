@@ -842,9 +842,19 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
   for (int hh = 0; hh < a.G; ++hh) {
     const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
     __syncthreads();
-    for (int e = tid; e < kBwdTile * D; e += 256) {
-      const int r = e / D, c = e % D;
-      Qh[r * QP + c] = p0 + r < a.n ? ld<T>(a.q, (bh * a.n + p0 + r) * D + c) : 0.f;
+    // q rows, 16 bytes per load
+    constexpr int VE = 16 / (int)sizeof(T);
+    for (int e = tid; e < kBwdTile * D / VE; e += 256) {
+      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (p0 + r < a.n) w = *(const u32x4*)((const T*)a.q + (bh * a.n + p0 + r) * D + c);
+      if constexpr (sizeof(T) == 2) {
+        *(f32x4*)(Qh + r * QP + c) = (f32x4){bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+        *(f32x4*)(Qh + r * QP + c + 4) =
+            (f32x4){bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+      } else {
+        *(u32x4*)(Qh + r * QP + c) = w;
+      }
     }
     float tau2[2];
 #pragma unroll
