@@ -839,6 +839,25 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
   const int rg = tid % 32, jg = tid / 32;   // phase A: rows rg + 32 i; candidates 4 jg + k
   const int rq = tid % 16, cq = tid / 16;   // dq: rows 4 rq + i; columns 64 v + 4 cq + [0, 4)
   const int jq = tid / 16, cc = tid % 16;   // ds: candidates 2 jq + {0, 1}; columns as dq's
+  // summary rows of the next chunk are loaded (16 bytes at a time) into
+  // registers while the current chunk is computed
+  constexpr int SV = kRtJ * D / 4 / 256;   // float4s per thread per chunk
+  f32x4 spre[SV];
+  auto load_s = [&](int j0) {
+#pragma unroll
+    for (int m = 0; m < SV; ++m) {
+      const int e = tid + 256 * m, jr = e / (D / 4), c4 = e % (D / 4);
+      spre[m] = j0 + jr < t ? *(const f32x4*)(srow + (int64_t)(j0 + jr) * D + 4 * c4)
+                            : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto store_s = [&]() {
+#pragma unroll
+    for (int m = 0; m < SV; ++m) {
+      const int e = tid + 256 * m, jr = e / (D / 4), c4 = e % (D / 4);
+      *(f32x4*)(Sc + jr * QP + 4 * c4) = spre[m];
+    }
+  };
   for (int hh = 0; hh < a.G; ++hh) {
     const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
     __syncthreads();
@@ -864,13 +883,12 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
     }
     // phase A: u and the row sums of u and u dp
     float su[2] = {0.f, 0.f}, sud[2] = {0.f, 0.f};
+    load_s(0);
     for (int j0 = 0; j0 < t; j0 += kRtJ) {
       __syncthreads();
-      for (int e = tid; e < kRtJ * D; e += 256) {
-        const int jr = e / D, c = e % D;
-        Sc[jr * QP + c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
-      }
+      store_s();
       __syncthreads();
+      if (j0 + kRtJ < t) load_s(j0 + kRtJ);
       // the routing inputs of this thread's (row, candidate) pairs, loaded
       // before the scores so that their latency hides behind the FMAs
       float lpv[2][4], dlv[2][4];
@@ -959,12 +977,10 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
       }
     };
     load_b(0);
+    load_s(0);
     for (int j0 = 0; j0 < t; j0 += kRtJ) {
       __syncthreads();
-      for (int e = tid; e < kRtJ * D; e += 256) {
-        const int jr = e / D, c = e % D;
-        Sc[jr * QP + c] = j0 + jr < t ? srow[(int64_t)(j0 + jr) * D + c] : 0.f;
-      }
+      store_s();
 #pragma unroll
       for (int m = 0; m < NB8; ++m) {
         const int e = tid + 256 * m, r = e % kBwdTile, jr = e / kBwdTile;
@@ -973,7 +989,10 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
         Zt[jr * ZP + r] = a.gamma * bu[m] * (dp - corr_s[r]);   // 0 outside (bu = 0)
       }
       __syncthreads();
-      if (j0 + kRtJ < t) load_b(j0 + kRtJ);
+      if (j0 + kRtJ < t) {
+        load_b(j0 + kRtJ);
+        load_s(j0 + kRtJ);
+      }
       const int jn = min(kRtJ, t - j0);
       for (int jr = 0; jr < jn; ++jr) {
         const f32x4 zv = *(const f32x4*)(Zt + jr * ZP + 4 * rq);
