@@ -17,12 +17,15 @@
 //   route   per (query tile, KV head): dpbar = dlogp / pbar, dp_h = dpbar / G,
 //           the entmax Jacobian with u = (x - tau)_+^((2-alpha)/(alpha-1)):
 //           dzbar = gamma (u dp - u (u.dp) / sum u); dq += dzbar . s / sqrt(d)
-//           and the summaries' gradient ds_j = sum over the rows and heads of
-//           dzbar_j q / sqrt(d) (atomics across tiles)
-//   means   dk of block j += (ds_j W_s^T) / bs; block means m_j
+//           and the tile's share of the summaries' gradient, the sum over its
+//           rows and heads of dzbar_j q / sqrt(d), into its own partial rows
+//   means   ds_j = sum of the tiles' partial rows; dk of block j +=
+//           (ds_j W_s^T) / bs; block means m_j
 //   w_s     dW_s = sum_j m_j^T ds_j
-// Every product is plain float32 FMAs (no MFMA); a row or key is spread over
-// 4 lanes of D/4 columns each, dot products reduced over those lanes.
+// bf16 inputs: the rows and keys products run on MFMA (bf16 operands, float32
+// accumulation).  float32 inputs keep plain float32 FMAs, a row or key spread
+// over 4 lanes of D/4 columns each.  The routing gradient is float32 FMAs
+// for both.
 #include "dash_internal.hpp"
 #include "device_common.hpp"
 
