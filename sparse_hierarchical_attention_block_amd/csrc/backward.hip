@@ -777,15 +777,25 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
                                       pack_bf16(dv8[4], dv8[5]), pack_bf16(dv8[6], dv8[7])});
         }
         // dV^T += dO^T P, dK^T += Q^T dS over the two 16-query k-steps
+        {   // A fragments read one step ahead of their MFMAs
+          auto toff = [&](int x) {
+            return (32 * (NDT * dh + x % NDT) + l32) * TP + 16 * (2 * qh + x / NDT) + 8 * lh;
+          };
+          u32x4 oa = *(const u32x4*)(Ot + toff(0)), qa = *(const u32x4*)(Qt + toff(0));
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int t = 0; t < NDT; ++t) {
-            const int dt = NDT * dh + t;
-            const int toff = (32 * dt + l32) * TP + 16 * (2 * qh + k2) + 8 * lh;
-            dva[t] = mfma32(as_bf16x8(*(const u32x4*)(Ot + toff)), pf[k2], dva[t]);
-            dka[t] = mfma32(as_bf16x8(*(const u32x4*)(Qt + toff)), dsf[k2], dka[t]);
+          for (int x = 0; x < 2 * NDT; ++x) {
+            const int k2 = x / NDT, t = x % NDT;
+            u32x4 on = oa, qn = qa;
+            if (x + 1 < 2 * NDT) {
+              on = *(const u32x4*)(Ot + toff(x + 1));
+              qn = *(const u32x4*)(Qt + toff(x + 1));
+            }
+            dva[t] = mfma32(as_bf16x8(oa), pf[k2], dva[t]);
+            dka[t] = mfma32(as_bf16x8(qa), dsf[k2], dka[t]);
+            oa = on;
+            qa = qn;
           }
+        }
       }
       tq = ntq;
       hh = nhh;
