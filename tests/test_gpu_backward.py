@@ -35,6 +35,10 @@ CASES = {
     "bf16_gqa4_d128": (W.get("prefill_8k").replace(seq_len=768, n_heads=8, n_kv_heads=2), 1e-2),
     "bf16_bs128_batch2": (W.get("tiny").replace(batch=2, n_heads=4, n_kv_heads=2, seq_len=700,
                                                 block_size=128, dtype="bf16", gamma=6.0), 1e-2),
+    # 128-key blocks with a two-block branch (the summary-gradient sum starts at tile 2 j + 4)
+    "bf16_bs128_window2": (W.get("tiny").replace(n_heads=4, n_kv_heads=2, seq_len=900,
+                                                 block_size=128, dtype="bf16", gamma=6.0,
+                                                 window=2), 1e-2),
     # one head per KV head (two-wave rows workgroups), ragged tail
     "bf16_mha_d128": (W.get("prefill_8k").replace(seq_len=600, n_heads=2, n_kv_heads=2), 1e-2),
     # eight heads per KV head (two workgroups per tile), window and prior strength
