@@ -300,6 +300,25 @@ dash_status dash_decode_paged(const dash_params* p, const void* q, const void* k
                               int64_t summ_blocks, void* o, const dash_route_buf* route,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Measurement helpers (not part of the attention computation) ---------
+ * What this GPU attains, in the same process, for stating each kernel's
+ * roofline fraction against a measured ceiling beside the nominal one.
+ *
+ * dash_peak_stream: one grid-stride pass of 16-byte loads over `bytes` bytes
+ * of src (a multiple of 16, both pointers 16-byte aligned).  mode 0 copies
+ * them to dst (dst holds `bytes` bytes); mode 1 only reads them and stores
+ * one 16-byte value per thread, so dst must hold 16 * dash_peak_stream_grid()
+ * bytes.  dash_peak_mfma: every wave of a chip-filling grid runs `iters`
+ * rounds of eight independent v_mfma_f32_32x32x16_bf16 on register operands
+ * (no memory traffic in the loop); *flops receives the flop count of the
+ * launch (host pointer), sink (device) one float per wave, sized by
+ * dash_peak_mfma_grid(). */
+dash_status dash_peak_stream_grid(int64_t* threads);
+dash_status dash_peak_stream(const void* src, void* dst, int64_t bytes, int32_t mode,
+                             void* stream);
+dash_status dash_peak_mfma_grid(int64_t* waves);
+dash_status dash_peak_mfma(int64_t iters, float* sink, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,11 @@ def _load():
             ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int, dp,
             ctypes.c_int64,
             ctypes.c_int64, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.oracle_prefill_backward.restype = ctypes.c_int
+        lib.oracle_prefill_backward.argtypes = [
+            fp, fp, fp, fp, fp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+            ctypes.c_int, dp, dp, dp, dp, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib

@@ -31,12 +31,19 @@ pinned forward oracle; the backward arithmetic is plain numpy.
 Parity pins (tests/test_oracle_backward.py): central finite differences of
 the forward oracle for every input, and the W_s = 0 reduction to the
 autograd of dense biased attention.
+
+``prefill_backward_native`` is the same chain rule written out in C
+(``oracle_prefill_backward`` in dash_oracle.c, one thread per (sequence, KV
+head) pair), for inputs too large for the numpy loops; it carries the same
+finite-difference pins and agrees with ``prefill_backward`` to rounding.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 
-from . import prefill
+from . import _load, _ptr, prefill
 
 
 def prefill_backward(q, k, v, w_s, d_o, *, bs: int, alpha: float, gamma: float,
@@ -117,3 +124,28 @@ def prefill_backward(q, k, v, w_s, d_o, *, bs: int, alpha: float, gamma: float,
     dm = ds @ ws64.T
     dk[:, :, :nb * bs] += np.repeat(dm / bs, bs, axis=2)
     return {"dq": dq, "dk": dk, "dv": dv, "dw_s": dws, "o": o, "o_forward": fwd["o"]}
+
+
+def prefill_backward_native(q, k, v, w_s, d_o, *, bs: int, alpha: float, gamma: float,
+                            sigma: float = 1.0, window: int = 1, threads: int = 0):
+    """prefill_backward computed by the C oracle: returns "dq", "dk", "dv"
+    (float64, shapes of q, k, v) and "dw_s" [d, d]."""
+    q = np.ascontiguousarray(q, np.float32)
+    k = np.ascontiguousarray(k, np.float32)
+    v = np.ascontiguousarray(v, np.float32)
+    w_s = np.ascontiguousarray(w_s, np.float32)
+    d_o = np.ascontiguousarray(d_o, np.float32)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape or d_o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    out = {"dq": np.empty(q.shape), "dk": np.empty(k.shape), "dv": np.empty(v.shape),
+           "dw_s": np.empty((d, d))}
+    fp, dp = ctypes.c_float, ctypes.c_double
+    rc = _load().oracle_prefill_backward(
+        _ptr(q, fp), _ptr(k, fp), _ptr(v, fp), _ptr(w_s, fp), _ptr(d_o, fp), B, H, Hkv, N, d,
+        bs, float(alpha), float(gamma), float(sigma), int(window), _ptr(out["dq"], dp),
+        _ptr(out["dk"], dp), _ptr(out["dv"], dp), _ptr(out["dw_s"], dp), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_prefill_backward rejected its arguments")
+    return out

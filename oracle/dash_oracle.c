@@ -335,6 +335,224 @@ int oracle_forward_rows(const float* q_rows, const int64_t* row_b, const int64_t
   return err ? -1 : 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Backward of the causal prefill (mean-pooled summaries, rule R3).         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages (explainer, "Technical summary" and "Contributions") stress that
+ * the hierarchy is differentiable end to end: alpha-entmax carries gradients
+ * from the fine attention back through the routing into the summaries.  This
+ * is the chain rule of oracle_forward_rows (causal, R1-R9) for one scalar
+ * loss L = sum(o * dO), one query row at a time, in IEEE double:
+ *   Stage 2   P = softmax(l), l_t = q.k_t/sqrt(d) + bias_t, o = sum_t P_t v_t
+ *             dv_t += P_t dO;  dl_t = P_t (dO.v_t - dO.o)
+ *             dq += sum_t dl_t k_t / sqrt(d);  dk_t += dl_t q / sqrt(d)
+ *             bias of a routed block j is sigma log pbar_j:
+ *             dpbar_j = sigma (sum_{t in j} dl_t) / pbar_j
+ *   GQA       pbar_j = (1/G) sum_h p_{h,j}:  dp_{h,j} = dpbar_j / G
+ *   Stage 1   p = alpha-entmax(x); on the support dp/dx = (diag(u) - u u^T /
+ *             sum u) / (alpha - 1) with u = p^(2-alpha), zero elsewhere;
+ *             x = (alpha-1) gamma q.s_j/sqrt(d), so
+ *             dzbar_j = gamma (u_j dp_j - u_j (u.dp) / sum u)
+ *             dq += sum_j dzbar_j s_j / sqrt(d);  ds_j += dzbar_j q / sqrt(d)
+ *   Stage 0   s_j = m_j W_s with m_j the mean of block j's keys:
+ *             dW_s += m_j^T ds_j;  dk_t += (ds_j W_s^T) / bs for t in block j
+ * Blocks with pbar = 0 are masked and take no gradient.
+ *   q, d_o [B, H, N, d]; k, v [B, Hkv, N, d]; w_s [d, d] (float32 values)
+ *   dq [B, H, N, d]; dk, dv [B, Hkv, N, d]; dws [d, d] (double, overwritten)
+ * The (sequence, KV head) pairs run in parallel: each owns its rows of dq,
+ * dk, dv and ds, so no output is written by two threads.  Returns 0, or -1
+ * on invalid arguments.
+ */
+int oracle_prefill_backward(const float* q, const float* k, const float* v, const float* w_s,
+                            const float* d_o, int B, int H, int Hkv, int64_t N, int d, int bs,
+                            double alpha, double gamma, double sigma, int window, double* dq,
+                            double* dk, double* dv, double* dws, int nthreads) {
+  if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || N < 1 || d < 1 || bs < 1) return -1;
+  if (alpha <= 1.0 || alpha > 2.0 || !(sigma >= 0.0) || window < 1) return -1;
+  const int G = H / Hkv;
+  const int64_t nb = N / bs;                     /* complete blocks */
+  const double rs = 1.0 / sqrt((double)d);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int64_t nbg = (int64_t)B * Hkv;
+  /* block means m and summaries s = m W_s, per (b, g) */
+  double* m = (double*)calloc((size_t)(nbg * (nb > 0 ? nb : 1) * d), sizeof(double));
+  double* s = (double*)calloc((size_t)(nbg * (nb > 0 ? nb : 1) * d), sizeof(double));
+  double* ds = (double*)calloc((size_t)(nbg * (nb > 0 ? nb : 1) * d), sizeof(double));
+  memset(dq, 0, sizeof(double) * (size_t)(B * (int64_t)H * N * d));
+  memset(dk, 0, sizeof(double) * (size_t)(nbg * N * d));
+  memset(dv, 0, sizeof(double) * (size_t)(nbg * N * d));
+  for (int64_t u = 0; u < nbg * nb; ++u) {
+    const int64_t bg = u / nb, j = u % nb;
+    const float* kb = k + (bg * N + j * bs) * d;
+    double* mj = m + u * d;
+    for (int t = 0; t < bs; ++t)
+      for (int c = 0; c < d; ++c) mj[c] += (double)kb[(int64_t)t * d + c];
+    for (int c = 0; c < d; ++c) mj[c] /= bs;
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int r = 0; r < d; ++r) acc += mj[r] * (double)w_s[(int64_t)r * d + c];
+      s[u * d + c] = acc;
+    }
+  }
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bg = 0; bg < nbg; ++bg) {
+    const int64_t b = bg / Hkv;
+    const int g = (int)(bg % Hkv);
+    const int64_t nc_max = nb > 0 ? nb : 1;
+    double* x = (double*)malloc(sizeof(double) * nc_max);
+    double* p = (double*)malloc(sizeof(double) * nc_max * G);
+    double* pbar = (double*)malloc(sizeof(double) * nc_max);
+    double* dlogpbar = (double*)malloc(sizeof(double) * nc_max);
+    double* dpbar = (double*)malloc(sizeof(double) * nc_max);
+    const int64_t nkeys_max = (nb + window + 1) * (int64_t)bs;
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * nkeys_max);
+    double* logit = (double*)malloc(sizeof(double) * nkeys_max);
+    double* P = (double*)malloc(sizeof(double) * nkeys_max);
+    double* orow = (double*)malloc(sizeof(double) * d);
+    const float* kg = k + bg * N * d;
+    const float* vg = v + bg * N * d;
+    double* dkg = dk + bg * N * d;
+    double* dvg = dv + bg * N * d;
+    for (int64_t i = 0; i < N; ++i) {
+      const int64_t own = i / bs;
+      const int64_t win0 = own - (window - 1) > 0 ? own - (window - 1) : 0;
+      const int64_t ncand = win0 < nb ? win0 : nb;
+      /* Stage 1 forward: entmax per head, then the group average */
+      for (int64_t j = 0; j < ncand; ++j) pbar[j] = 0.0;
+      for (int hh = 0; hh < G; ++hh) {
+        const float* qv = q + (((b * H) + g * G + hh) * N + i) * d;
+        for (int64_t j = 0; j < ncand; ++j) {
+          const double* sj = s + (bg * nb + j) * d;
+          double z = 0.0;
+          for (int c = 0; c < d; ++c) z += (double)qv[c] * sj[c];
+          x[j] = (alpha - 1.0) * gamma * z * rs;
+        }
+        if (ncand > 0) oracle_entmax(x, (int)ncand, alpha, 0, p + hh * ncand);
+        for (int64_t j = 0; j < ncand; ++j) pbar[j] += p[hh * ncand + j] / G;
+      }
+      /* Stage 2 keys: routed blocks (bias sigma log pbar), then the branch */
+      int64_t nk = 0, nrt = 0;
+      for (int64_t j = 0; j < ncand; ++j) {
+        if (!(pbar[j] > 0.0)) continue;
+        for (int64_t t = j * bs; t < (j + 1) * bs; ++t) {
+          key[nk] = t;
+          logit[nk++] = sigma * log(pbar[j]);
+        }
+      }
+      nrt = nk;
+      for (int64_t t = win0 * bs; t <= i; ++t) {
+        key[nk] = t;
+        logit[nk++] = 0.0;
+      }
+      for (int64_t j = 0; j < ncand; ++j) dlogpbar[j] = 0.0;
+      for (int hh = 0; hh < G; ++hh) {
+        const int64_t hrow = ((b * H) + g * G + hh) * N + i;
+        const float* qv = q + hrow * d;
+        const float* dov = d_o + hrow * d;
+        double* dqv = dq + hrow * d;
+        double mx = -INFINITY;
+        for (int64_t a = 0; a < nk; ++a) {
+          const float* kt = kg + key[a] * d;
+          double dot = 0.0;
+          for (int c = 0; c < d; ++c) dot += (double)qv[c] * (double)kt[c];
+          P[a] = logit[a] + dot * rs;
+          if (P[a] > mx) mx = P[a];
+        }
+        double den = 0.0;
+        for (int64_t a = 0; a < nk; ++a) {
+          P[a] = exp(P[a] - mx);
+          den += P[a];
+        }
+        for (int c = 0; c < d; ++c) orow[c] = 0.0;
+        for (int64_t a = 0; a < nk; ++a) {
+          P[a] /= den;
+          const float* vt = vg + key[a] * d;
+          for (int c = 0; c < d; ++c) orow[c] += P[a] * (double)vt[c];
+        }
+        double doo = 0.0;
+        for (int c = 0; c < d; ++c) doo += (double)dov[c] * orow[c];
+        for (int64_t a = 0; a < nk; ++a) {
+          const float* kt = kg + key[a] * d;
+          const float* vt = vg + key[a] * d;
+          double dov_v = 0.0;
+          for (int c = 0; c < d; ++c) dov_v += (double)dov[c] * (double)vt[c];
+          const double dl = P[a] * (dov_v - doo);
+          double* dkt = dkg + key[a] * d;
+          double* dvt = dvg + key[a] * d;
+          for (int c = 0; c < d; ++c) {
+            dvt[c] += P[a] * (double)dov[c];
+            dqv[c] += dl * (double)kt[c] * rs;
+            dkt[c] += dl * (double)qv[c] * rs;
+          }
+          if (a < nrt) dlogpbar[key[a] / bs] += sigma * dl;
+        }
+      }
+      if (ncand == 0) continue;
+      /* through the bias into pbar, the group average and each head's entmax */
+      for (int64_t j = 0; j < ncand; ++j) dpbar[j] = pbar[j] > 0.0 ? dlogpbar[j] / pbar[j] : 0.0;
+      for (int hh = 0; hh < G; ++hh) {
+        const int64_t hrow = ((b * H) + g * G + hh) * N + i;
+        const float* qv = q + hrow * d;
+        double* dqv = dq + hrow * d;
+        const double* ph = p + hh * ncand;
+        double su = 0.0, sud = 0.0;
+        for (int64_t j = 0; j < ncand; ++j) {
+          const double u = ph[j] > 0.0 ? pow(ph[j], 2.0 - alpha) : 0.0;
+          su += u;
+          sud += u * dpbar[j] / G;
+        }
+        for (int64_t j = 0; j < ncand; ++j) {
+          const double u = ph[j] > 0.0 ? pow(ph[j], 2.0 - alpha) : 0.0;
+          const double dz = gamma * (u * dpbar[j] / G - u * sud / su);
+          if (dz == 0.0) continue;
+          const double* sj = s + (bg * nb + j) * d;
+          double* dsj = ds + (bg * nb + j) * d;
+          for (int c = 0; c < d; ++c) {
+            dqv[c] += dz * sj[c] * rs;
+            dsj[c] += dz * (double)qv[c] * rs;
+          }
+        }
+      }
+    }
+    /* Stage 0: the block means carry ds_j W_s^T / bs to every key of block j */
+    for (int64_t j = 0; j < nb; ++j) {
+      const double* dsj = ds + (bg * nb + j) * d;
+      for (int r = 0; r < d; ++r) {
+        double dm = 0.0;
+        for (int c = 0; c < d; ++c) dm += dsj[c] * (double)w_s[(int64_t)r * d + c];
+        for (int64_t t = j * bs; t < (j + 1) * bs; ++t) dkg[t * d + r] += dm / bs;
+      }
+    }
+    free(x);
+    free(p);
+    free(pbar);
+    free(dlogpbar);
+    free(dpbar);
+    free(key);
+    free(logit);
+    free(P);
+    free(orow);
+  }
+  /* dW_s = sum over every (b, g, j) of m_j^T ds_j */
+  for (int r = 0; r < d; ++r)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t u = 0; u < nbg * nb; ++u) acc += m[u * d + r] * ds[u * d + c];
+      dws[(int64_t)r * d + c] = acc;
+    }
+  free(m);
+  free(s);
+  free(ds);
+  return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

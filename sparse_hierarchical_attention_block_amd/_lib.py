@@ -94,13 +94,22 @@ _lib.dash_decode_paged.argtypes = [_P, _V, _V, _V, _I, _V, _I, _V, _I, _V, _V, _
 _lib.dash_decode.restype = ctypes.c_int
 _lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _V, _I, _V, _R, _V, ctypes.c_size_t,
                              _V]
+_lib.dash_peak_stream_grid.restype = ctypes.c_int
+_lib.dash_peak_stream_grid.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+_lib.dash_peak_stream.restype = ctypes.c_int
+_lib.dash_peak_stream.argtypes = [_V, _V, _I, ctypes.c_int32, _V]
+_lib.dash_peak_mfma_grid.restype = ctypes.c_int
+_lib.dash_peak_mfma_grid.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+_lib.dash_peak_mfma.restype = ctypes.c_int
+_lib.dash_peak_mfma.argtypes = [_I, _V, ctypes.POINTER(ctypes.c_double), _V]
 
 EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
             "dash_route_sizes_decode", "dash_prefill_workspace_bytes",
             "dash_decode_workspace_bytes", "dash_summarize", "dash_route", "dash_attend",
             "dash_mask_to_list", "dash_prefill", "dash_prefill_varlen", "dash_decode",
             "dash_decode_paged", "dash_prefill_backward_workspace_bytes",
-            "dash_prefill_backward")
+            "dash_prefill_backward", "dash_peak_stream_grid", "dash_peak_stream",
+            "dash_peak_mfma_grid", "dash_peak_mfma")
 
 
 # ---------------------------------------------------------------------------------------
@@ -387,3 +396,39 @@ def dash_prefill_backward(p, q, k, v, o, d_o, n, w_s, summ, summ_blocks, route: 
         _dev(dq, "dq", B * H * n * d, f32), _dev(dk, "dk", B * Hkv * n * d, f32),
         _dev(dv, "dv", B * Hkv * n * d, f32), _dev(dw_s, "dw_s", d * d, f32),
         _dev(ws, "ws", 0), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------------------
+# measurement helpers
+# ---------------------------------------------------------------------------------------
+
+def dash_peak_stream_grid() -> int:
+    """Threads of a dash_peak_stream launch (one 16-byte store each in read mode)."""
+    out = ctypes.c_int64()
+    _check("dash_peak_stream_grid", _lib.dash_peak_stream_grid(ctypes.byref(out)))
+    return out.value
+
+
+def dash_peak_stream(src, dst, nbytes, mode, stream=None):
+    """mode 0: copy nbytes of src into dst; mode 1: read nbytes of src only
+    (dst holds 16 bytes per launched thread)."""
+    need = nbytes if mode == 0 else 16 * dash_peak_stream_grid()
+    _check("dash_peak_stream", _lib.dash_peak_stream(
+        _dev(src, "src", nbytes // src.element_size()),
+        _dev(dst, "dst", need // dst.element_size()), int(nbytes), int(mode), _stream(stream)))
+
+
+def dash_peak_mfma_grid() -> int:
+    """Waves of a dash_peak_mfma launch (one float of sink each)."""
+    out = ctypes.c_int64()
+    _check("dash_peak_mfma_grid", _lib.dash_peak_mfma_grid(ctypes.byref(out)))
+    return out.value
+
+
+def dash_peak_mfma(iters, sink, stream=None) -> float:
+    """Launch the register-resident bf16 MFMA loop; returns its flop count."""
+    flops = ctypes.c_double()
+    _check("dash_peak_mfma", _lib.dash_peak_mfma(
+        int(iters), _dev(sink, "sink", dash_peak_mfma_grid(), torch.float32),
+        ctypes.byref(flops), _stream(stream)))
+    return flops.value

@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library ``libdash.so`` in-tree with hipcc.
 
-    python -m sparse_hierarchical_attention_block_amd.build
+    python sparse_hierarchical_attention_block_amd/build.py [--incremental]
 
 Every HIP source is compiled for gfx950 only, with packed-FP32 instruction
 selection disabled, then linked into one shared library next to this file.
@@ -17,15 +17,27 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "dash")
 LIB = os.path.join(PKG, "libdash.so")
-SOURCES = ["summarize.hip", "route.hip", "attend.hip", "decode.hip", "backward.hip", "api.cpp"]
+SOURCES = ["summarize.hip", "route.hip", "attend.hip", "decode.hip", "backward.hip", "peaks.hip",
+           "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src: str) -> str:
+def _headers_mtime() -> float:
+    hdrs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".h"))]
+    hdrs.append(os.path.join(ROOT, "include", "dash.h"))
+    return max(os.path.getmtime(h) for h in hdrs)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if incremental and os.path.exists(out):
+        newest = max(os.path.getmtime(os.path.join(CSRC, src)), _headers_mtime(),
+                     os.path.getmtime(os.path.abspath(__file__)))
+        if os.path.getmtime(out) > newest:
+            return out
     cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -33,10 +45,12 @@ def _compile(src: str) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (incremental: only those older than their .o or
+    any header) and link libdash.so."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, incremental), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "--offload-arch=gfx950", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,4 +63,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
