@@ -248,7 +248,11 @@ dash_status dash_prefill_varlen(const dash_params* p, const void* q, const void*
  * The gradient reaches q through both the fine attention and the coarse
  * scores, k through the attention and the block means, and W_s through the
  * summaries.  Blocks with pbar = 0 take no gradient.  Accumulation in float32
- * (bf16 inputs: the attention products on bf16 MFMA). */
+ * (bf16 inputs: the attention products on bf16 MFMA), every sum in a fixed
+ * order (bitwise reproducible, like the forward).  The per-query-tile arrays
+ * of the workspace hold one slab of tiles at a time, sized so that they stay
+ * within about 1 GiB; the rest grows as n.  DASH_ERR_UNSUPPORTED under the
+ * same 2 GiB per-(sequence, KV head) limit as dash_attend. */
 dash_status dash_prefill_backward_workspace_bytes(const dash_params* p, int64_t n,
                                                   size_t* bytes);
 dash_status dash_prefill_backward(const dash_params* p, const void* q, const void* k,

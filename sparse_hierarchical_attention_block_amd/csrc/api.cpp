@@ -310,7 +310,10 @@ dash_status dash_prefill_backward(const dash_params* p, const void* q, const voi
   const dash::BwdLayout L = dash::bwd_layout(s, n);
   if (!ws || ((uintptr_t)ws % kAlign) != 0) return DASH_ERR_INVALID_ARG;
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE_TOO_SMALL;
-  if (!grid_ok(n * s.B * s.Hkv) || !grid_ok(((n + kQT - 1) / kQT) * s.B * s.H))
+  // the rows kernels address one (sequence, KV head)'s keys and values
+  // through a 31-bit buffer range, as the attend kernel does
+  if (!grid_ok(n * s.B * s.Hkv) || !grid_ok(((n + kQT - 1) / kQT) * s.B * s.H) ||
+      !seq_bytes_ok(s, n))
     return DASH_ERR_UNSUPPORTED;
   return hip_status(dash::launch_prefill_backward(s, q, k, v, o, d_o, n, w_s, summ, summ_blocks,
                                                   *route, dq, dk, dv, dw_s, L, (char*)ws,

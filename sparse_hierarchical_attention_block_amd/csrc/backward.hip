@@ -9,19 +9,27 @@
 //   rows    per (query tile, head): log-sum-exp and delta = dO.o by a first
 //           pass over the tile's chunks, then dl_t = P_t (dO.v_t - delta),
 //           dq = sum dl_t k_t / sqrt(d), and the bias gradient of every
-//           routed block, sigma * sum_{t in block} dl_t, added over the
-//           group's heads into dlogp[tile, block, row]
-//   keys    per 64-key chunk of a (sequence, KV head): every later tile that
-//           attends the chunk (branch or list), every head and row of it:
-//           dk_t = sum dl_t q / sqrt(d), dv_t = sum P_t dO
-//   route   per (query tile, KV head): dpbar = dlogp / pbar, dp_h = dpbar / G,
-//           the entmax Jacobian with u = (x - tau)_+^((2-alpha)/(alpha-1)):
+//           listed block, sigma * sum_{t in block} dl_t, into the head's own
+//           slot dlogp[tile, head, list position, row]
+//   route   per (query tile, KV head), over the tile's listed blocks only
+//           (every other candidate has p = 0 for every head of the group, so
+//           no entmax gradient): dpbar = (sum over the heads' slots) / pbar,
+//           dp_h = dpbar / G, the entmax Jacobian with
+//           u = (x - tau)_+^((2-alpha)/(alpha-1)):
 //           dzbar = gamma (u dp - u (u.dp) / sum u); dq += dzbar . s / sqrt(d)
 //           and the tile's share of the summaries' gradient, the sum over its
 //           rows and heads of dzbar_j q / sqrt(d), into its own partial rows
-//   means   ds_j = sum of the tiles' partial rows; dk of block j +=
-//           (ds_j W_s^T) / bs; block means m_j
-//   w_s     dW_s = sum_j m_j^T ds_j
+//   dsum    ds_j += the partial rows of the tiles that list block j, in tile
+//           order
+//   keys    per 64-key chunk of a (sequence, KV head): every later tile that
+//           attends the chunk (branch or list), every head and row of it:
+//           dk_t = sum dl_t q / sqrt(d), dv_t = sum P_t dO
+//   means   dk of block j += (ds_j W_s^T) / bs; block means m_j
+//   w_s     dW_s = sum_j m_j^T ds_j, in slices summed in a fixed order
+// The per-tile arrays (dlogp, u, partial summary rows) hold one slab of
+// query tiles at a time; rows, route and dsum run slab after slab, so the
+// workspace stays bounded for long sequences.  No floating-point atomics:
+// every output element is written by one thread, every sum in a fixed order.
 // bf16 inputs: the rows and keys products run on MFMA (bf16 operands, float32
 // accumulation).  float32 inputs keep plain float32 FMAs, a row or key spread
 // over 4 lanes of D/4 columns each.  The routing gradient is float32 FMAs
@@ -53,12 +61,15 @@ struct BwdArgs {
   float* dw_s;              // [D, D]
   float* lse2;              // [B, H, n] log2-sum-exp2 of the scaled logits
   float* delta;             // [B, H, n] dO . o
-  float* dlogp;             // [B, Hkv, n_qt, nb, 64]
-  float* ucoarse;           // [B, Hkv, n_qt, G, nb, 64] entmax u of the coarse scores
+  // per slab of query tiles (slot st = qt - slab_q0 < slab), by list position e
+  float* dlogp;             // [B, Hkv, slab, G, nb, 64] each head's bias gradient
+  float* ucoarse;           // [B, Hkv, slab, G, nb, 64] entmax u of the coarse scores
+  float* dspart;            // [B, Hkv, slab, nb, D] each tile's share of ds
   float* ds;                // [B, Hkv, nb, D]
-  float* dspart;            // [B, Hkv, n_qt, nb, D] each tile's share of ds (its candidates)
   float* mean;              // [B, Hkv, nb, D]
+  float* wspart;            // [kWsSplit, D, D] slices of dW_s
   int64_t n, n_qt, nb;
+  int64_t slab, slab_q0, slab_nq;   // slab capacity; this slab's first tile and size
   int B, H, Hkv, G, bs, window;
   float scale_log2;         // log2(e) / sqrt(d)
   float rs;                 // 1 / sqrt(d)
@@ -126,8 +137,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds_rows[];
   T(*Kc)[D] = (T(*)[D])lds_rows;
   T(*Vc)[D] = (T(*)[D])(lds_rows + sizeof(T) * kBwdChunk * D);
-  const int64_t qt = blockIdx.x % a.n_qt;
-  const int64_t bh = blockIdx.x / a.n_qt;   // b * H + h
+  const int64_t qt = a.slab_q0 + blockIdx.x % a.slab_nq;
+  const int64_t bh = blockIdx.x / a.slab_nq;   // b * H + h
   const int b = (int)(bh / a.H), h = (int)(bh % a.H), g = h / a.G;
   const int64_t bg = (int64_t)b * a.Hkv + g;
   const int64_t tile = bg * a.n_qt + qt;
@@ -230,10 +241,12 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
           acc[cc] = fmaf(dl * a.rs, to_f32(Kc[kk][sl * S + cc]), acc[cc]);
       }
     }
-    // end of a listed block: its bias gradient, added over the group's heads
+    // end of a listed block: its bias gradient, into this head's slot
     if (blk >= 0 && (c - w.n_own) % w.cpb == w.cpb - 1) {
-      if (valid && sl == 0 && bias2 != -INFINITY)
-        atomicAdd(&a.dlogp[(tile * a.nb + blk) * kBwdTile + row], a.sigma * bacc);
+      const int e = (c - w.n_own) / w.cpb;
+      if (valid && sl == 0)
+        a.dlogp[(((bg * a.slab + (qt - a.slab_q0)) * a.G + h % a.G) * a.nb + e) * kBwdTile +
+                row] = a.sigma * bacc;
       bacc = 0.f;
     }
   }
@@ -267,7 +280,7 @@ void bwd_rows_mfma_kernel(BwdArgs a) {
   const int wpt = (2 * a.G + NT / kWave - 1) / (NT / kWave);   // workgroups per tile
   const int64_t rank = blockIdx.x / wpt;
   const int gw = (int)(blockIdx.x % wpt) * (NT / kWave) + wave;   // wave within the tile
-  const int64_t qt = a.n_qt - 1 - rank / nbg;   // heaviest tiles first
+  const int64_t qt = a.slab_q0 + a.slab_nq - 1 - rank / nbg;   // heaviest tiles first
   const int64_t bg = rank % nbg;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t tile = bg * a.n_qt + qt;
@@ -472,8 +485,10 @@ void bwd_rows_mfma_kernel(BwdArgs a) {
       }
     }
     if (blk >= 0 && (c - w.n_own) % w.cpb == w.cpb - 1) {
-      if (valid && lh == 0 && bias2 != -INFINITY)
-        atomicAdd(&a.dlogp[(tile * a.nb + blk) * kBwdTile + qloc], a.sigma * bacc);
+      const int e = (c - w.n_own) / w.cpb;
+      if (valid && lh == 0)
+        a.dlogp[(((bg * a.slab + (qt - a.slab_q0)) * a.G + gw / 2) * a.nb + e) * kBwdTile +
+                qloc] = a.sigma * bacc;
       bacc = 0.f;
     }
   }
@@ -498,7 +513,6 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
   float* rowl = (float*)(lds_keys + sizeof(T) * 2 * kBwdTile * D);
   float* rowd = rowl + kBwdTile;
   float* rowb = rowd + kBwdTile;
-  const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
   const int64_t nbg = (int64_t)a.B * a.Hkv;
   const int64_t ch = blockIdx.x / nbg;   // early chunks, attended by the most tiles, first
   const int64_t bg = blockIdx.x % nbg;
@@ -608,7 +622,6 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int l32 = lane % 32, lh = lane / 32;
   const int kt = wave / 2, dh = wave % 2;
-  const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
   const int64_t nbg = (int64_t)a.B * a.Hkv;
   const int64_t ch = blockIdx.x / nbg;   // early chunks, attended by the most tiles, first
   const int64_t bg = blockIdx.x % nbg;
@@ -817,17 +830,18 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
 }
 
 // ---- route, tiled: one workgroup per (query tile, KV head) -----------------------------------
-// All 64 positions of a tile share their candidates (j < t), so per head the
-// coarse scores X = Q S^T (64 x t), the entmax Jacobian, the coarse dq =
-// dZ S (64 x d) and the tile's share of the summary gradient dZ^T Q (t x d)
-// are small dense products: summary rows come through LDS 32 at a time, each
-// thread owns a 2 x 4 block of X, a 4 x (D / 16) block of dq and a 2 x (D / 16)
-// block of the summary gradient, which goes to the tile's own rows of dspart
-// (the first head stores, the others add; the block-means kernel sums the
-// tiles).  LDS
-// rows are read 4 floats at a time; the row pitch D + 4 and the assignment of
-// rows {r, r + 32} and of column groups {4 c, 64 + 4 c} to threads keep the
-// 8 lanes of each 16-byte read on distinct banks.
+// All 64 positions of a tile share their candidates, and only the blocks on
+// the tile's list can be in any head's support, so per head the coarse
+// scores X = Q S^T (64 x count), the entmax Jacobian, the coarse dq = dZ S
+// (64 x d) and the tile's share of the summary gradient dZ^T Q (count x d)
+// are small dense products over the listed summary rows: those rows come
+// through LDS 32 at a time, each thread owns a 2 x 4 block of X, a 4 x (D / 16)
+// block of dq and a 2 x (D / 16) block of the summary gradient, which goes to
+// the tile's own rows of dspart (the first head stores, the others add; the
+// dsum kernel sums the tiles).  LDS rows are read 4 floats at a time; the row
+// pitch D + 4 and the assignment of rows {r, r + 32} and of column groups
+// {4 c, 64 + 4 c} to threads keep the 8 lanes of each 16-byte read on
+// distinct banks.
 constexpr int kRtJ = 32;   // summary rows per LDS chunk
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
@@ -836,32 +850,54 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
   constexpr int NV = D / 64;     // float4 column groups per thread (64 apart)
   __shared__ __attribute__((aligned(16))) float Qh[kBwdTile * QP];
   __shared__ __attribute__((aligned(16))) float Sc[kRtJ * QP];
-  __shared__ __attribute__((aligned(16))) float Zt[kRtJ * ZP];   // dz, candidate-major
+  __shared__ __attribute__((aligned(16))) float Zt[kRtJ * ZP];   // dz, list-major
   __shared__ float red[2][8][kBwdTile];
   __shared__ float corr_s[kBwdTile];
   const int64_t nbg = (int64_t)a.B * a.Hkv;
-  const int64_t qt = a.n_qt - 1 - blockIdx.x / nbg;   // most candidates first
+  const int64_t qt = a.slab_q0 + a.slab_nq - 1 - blockIdx.x / nbg;   // most candidates first
   const int64_t bg = blockIdx.x % nbg;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t p0 = qt * kBwdTile;
-  const int t = (int)max((int64_t)0, p0 / a.bs - (a.window - 1));   // candidates
-  if (t == 0) return;
   const int64_t tile = bg * a.n_qt + qt;
+  const int cnt = a.sel_count[tile];
+  if (cnt == 0) return;
+  const int32_t* lst = a.sel_idx + tile * a.nb;
+  const int64_t slot = bg * a.slab + (qt - a.slab_q0);
+  // [G][nb][64] per slot; the head-0 plane is overwritten with dp below
+  float* dlg = a.dlogp + slot * a.G * a.nb * kBwdTile;
+  float* ucg = a.ucoarse + slot * a.G * a.nb * kBwdTile;
   const int tid = threadIdx.x;
   const float* srow = a.summ + bg * a.summ_blocks * D;
-  const int rg = tid % 32, jg = tid / 32;   // phase A: rows rg + 32 i; candidates 4 jg + k
+
+  // dp = (sum of the heads' bias gradients) / pbar / G per (listed block, row),
+  // pbar = exp(bias / sigma); with sigma = 0 the bias is 0 on the support and
+  // the routing takes no gradient
+  for (int e2 = tid; e2 < cnt * kBwdTile; e2 += 256) {
+    const int e = e2 / kBwdTile, r = e2 % kBwdTile;
+    if (p0 + r >= a.n) continue;
+    const float lp = a.sel_logp[(tile * a.nb + lst[e]) * kBwdTile + r];
+    float sum = 0.f;
+    for (int hh = 0; hh < a.G; ++hh) sum += dlg[((int64_t)hh * a.nb + e) * kBwdTile + r];
+    float dp = 0.f;
+    if (a.sigma > 0.f && lp != -INFINITY) dp = sum / expf(lp / a.sigma) / (float)a.G;
+    dlg[(int64_t)e * kBwdTile + r] = dp;
+  }
+  // (the __syncthreads() at the top of the head loop orders these stores
+  // before the reads of other threads)
+
+  const int rg = tid % 32, jg = tid / 32;   // phase A: rows rg + 32 i; list entries 4 jg + k
   const int rq = tid % 16, cq = tid / 16;   // dq: rows 4 rq + i; columns 64 v + 4 cq + [0, 4)
-  const int jq = tid / 16, cc = tid % 16;   // ds: candidates 2 jq + {0, 1}; columns as dq's
-  // summary rows of the next chunk are loaded (16 bytes at a time) into
-  // registers while the current chunk is computed
+  const int jq = tid / 16, cc = tid % 16;   // ds: entries 2 jq + {0, 1}; columns as dq's
+  // the listed summary rows of the next chunk are loaded (16 bytes at a
+  // time) into registers while the current chunk is computed
   constexpr int SV = kRtJ * D / 4 / 256;   // float4s per thread per chunk
   f32x4 spre[SV];
   auto load_s = [&](int j0) {
 #pragma unroll
     for (int m = 0; m < SV; ++m) {
       const int e = tid + 256 * m, jr = e / (D / 4), c4 = e % (D / 4);
-      spre[m] = j0 + jr < t ? *(const f32x4*)(srow + (int64_t)(j0 + jr) * D + 4 * c4)
-                            : (f32x4){0.f, 0.f, 0.f, 0.f};
+      spre[m] = j0 + jr < cnt ? *(const f32x4*)(srow + (int64_t)lst[j0 + jr] * D + 4 * c4)
+                              : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
   };
   auto store_s = [&]() {
@@ -894,26 +930,25 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
       const int64_t pos = p0 + rg + 32 * i;
       tau2[i] = pos < a.n ? a.tau[bh * a.n + pos] : 0.f;
     }
+    float* uh = ucg + (int64_t)hh * a.nb * kBwdTile;
     // phase A: u and the row sums of u and u dp
     float su[2] = {0.f, 0.f}, sud[2] = {0.f, 0.f};
     load_s(0);
-    for (int j0 = 0; j0 < t; j0 += kRtJ) {
+    for (int j0 = 0; j0 < cnt; j0 += kRtJ) {
       __syncthreads();
       store_s();
       __syncthreads();
-      if (j0 + kRtJ < t) load_s(j0 + kRtJ);
-      // the routing inputs of this thread's (row, candidate) pairs, loaded
-      // before the scores so that their latency hides behind the FMAs
-      float lpv[2][4], dlv[2][4];
+      if (j0 + kRtJ < cnt) load_s(j0 + kRtJ);
+      // dp of this thread's (row, entry) pairs, loaded before the scores so
+      // that their latency hides behind the FMAs
+      float dlv[2][4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int j = j0 + 4 * jg + k;
-          const bool in = j < t && p0 + rg + 32 * i < a.n;
-          const int64_t li = (tile * a.nb + j) * kBwdTile + rg + 32 * i;
-          lpv[i][k] = in ? a.sel_logp[li] : -INFINITY;
-          dlv[i][k] = in ? a.dlogp[li] : 0.f;
+          const int e = j0 + 4 * jg + k;
+          const bool in = e < cnt && p0 + rg + 32 * i < a.n;
+          dlv[i][k] = in ? dlg[(int64_t)e * kBwdTile + rg + 32 * i] : 0.f;
         }
       float x[2][4];
 #pragma unroll
@@ -940,16 +975,13 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
         if (pos >= a.n) continue;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int j = j0 + 4 * jg + k;
-          if (j >= t) continue;
+          const int e = j0 + 4 * jg + k;
+          if (e >= cnt) continue;
           const float y = x[i][k] * a.xscale - tau2[i];
           const float u = y > 0.f ? (a.ue == 0.f ? 1.f : powf(y, a.ue)) : 0.f;
-          const float lp = lpv[i][k];
-          float dp = 0.f;
-          if (a.sigma > 0.f && lp != -INFINITY) dp = dlv[i][k] / expf(lp / a.sigma) / (float)a.G;
           su[i] += u;
-          sud[i] = fmaf(u, dp, sud[i]);
-          a.ucoarse[((tile * a.G + hh) * a.nb + j) * kBwdTile + r] = u;
+          sud[i] = fmaf(u, dlv[i][k], sud[i]);
+          uh[(int64_t)e * kBwdTile + r] = u;
         }
       }
     }
@@ -974,39 +1006,35 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < NV; ++v) dqa[i][v] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    // phase B inputs of a chunk (8 (row, candidate) pairs per thread), loaded
+    // phase B inputs of a chunk (8 (row, entry) pairs per thread), loaded
     // one chunk ahead
     constexpr int NB8 = kBwdTile * kRtJ / 256;
-    float blp[NB8], bdl[NB8], bu[NB8];
+    float bdl[NB8], bu[NB8];
     auto load_b = [&](int j0) {
 #pragma unroll
       for (int m = 0; m < NB8; ++m) {
         const int e = tid + 256 * m, r = e % kBwdTile, j = j0 + e / kBwdTile;
-        const bool in = j < t && p0 + r < a.n;
-        const int64_t li = (tile * a.nb + j) * kBwdTile + r;
-        blp[m] = in ? a.sel_logp[li] : -INFINITY;
-        bdl[m] = in ? a.dlogp[li] : 0.f;
-        bu[m] = in ? a.ucoarse[((tile * a.G + hh) * a.nb + j) * kBwdTile + r] : 0.f;
+        const bool in = j < cnt && p0 + r < a.n;
+        bdl[m] = in ? dlg[(int64_t)j * kBwdTile + r] : 0.f;
+        bu[m] = in ? uh[(int64_t)j * kBwdTile + r] : 0.f;
       }
     };
     load_b(0);
     load_s(0);
-    for (int j0 = 0; j0 < t; j0 += kRtJ) {
+    for (int j0 = 0; j0 < cnt; j0 += kRtJ) {
       __syncthreads();
       store_s();
 #pragma unroll
       for (int m = 0; m < NB8; ++m) {
         const int e = tid + 256 * m, r = e % kBwdTile, jr = e / kBwdTile;
-        float dp = 0.f;
-        if (a.sigma > 0.f && blp[m] != -INFINITY) dp = bdl[m] / expf(blp[m] / a.sigma) / (float)a.G;
-        Zt[jr * ZP + r] = a.gamma * bu[m] * (dp - corr_s[r]);   // 0 outside (bu = 0)
+        Zt[jr * ZP + r] = a.gamma * bu[m] * (bdl[m] - corr_s[r]);   // 0 outside (bu = 0)
       }
       __syncthreads();
-      if (j0 + kRtJ < t) {
+      if (j0 + kRtJ < cnt) {
         load_b(j0 + kRtJ);
         load_s(j0 + kRtJ);
       }
-      const int jn = min(kRtJ, t - j0);
+      const int jn = min(kRtJ, cnt - j0);
       for (int jr = 0; jr < jn; ++jr) {
         const f32x4 zv = *(const f32x4*)(Zt + jr * ZP + 4 * rq);
 #pragma unroll
@@ -1039,11 +1067,11 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const int j = j0 + 2 * jq + jj;
-          if (j < t)
+          const int e = j0 + 2 * jq + jj;
+          if (e < cnt)
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-              f32x4* dst = (f32x4*)(a.dspart + (tile * a.nb + j) * D + 64 * v + 4 * cc);
+              f32x4* dst = (f32x4*)(a.dspart + (slot * a.nb + e) * D + 64 * v + 4 * cc);
               const f32x4 val = dsa[jj][v] * a.rs;
               *dst = hh == 0 ? val : *dst + val;
             }
@@ -1063,6 +1091,43 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
   }
 }
 
+// ---- ds_j += the partial rows of this slab's tiles that list block j ---------------------------
+// One workgroup per (sequence, KV head, complete block); the tiles' list
+// positions of the block are found first (one binary search per tile, side
+// by side), then every thread adds its column over the tiles in order.
+constexpr int kSlabMax = 256;   // tiles per slab (one search per thread)
+template <int D>
+__global__ __launch_bounds__(D) void bwd_dsum_kernel(BwdArgs a) {
+  __shared__ int pos[kSlabMax];
+  const int64_t nbc = a.n / a.bs;
+  const int64_t j = blockIdx.x % nbc;
+  const int64_t bg = blockIdx.x / nbc;
+  // tiles before qt0 have block j in their branch or past their end
+  const int64_t qt0 = ((j + a.window) * a.bs + kBwdTile - 1) / kBwdTile;
+  for (int e = threadIdx.x; e < kSlabMax; e += D) {
+    const int64_t qt = a.slab_q0 + e;
+    int found = -1;
+    if (e < a.slab_nq && qt >= qt0) {
+      const int64_t tile = bg * a.n_qt + qt;
+      const int cnt = a.sel_count[tile];
+      const int32_t* lst = a.sel_idx + tile * a.nb;
+      int lo = 0, hi = cnt;
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (lst[mid] < j) lo = mid + 1; else hi = mid;
+      }
+      if (lo < cnt && lst[lo] == j) found = lo;
+    }
+    pos[e] = found;
+  }
+  __syncthreads();
+  const int r = threadIdx.x;
+  float acc = 0.f;
+  for (int e = 0; e < a.slab_nq; ++e)
+    if (pos[e] >= 0) acc += a.dspart[((bg * a.slab + e) * a.nb + pos[e]) * D + r];
+  a.ds[(bg * a.nb + j) * D + r] += acc;
+}
+
 // ---- block means, and dk += (ds_j W_s^T) / bs over the block ---------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
@@ -1078,16 +1143,8 @@ __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
   float m = 0.f;
   for (int t = 0; t < a.bs; ++t) m += ld<T>(a.k, (k0 + t) * D + r);
   mrow[r] = m / (float)a.bs;
-  // ds_j: the shares of the tiles that have block j among their candidates,
-  // floor(64 qt / bs) - (window - 1) > j
   __shared__ float dsr[D];
-  const int64_t qt0 = ((j + a.window) * a.bs + kBwdTile - 1) / kBwdTile;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int64_t qt = qt0; qt < a.n_qt; ++qt)
-    acc += a.dspart[((bg * a.n_qt + qt) * a.nb + j) * D + r];
-  a.ds[(bg * a.nb + j) * D + r] = acc;
-  dsr[r] = acc;
+  dsr[r] = a.ds[(bg * a.nb + j) * D + r];
   __syncthreads();
   float dm = 0.f;
   for (int c = 0; c < D; ++c) dm = fmaf(dsr[c], a.w_s[r * D + c], dm);
@@ -1097,8 +1154,8 @@ __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
 
 // ---- dW_s = sum_j m_j^T ds_j ---------------------------------------------------------------
 // The sum over all blocks of all (sequence, KV head) pairs is cut into
-// kWsSplit slices (blockIdx.y); each adds its partial sum into the zeroed
-// dW_s with one atomic per entry.
+// kWsSplit slices (blockIdx.y), each written to its own plane of wspart;
+// bwd_ws_sum_kernel adds the planes in slice order.
 constexpr int kWsSplit = 32;
 template <int D>
 __global__ __launch_bounds__(256) void bwd_ws_kernel(BwdArgs a) {
@@ -1107,12 +1164,19 @@ __global__ __launch_bounds__(256) void bwd_ws_kernel(BwdArgs a) {
   const int r = (int)(idx / D), c = (int)(idx % D);
   const int64_t nblk = (int64_t)a.B * a.Hkv * a.nb;
   const int64_t per = (nblk + kWsSplit - 1) / kWsSplit;
-  const int64_t u0 = blockIdx.y * per, u1 = min(nblk, u0 + per);
-  if (u0 >= u1) return;
+  const int64_t u0 = min(nblk, blockIdx.y * per), u1 = min(nblk, u0 + per);
   float acc = 0.f;
 #pragma unroll 4
   for (int64_t u = u0; u < u1; ++u) acc = fmaf(a.mean[u * D + r], a.ds[u * D + c], acc);
-  atomicAdd(a.dw_s + idx, acc);
+  a.wspart[blockIdx.y * (int64_t)D * D + idx] = acc;
+}
+template <int D>
+__global__ __launch_bounds__(256) void bwd_ws_sum_kernel(BwdArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)D * D) return;
+  float acc = 0.f;
+  for (int sl = 0; sl < kWsSplit; ++sl) acc += a.wspart[sl * (int64_t)D * D + idx];
+  a.dw_s[idx] = acc;
 }
 
 __global__ void bwd_zero_kernel(float* p, int64_t n) {
@@ -1121,44 +1185,66 @@ __global__ void bwd_zero_kernel(float* p, int64_t n) {
     p[i] = 0.f;
 }
 
+// Query tiles per slab: the per-tile arrays of one slab stay within
+// kBwdSlabBytes (at least one tile, at most kSlabMax).
+constexpr int64_t kBwdSlabBytes = (int64_t)1 << 30;
+static int64_t bwd_slab_tiles(const Shape& s, int64_t n) {
+  const int64_t n_qt = (n + kBwdTile - 1) / kBwdTile, nb = (n + s.bs - 1) / s.bs;
+  const int64_t per_tile = (int64_t)sizeof(float) * s.B * s.Hkv * nb *
+                           (2 * (int64_t)s.G * kBwdTile + s.d);
+  int64_t slab = kBwdSlabBytes / per_tile;
+  slab = slab < 1 ? 1 : slab;
+  slab = slab > kSlabMax ? kSlabMax : slab;
+  return slab < n_qt ? slab : n_qt;
+}
+
 BwdLayout bwd_layout(const Shape& s, int64_t n) {
   BwdLayout L;
-  const int64_t n_qt = (n + kBwdTile - 1) / kBwdTile, nb = (n + s.bs - 1) / s.bs;
+  const int64_t nb = (n + s.bs - 1) / s.bs, slab = bwd_slab_tiles(s, n);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t per_slot = sizeof(float) * s.B * s.Hkv * slab * s.G * nb * kBwdTile;
   size_t off = 0;
-  L.off_lse = off;   off = al(off + sizeof(float) * s.B * s.H * n);
-  L.off_delta = off; off = al(off + sizeof(float) * s.B * s.H * n);
-  L.off_dlogp = off; off = al(off + sizeof(float) * s.B * s.Hkv * n_qt * nb * kBwdTile);
-  L.off_u = off;    off = al(off + sizeof(float) * s.B * s.H * n_qt * kBwdTile * nb);
-  L.off_ds = off;    off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
-  L.off_mean = off;  off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
-  L.off_dspart = off;
-  off = al(off + sizeof(float) * s.B * s.Hkv * n_qt * nb * s.d);
+  L.off_lse = off;    off = al(off + sizeof(float) * s.B * s.H * n);
+  L.off_delta = off;  off = al(off + sizeof(float) * s.B * s.H * n);
+  L.off_dlogp = off;  off = al(off + per_slot);
+  L.off_u = off;      off = al(off + per_slot);
+  L.off_ds = off;     off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
+  L.off_mean = off;   off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
+  L.off_dspart = off; off = al(off + sizeof(float) * s.B * s.Hkv * slab * nb * s.d);
+  L.off_wspart = off; off = al(off + sizeof(float) * kWsSplit * s.d * s.d);
+  L.slab = slab;
   L.total = off;
   return L;
 }
 
 template <typename T, int D>
-static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
+static hipError_t bwd_t(BwdArgs a, hipStream_t st) {
   const int64_t nbg = (int64_t)a.B * a.Hkv;
-  const int64_t nzero = nbg * a.n_qt * a.nb * kBwdTile;
-  hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, st, a.dlogp, nzero);
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(256), dim3(256), 0, st, a.ds, nbg * a.nb * D);
-  hipLaunchKernelGGL(bwd_zero_kernel, dim3(64), dim3(256), 0, st, a.dw_s, (int64_t)D * D);
-  if constexpr (sizeof(T) == 2) {
-    // 2 G waves of 32 queries per tile, at most 8 per workgroup
-    const int waves = 2 * a.G, wpt = (waves + 7) / 8;
-    const dim3 grid((unsigned)(a.n_qt * nbg * wpt));
-    if (waves == 2) hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 128>), grid, dim3(128), 0, st, a);
-    else if (waves == 4)
-      hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 256>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 512>), grid, dim3(512), 0, st, a);
-  } else {
-    const size_t lds_r = sizeof(T) * 2 * kBwdChunk * D;
-    (void)hipFuncSetAttribute((const void*)bwd_rows_kernel<T, D>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
-    hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3((unsigned)(a.n_qt * a.B * a.H)), dim3(256),
-                       lds_r, st, a);
+  const int64_t nbc = a.n / a.bs;   // complete blocks
+  for (int64_t q0 = 0; q0 < a.n_qt; q0 += a.slab) {
+    a.slab_q0 = q0;
+    a.slab_nq = a.n_qt - q0 < a.slab ? a.n_qt - q0 : a.slab;
+    if constexpr (sizeof(T) == 2) {
+      // 2 G waves of 32 queries per tile, at most 8 per workgroup
+      const int waves = 2 * a.G, wpt = (waves + 7) / 8;
+      const dim3 grid((unsigned)(a.slab_nq * nbg * wpt));
+      if (waves == 2)
+        hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 128>), grid, dim3(128), 0, st, a);
+      else if (waves == 4)
+        hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 256>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((bwd_rows_mfma_kernel<D, 512>), grid, dim3(512), 0, st, a);
+    } else {
+      const size_t lds_r = sizeof(T) * 2 * kBwdChunk * D;
+      (void)hipFuncSetAttribute((const void*)bwd_rows_kernel<T, D>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r);
+      hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3((unsigned)(a.slab_nq * a.B * a.H)),
+                         dim3(256), lds_r, st, a);
+    }
+    hipLaunchKernelGGL((bwd_route_tile_kernel<T, D>), dim3((unsigned)(a.slab_nq * nbg)),
+                       dim3(256), 0, st, a);
+    if (nbc > 0)
+      hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)(nbc * nbg)), dim3(D), 0, st, a);
   }
   const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
   if constexpr (sizeof(T) == 2) {
@@ -1175,12 +1261,11 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_keys_kernel<T, D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_k,
                        st, a);
   }
-  hipLaunchKernelGGL((bwd_route_tile_kernel<T, D>), dim3((unsigned)(a.n_qt * nbg)), dim3(256), 0,
-                     st, a);
-
   hipLaunchKernelGGL((bwd_means_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
   hipLaunchKernelGGL((bwd_ws_kernel<D>), dim3((unsigned)((D * D + 255) / 256), kWsSplit),
                      dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_ws_sum_kernel<D>), dim3((unsigned)((D * D + 255) / 256)), dim3(256), 0,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -1214,6 +1299,10 @@ hipError_t launch_prefill_backward(const Shape& s, const void* q, const void* k,
   a.ds = (float*)(ws + L.off_ds);
   a.mean = (float*)(ws + L.off_mean);
   a.dspart = (float*)(ws + L.off_dspart);
+  a.wspart = (float*)(ws + L.off_wspart);
+  a.slab = L.slab;
+  a.slab_q0 = 0;
+  a.slab_nq = 0;
   a.n = n;
   a.n_qt = (n + kBwdTile - 1) / kBwdTile;
   a.nb = (n + s.bs - 1) / s.bs;
