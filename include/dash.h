@@ -304,6 +304,24 @@ dash_status dash_decode_paged(const dash_params* p, const void* q, const void* k
                               int64_t summ_blocks, void* o, const dash_route_buf* route,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* dash_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same step, kernels and result as dash_decode (bitwise), but the workspace
+ * is the library's own static device scratch, 32 MiB per GPU, held until the
+ * process ends; nothing is allocated or freed.  DASH_ERR_WORKSPACE_TOO_SMALL
+ * (nothing launched) when dash_decode_workspace_bytes(p, max_len) exceeds
+ * 32 MiB, which covers e.g. 32 sequences x 32K and 8 x 128K with 64 query
+ * heads.  The first call on a device looks up that device's scratch address
+ * (once per device, with the device current).  Every call on one GPU shares
+ * its scratch: calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialised by the caller.  The scratch keeps the last call's
+ * contents; no part of it needs to start at zero. */
+dash_status dash_decode_noalloc(const dash_params* p, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* cache_len, int64_t max_len,
+                                const float* w_s, const float* q_bar, float* summ,
+                                int64_t summ_blocks, void* o, const dash_route_buf* route,
+                                void* stream);
+
 /* ---- Measurement helpers (not part of the attention computation) ---------
  * What this GPU attains, in the same process, for stating each kernel's
  * roofline fraction against a measured ceiling beside the nominal one.

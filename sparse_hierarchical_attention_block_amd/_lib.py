@@ -94,6 +94,8 @@ _lib.dash_decode_paged.argtypes = [_P, _V, _V, _V, _I, _V, _I, _V, _I, _V, _V, _
 _lib.dash_decode.restype = ctypes.c_int
 _lib.dash_decode.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _V, _I, _V, _R, _V, ctypes.c_size_t,
                              _V]
+_lib.dash_decode_noalloc.restype = ctypes.c_int
+_lib.dash_decode_noalloc.argtypes = [_P, _V, _V, _V, _V, _I, _V, _V, _V, _I, _V, _R, _V]
 _lib.dash_peak_stream_grid.restype = ctypes.c_int
 _lib.dash_peak_stream_grid.argtypes = [ctypes.POINTER(ctypes.c_int64)]
 _lib.dash_peak_stream.restype = ctypes.c_int
@@ -108,7 +110,8 @@ EXPORTED = ("dash_status_string", "dash_version", "dash_route_sizes_prefill",
             "dash_decode_workspace_bytes", "dash_summarize", "dash_route", "dash_attend",
             "dash_mask_to_list", "dash_prefill", "dash_prefill_varlen", "dash_decode",
             "dash_decode_paged", "dash_prefill_backward_workspace_bytes",
-            "dash_prefill_backward", "dash_peak_stream_grid", "dash_peak_stream",
+            "dash_prefill_backward", "dash_decode_noalloc", "dash_peak_stream_grid",
+            "dash_peak_stream",
             "dash_peak_mfma_grid", "dash_peak_mfma")
 
 
@@ -336,6 +339,29 @@ def dash_decode(p, q, k_cache, v_cache, cache_len, max_len, w_s, summ, summ_bloc
         _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
         _dev(o, "o", B * H * d, dt), rb, _dev(ws, "ws", 0), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def dash_decode_noalloc(p, q, k_cache, v_cache, cache_len, max_len, w_s, summ, summ_blocks, o,
+                        route: RouteBuffers | None = None, stream=None, q_bar=None):
+    """dash_decode with the library's static device scratch as its workspace
+    (for callers that cannot allocate); calls on one GPU must not overlap."""
+    B, H, Hkv, d = p.batch, p.n_heads, p.n_kv_heads, p.head_dim
+    dt = torch_dtype(p)
+    rb = None
+    if route is not None:
+        if route.sizes != dash_route_sizes_decode(p, max_len):
+            raise ValueError("route buffers were sized for another problem")
+        rb_struct = route.struct()
+        rb = ctypes.byref(rb_struct)
+    _check("dash_decode_noalloc", _lib.dash_decode_noalloc(
+        ctypes.byref(p), _dev(q, "q", B * H * d, dt),
+        _dev(k_cache, "k_cache", B * Hkv * max_len * d, dt),
+        _dev(v_cache, "v_cache", B * Hkv * max_len * d, dt),
+        _dev(cache_len, "cache_len", B, torch.int32), max_len,
+        _dev(w_s, "w_s", d * d, torch.float32),
+        _opt_dev(q_bar, "q_bar", Hkv * d, torch.float32),
+        _dev(summ, "summ", B * Hkv * summ_blocks * d, torch.float32), summ_blocks,
+        _dev(o, "o", B * H * d, dt), rb, _stream(stream)))
 
 
 def dash_decode_paged(p, q, k_pages, v_pages, block_table, cache_len, max_len, w_s, summ,

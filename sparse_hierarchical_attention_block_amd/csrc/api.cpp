@@ -4,6 +4,7 @@
 // synchronises; no C++ exception crosses the ABI.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "dash.h"
 #include "dash_internal.hpp"
@@ -111,6 +112,34 @@ dash_status check_route_buf(const dash_route_buf* rb) {
   if (!rb || !rb->tau || !rb->sel_count || !rb->sel_idx || !rb->sel_logp)
     return DASH_ERR_INVALID_ARG;
   return DASH_OK;
+}
+
+// ---- scratch of dash_decode_noalloc ------------------------------------------------------
+// One copy per GPU (a device array, held until the process ends).  Host code
+// never passes the array's own name (on the host it is only a stand-in for
+// the symbol): its device address is looked up once per device, with that
+// device current, and that address is what the kernels receive.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[dash::kMaxDevices];
+
+hipError_t decode_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= dash::kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once,
+                 [&slot] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+  if (slot.err != hipSuccess) return slot.err;
+  *out = slot.ptr;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -360,6 +389,23 @@ dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache
                         void* stream) {
   return decode_impl(p, q, k_cache, v_cache, cache_len, max_len, w_s, q_bar, summ, summ_blocks,
                      o, route, ws, ws_bytes, stream, nullptr, 0, 0);
+}
+
+dash_status dash_decode_noalloc(const dash_params* p, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* cache_len, int64_t max_len,
+                                const float* w_s, const float* q_bar, float* summ,
+                                int64_t summ_blocks, void* o, const dash_route_buf* route,
+                                void* stream) {
+  Shape s;
+  dash_status st = check_params(p, &s);
+  if (st != DASH_OK) return st;
+  if (max_len < 1) return DASH_ERR_INVALID_ARG;
+  if (dash::decode_layout(s, max_len).total > kDecodeScratchBytes)
+    return DASH_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (decode_scratch(&ws) != hipSuccess) return DASH_ERR_HIP;
+  return decode_impl(p, q, k_cache, v_cache, cache_len, max_len, w_s, q_bar, summ, summ_blocks,
+                     o, route, ws, kDecodeScratchBytes, stream, nullptr, 0, 0);
 }
 
 dash_status dash_decode_paged(const dash_params* p, const void* q, const void* k_pages,

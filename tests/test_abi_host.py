@@ -190,3 +190,16 @@ def test_binding_rejects_host_tensors():
     t = torch.zeros(2 * 64 * 64)
     with pytest.raises(ValueError, match="GPU tensor"):
         dash.dash_summarize(p, t.bfloat16(), 64, 0, 1, torch.zeros(64 * 64), t, 1)
+
+
+def test_decode_noalloc_rejects_oversized_problem_before_launch():
+    # 64 sequences x 128K, 64 query heads: ~170 MiB of workspace, above the
+    # 32 MiB static scratch; rejected on the host, nothing touches a device
+    p = P(batch=64, n_heads=64, n_kv_heads=8)
+    assert dash.dash_decode_workspace_bytes(p, 131072) > 32 << 20
+    st = L._lib.dash_decode_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 131072, FAKE, None,
+                                    FAKE, 2048, FAKE, None, None)
+    assert st == L.DASH_ERR_WORKSPACE_TOO_SMALL
+    st = L._lib.dash_decode_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 0, FAKE, None,
+                                    FAKE, 2048, FAKE, None, None)
+    assert st == L.DASH_ERR_INVALID_ARG
