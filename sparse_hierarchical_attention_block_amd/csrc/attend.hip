@@ -18,9 +18,11 @@
 //   O^T (d x 32 queries) += V^T P^T        4 x 4 MFMA 32x32x16
 // Keys are the MFMA rows of S^T, so the accumulator of S^T already has the
 // register layout of the P^T operand (the k index of the PV product is a
-// permutation of the chunk's keys).  V is transposed into LDS in 4x4 blocks
-// while it is staged, with the keys of each group of 16 stored in the order
-// of that permutation, so every V^T operand fragment is one 16-byte read.
+// permutation of the chunk's keys).  V is transposed into LDS while it is
+// staged, with the keys of each group of 16 stored in the order of that
+// permutation, so every V^T operand fragment is one 16-byte read; the 16-byte
+// segments of each V^T row are XOR-swizzled by the row index so that both
+// the staging stores and the fragment reads hit distinct LDS banks.
 #include "dash_internal.hpp"
 #include "device_common.hpp"
 
@@ -87,24 +89,33 @@ __device__ __forceinline__ ChunkRef chunk_ref(int c, int n_own, int64_t own_c0, 
 // ------------------------------------------------------------------------------------------
 // bf16, MFMA
 // ------------------------------------------------------------------------------------------
-// Staging of one 64-key chunk: K row-major [64][D + 8], V transposed [D][64 + 8]
-// (keys permuted within each group of 16, see store())
+// V^T row r (one d, 64 keys = 128 bytes = 8 segments of 16 bytes): logical
+// segment s is stored at s ^ vt_swizzle(r).  Staging writes rows 2 dp + {0,1}
+// for 8 consecutive d pairs per 8 lanes, fragment reads take 8 consecutive
+// rows per 8 lanes: both map those 8 lanes to 8 distinct segments, i.e. to
+// distinct banks.  Rows 32 apart share the swizzle, so a lane's read offsets
+// are the same for every 32-row tile.
+__device__ __forceinline__ int vt_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+
+// Staging of one 64-key chunk: K row-major [64][D + 8], V transposed [D][64]
+// (keys permuted within each group of 16 and segments swizzled, see store())
 // (bf16), and the chunk's 64 per-query biases (float, log pbar of the chunk's
 // block; 0 for own-block chunks).  NT threads; each thread owns KPT 16-byte
-// pieces of K and VPT 4x4 blocks of V; lanes 0..15 of wave 0 own the bias.
+// pieces of K and VPT (segment, d pair) units of V^T -- the 8 keys of one
+// V^T segment at two adjacent d; lanes 0..15 of wave 0 own the bias.
 // Loads go through buffer resources, so keys at or past n read as zeros
 // without branches, and the bias rides the same in-order load queue as K/V
 // (no wait on it can stall on a younger K/V load).
 template <int D, int NT>
 struct ChunkStage {
   static constexpr int KP = D + 8;
-  static constexpr int VP = kChunk + 8;   // 144-byte rows: 16-byte aligned, 36-bank shift
+  static constexpr int VP = kChunk;                      // 128-byte rows, swizzled segments
   static constexpr int KTOT = kChunk * (D / 8);          // 16-byte pieces of K
-  static constexpr int VTOT = (kChunk / 4) * (D / 4);    // 4x4 blocks of V
+  static constexpr int VTOT = 8 * (D / 2);               // (segment, d pair) units of V^T
   static constexpr int KPT = (KTOT + NT - 1) / NT;
   static constexpr int VPT = (VTOT + NT - 1) / NT;
   u32x4 kr[KPT];
-  u32x2 vr[VPT][4];
+  uint32_t vr[VPT][8];
   u32x4 br;
 
   // key0: first key of the chunk; block: its block id, -1 for an own-block
@@ -118,15 +129,21 @@ struct ChunkStage {
       const uint32_t off = (uint32_t)((key0 + key) * (D * 2) + seg * 16);
       if (KTOT % NT == 0 || e < KTOT) kr[i] = buf_load16(rk, off);
     }
+    // V^T unit (segment sg, d pair dp): the keys 16 (sg / 2) + 4 (sg % 2) +
+    // 8 a + j (a < 2, j < 4) at d = 2 dp, 2 dp + 1; a wave's lanes take
+    // consecutive d pairs, so each load reads whole key rows
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int e = threadIdx.x + i * NT;
-      const int db = e % (D / 4), kb = e / (D / 4);
+      const int dp = e % (D / 2), sg = e / (D / 2);
+      const int kbase = 16 * (sg >> 1) + 4 * (sg & 1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t off = (uint32_t)((key0 + 4 * kb + r) * (D * 2) + db * 8);
-        if (VTOT % NT == 0 || e < VTOT) vr[i][r] = buf_load8(rv, off);
-      }
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t off = (uint32_t)((key0 + kbase + 8 * a + j) * (D * 2) + dp * 4);
+          if (VTOT % NT == 0 || e < VTOT) vr[i][4 * a + j] = buf_load4(rv, off);
+        }
     }
     if (threadIdx.x < kWave) {   // wave-uniform
       br = (u32x4){0u, 0u, 0u, 0u};
@@ -141,23 +158,21 @@ struct ChunkStage {
       const int key = e / (D / 8), seg = e % (D / 8);
       if (KTOT % NT == 0 || e < KTOT) *(u32x4*)(Ks + key * KP + seg * 8) = kr[i];
     }
+    // keys 16 m + 8 a + 4 b + [0, 4) go to columns 16 m + 8 b + 4 a + [0, 4):
+    // the 8 keys one lane needs for a PV k-step form logical segment 2 m + b
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int e = threadIdx.x + i * NT;
       if (VTOT % NT != 0 && e >= VTOT) continue;
-      const int db = e % (D / 4), kb = e / (D / 4);
-      const u32x2* in = vr[i];
-      const u32x2 o0 = {pack_lo(in[0].x, in[1].x), pack_lo(in[2].x, in[3].x)};
-      const u32x2 o1 = {pack_hi(in[0].x, in[1].x), pack_hi(in[2].x, in[3].x)};
-      const u32x2 o2 = {pack_lo(in[0].y, in[1].y), pack_lo(in[2].y, in[3].y)};
-      const u32x2 o3 = {pack_hi(in[0].y, in[1].y), pack_hi(in[2].y, in[3].y)};
-      // keys 16 m + 8 a + 4 b + [0, 4) go to columns 16 m + 8 b + 4 a + [0, 4):
-      // the 8 keys one lane needs for a PV k-step become one 16-byte run
-      const int col = 16 * (kb / 4) + 8 * (kb % 2) + 4 * ((kb / 2) % 2);
-      *(u32x2*)(Vt + (4 * db + 0) * VP + col) = o0;
-      *(u32x2*)(Vt + (4 * db + 1) * VP + col) = o1;
-      *(u32x2*)(Vt + (4 * db + 2) * VP + col) = o2;
-      *(u32x2*)(Vt + (4 * db + 3) * VP + col) = o3;
+      const int dp = e % (D / 2), sg = e / (D / 2);
+      const uint32_t* w = vr[i];
+      const u32x4 lo = {pack_lo(w[0], w[1]), pack_lo(w[2], w[3]), pack_lo(w[4], w[5]),
+                        pack_lo(w[6], w[7])};
+      const u32x4 hi = {pack_hi(w[0], w[1]), pack_hi(w[2], w[3]), pack_hi(w[4], w[5]),
+                        pack_hi(w[6], w[7])};
+      const int r0 = 2 * dp, r1 = 2 * dp + 1;
+      *(u32x4*)(Vt + r0 * VP + 8 * (sg ^ vt_swizzle(r0))) = lo;
+      *(u32x4*)(Vt + r1 * VP + 8 * (sg ^ vt_swizzle(r1))) = hi;
     }
     if (threadIdx.x < kQTa / 4) *(u32x4*)(Bs + 4 * threadIdx.x) = br;
   }
@@ -227,6 +242,11 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   const buf_rsrc rk = make_rsrc((const __bf16*)a.k + (bg * a.n) * D, seq_bytes);
   const buf_rsrc rv = make_rsrc((const __bf16*)a.v + (bg * a.n) * D, seq_bytes);
   const buf_rsrc rb = make_rsrc(a.sel_logp + tile * a.nb * kQTa, (uint32_t)(a.nb * kQTa * 4));
+
+  // this lane's V^T fragment of PV k-step ks and d tile dt: row 32 dt + l32
+  // (rows 32 apart share the swizzle), logical segment 2 ks + lh, i.e. the
+  // element offset vrow + 32 dt VP + (vx ^ 16 ks)
+  const int vrow = l32 * VP, vx = 8 * (lh ^ vt_swizzle(l32));
 
   // Q^T operand fragments: column = query l32, k = d in [16 s + 8 lh, +8)
   bf16x8 qf[D / 16];
@@ -327,7 +347,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        vw[ks][dt] = *(const u32x4*)(Vc + (32 * dt + l32) * VP + 16 * ks + 8 * lh);
+        vw[ks][dt] = *(const u32x4*)(Vc + vrow + 32 * dt * VP + (vx ^ (16 * ks)));
       }
 
     // ---- online softmax of chunk c, exp2 domain: logit2 = s * scale_log2 + bias2 ----
