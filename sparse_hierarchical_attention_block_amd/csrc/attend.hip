@@ -351,7 +351,10 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
       }
 
     // ---- online softmax of chunk c, exp2 domain: logit2 = s * scale_log2 + bias2 ----
-    const float bias2 = Bs[bcur][qloc] * kLog2e;
+    // (rows past the sequence's end have no stored bias: Stage 1 writes only
+    // valid rows, and a value left in memory could otherwise trigger the
+    // wave's lazy rescale and change the rounding of the valid rows)
+    const float bias2 = qpos < nv ? Bs[bcur][qloc] * kLog2e : 0.f;
     if (c == n_own - 1) {   // the diagonal chunk starts at the tile's first position
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)

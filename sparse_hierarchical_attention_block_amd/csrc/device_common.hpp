@@ -6,7 +6,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dash {
+
+// f(std::integral_constant<int, I>{}) for I = Begin .. End - 1, expanded by
+// template instantiation: register arrays indexed by I stay in registers
+// however long the body (the loop unroller gives up above a size limit and
+// leaves such arrays in scratch memory).
+template <int Begin, int End, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (Begin < End) {
+    f(std::integral_constant<int, Begin>{});
+    static_for<Begin + 1, End>(f);
+  }
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

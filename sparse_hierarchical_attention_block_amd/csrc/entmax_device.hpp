@@ -169,24 +169,25 @@ __device__ __forceinline__ void entmax_accumulate(const float (&xv)[VPL], float 
   s1 = 0.f;
   s2 = 0.f;
   ymin = INFINITY;
+  static_for<0, VPL / 4>([&](auto G4) {
+    constexpr int g4 = decltype(G4)::value;
+    if (g4 < nact4) {   // the active groups come first
 #pragma unroll
-  for (int g4 = 0; g4 < VPL / 4; ++g4) {
-    if (g4 >= nact4) break;   // the active groups come first
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const float y = xv[4 * g4 + ii] - tau;
-      const bool in = y > 0.f;
-      const float yp = fmaxf(y, 0.f);
-      kc += in ? 1 : 0;
-      // min(ymin, y over the support) as v_med3(z, ymin, -inf): no NaN
-      // quieting of the loop-carried ymin as fminf would need
-      ymin = __builtin_amdgcn_fmed3f(in ? y : INFINITY, ymin, -INFINITY);
-      if constexpr (mode == kEntmax15) { s1 += yp; s2 = fmaf(yp, yp, s2); }
-      else if constexpr (mode == kSparsemax) { s1 += yp; }
-      else if constexpr (mode == kEntmaxQuartic) { const float y2 = yp * yp; s1 = fmaf(y2, yp, s1); s2 = fmaf(y2, y2, s2); }
-      else if (in) { const float l = __log2f(y); s1 += exp2f((e - 1.f) * l); s2 += exp2f(e * l); }
+      for (int ii = 0; ii < 4; ++ii) {
+        const float y = xv[4 * g4 + ii] - tau;
+        const bool in = y > 0.f;
+        const float yp = fmaxf(y, 0.f);
+        kc += in ? 1 : 0;
+        // min(ymin, y over the support) as v_med3(z, ymin, -inf): no NaN
+        // quieting of the loop-carried ymin as fminf would need
+        ymin = __builtin_amdgcn_fmed3f(in ? y : INFINITY, ymin, -INFINITY);
+        if constexpr (mode == kEntmax15) { s1 += yp; s2 = fmaf(yp, yp, s2); }
+        else if constexpr (mode == kSparsemax) { s1 += yp; }
+        else if constexpr (mode == kEntmaxQuartic) { const float y2 = yp * yp; s1 = fmaf(y2, yp, s1); s2 = fmaf(y2, y2, s2); }
+        else if (in) { const float l = __log2f(y); s1 += exp2f((e - 1.f) * l); s2 += exp2f(e * l); }
+      }
     }
-  }
+  });
 }
 
 // One update of tau from the statistics of the row's support at tau (k, s1,
@@ -223,12 +224,12 @@ __device__ __forceinline__ bool entmax_update(float k, float s1, float s2, float
 template <int VPL, int mode, typename Red>
 __device__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int nact4 = VPL / 4) {
   float xmax = -INFINITY;
+  static_for<0, VPL / 4>([&](auto G4) {
+    constexpr int g4 = decltype(G4)::value;
+    if (g4 < nact4)
 #pragma unroll
-  for (int g4 = 0; g4 < VPL / 4; ++g4) {
-    if (g4 >= nact4) break;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) xmax = fmaxf(xmax, xv[4 * g4 + ii]);
-  }
+      for (int ii = 0; ii < 4; ++ii) xmax = fmaxf(xmax, xv[4 * g4 + ii]);
+  });
   xmax = red.max(xmax);
   float tau = xmax - 1.0f;
   for (int it = 0; it < 64; ++it) {

@@ -52,6 +52,20 @@ PREFILL_CASES = {
     "window_covers_all_bf16": tiny(seq_len=700, dtype="bf16", gamma=8.0, window=11),
     # 64 < candidates <= 128 in the last tiles, full oracle parity
     "cand74_gqa4": W.get("prefill_8k").replace(seq_len=4800, n_heads=8, n_kv_heads=2),
+    # more than 128 candidates in the last tiles (bf16, G >= 2: the long-row
+    # routing kernel; G / 2 workgroups per tile whose unions are merged),
+    # ragged tails
+    "long_rows_gqa2_d64": W.get("prefill_8k").replace(seq_len=9000, n_heads=4, n_kv_heads=2,
+                                                      head_dim=64),
+    "long_rows_gqa4_bs128": W.get("prefill_64k").replace(seq_len=18000, n_heads=4,
+                                                         n_kv_heads=1),
+    "long_rows_gqa8_window2": W.get("prefill_8k").replace(seq_len=8800, n_heads=8,
+                                                          n_kv_heads=1, head_dim=64, window=2,
+                                                          sigma=0.5),
+    "long_rows_alpha125_gqa4": W.get("prefill_8k").replace(seq_len=8500, n_heads=8,
+                                                           n_kv_heads=2, alpha=1.25),
+    "long_rows_alpha2_gqa4": W.get("prefill_8k").replace(seq_len=8500, n_heads=4, n_kv_heads=1,
+                                                         alpha=2.0),
 }
 
 
@@ -404,3 +418,29 @@ def test_decode_matches_prefill_last_row():
     g = run_decode(wd, dinp, route=False)
     err = np.abs(g["o"][0] - pre[0, :, L - 1]).max()
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("fill", [1e30, float("nan"), -1e30])
+def test_attend_ignores_unwritten_bias_rows(fill):
+    """Stage 1 writes the bias of valid rows only; whatever the rest of the
+    buffer holds (rows past the end of a ragged last tile) must not change any
+    valid output bit (it could otherwise trigger the wave's lazy rescale)."""
+    w = W.get("prefill_8k").replace(seq_len=8500, n_heads=8, n_kv_heads=2, alpha=1.25)
+    inp = W.make_prefill(w)
+    p = params(w)
+    B, Hkv, N, d, bs = w.batch, w.n_kv_heads, w.seq_len, w.head_dim, w.block_size
+    q, k, v = (to_dev(inp[x], w.dtype) for x in ("q", "k", "v"))
+    ws = torch.from_numpy(inp["w_s"]).to(dev())
+    nb = N // bs
+    summ = torch.zeros(B * Hkv * nb * d, dtype=torch.float32, device=dev())
+    dash.dash_summarize(p, k, N, 0, nb, ws, summ, nb)
+    outs = []
+    for value in (0.0, fill):
+        rb = dash.RouteBuffers(dash.dash_route_sizes_prefill(p, N), dev())
+        rb.sel_logp.fill_(value)
+        dash.dash_route(p, q, N, summ, nb, rb)
+        o = torch.empty_like(q)
+        dash.dash_attend(p, q, k, v, N, rb, o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
