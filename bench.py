@@ -151,8 +151,8 @@ def _kv_file(path):
     return kv
 
 
-def counted_traffic(kernel_file, sources, workload):
-    """HBM bytes per launch from a committed counter summary, or None when the
+def counted(kernel_file, sources, workload, key="hbm_bytes_per_launch"):
+    """A figure from a committed counter summary (profiles/), or None when the
     counters were taken on another workload or a kernel source has changed
     since they were taken."""
     kv = _kv_file(os.path.join(PROFILES, kernel_file))
@@ -163,10 +163,13 @@ def counted_traffic(kernel_file, sources, workload):
         h.update(open(os.path.join(CSRC, s), "rb").read())
     if kv.get("source_sha256") != h.hexdigest() or kv.get("workload") != workload:
         return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    for k, v in kv.items():
+        if k == key or k.startswith(key + " "):
+            try:
+                return float(v)
+            except ValueError:
+                return None
+    return None
 
 
 # ---------------------------------------------------------------------------------------
@@ -533,6 +536,8 @@ def decode_leg(args, torch, dash, W, tm, name, paged=False, peaks=None):
            "all_bytes_gbs": round((sel_bytes + summ_bytes) / (ms * 1e-3) / 1e9, 1)}
     if peaks:
         out["roofline"]["frac_of_measured_read"] = rnd(gbs / peaks["hbm_read_gbs"])
+    out["roofline"]["traffic"] = counted(f"{w.name}_traffic.txt", ["decode.hip"], w.name,
+                                         "hbm_bytes_per_step")
     if paged:
         nblk = (L + bs - 1) // bs
         gen = torch.Generator(device="cpu").manual_seed(1234)
@@ -599,6 +604,56 @@ def cpu_baseline(args, W, count, every=16):
 
 # ---------------------------------------------------------------------------------------
 
+def headline(line, pre, peaks):
+    """The driver-facing keys of the JSON line from the headline prefill leg."""
+    w = pre["workload"]
+    line.update({
+        "value": round(w.batch * w.seq_len / (pre["cold"]["median"] * 1e-3), 1),
+        "ms_per_step": rnd(pre["cold"]["median"]),
+        "dtype": w.dtype,
+        "config": {"workload": describe_prefill(w), "global_batch": w.batch,
+                   "seq_len": w.seq_len,
+                   "tile_union_block_density": rnd(pre["tile_union_density"]),
+                   "per_query_block_density": rnd(pre["per_query_density"]),
+                   "parallelism": "single GPU"},
+    })
+    ach = pre["attend_tflops"]
+    line["roofline"] = {
+        "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": rnd(ach / PEAK_BF16_TFLOPS),
+        "traffic": counted("attend_prefill_64k_traffic.txt", ["attend.hip"], w.name),
+        "kernel": "attend_bf16_kernel (Stage 2)",
+        "per_launch_gflop": round(pre["attend_flops"] / 1e9, 2)}
+    if peaks:
+        line["roofline"]["frac_of_measured_mfma"] = rnd(ach / peaks["mfma_bf16_tflops"])
+    line["timing"] = {
+        "protocol": "per-step HIP events; a 1 GiB scratch read before every cold step",
+        "cold_ms": {k2: rnd(v2) for k2, v2 in pre["cold"].items()},
+        "warm_ms": {k2: rnd(v2) for k2, v2 in pre["warm"].items()}}
+    line["step_roofline"] = {
+        "achieved": round(pre["attend_flops"] / (pre["cold"]["median"] * 1e-3) / 1e12, 2),
+        "frac": rnd(pre["attend_flops"] / (pre["cold"]["median"] * 1e-3) / 1e12 /
+                    PEAK_BF16_TFLOPS),
+        "scope": "selected-tile attend flops / whole fused step (summaries + routing + attend)"}
+    line["stages_ms"] = {k2: rnd(v2) for k2, v2 in pre["stages_ms"].items()}
+    rsrc = ["route.hip", "entmax_device.hpp"]
+    rbytes = [counted("route_prefill_64k_counters.txt", rsrc, w.name, f"route_long_kernel.{k}")
+              for k in ("hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch")]
+    t_route = pre["stages_ms"]["route"]
+    line["route"] = {
+        "ms": rnd(t_route),
+        "share_of_step": rnd(t_route / pre["cold"]["median"]),
+        "hbm_bytes_counted": None if None in rbytes else sum(rbytes),
+        "hbm_gbs": None if None in rbytes else round(sum(rbytes) / (t_route * 1e-3) / 1e9, 1),
+        "valu_busy_fraction_counted": counted("route_prefill_64k_counters.txt", rsrc, w.name,
+                                              "route_long_kernel.valu_busy_fraction"),
+        "bound": "latency: neither HBM (see hbm_gbs) nor VALU (see the counted busy fraction)"}
+    if pre["sweep"]:
+        line["alpha_sweep"] = pre["sweep"]
+    if "dense" in pre:
+        line["dense"] = pre["dense"]
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -632,53 +687,18 @@ def main():
     if "peaks" in legs:
         peaks = peaks_leg(args, torch, dash, tm)
         log(f"peaks {peaks}")
-    pre = prefill_leg(args, torch, dash, W, tm, legs)
-    w = pre["workload"]
-    log(f"prefill {w.name}: {pre['cold']['median']:.4f} ms cold")
-    count = pre["count"]
-    torch.cuda.empty_cache()
-    line = {
-        "metric": METRIC,
-        "value": round(w.batch * w.seq_len / (pre["cold"]["median"] * 1e-3), 1),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": rnd(pre["cold"]["median"]),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": describe_prefill(w), "global_batch": w.batch,
-                   "seq_len": w.seq_len,
-                   "tile_union_block_density": rnd(pre["tile_union_density"]),
-                   "per_query_block_density": rnd(pre["per_query_density"]),
-                   "parallelism": "single GPU"},
-    }
-    ach = pre["attend_tflops"]
-    line["roofline"] = {
-        "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": rnd(ach / PEAK_BF16_TFLOPS),
-        "traffic": counted_traffic("attend_prefill_64k_traffic.txt", ["attend.hip"], w.name),
-        "kernel": "attend_bf16_kernel (Stage 2)",
-        "per_launch_gflop": round(pre["attend_flops"] / 1e9, 2)}
-    if peaks:
-        line["roofline"]["frac_of_measured_mfma"] = rnd(ach / peaks["mfma_bf16_tflops"])
-    line["timing"] = {
-        "protocol": "per-step HIP events; a 1 GiB scratch read before every cold step",
-        "cold_ms": {k2: rnd(v2) for k2, v2 in pre["cold"].items()},
-        "warm_ms": {k2: rnd(v2) for k2, v2 in pre["warm"].items()}}
-    line["step_roofline"] = {
-        "achieved": round(pre["attend_flops"] / (pre["cold"]["median"] * 1e-3) / 1e12, 2),
-        "frac": rnd(pre["attend_flops"] / (pre["cold"]["median"] * 1e-3) / 1e12 /
-                    PEAK_BF16_TFLOPS),
-        "scope": "selected-tile attend flops / whole fused step (summaries + routing + attend)"}
-    line["stages_ms"] = {k2: rnd(v2) for k2, v2 in pre["stages_ms"].items()}
-    if pre["sweep"]:
-        line["alpha_sweep"] = pre["sweep"]
-    if "dense" in pre:
-        line["dense"] = pre["dense"]
+    line = {"metric": METRIC, "value": None, "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "headline prefill leg not run"}}
+    count = None
+    if "prefill" in legs:
+        pre = prefill_leg(args, torch, dash, W, tm, legs)
+        w = pre["workload"]
+        log(f"prefill {w.name}: {pre['cold']['median']:.4f} ms cold")
+        count = pre["count"]
+        torch.cuda.empty_cache()
+        headline(line, pre, peaks)
     if "decode" in legs:
         line["decode"] = decode_leg(args, torch, dash, W, tm, args.decode_workload, peaks=peaks)
         log(f"decode {line['decode']['us_per_step']} us")
@@ -700,7 +720,8 @@ def main():
         line["secondary"] = secondary
     if peaks:
         line["measured_peaks"] = peaks
-    line["cpu_baseline"] = cpu_baseline(args, W, count) if "cpu" in legs else None
+    line["cpu_baseline"] = cpu_baseline(args, W, count) if "cpu" in legs and count is not None \
+        else None
     print(json.dumps(line), flush=True)
 
 
