@@ -277,7 +277,7 @@ __device__ __forceinline__ void route_union(const DecodeArgs& a, int64_t bg, int
     if (j < je) {
       for (int h = 0; h < a.G; ++h) pb += Ps[h * pitch + j];
       pb *= invG;
-      a.logp[bg * a.nb + j] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
+      a.logp[bg * a.nb + j] = prior_bias(pb, a.sigma * kLn2);
       Ps[j] = pb;   // column j is only touched by this lane
     }
     cnt += __popcll(__ballot(pb > 0.f));

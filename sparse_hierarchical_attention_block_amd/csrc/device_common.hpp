@@ -86,6 +86,11 @@ __device__ __forceinline__ uint32_t buf_load4(buf_rsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// a store at or beyond the resource's size is dropped
+__device__ __forceinline__ void buf_store4(float v, buf_rsrc r, uint32_t off, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, soff, 0);
+}
+
 // ---- cross-lane exchange without LDS (DPP and gfx950 permlane swaps) -------
 template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
 __device__ __forceinline__ float dpp_src(float v, float old) {

@@ -48,6 +48,24 @@ __device__ __forceinline__ float entmax_pow(float y, int mode, float e) {
   return exp2f(e * __log2f(y));
 }
 
+// [y]_+^e for any y (0 at and below 0); MODE fixed at compile time
+template <int MODE>
+__device__ __forceinline__ float entmax_prob(float y, float e) {
+  const float yp = fmaxf(y, 0.f);
+  if constexpr (MODE == kSparsemax) return yp;
+  else if constexpr (MODE == kEntmax15) return yp * yp;
+  else if constexpr (MODE == kEntmaxQuartic) { const float y2 = yp * yp; return y2 * y2; }
+  else return y > 0.f ? __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(y)) : 0.f;
+}
+
+// The Stage 2 bias sigma * log(pbar) from sigma * ln 2 and pbar >= 0 (-inf at
+// pbar = 0): the hardware log2, its argument held at or above the smallest
+// normal float (a pbar below it, a weight under 1e-38 of the row's, gets the
+// bias of 2^-126)
+__device__ __forceinline__ float prior_bias(float pb, float sigma_ln2) {
+  return pb > 0.f ? sigma_ln2 * __builtin_amdgcn_logf(fmaxf(pb, 1.17549435e-38f)) : -INFINITY;
+}
+
 // log(y^e) for y > 0
 __device__ __forceinline__ float entmax_logpow(float y, int mode, float e) {
   float l = __logf(y);

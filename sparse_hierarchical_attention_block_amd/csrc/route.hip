@@ -9,8 +9,10 @@
 // tiles (most candidate blocks) first.  Candidates of tile qt are the complete
 // blocks before its near-diagonal branch, j < floor(64 qt / bs) - (window - 1).
 // Rows are (position, head of the group)
-// pairs; for tiles with more than 128 candidates (or float32 queries) they are
-// processed in passes of PP positions, PP as large as an 80 KB LDS score
+// pairs.  Tiles of at most 128 candidates keep their scores in MFMA
+// accumulators (route_tile_kernel); bf16 rows of 129 to 512 candidates with
+// G >= 2 go to route_long.hip; the rest (float32 queries, G = 1, longer rows)
+// are processed in passes of PP positions, PP as large as an 80 KB LDS score
 // buffer allows:
 //   1. scores X[row][j] = scale * q_row . s_j into an LDS buffer; bf16 queries
 //      use MFMA 16x16x32 with the float32 summaries split into three bf16
@@ -24,74 +26,13 @@
 #include "dash_internal.hpp"
 #include "device_common.hpp"
 #include "entmax_device.hpp"
+#include "route_common.hpp"
 
 namespace dash {
 
 constexpr int kRoutePassThreads = DASH_ROUTE_PASS_THREADS;   // pass-based path
 constexpr size_t kRouteXBudget = DASH_ROUTE_X_BUDGET;         // its LDS score buffer
-constexpr int kQT = DASH_QUERY_TILE;
 constexpr int kRouteMaxRowTiles = 4;   // rows per pass <= 64
-
-struct RouteArgs {
-  const void* q;
-  int64_t n;            // positions per sequence in memory (the row stride)
-  const int32_t* seq_len;  // [B] valid positions per sequence, or null (all n)
-  int64_t nv;           // valid positions of the workgroup's sequence
-  const float* summ;
-  int64_t summ_blocks;
-  float* tau;
-  int32_t* sel_count;
-  int32_t* sel_idx;
-  float* sel_logp;
-  uint32_t* bits;
-  uint32_t* tile_bits;   // optional bit-packed union per tile
-  int64_t n_qt, nb;
-  int nwords;
-  int H, Hkv, G, bs, B;
-  int mode;
-  float e, scale;
-  float sigma;  // prior strength: sel_logp = sigma * log pbar
-  int window;   // near-diagonal branch in blocks
-  int PP;      // positions per pass
-  int pitch;   // X row pitch in floats (multiple of 4)
-};
-
-__host__ __device__ inline int round_up16(int x) { return (x + 15) & ~15; }
-
-// Valid positions of sequence b: seq_len[b] clamped into [0, n], or n.
-__device__ __forceinline__ int64_t valid_len(const int32_t* seq_len, int b, int64_t n) {
-  if (!seq_len) return n;
-  const int64_t l = seq_len[b];
-  return l < 0 ? 0 : (l > n ? n : l);
-}
-
-// A tile at or past its sequence's end: an empty list (its rows are not written).
-__device__ __forceinline__ void route_tile_past_end(const RouteArgs& a, int64_t tile) {
-  if (threadIdx.x == 0) a.sel_count[tile] = 0;
-  if (a.tile_bits)
-    for (int w = threadIdx.x; w < a.nwords; w += blockDim.x) a.tile_bits[tile * a.nwords + w] = 0u;
-}
-
-// Compaction of the tile's union flags (blocks j < t) into the ascending list
-// sel_idx / sel_count, and the same set as the tile's bit-packed mask when
-// asked for (words past the candidates are zero).  One wave calls.
-__device__ void compact_union(const RouteArgs& a, const int* uflag, int t, int64_t tile) {
-  const int lane = threadIdx.x % kWave;
-  uint32_t* tb = a.tile_bits ? a.tile_bits + tile * a.nwords : nullptr;
-  int base = 0;
-  for (int j0 = 0; j0 < t; j0 += kWave) {
-    const int j = j0 + lane;
-    const bool f = j < t && uflag[j] != 0;
-    const uint64_t mask = __ballot(f);
-    if (f) a.sel_idx[tile * a.nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
-    base += __popcll(mask);
-    if (tb && lane < 2 && j0 / 32 + lane < a.nwords)
-      tb[j0 / 32 + lane] = (uint32_t)(mask >> (32 * lane));
-  }
-  if (tb)
-    for (int w = 2 * ((t + kWave - 1) / kWave) + lane; w < a.nwords; w += kWave) tb[w] = 0u;
-  if (lane == 0) a.sel_count[tile] = base;
-}
 
 // ---- step 1, bf16: MFMA with a 3-way bf16 split of the summaries ----------------
 // Wave w computes candidate tiles w, w + NT/64, ... against every row tile of
@@ -301,7 +242,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
           const int j = sub + lpr * (s2 | h);
           if (j < t) {
             const float pb = pv[s2] * invG;
-            a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
+            a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = prior_bias(pb, a.sigma * kLn2);
             if (pb > 0.f) uflag[j] = 1;
           }
         }
@@ -341,7 +282,7 @@ __global__ __launch_bounds__(NT) void route_prefill_kernel(RouteArgs a) {
           if (y > 0.f) pb += entmax_pow(y, a.mode, a.e);
         }
         pb *= invG;
-        a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
+        a.sel_logp[(tile * a.nb + j) * kQT + pp + m] = prior_bias(pb, a.sigma * kLn2);
         if (pb > 0.f) uflag[j] = 1;
       }
     }
@@ -572,7 +513,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
         const int j = 16 * (slot >> 2) + 4 * lg + (slot & 3);
         if (j < t) {
           const float pb = xv[s2] * invG;
-          lp[j * kQT] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
+          lp[j * kQT] = prior_bias(pb, a.sigma * kLn2);
           if (pb > 0.f) uflag[j] = 1;
         }
       }
@@ -582,273 +523,6 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
 
   // ---- compaction (ascending block ids) ----
   if (threadIdx.x < kWave) compact_union(a, uflag, t, tile);
-}
-
-// ------------------------------------------------------------------------------------------
-// Long rows (up to 512 candidates, bf16 queries, G >= 2).  The tile's 64 G
-// rows are cut into G / 2 parts of 128 rows (128 / G positions x the G heads
-// of a position), one workgroup of 8 waves per part and 16 rows per wave.
-// As in the tile-resident kernel, a row's scores stay in MFMA accumulators --
-// here for 32 candidate tiles of 16 -- but the summaries stream through LDS
-// 64 candidates at a time: each part loads and splits every summary row once
-// (the pass-based kernel reloads and resplits them for every pass of a few
-// positions).  With one part (G = 2) the workgroup compacts the tile's list
-// itself; otherwise each part leaves its union as bit-packed words at the
-// front of the tile's sel_idx row and route_merge_kernel ORs the parts and
-// compacts.
-// ------------------------------------------------------------------------------------------
-constexpr int kLongMaxCT = 32;     // candidate tiles of 16 per row (512 candidates)
-constexpr int kLongChunk = 64;     // candidates per staged chunk
-constexpr int kLongThreads = 512;  // 8 waves x 16 rows
-
-template <int D, int MODE>
-__global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
-  constexpr int SP = D + 8;                                 // plane row pitch (bf16)
-  constexpr int KS = D / 32;
-  constexpr int CCT = kLongChunk / 16;                      // candidate tiles per chunk
-  constexpr int SV = kLongChunk * (D / 4) / kLongThreads;   // float4s per thread per chunk
-  static_assert(SV >= 1, "one chunk covers every thread");
-  __shared__ __attribute__((aligned(16))) __bf16 planes[3 * kLongChunk * SP];   // hi, mid, lo
-  extern __shared__ int lflag[];                            // [pitch] union flags of the part
-
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int l16 = lane % 16, lg = lane / 16;
-  const int G = a.G;
-  const int parts = G / 2, ppos = kQT / parts;               // positions per part
-  const int64_t nbg = (int64_t)a.B * a.Hkv;
-  const int part = (int)(blockIdx.x % parts);
-  const int64_t rank = blockIdx.x / parts;
-  const int64_t qt = a.n_qt - 1 - rank / nbg;               // heaviest tiles first
-  const int64_t bg = rank % nbg;
-  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
-  const int64_t p_begin = qt * kQT;
-  const int t = max(0, (int)(p_begin / a.bs) - (a.window - 1));   // candidates
-  const int64_t tile = bg * a.n_qt + qt;
-  a.nv = valid_len(a.seq_len, b, a.n);
-  if (p_begin >= a.nv) {
-    if (parts == 1) route_tile_past_end(a, tile);
-    return;
-  }
-  const int r = 16 * wave + l16;          // row within the part
-  const int m = r / G, h = r % G;
-  const int64_t pos = p_begin + part * ppos + m;
-  const int64_t rglob = ((int64_t)b * a.H + g * G + h) * a.n + pos;
-  if (t == 0) {
-    if (lg == 0 && pos < a.nv) {
-      a.tau[rglob] = __builtin_nanf("");
-      if (a.bits)
-        for (int w = 0; w < a.nwords; ++w) a.bits[rglob * a.nwords + w] = 0u;
-    }
-    if (parts == 1) {
-      if (threadIdx.x == 0) a.sel_count[tile] = 0;
-      if (a.tile_bits)
-        for (int w = threadIdx.x; w < a.nwords; w += kLongThreads) a.tile_bits[tile * a.nwords + w] = 0u;
-    }
-    return;
-  }
-  const int CT = (t + 15) / 16;
-  for (int j = threadIdx.x; j < a.pitch; j += kLongThreads) lflag[j] = 0;
-
-  // Q^T fragments of the wave's 16 rows: column = row l16, k = d in [32 s + 8 lg, +8)
-  bf16x8 qf[KS];
-  {
-    const __bf16* qrow = (const __bf16*)a.q + rglob * D;
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      u32x4 qv = {0u, 0u, 0u, 0u};
-      if (pos < a.nv) qv = *(const u32x4*)(qrow + 32 * s2 + 8 * lg);
-      qf[s2] = as_bf16x8(qv);
-    }
-  }
-  // a chunk of summary rows: loaded into registers one chunk ahead, split
-  // into the three bf16 planes when stored
-  f32x4 pre[SV];
-  auto load_chunk = [&](int c0) {
-#pragma unroll
-    for (int u = 0; u < SV; ++u) {
-      const int e = threadIdx.x + u * kLongThreads;
-      const int cand = e / (D / 4), c4 = e % (D / 4);
-      pre[u] = c0 + cand < t
-                   ? *(const f32x4*)(a.summ + (bg * a.summ_blocks + c0 + cand) * D + 4 * c4)
-                   : (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int u = 0; u < SV; ++u) {
-      const int e = threadIdx.x + u * kLongThreads;
-      const int cand = e / (D / 4), c4 = e % (D / 4);
-      const float xs[4] = {pre[u].x, pre[u].y, pre[u].z, pre[u].w};
-      uint32_t hw[2], mw[2], lw[2];
-#pragma unroll
-      for (int p2 = 0; p2 < 2; ++p2) {
-        float hv[2], mv[2], lv[2];
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const float x = xs[2 * p2 + q2];
-          const float hh = (float)(__bf16)x;
-          const float r1 = x - hh;
-          const float mm = (float)(__bf16)r1;
-          hv[q2] = hh;
-          mv[q2] = mm;
-          lv[q2] = r1 - mm;
-        }
-        hw[p2] = pack_bf16(hv[0], hv[1]);
-        mw[p2] = pack_bf16(mv[0], mv[1]);
-        lw[p2] = pack_bf16(lv[0], lv[1]);
-      }
-      const int off = cand * SP + 4 * c4;
-      *(u32x2*)(planes + off) = (u32x2){hw[0], hw[1]};
-      *(u32x2*)(planes + kLongChunk * SP + off) = (u32x2){mw[0], mw[1]};
-      *(u32x2*)(planes + 2 * kLongChunk * SP + off) = (u32x2){lw[0], lw[1]};
-    }
-  };
-
-  // ---- scores: X[ct][i] = x(row r, cand 16 ct + 4 lg + i) ----
-  f32x4 X[kLongMaxCT];
-#pragma unroll
-  for (int ct = 0; ct < kLongMaxCT; ++ct) X[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  load_chunk(0);
-#pragma unroll
-  for (int c = 0; c < kLongMaxCT / CCT; ++c) {
-    if (c * CCT >= CT) break;
-    __syncthreads();   // every wave is done with the previous chunk's planes
-    store_chunk();
-    __syncthreads();
-    if ((c + 1) * CCT < CT) load_chunk((c + 1) * kLongChunk);
-#pragma unroll
-    for (int k = 0; k < CCT; ++k) {
-      if (c * CCT + k < CT) {
-#pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) {
-          const int off = (16 * k + l16) * SP + 32 * s2 + 8 * lg;
-          const bf16x8 hi = as_bf16x8(*(const u32x4*)(planes + off));
-          const bf16x8 mid = as_bf16x8(*(const u32x4*)(planes + kLongChunk * SP + off));
-          const bf16x8 lo = as_bf16x8(*(const u32x4*)(planes + 2 * kLongChunk * SP + off));
-          X[c * CCT + k] = mfma16(lo, qf[s2], X[c * CCT + k]);
-          X[c * CCT + k] = mfma16(mid, qf[s2], X[c * CCT + k]);
-          X[c * CCT + k] = mfma16(hi, qf[s2], X[c * CCT + k]);
-        }
-      }
-    }
-  }
-
-  // ---- threshold, support bits, pbar and the Stage 2 bias ----
-  float xv[4 * kLongMaxCT];
-#pragma unroll
-  for (int ct = 0; ct < kLongMaxCT; ++ct)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xv[4 * ct + i] = (16 * ct + 4 * lg + i < t) ? X[ct][i] * a.scale : -INFINITY;
-  const float tau = entmax_tau_reg<4 * kLongMaxCT, MODE>(xv, Stride16Reduce{}, a.e, CT);
-  if (a.bits) {
-    // ballots give, for each (ct, i), the bit of every (row, lg) pair
-    uint32_t chunk[kLongMaxCT];
-#pragma unroll
-    for (int ct = 0; ct < kLongMaxCT; ++ct) {
-      chunk[ct] = 0u;
-      if (ct < CT) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint64_t mk = __ballot(xv[4 * ct + i] > tau);
-#pragma unroll
-          for (int l2 = 0; l2 < 4; ++l2)
-            chunk[ct] |= (uint32_t)((mk >> (16 * l2 + l16)) & 1ull) << (4 * l2 + i);
-        }
-      }
-    }
-    if (lg == 0 && pos < a.nv)
-      for (int w = 0; w < a.nwords; ++w) {
-        uint32_t word = 0u;
-#pragma unroll
-        for (int ct = 0; ct < kLongMaxCT; ++ct)
-          if (ct / 2 == w) word |= chunk[ct] << (16 * (ct % 2));
-        a.bits[rglob * a.nwords + w] = word;
-      }
-  }
-  if (lg == 0 && pos < a.nv) a.tau[rglob] = tau;
-#pragma unroll
-  for (int ct = 0; ct < kLongMaxCT; ++ct)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float y = xv[4 * ct + i] - tau;
-      xv[4 * ct + i] = ct < CT && y > 0.f ? entmax_pow(y, MODE, a.e) : 0.f;
-    }
-  // GQA sum as a reduce-scatter over the G rows of a position (lanes whose
-  // l16 differ in the bits of h = l16 % G), as in the tile-resident kernel
-#pragma unroll
-  for (int bb = 0; bb < 3; ++bb) {
-    const int bit = 1 << bb;
-    if (bit < G) {
-      const bool up = (h & bit) != 0;
-#pragma unroll
-      for (int s2 = 0; s2 < 4 * kLongMaxCT; ++s2) {
-        if ((s2 & (2 * bit - 1)) != 0 || (s2 >> 2) >= CT) continue;
-        const float lo = xv[s2], hi = xv[s2 | bit];
-        const float send = up ? lo : hi, keep = up ? hi : lo;
-        xv[s2] = keep + lane_xor_c(send, bit);
-      }
-    }
-  }
-  const float invG = 1.0f / (float)G;
-  if (pos < a.nv) {
-    float* lp = a.sel_logp + tile * a.nb * kQT + (pos - p_begin);
-#pragma unroll
-    for (int s2 = 0; s2 < 4 * kLongMaxCT; ++s2) {
-      if (s2 % G != 0 || (s2 >> 2) >= CT) continue;
-      const int slot = s2 | h;
-      const int j = 16 * (slot >> 2) + 4 * lg + (slot & 3);
-      if (j < t) {
-        const float pb = xv[s2] * invG;
-        lp[j * kQT] = pb > 0.f ? a.sigma * __logf(pb) : -INFINITY;
-        if (pb > 0.f) lflag[j] = 1;
-      }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x >= kWave) return;
-  if (parts == 1) {
-    compact_union(a, lflag, t, tile);
-    return;
-  }
-  // this part's union, bit-packed, at words part * nwords + w (w < ceil(t /
-  // 32), so no part writes into the next one's words) of the tile's sel_idx
-  // row (parts * nwords <= nb whenever t > 128)
-  uint32_t* words = (uint32_t*)(a.sel_idx + tile * a.nb) + part * a.nwords;
-  const int nwt = (t + 31) / 32;
-  for (int j0 = 0; j0 < t; j0 += kWave) {
-    const uint64_t mask = __ballot(j0 + lane < t && lflag[j0 + lane] != 0);
-    if (lane < 2 && j0 / 32 + lane < nwt) words[j0 / 32 + lane] = (uint32_t)(mask >> (32 * lane));
-  }
-}
-
-// The parts' union words of each tile (route_long_kernel) ORed into the
-// tile's list: one wave per tile.  Every word is read into a register before
-// the list, which overwrites them, is written.
-__global__ __launch_bounds__(kWave) void route_merge_kernel(RouteArgs a, int parts) {
-  const int64_t tile = blockIdx.x;
-  const int64_t qt = tile % a.n_qt, bg = tile / a.n_qt;
-  const int b = (int)(bg / a.Hkv);
-  const int lane = threadIdx.x;
-  const int64_t p_begin = qt * kQT;
-  const int t = p_begin < valid_len(a.seq_len, b, a.n)
-                    ? max(0, (int)(p_begin / a.bs) - (a.window - 1)) : 0;
-  const int nwt = (t + 31) / 32;   // <= 16 words (t <= 512)
-  int32_t* row = a.sel_idx + tile * a.nb;
-  uint32_t wv = 0u;
-  if (lane < nwt)
-    for (int p = 0; p < parts; ++p) wv |= ((const uint32_t*)row)[p * a.nwords + lane];
-  int base = 0;
-  for (int j0 = 0; j0 < t; j0 += kWave) {
-    const uint32_t w0 = __shfl(wv, j0 / 32), w1 = __shfl(wv, j0 / 32 + 1);
-    const uint64_t mask = ((uint64_t)w1 << 32 | w0) &
-                          (t - j0 >= kWave ? ~0ull : ((1ull << (t - j0)) - 1ull));
-    if ((mask >> lane) & 1ull) row[base + __popcll(mask & ((1ull << lane) - 1ull))] = j0 + lane;
-    base += __popcll(mask);
-  }
-  if (a.tile_bits)   // nwt <= 16, so a word below nwt is this lane's own
-    for (int w = lane; w < a.nwords; w += kWave) a.tile_bits[tile * a.nwords + w] = w < nwt ? wv : 0u;
-  if (lane == 0) a.sel_count[tile] = base;
 }
 
 // positions per pass: largest power of two in [16/G, 64] whose score buffer
@@ -923,29 +597,8 @@ hipError_t launch_route_prefill(const Shape& s, const void* q, int64_t n, const 
   a.sigma = s.sigma;
   a.window = s.window;
   const int t_max = max(0, (int)(((a.n_qt - 1) * kQT) / s.bs) - (s.window - 1));
-  if (s.dtype == DASH_BF16 && t_max > 16 * kTileMaxCT && t_max <= 16 * kLongMaxCT && s.G >= 2) {
-    // long rows: workgroups of 128 rows, scores in registers
-    a.pitch = round_up16(t_max);
-    const int parts = s.G / 2;
-    const size_t lds = (size_t)a.pitch * 4;
-    dim3 grid_l((unsigned)(a.n_qt * s.B * s.Hkv * parts));
-#define DASH_RL(D, M) \
-  hipLaunchKernelGGL((route_long_kernel<D, M>), grid_l, dim3(kLongThreads), lds, st, a)
-#define DASH_RL2(D)                                                           \
-  do {                                                                        \
-    if (a.mode == kEntmax15) DASH_RL(D, kEntmax15);                           \
-    else if (a.mode == kSparsemax) DASH_RL(D, kSparsemax);                    \
-    else if (a.mode == kEntmaxQuartic) DASH_RL(D, kEntmaxQuartic);            \
-    else DASH_RL(D, kEntmaxGeneral);                                          \
-  } while (0)
-    if (s.d == 64) DASH_RL2(64); else DASH_RL2(128);
-#undef DASH_RL2
-#undef DASH_RL
-    if (parts > 1)
-      hipLaunchKernelGGL(route_merge_kernel, dim3((unsigned)(a.n_qt * s.B * s.Hkv)), dim3(kWave),
-                         0, st, a, parts);
-    return hipGetLastError();
-  }
+  if (s.dtype == DASH_BF16 && t_max > 16 * kTileMaxCT && t_max <= 16 * kLongMaxCT && s.G >= 2)
+    return launch_route_long(a, s, t_max, st);
   if (s.dtype == DASH_BF16 && t_max <= 16 * kTileMaxCT) {
     // tile-resident path: one wave per 64 rows of the tile
     a.pitch = round_up16(t_max > 0 ? t_max : 1);

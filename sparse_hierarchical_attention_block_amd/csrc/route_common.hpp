@@ -1,0 +1,80 @@
+// route_common.hpp -- what the prefill routing kernels share: their argument
+// block, sequence bounds and the compaction of a tile's union flags into its
+// ascending block list (Stage 1 output, "entmax chunk routing", DashAttention
+// explainer, Technical summary).
+#pragma once
+
+#include "dash_internal.hpp"
+#include "device_common.hpp"
+
+namespace dash {
+
+constexpr int kQT = DASH_QUERY_TILE;
+
+struct RouteArgs {
+  const void* q;
+  int64_t n;            // positions per sequence in memory (the row stride)
+  const int32_t* seq_len;  // [B] valid positions per sequence, or null (all n)
+  int64_t nv;           // valid positions of the workgroup's sequence
+  const float* summ;
+  int64_t summ_blocks;
+  float* tau;
+  int32_t* sel_count;
+  int32_t* sel_idx;
+  float* sel_logp;
+  uint32_t* bits;
+  uint32_t* tile_bits;   // optional bit-packed union per tile
+  int64_t n_qt, nb;
+  int nwords;
+  int H, Hkv, G, bs, B;
+  int mode;
+  float e, scale;
+  float sigma;  // prior strength: sel_logp = sigma * log pbar
+  int window;   // near-diagonal branch in blocks
+  int PP;      // positions per pass
+  int pitch;   // X row pitch in floats (multiple of 4)
+};
+
+__host__ __device__ inline int round_up16(int x) { return (x + 15) & ~15; }
+
+// Valid positions of sequence b: seq_len[b] clamped into [0, n], or n.
+__device__ __forceinline__ int64_t valid_len(const int32_t* seq_len, int b, int64_t n) {
+  if (!seq_len) return n;
+  const int64_t l = seq_len[b];
+  return l < 0 ? 0 : (l > n ? n : l);
+}
+
+// A tile at or past its sequence's end: an empty list (its rows are not written).
+__device__ __forceinline__ void route_tile_past_end(const RouteArgs& a, int64_t tile) {
+  if (threadIdx.x == 0) a.sel_count[tile] = 0;
+  if (a.tile_bits)
+    for (int w = threadIdx.x; w < a.nwords; w += blockDim.x) a.tile_bits[tile * a.nwords + w] = 0u;
+}
+
+// Compaction of the tile's union flags (blocks j < t) into the ascending list
+// sel_idx / sel_count, and the same set as the tile's bit-packed mask when
+// asked for (words past the candidates are zero).  One wave calls.
+__device__ __forceinline__ void compact_union(const RouteArgs& a, const int* uflag, int t,
+                                              int64_t tile) {
+  const int lane = threadIdx.x % kWave;
+  uint32_t* tb = a.tile_bits ? a.tile_bits + tile * a.nwords : nullptr;
+  int base = 0;
+  for (int j0 = 0; j0 < t; j0 += kWave) {
+    const int j = j0 + lane;
+    const bool f = j < t && uflag[j] != 0;
+    const uint64_t mask = __ballot(f);
+    if (f) a.sel_idx[tile * a.nb + base + __popcll(mask & ((1ull << lane) - 1ull))] = j;
+    base += __popcll(mask);
+    if (tb && lane < 2 && j0 / 32 + lane < a.nwords)
+      tb[j0 / 32 + lane] = (uint32_t)(mask >> (32 * lane));
+  }
+  if (tb)
+    for (int w = 2 * ((t + kWave - 1) / kWave) + lane; w < a.nwords; w += kWave) tb[w] = 0u;
+  if (lane == 0) a.sel_count[tile] = base;
+}
+
+// Rows of 129 to 512 candidates (bf16 queries, G >= 2): route_long.hip.
+constexpr int kLongMaxCT = 32;     // candidate tiles of 16 per row (512 candidates)
+hipError_t launch_route_long(RouteArgs a, const Shape& s, int t_max, hipStream_t st);
+
+}  // namespace dash
