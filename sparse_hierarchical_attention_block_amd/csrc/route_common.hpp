@@ -6,6 +6,7 @@
 
 #include "dash_internal.hpp"
 #include "device_common.hpp"
+#include "entmax_device.hpp"
 
 namespace dash {
 
@@ -72,6 +73,55 @@ __device__ __forceinline__ void compact_union(const RouteArgs& a, const int* ufl
     for (int w = 2 * ((t + kWave - 1) / kWave) + lane; w < a.nwords; w += kWave) tb[w] = 0u;
   if (lane == 0) a.sel_count[tile] = base;
 }
+
+// GQA sum of a row's probabilities and the Stage 2 bias, for rows whose
+// scores sit in MFMA 16x16 accumulators (lane l16 + 16 lg of a wave holds
+// row l16's candidates 16 ct + 4 lg + i, i < 4, in slot 4 ct + i).  The sum over
+// the G rows of a position is a reduce-scatter over the lanes whose l16
+// differ in the bits of h = l16 % G: after it, the lane of head h holds the
+// sum for the slots s with s % G == h (slot s = 4 ct + i is candidate
+// 16 ct + 4 lg + i), which it writes.  Slots of candidate tiles at or past
+// CT are never written (their j is at least t).
+template <int G, int MAXCT>
+__device__ __forceinline__ void route_rows_bias(const RouteArgs& a, float (&xv)[4 * MAXCT],
+                                                int CT, int t, int lg, int h, int64_t pos,
+                                                int64_t p_begin, int64_t tile, int* lflag) {
+  static_for<0, 3>([&](auto BB) {
+    constexpr int bit = 1 << decltype(BB)::value;
+    if constexpr (bit < G) {
+      const bool up = (h & bit) != 0;
+      static_for<0, 4 * MAXCT / (2 * bit)>([&](auto K) {
+        constexpr int s2 = 2 * bit * decltype(K)::value;
+        if ((s2 >> 2) < CT) {
+          const float lo = xv[s2], hi = xv[s2 | bit];
+          const float send = up ? lo : hi, keep = up ? hi : lo;
+          xv[s2] = keep + lane_xor<bit>(send);
+        }
+      });
+    }
+  });
+  if (pos >= a.nv) return;
+  constexpr float invG = 1.0f / (float)G;
+  const float sl2 = a.sigma * kLn2;
+  // the bias rows of the tile's t candidates through a buffer resource of
+  // their size (32-bit offsets)
+  const buf_rsrc lp = make_rsrc(a.sel_logp + tile * a.nb * kQT, (uint32_t)t * kQT * 4);
+  const int jl = 16 * (h >> 2) + (h & 3) + 4 * lg;   // lane part of j
+  const uint32_t voff = (uint32_t)(jl * kQT + (pos - p_begin)) * 4;
+  static_for<0, 4 * MAXCT / G>([&](auto K) {
+    constexpr int s2 = G * decltype(K)::value;
+    constexpr int jc = 16 * (s2 >> 2) + (s2 & 3);     // j = jc + jl
+    if ((s2 >> 2) < CT && jc + jl < t) {
+      const float pb = xv[s2] * invG;
+      buf_store4(prior_bias(pb, sl2), lp, voff + (uint32_t)jc * kQT * 4, 0u);
+      if (pb > 0.f) lflag[jc + jl] = 1;
+    }
+  });
+}
+
+// Rows of at most 128 candidates (bf16 queries): route_tile.hip.
+constexpr int kTileMaxCT = 8;      // candidate tiles of 16 per row (128 candidates)
+hipError_t launch_route_tile(RouteArgs a, const Shape& s, int t_max, hipStream_t st);
 
 // Rows of 129 to 512 candidates (bf16 queries, G >= 2): route_long.hip.
 constexpr int kLongMaxCT = 32;     // candidate tiles of 16 per row (512 candidates)

@@ -27,49 +27,6 @@ namespace dash {
 constexpr int kLongChunk = 64;     // candidates per staged chunk
 constexpr int kLongThreads = 512;  // 8 waves x 16 rows
 
-// GQA sum of a long row's probabilities and the Stage 2 bias.  The sum over
-// the G rows of a position is a reduce-scatter over the lanes whose l16
-// differ in the bits of h = l16 % G: after it, the lane of head h holds the
-// sum for the slots s with s % G == h (slot s = 4 ct + i is candidate
-// 16 ct + 4 lg + i), which it writes.  Slots of candidate tiles at or past
-// CT are never written (their j is at least t).
-template <int G>
-__device__ __forceinline__ void route_long_bias(const RouteArgs& a, float (&xv)[4 * kLongMaxCT],
-                                                int CT, int t, int lg, int h, int64_t pos,
-                                                int64_t p_begin, int64_t tile, int* lflag) {
-  static_for<0, 3>([&](auto BB) {
-    constexpr int bit = 1 << decltype(BB)::value;
-    if constexpr (bit < G) {
-      const bool up = (h & bit) != 0;
-      static_for<0, 4 * kLongMaxCT / (2 * bit)>([&](auto K) {
-        constexpr int s2 = 2 * bit * decltype(K)::value;
-        if ((s2 >> 2) < CT) {
-          const float lo = xv[s2], hi = xv[s2 | bit];
-          const float send = up ? lo : hi, keep = up ? hi : lo;
-          xv[s2] = keep + lane_xor<bit>(send);
-        }
-      });
-    }
-  });
-  if (pos >= a.nv) return;
-  constexpr float invG = 1.0f / (float)G;
-  const float sl2 = a.sigma * kLn2;
-  // the bias rows of the tile's t candidates through a buffer resource of
-  // their size (32-bit offsets)
-  const buf_rsrc lp = make_rsrc(a.sel_logp + tile * a.nb * kQT, (uint32_t)t * kQT * 4);
-  const int jl = 16 * (h >> 2) + (h & 3) + 4 * lg;   // lane part of j
-  const uint32_t voff = (uint32_t)(jl * kQT + (pos - p_begin)) * 4;
-  static_for<0, 4 * kLongMaxCT / G>([&](auto K) {
-    constexpr int s2 = G * decltype(K)::value;
-    constexpr int jc = 16 * (s2 >> 2) + (s2 & 3);     // j = jc + jl
-    if ((s2 >> 2) < CT && jc + jl < t) {
-      const float pb = xv[s2] * invG;
-      buf_store4(prior_bias(pb, sl2), lp, voff + (uint32_t)jc * kQT * 4, 0u);
-      if (pb > 0.f) lflag[jc + jl] = 1;
-    }
-  });
-}
-
 template <int D, int MODE, int G>
 __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
   constexpr int SP = D + 8;                                 // plane row pitch (bf16)
@@ -248,7 +205,7 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
       for (int i = 0; i < 4; ++i) xv[4 * ct + i] = entmax_prob<MODE>(xv[4 * ct + i] - tau, a.e);
     }
   });
-  route_long_bias<G>(a, xv, CT, t, lg, h, pos, p_begin, tile, lflag);
+  route_rows_bias<G, kLongMaxCT>(a, xv, CT, t, lg, h, pos, p_begin, tile, lflag);
   __syncthreads();
   if (threadIdx.x >= kWave) return;
   if (parts == 1) {
