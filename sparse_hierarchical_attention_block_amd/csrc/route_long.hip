@@ -26,6 +26,7 @@ namespace dash {
 // ------------------------------------------------------------------------------------------
 constexpr int kLongChunk = 64;     // candidates per staged chunk
 constexpr int kLongThreads = 512;  // 8 waves x 16 rows
+constexpr int kLongRows = 16 * kLongThreads / kWave;   // rows per part
 
 template <int D, int MODE, int G>
 __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int l16 = lane % 16, lg = lane / 16;
-  constexpr int parts = G / 2, ppos = kQT / parts;           // positions per part
+  constexpr int parts = kQT * G / kLongRows, ppos = kQT / parts;   // positions per part
   const int64_t nbg = (int64_t)a.B * a.Hkv;
   const int part = (int)(blockIdx.x % parts);
   const int64_t rank = blockIdx.x / parts;
@@ -87,15 +88,16 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
   }
   // a chunk of summary rows: loaded into registers one chunk ahead, split
   // into the three bf16 planes when stored
+  // (a buffer resource over the t candidate rows: loads past them return
+  // zeros without a branch, so nothing waits on them before the next store)
+  const buf_rsrc srs = make_rsrc(a.summ + bg * a.summ_blocks * D, (uint32_t)t * D * 4);
   f32x4 pre[SV];
   auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < SV; ++u) {
       const int e = threadIdx.x + u * kLongThreads;
       const int cand = e / (D / 4), c4 = e % (D / 4);
-      pre[u] = c0 + cand < t
-                   ? *(const f32x4*)(a.summ + (bg * a.summ_blocks + c0 + cand) * D + 4 * c4)
-                   : (f32x4){0.f, 0.f, 0.f, 0.f};
+      pre[u] = __builtin_bit_cast(f32x4, buf_load16(srs, (uint32_t)(((c0 + cand) * D + 4 * c4) * 4)));
     }
   };
   auto store_chunk = [&]() {
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(kWave) void route_merge_kernel(RouteArgs a, int par
 hipError_t launch_route_long(RouteArgs a, const Shape& s, int t_max, hipStream_t st) {
   // workgroups of 128 rows, scores in registers
   a.pitch = round_up16(t_max);
-  const int parts = s.G / 2;
+  const int parts = kQT * s.G / kLongRows;
   const size_t lds = (size_t)a.pitch * 4;
   dim3 grid_l((unsigned)(a.n_qt * s.B * s.Hkv * parts));
 #define DASH_RL(D, M)                                                                        \
