@@ -268,7 +268,7 @@ constexpr float kEntmaxSumsStop = 1e-2f;
 // once a step falls below kEntmaxSumsStop the passes gather the full support
 // statistics, so that the closed-form solve can end the search as before.
 template <int VPL, int mode, typename Red>
-__device__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int nact4 = VPL / 4) {
+__device__ __forceinline__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int nact4 = VPL / 4) {
   float xmax = -INFINITY;
   static_for<0, VPL / 4>([&](auto G4) {
     constexpr int g4 = decltype(G4)::value;

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
         float hv[2], mv[2], lv[2];
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
-          const float x = xs[2 * p2 + q2];
+          const float x = xs[2 * p2 + q2] * a.scale;   // scale folded into the summaries
           const float hh = (float)(__bf16)x;
           const float r1 = x - hh;
           const float mm = (float)(__bf16)r1;
@@ -164,10 +164,13 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
   float xv[4 * kLongMaxCT];
   static_for<0, kLongMaxCT>([&](auto CTc) {
     constexpr int ct = decltype(CTc)::value;
-    if (ct < CT) {
+    if (ct < CT - 1) {   // every candidate of the tile exists
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[4 * ct + i] = X[ct][i];
+    } else if (ct == CT - 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        xv[4 * ct + i] = (16 * ct + 4 * lg + i < t) ? X[ct][i] * a.scale : -INFINITY;
+        xv[4 * ct + i] = 16 * ct + 4 * lg + i < t ? X[ct][i] : -INFINITY;
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) xv[4 * ct + i] = 0.f;
