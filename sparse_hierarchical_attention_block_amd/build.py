@@ -17,8 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "dash")
 LIB = os.path.join(PKG, "libdash.so")
-SOURCES = ["summarize.hip", "route.hip", "route_tile.hip", "route_long.hip", "attend.hip", "decode.hip", "backward.hip", "peaks.hip",
-           "api.cpp"]
+SOURCES = ["summarize.hip", "route.hip", "route_tile.hip", "route_long.hip", "attend.hip",
+           "decode.hip", "backward.hip", "peaks.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
