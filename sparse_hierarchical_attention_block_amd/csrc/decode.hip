@@ -779,13 +779,15 @@ __global__ __launch_bounds__(256) void decode_attend_f32_kernel(DecodeArgs a) {
 // ---- 4. combine ----------------------------------------------------------------------------
 // grid (ceil(G D / 256), B Hkv): workgroup x merges outputs [256 x, 256 x + 256)
 // of the G heads x D columns of one (sequence, KV head), one output per
-// thread.  The split maxima and sums of the heads it covers are staged in LDS
-// and turned into weights exp2(m_s - M) by one thread per head; every thread
-// then reads its column of all ns splits, 16 loads in flight.  Fixed order in s.
+// thread.  Each thread reads the maximum, sum and its column of up to
+// kCombineChunk splits at once (one memory round trip per chunk; the split
+// maxima and sums are the same for the D threads of a head and arrive as one
+// request per wave) and merges them in split order, rescaling the running
+// column when a later chunk raises the maximum.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineChunk = 16;
 template <typename T, int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a) {
-  extern __shared__ float wts[];   // [HPW][ns] weights, [HPW][ns] l_s, [HPW] 1 / L
   constexpr int HPW = kCombineThreads / D;   // heads per workgroup (D <= 256)
   static_assert(kCombineThreads == kSumThreads, "summary column runs summarize_blocks");
   const int bgi = blockIdx.y;
@@ -807,50 +809,39 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
       decode_nbranch(a, clamp_len(a.cache_len[b], a.max_len)) + a.count[bg];
   const int ns = (n_entries + kDecodeSplit - 1) / kDecodeSplit;
   const int G = a.G;
-  const int q0 = blockIdx.x * HPW;                 // first head of this workgroup
-  const int64_t stride = (int64_t)G * (D + 2);     // one split: G rows of [m, l, o(D)]
-  const float* part = a.part + bg * a.n_split * stride;
-  float* ls = wts + HPW * ns;
-  float* inv_l = ls + HPW * ns;
-  for (int e = threadIdx.x; e < HPW * ns; e += kCombineThreads) {
-    const int hq = e / ns, sp = e % ns;
-    if (q0 + hq < G) {
-      const float* pr = part + sp * stride + (q0 + hq) * (D + 2);
-      wts[e] = pr[0];
-      ls[e] = pr[1];
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < HPW && q0 + (int)threadIdx.x < G) {
-    float* w = wts + threadIdx.x * ns;
-    const float* l = ls + threadIdx.x * ns;
-    float M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, w[sp]);
-    float L = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float f = w[sp] == -INFINITY ? 0.f : fast_exp2(w[sp] - M);
-      w[sp] = f;
-      L += l[sp] * f;
-    }
-    inv_l[threadIdx.x] = 1.0f / L;
-  }
-  __syncthreads();
   const int hq = threadIdx.x / D, d = threadIdx.x % D;
-  const int qr = q0 + hq;
+  const int qr = blockIdx.x * HPW + hq;
   if (qr >= G) return;
-  const float* col = part + qr * (D + 2) + 2 + d;
-  const float* w = wts + hq * ns;
-  float O = 0.f;
-  int sp = 0;
-  for (; sp + 16 <= ns; sp += 16) {
-    float v[16];
+  const int stride = G * (D + 2);   // one split: G rows of [m, l, o(D)]
+  // the pair's ns splits; offsets past them read as zeros
+  const buf_rsrc rp = make_rsrc(a.part + bg * a.n_split * stride, (uint32_t)(ns * stride * 4));
+  const uint32_t row = (uint32_t)(qr * (D + 2)) * 4;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kCombineChunk) {
+    float mv[kCombineChunk], lv[kCombineChunk], ov[kCombineChunk];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = col[(sp + u) * stride];
+    for (int u = 0; u < kCombineChunk; ++u) {
+      const uint32_t off = (uint32_t)((s0 + u) * stride) * 4 + row;
+      mv[u] = __builtin_bit_cast(float, buf_load4(rp, off));
+      lv[u] = __builtin_bit_cast(float, buf_load4(rp, off + 4));
+      ov[u] = __builtin_bit_cast(float, buf_load4(rp, off + 8 + 4 * d));
+    }
+    float Mc = M;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) O += v[u] * w[sp + u];
+    for (int u = 0; u < kCombineChunk; ++u)
+      if (s0 + u < ns) Mc = fmaxf(Mc, mv[u]);
+    const float f0 = M == -INFINITY ? 0.f : fast_exp2(M - Mc);
+    L *= f0;
+    O *= f0;
+#pragma unroll
+    for (int u = 0; u < kCombineChunk; ++u) {
+      const float f = s0 + u >= ns || mv[u] == -INFINITY ? 0.f : fast_exp2(mv[u] - Mc);
+      L += lv[u] * f;
+      O += ov[u] * f;
+    }
+    M = Mc;
   }
-  for (; sp < ns; ++sp) O += col[sp * stride] * w[sp];
-  ((T*)a.o)[((int64_t)b * a.H + g * G + qr) * D + d] = from_f32<T>(O * inv_l[hq]);
+  ((T*)a.o)[((int64_t)b * a.H + g * G + qr) * D + d] = from_f32<T>(O / L);
 }
 
 // Workgroups of decode_attend_bf16_kernel<D> resident on the current device at
@@ -1018,9 +1009,8 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
   const int hpw = kCombineThreads / s.d;
   // one more column of workgroups writes the completed blocks' summaries
   dim3 g4((unsigned)((s.G + hpw - 1) / hpw + 1), nbg);
-  const size_t lds4 = sizeof(float) * (2 * L.n_split + 1) * hpw;
 #define DASH_DC(T, D) \
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), g4, dim3(kCombineThreads), lds4, st, a)
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), g4, dim3(kCombineThreads), 0, st, a)
   if (bf16) { if (s.d == 64) DASH_DC(__bf16, 64); else DASH_DC(__bf16, 128); }
   else { if (s.d == 64) DASH_DC(float, 64); else DASH_DC(float, 128); }
 #undef DASH_DC
