@@ -150,7 +150,7 @@ __device__ __forceinline__ void score_groups(const DecodeArgs& a, int64_t bg, in
       const uint32_t r = (uint32_t)(16 * (g0 + g_step * gi) + 4 * rq + m);
 #pragma unroll
       for (int u = 0; u < NU; ++u)
-        sv[gi][u] = __builtin_bit_cast(f32x4, buf_load16(rs, (r * D + 16 * u + 4 * ks) * 4));
+        sv[gi][u] = __builtin_bit_cast(f32x4, buf_load16_nt(rs, (r * D + 16 * u + 4 * ks) * 4));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -511,7 +511,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int sp = 0; sp < D / 32; ++sp)
-          kw[kt][sp] = buf_load16(rk, c0 + (16 * kt + l16) * (D * 2) + (32 * sp + 8 * lg) * 2);
+          kw[kt][sp] = buf_load16_nt(rk, c0 + (16 * kt + l16) * (D * 2) + (32 * sp + 8 * lg) * 2);
       // V rows this lane needs: k = 8 lg + e' <-> key 32 ks + 16 (e'/4) + 4 lg + e'%4,
       // DPL consecutive d starting at DPL * l16
       uint32_t vin[2][8][DPL / 2];
@@ -522,10 +522,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int bgi, int s,
           const uint32_t off =
               c0 + (32 * ks + 16 * (ep / 4) + 4 * lg + (ep % 4)) * (D * 2) + DPL * l16 * 2;
           if constexpr (DPL == 8) {
-            const u32x4 t = buf_load16(rv, off);
+            const u32x4 t = buf_load16_nt(rv, off);
             vin[ks][ep][0] = t.x; vin[ks][ep][1] = t.y; vin[ks][ep][2] = t.z; vin[ks][ep][3] = t.w;
           } else {
-            const u32x2 t = buf_load8(rv, off);
+            const u32x2 t = buf_load8_nt(rv, off);
             vin[ks][ep][0] = t.x; vin[ks][ep][1] = t.y;
           }
         }

@@ -86,6 +86,17 @@ __device__ __forceinline__ uint32_t buf_load4(buf_rsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// The same loads with the non-temporal cache policy, for data read once per
+// call (decode's K/V blocks and summaries): streamed reads reach ~10 % more
+// HBM bandwidth on this part than loads that allocate normally.
+constexpr int kCacheNT = 2;
+__device__ __forceinline__ u32x4 buf_load16_nt(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCacheNT);
+}
+__device__ __forceinline__ u32x2 buf_load8_nt(buf_rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCacheNT);
+}
+
 // a store at or beyond the resource's size is dropped
 __device__ __forceinline__ void buf_store4(float v, buf_rsrc r, uint32_t off, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, soff, 0);
