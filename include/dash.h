@@ -328,9 +328,12 @@ dash_status dash_decode_noalloc(const dash_params* p, const void* q, const void*
  *
  * dash_peak_stream: one grid-stride pass of 16-byte loads over `bytes` bytes
  * of src (a multiple of 16, both pointers 16-byte aligned).  mode 0 copies
- * them to dst (dst holds `bytes` bytes); mode 1 only reads them and stores
- * one 16-byte value per thread, so dst must hold 16 * dash_peak_stream_grid()
- * bytes.  dash_peak_mfma: every wave of a chip-filling grid runs `iters`
+ * them to dst (dst holds `bytes` bytes); modes 1 and 2 only read them and
+ * store one 16-byte value per thread, so dst must hold
+ * 16 * dash_peak_stream_grid() bytes.  Mode 1 loads allocate in the caches
+ * (a read of more than their size empties them); mode 2 loads use the
+ * non-temporal policy of the decode step's K/V loads.  Other modes return
+ * DASH_ERR_INVALID_ARG.  dash_peak_mfma: every wave of a chip-filling grid runs `iters`
  * rounds of eight independent v_mfma_f32_32x32x16_bf16 on register operands
  * (no memory traffic in the loop); *flops receives the flop count of the
  * launch (host pointer), sink (device) one float per wave, sized by

@@ -437,7 +437,8 @@ def dash_peak_stream_grid() -> int:
 
 def dash_peak_stream(src, dst, nbytes, mode, stream=None):
     """mode 0: copy nbytes of src into dst; mode 1: read nbytes of src only
-    (dst holds 16 bytes per launched thread)."""
+    (loads that allocate in the caches); mode 2: the same read with
+    non-temporal loads (dst holds 16 bytes per launched thread in modes 1, 2)."""
     need = nbytes if mode == 0 else 16 * dash_peak_stream_grid()
     _check("dash_peak_stream", _lib.dash_peak_stream(
         _dev(src, "src", nbytes // src.element_size()),

@@ -4,9 +4,11 @@
 // bf16) and what a plain kernel reaches on the same part in the same run.
 //
 //   peak_stream_kernel  grid-stride 16-byte loads over a buffer; mode 0 also
-//                       stores every vector to a second buffer (a copy), mode
-//                       1 only folds the loaded words into one value per
-//                       thread (a read stream, the access mix of decode)
+//                       stores every vector to a second buffer (a copy), modes
+//                       1 and 2 only fold the loaded words into one value per
+//                       thread (a read stream; mode 2 with the non-temporal
+//                       cache policy of decode's K/V loads, mode 1 with loads
+//                       that allocate in the caches, which evicts them)
 //   peak_mfma_kernel    back-to-back v_mfma_f32_32x32x16_bf16 on eight
 //                       independent accumulators held in registers; no memory
 //                       traffic inside the loop
@@ -38,11 +40,17 @@ __global__ __launch_bounds__(kPeakThreads) void peak_stream_kernel(const u32x4* 
     for (; i < n16; i += stride) dst[i] = src[i];
   } else {
     // eight loads in flight per thread before any is consumed
+    const bool nt = mode == 2;
     u32x4 acc = {0u, 0u, 0u, 0u};
     for (; i + 7 * stride < n16; i += 8 * stride) {
       u32x4 r[8];
+      if (nt) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) r[m] = src[i + m * stride];
+        for (int m = 0; m < 8; ++m) r[m] = __builtin_nontemporal_load(src + i + m * stride);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) r[m] = src[i + m * stride];
+      }
 #pragma unroll
       for (int m = 0; m < 8; ++m) acc ^= r[m];
     }
@@ -98,7 +106,7 @@ dash_status dash_peak_stream_grid(int64_t* threads) {
 
 dash_status dash_peak_stream(const void* src, void* dst, int64_t bytes, int32_t mode,
                              void* stream) {
-  if (!src || !dst || bytes < 16 || bytes % 16 != 0 || (mode != 0 && mode != 1))
+  if (!src || !dst || bytes < 16 || bytes % 16 != 0 || mode < 0 || mode > 2)
     return DASH_ERR_INVALID_ARG;
   if (((uintptr_t)src % 16) != 0 || ((uintptr_t)dst % 16) != 0) return DASH_ERR_INVALID_ARG;
   const int cus = dash::device_cus();

@@ -166,7 +166,8 @@ void bad_calls() {
          "allocation-free decode above its scratch");
 
   expect(dash_peak_stream(FAKE, FAKE, 15, 0, nullptr) == DASH_ERR_INVALID_ARG, "stream size");
-  expect(dash_peak_stream(FAKE, FAKE, 1024, 2, nullptr) == DASH_ERR_INVALID_ARG, "stream mode");
+  expect(dash_peak_stream(FAKE, FAKE, 1024, 3, nullptr) == DASH_ERR_INVALID_ARG, "stream mode");
+  expect(dash_peak_stream(FAKE, FAKE, 1024, -1, nullptr) == DASH_ERR_INVALID_ARG, "stream mode");
   expect(dash_peak_stream_grid(nullptr) == DASH_ERR_INVALID_ARG, "stream grid out");
   double flops = 0.0;
   expect(dash_peak_mfma(0, FF, &flops, nullptr) == DASH_ERR_INVALID_ARG, "mfma iterations");
