@@ -382,6 +382,8 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
       m_ref = m_new;
     }
     const float off = m_ref == -INFINITY ? 0.f : bias2 - m_ref;
+    // the row sum adds the bf16 weights the P V product uses, two per
+    // v_dot2c_f32_bf16 against (1, 1)
     float psum = 0.f;
     bf16x8 pf[4];
 #pragma unroll
@@ -389,12 +391,10 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
       const int kt = ks / 2, i0 = 8 * (ks % 2);
       float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = fast_exp2(fmaf(st[kt][i0 + e], a.scale_log2, off));
-        psum += pv[e];
-      }
+      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(st[kt][i0 + e], a.scale_log2, off));
       const u32x4 pw = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
                         pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
+      psum = sum2_bf16(pw.x, sum2_bf16(pw.y, sum2_bf16(pw.z, sum2_bf16(pw.w, psum))));
       pf[ks] = as_bf16x8(pw);
     }
     psum = xor_reduce<32>(psum, DppAdd{});

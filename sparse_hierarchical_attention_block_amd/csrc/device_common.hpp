@@ -66,6 +66,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
 // results below 2^-126 flush to zero, which softmax weights can afford.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// c + the two bf16 halves of w (products with 1 are exact): v_dot2c_f32_bf16
+__device__ __forceinline__ float sum2_bf16(uint32_t w, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, c, false);
+}
+
 // ---- buffer loads with hardware range checking -----------------------------
 // A raw buffer resource covers `bytes` bytes from `base`; a load whose byte
 // offset lies at or beyond that size returns zeros and touches no memory,
