@@ -335,12 +335,16 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
     return;
   }
   if constexpr (VPL > 0) {
+    // every load issued before any is used: a buffer resource over the row's
+    // ncand scores returns zeros past them, masked to -inf after the loads
+    const buf_rsrc rx = make_rsrc(xr, (uint32_t)ncand * 4);
     float xv[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int j = lane + kWave * i;
-      xv[i] = j < ncand ? xr[j] : -INFINITY;
-    }
+    for (int i = 0; i < VPL; ++i)
+      xv[i] = __builtin_bit_cast(float, buf_load4(rx, (uint32_t)(lane + kWave * i) * 4));
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (lane + kWave * i >= ncand) xv[i] = -INFINITY;
     route_row_reg<VPL, MODE>(a, row, ncand, xv, Ps + hh * a.nb);
   } else {
     const float tau = entmax_tau([&](int j) { return xr[j]; }, ncand, lane, kWave, a.mode, a.e);
