@@ -66,6 +66,9 @@ PREFILL_CASES = {
                                                            n_kv_heads=2, alpha=1.25),
     "long_rows_alpha2_gqa4": W.get("prefill_8k").replace(seq_len=8500, n_heads=4, n_kv_heads=1,
                                                          alpha=2.0),
+    # general alpha (Newton steps with log / exp) on the long-row kernel with one part per tile
+    "long_rows_alpha175_gqa2": W.get("prefill_8k").replace(seq_len=9000, n_heads=4, n_kv_heads=2,
+                                                           alpha=1.75),
 }
 
 
