@@ -74,6 +74,27 @@ __device__ __forceinline__ void compact_union(const RouteArgs& a, const int* ufl
   if (lane == 0) a.sel_count[tile] = base;
 }
 
+// Two summary values split into three bf16 parts each, packed in pairs
+// (value 0 in the low half): hi is x with the low 16 bits of its pattern
+// cleared, mid the same of x - hi (exact: hi holds x's leading bits), lo the
+// rest (at most 8 significant bits, so exactly a bf16), hence hi + mid + lo
+// = x exactly; the pairs are packed by byte permutes of the upper halves.
+__device__ __forceinline__ void split3_bf16(float x0, float x1, uint32_t& hw, uint32_t& mw,
+                                            uint32_t& lw) {
+  constexpr uint32_t kUpper = 0x07060302u;   // upper halves of (src1, src0) -> (lo, hi)
+  constexpr uint32_t kMask = 0xffff0000u;
+  const uint32_t b0 = __builtin_bit_cast(uint32_t, x0), b1 = __builtin_bit_cast(uint32_t, x1);
+  hw = __builtin_amdgcn_perm(b1, b0, kUpper);
+  const float r0 = x0 - __builtin_bit_cast(float, b0 & kMask);
+  const float r1 = x1 - __builtin_bit_cast(float, b1 & kMask);
+  const uint32_t c0 = __builtin_bit_cast(uint32_t, r0), c1 = __builtin_bit_cast(uint32_t, r1);
+  mw = __builtin_amdgcn_perm(c1, c0, kUpper);
+  const float l0 = r0 - __builtin_bit_cast(float, c0 & kMask);
+  const float l1 = r1 - __builtin_bit_cast(float, c1 & kMask);
+  lw = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, l1), __builtin_bit_cast(uint32_t, l0),
+                             kUpper);
+}
+
 // GQA sum of a row's probabilities and the Stage 2 bias, for rows whose
 // scores sit in MFMA 16x16 accumulators (lane l16 + 16 lg of a wave holds
 // row l16's candidates 16 ct + 4 lg + i, i < 4, in slot 4 ct + i).  The sum over

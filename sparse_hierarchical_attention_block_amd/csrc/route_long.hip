@@ -106,24 +106,11 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
       const int e = threadIdx.x + u * kLongThreads;
       const int cand = e / (D / 4), c4 = e % (D / 4);
       const float xs[4] = {pre[u].x, pre[u].y, pre[u].z, pre[u].w};
+      // scale folded into the summaries, then split exactly into hi + mid + lo
       uint32_t hw[2], mw[2], lw[2];
 #pragma unroll
-      for (int p2 = 0; p2 < 2; ++p2) {
-        float hv[2], mv[2], lv[2];
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const float x = xs[2 * p2 + q2] * a.scale;   // scale folded into the summaries
-          const float hh = (float)(__bf16)x;
-          const float r1 = x - hh;
-          const float mm = (float)(__bf16)r1;
-          hv[q2] = hh;
-          mv[q2] = mm;
-          lv[q2] = r1 - mm;
-        }
-        hw[p2] = pack_bf16(hv[0], hv[1]);
-        mw[p2] = pack_bf16(mv[0], mv[1]);
-        lw[p2] = pack_bf16(lv[0], lv[1]);
-      }
+      for (int p2 = 0; p2 < 2; ++p2)
+        split3_bf16(xs[2 * p2] * a.scale, xs[2 * p2 + 1] * a.scale, hw[p2], mw[p2], lw[p2]);
       const int off = cand * SP + 4 * c4;
       *(u32x2*)(planes + off) = (u32x2){hw[0], hw[1]};
       *(u32x2*)(planes + kLongChunk * SP + off) = (u32x2){mw[0], mw[1]};
