@@ -78,7 +78,8 @@ void prefill_sizes(const Shape& s, int64_t n, dash_route_sizes* r) {
   r->tile_bits = r->sel_count * ((r->nb + 31) / 32);
 }
 
-// LDS needed by the prefill routing kernel (must match route.hip)
+// LDS needed by the pass-based prefill routing kernel, the one with the largest
+// buffer (must match launch_route_prefill in route.hip)
 bool route_lds_ok(const Shape& s, int64_t n) {
   const int64_t n_qt = (n + kQT - 1) / kQT;
   const int64_t t_max = ((n_qt - 1) * kQT) / s.bs;
