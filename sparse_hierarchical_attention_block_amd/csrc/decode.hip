@@ -326,7 +326,9 @@ __global__ __launch_bounds__(512) void decode_route_kernel(DecodeArgs a) {
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int64_t len = clamp_len(a.cache_len[b], a.max_len);
   const int ncand = decode_ncand(a, len);
-  const int lane = threadIdx.x % kWave, hh = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  // the wave index as a scalar, so that the row's buffer resource is too
+  const int hh = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t row = (int64_t)b * a.H + g * a.G + hh;
   const float* xr = a.x + row * a.nb;
   if (ncand == 0) {
