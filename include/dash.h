@@ -278,7 +278,9 @@ dash_status dash_prefill_backward(const dash_params* p, const void* q, const voi
  *   ws              >= dash_decode_workspace_bytes(p, max_len) bytes
  * Values of cache_len outside [1, max_len] are clamped into that range.
  * DASH_ERR_UNSUPPORTED when (max_len + 64) * d * element size >= 2^31, when
- * B * Hkv > 65535, or for bf16 when B * Hkv > 8192. */
+ * (H / Hkv) * ceil(max_len / block_size) * 4 bytes (one routing
+ * workgroup's LDS) exceed 160 KiB, when B * Hkv > 65535, or for bf16 when
+ * B * Hkv > 8192. */
 dash_status dash_decode(const dash_params* p, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* cache_len, int64_t max_len,
                         const float* w_s, const float* q_bar, float* summ, int64_t summ_blocks,

@@ -115,9 +115,11 @@ __device__ __forceinline__ int decode_nbranch(const DecodeArgs& a, int64_t len) 
 // (B operand from the same lane) over that d slice; two row rotations add
 // the four ks partial sums, after which lane (rq, 0, m) holds x of rows
 // 4 rq + i, head 4 hs + m in element i.  The wave takes groups g_first,
-// g_first + g_step, ... < g_end, NG of them in flight; x of row j, head h
-// goes to out[h * pitch + j] (rows < ncand only).
-template <typename T, int D, int NG>
+// g_first + g_step, ... < g_end in batches of NG; with PIPE the next batch's
+// loads are issued before the current batch is multiplied, so a wave's
+// arithmetic overlaps its own loads instead of waiting for all of them.  x of
+// row j, head h goes to out[h * pitch + j] (rows < ncand only).
+template <typename T, int D, int NG, bool PIPE = false>
 __device__ __forceinline__ void score_groups(const DecodeArgs& a, int64_t bg, int64_t row0,
                                              int ncand, int g_first, int g_step, int g_end,
                                              float* out, int64_t pitch) {
@@ -142,9 +144,8 @@ __device__ __forceinline__ void score_groups(const DecodeArgs& a, int64_t bg, in
       }
   }
   const buf_rsrc rs = make_rsrc(a.summ + bg * a.summ_blocks * D, (uint32_t)(ncand * D * 4));
-  for (int g0 = g_first; g0 < g_end; g0 += g_step * NG) {
-    // rows past ncand read as zeros; their scores are never stored
-    f32x4 sv[NG][NU];
+  // rows past ncand read as zeros; their scores are never stored
+  auto load_batch = [&](int g0, f32x4 (&sv)[NG][NU]) {
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       const uint32_t r = (uint32_t)(16 * (g0 + g_step * gi) + 4 * rq + m);
@@ -152,7 +153,8 @@ __device__ __forceinline__ void score_groups(const DecodeArgs& a, int64_t bg, in
       for (int u = 0; u < NU; ++u)
         sv[gi][u] = __builtin_bit_cast(f32x4, buf_load16_nt(rs, (r * D + 16 * u + 4 * ks) * 4));
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mul_batch = [&](int g0, const f32x4 (&sv)[NG][NU]) {
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) {
       if (hs * 4 >= G) break;
@@ -193,13 +195,41 @@ __device__ __forceinline__ void score_groups(const DecodeArgs& a, int64_t bg, in
         }
       }
     }
+  };
+  if constexpr (!PIPE) {
+    for (int g0 = g_first; g0 < g_end; g0 += g_step * NG) {
+      f32x4 sv[NG][NU];
+      load_batch(g0, sv);
+      __builtin_amdgcn_sched_barrier(0);
+      mul_batch(g0, sv);
+    }
+  } else {
+    f32x4 cur[NG][NU];
+    if (g_first < g_end) load_batch(g_first, cur);
+    for (int g0 = g_first; g0 < g_end; g0 += g_step * NG) {
+      const int g1 = g0 + g_step * NG;
+      f32x4 nxt[NG][NU];
+      if (g1 < g_end) load_batch(g1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      mul_batch(g0, cur);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g1 < g_end) {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+          for (int u = 0; u < NU; ++u) cur[gi][u] = nxt[gi][u];
+      }
+    }
   }
 }
 
-// Score kernel for the two-kernel path: grid (ceil(ncand_max / 256), B Hkv),
-// 4 waves x 4 groups = 256 rows per workgroup.
+// Score kernel for the two-kernel path: grid (ceil(ncand_max / kScoreRows), B Hkv),
+// 4 waves x 8 groups = 512 rows per workgroup, in batches of 2 groups per wave.
+// (One workgroup per CU at decode_128k: while a wave multiplies one batch,
+// the next batch's loads, 16 KB per wave and 64 KB per CU, are in flight.)
 constexpr int kScoreThreads = 256;
-constexpr int kScoreGroups = 4;
+constexpr int kScoreGroups = 8;
+constexpr int kScoreNG = 2;   // groups per batch, pipelined
 constexpr int kScoreRows = kScoreThreads / kWave * kScoreGroups * 16;
 template <typename T, int D>
 __global__ __launch_bounds__(kScoreThreads) void decode_scores_kernel(DecodeArgs a) {
@@ -212,8 +242,8 @@ __global__ __launch_bounds__(kScoreThreads) void decode_scores_kernel(DecodeArgs
   const int ge = min((ncand + 15) >> 4, gb + kScoreRows / 16);
   if (gb >= ge) return;
   const int64_t row0 = (int64_t)b * a.H + g * a.G;
-  score_groups<T, D, kScoreGroups>(a, bg, row0, ncand, gb + wave, kScoreThreads / kWave, ge,
-                                   a.x + row0 * a.nb, a.nb);
+  score_groups<T, D, kScoreNG, true>(a, bg, row0, ncand, gb + wave, kScoreThreads / kWave, ge,
+                                     a.x + row0 * a.nb, a.nb);
 }
 
 // ---- 2. threshold, GQA average, union, compaction ------------------------------------------
