@@ -61,6 +61,9 @@ def run_prefill(w, inp, bits=True):
     dash.dash_summarize(p, k, N, 0, nbf, ws, summ, summ_blocks, q_bar=qbar_dev(inp))
     sizes = dash.dash_route_sizes_prefill(p, N)
     rb = dash.RouteBuffers(sizes, dev(), bits=bits, tile_bits=True)
+    # NaN in every bias entry Stage 1 does not write: a listed row it left
+    # out, or an entry Stage 2 reads without its being written, shows
+    rb.sel_logp.fill_(float("nan"))
     dash.dash_route(p, q, N, summ, summ_blocks, rb)
     o = torch.empty_like(q)
     dash.dash_attend(p, q, k, v, N, rb, o)

@@ -29,6 +29,9 @@ def _prefill_full(w):
     summ = torch.zeros(B * Hkv * nb * d, dtype=torch.float32, device=dev())
     o = torch.empty_like(q)
     ws = dash.workspace(dash.dash_prefill_workspace_bytes(p, N), dev())
+    # all bits set: the bias rows Stage 1 does not write read as NaN, so an
+    # output that used one would show it
+    ws.fill_(255)
     dash.dash_prefill(p, q, k, v, N, ws_mat, summ, nb, o, ws)
     # stage-wise run with per-head supports (same kernels, same launch shapes)
     sizes = dash.dash_route_sizes_prefill(p, N)
