@@ -194,7 +194,12 @@ template <int D, int NT>
 __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
   using Stage = ChunkStage<D, NT>;
   constexpr int KP = Stage::KP, VP = Stage::VP;
-  constexpr int NBUF = 3;
+  // LDS ring of NBUF chunk buffers: chunk c + 2 is stored while chunk c is
+  // computed, so a workgroup barrier is needed once every NBUF - 2 chunks.
+  // d = 128: four buffers (133 KB; one workgroup per CU with three as well),
+  // a barrier every second chunk; d = 64: three, which keeps more
+  // workgroups resident.
+  constexpr int NBUF = D == 128 ? 4 : 3;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][kChunk * KP];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[NBUF][D * VP];
   __shared__ __attribute__((aligned(16))) float Bs[NBUF][kQTa];
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f;
 
-  // Chunk c sits in LDS buffer c % 3; chunk c+1 is already staged and chunk
+  // Chunk c sits in LDS buffer c % NBUF; chunk c+1 is already staged and chunk
   // c+2's K/V/bias are in flight from HBM into registers, preceded in the
   // load queue by the block id of chunk c+3.
   // Prologue: the block ids of chunks 0..3 arrive with one load (slots of
@@ -406,9 +411,10 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma32(as_bf16x8(vw[ks][dt]), pf[ks], acc[dt]);
 
-    // chunk c+2 into the buffer chunk c-1 used (every wave is past it)
+    // chunk c+2 into the buffer chunk c+2-NBUF used (every wave is past it:
+    // the last barrier came after that chunk)
     if (c + 2 < n_chunks) stage.store(Ks[bnx2], Vt[bnx2], Bs[bnx2]);
-    __syncthreads();
+    if (c % (NBUF - 2) == NBUF - 3) __syncthreads();
     const int c3 = c + 3;
     if (c3 < n_chunks) {
       const int j = __builtin_amdgcn_readfirstlane(jv);
