@@ -406,10 +406,15 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     l_run += psum;
 
     // ---- O^T += V^T P^T : 4 k-steps of 16 keys ----
+    // issued at raised wave priority (the compiler then places the chunk's
+    // exponentials before them): the SIMD's other wave, in its softmax,
+    // yields the issue slots to these MFMAs (8K attend -1.7 %, 64K -0.7 %)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma32(as_bf16x8(vw[ks][dt]), pf[ks], acc[dt]);
+    __builtin_amdgcn_s_setprio(0);
 
     // chunk c+2 into the buffer chunk c+2-NBUF used (every wave is past it:
     // the last barrier came after that chunk)
