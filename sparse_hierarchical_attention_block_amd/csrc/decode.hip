@@ -119,10 +119,19 @@ __device__ __forceinline__ int decode_nbranch(const DecodeArgs& a, int64_t len) 
 // loads are issued before the current batch is multiplied, so a wave's
 // arithmetic overlaps its own loads instead of waiting for all of them.  x of
 // row j, head h goes to out[h * pitch + j] (rows < ncand only).
-template <typename T, int D, int NG, bool PIPE = false>
+// With XL (the pipelined scan of decode_scores_kernel) the loads are laid out
+// for the memory system instead -- lane L reads row 8 sb + L / 8 of a group,
+// floats 32 u + 4 (L % 8) + [0, 4), so one instruction covers 8 rows x 128
+// contiguous bytes (the MFMA layout puts four consecutive lanes on four
+// rows, which reads measurably slower) -- and each wave moves its batch
+// through a private LDS region xl (rows kXlPitch floats apart, a pitch at
+// which both the row-wise stores and the MFMA-layout reads are free of bank
+// conflicts) into the MFMA layout.
+constexpr int kXlPitch = 144;
+template <typename T, int D, int NG, bool PIPE = false, bool XL = false>
 __device__ __forceinline__ void score_groups(const DecodeArgs& a, int64_t bg, int64_t row0,
                                              int ncand, int g_first, int g_step, int g_end,
-                                             float* out, int64_t pitch) {
+                                             float* out, int64_t pitch, float* xl = nullptr) {
   constexpr int NU = D / 16;
   constexpr bool kBf16 = sizeof(T) == 2;
   const int lane = threadIdx.x % kWave;
@@ -148,13 +157,45 @@ __device__ __forceinline__ void score_groups(const DecodeArgs& a, int64_t bg, in
   auto load_batch = [&](int g0, f32x4 (&sv)[NG][NU]) {
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      const uint32_t r = (uint32_t)(16 * (g0 + g_step * gi) + 4 * rq + m);
+      if constexpr (XL) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u)
-        sv[gi][u] = __builtin_bit_cast(f32x4, buf_load16_nt(rs, (r * D + 16 * u + 4 * ks) * 4));
+        for (int u = 0; u < NU; ++u) {
+          const uint32_t r = (uint32_t)(16 * (g0 + g_step * gi) + 8 * (u & 1) + (lane >> 3));
+          sv[gi][u] = __builtin_bit_cast(
+              f32x4, buf_load16_nt(rs, (r * D + 32 * (u >> 1) + 4 * (lane & 7)) * 4));
+        }
+      } else {
+        const uint32_t r = (uint32_t)(16 * (g0 + g_step * gi) + 4 * rq + m);
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          sv[gi][u] = __builtin_bit_cast(f32x4, buf_load16_nt(rs, (r * D + 16 * u + 4 * ks) * 4));
+      }
     }
   };
-  auto mul_batch = [&](int g0, const f32x4 (&sv)[NG][NU]) {
+  auto mul_batch = [&](int g0, const f32x4 (&lv)[NG][NU]) {
+    f32x4 sv[NG][NU];
+    if constexpr (XL) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          *(f32x4*)(xl + (16 * gi + 8 * (u & 1) + (lane >> 3)) * kXlPitch + 32 * (u >> 1) +
+                    4 * (lane & 7)) = lv[gi][u];
+      // the rows are read back by other lanes of the same wave
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          sv[gi][u] = *(const f32x4*)(xl + (16 * gi + 4 * rq + m) * kXlPitch + 16 * u + 4 * ks);
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int u = 0; u < NU; ++u) sv[gi][u] = lv[gi][u];
+    }
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) {
       if (hs * 4 >= G) break;
@@ -242,8 +283,9 @@ __global__ __launch_bounds__(kScoreThreads) void decode_scores_kernel(DecodeArgs
   const int ge = min((ncand + 15) >> 4, gb + kScoreRows / 16);
   if (gb >= ge) return;
   const int64_t row0 = (int64_t)b * a.H + g * a.G;
-  score_groups<T, D, kScoreNG, true>(a, bg, row0, ncand, gb + wave, kScoreThreads / kWave, ge,
-                                     a.x + row0 * a.nb, a.nb);
+  __shared__ __attribute__((aligned(16))) float xl[kScoreThreads / kWave][kScoreNG * 16 * kXlPitch];
+  score_groups<T, D, kScoreNG, true, true>(a, bg, row0, ncand, gb + wave, kScoreThreads / kWave,
+                                           ge, a.x + row0 * a.nb, a.nb, xl[wave]);
 }
 
 // ---- 2. threshold, GQA average, union, compaction ------------------------------------------
