@@ -120,13 +120,17 @@ struct ChunkStage {
 
   // key0: first key of the chunk; block: its block id, -1 for an own-block
   // chunk.  rk / rv cover one sequence's keys / values, rb the tile's bias rows.
+  // (32-bit byte offsets: one sequence's keys span less than 2 GiB; the chunk
+  // base plus a per-thread part, with the per-key steps of V as instruction
+  // offsets)
   __device__ __forceinline__ void load(buf_rsrc rk, buf_rsrc rv, buf_rsrc rb, int64_t key0,
                                        int block) {
+    const uint32_t cb = (uint32_t)key0 * (uint32_t)(D * 2);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int e = threadIdx.x + i * NT;
       const int key = e / (D / 8), seg = e % (D / 8);
-      const uint32_t off = (uint32_t)((key0 + key) * (D * 2) + seg * 16);
+      const uint32_t off = cb + (uint32_t)(key * (D * 2) + seg * 16);
       if (KTOT % NT == 0 || e < KTOT) kr[i] = buf_load16(rk, off);
     }
     // V^T unit (segment sg, d pair dp): the keys 16 (sg / 2) + 4 (sg % 2) +
@@ -137,11 +141,12 @@ struct ChunkStage {
       const int e = threadIdx.x + i * NT;
       const int dp = e % (D / 2), sg = e / (D / 2);
       const int kbase = 16 * (sg >> 1) + 4 * (sg & 1);
+      const uint32_t vb = cb + (uint32_t)(kbase * (D * 2) + dp * 4);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t off = (uint32_t)((key0 + kbase + 8 * a + j) * (D * 2) + dp * 4);
+          const uint32_t off = vb + (uint32_t)((8 * a + j) * (D * 2));
           if (VTOT % NT == 0 || e < VTOT) vr[i][4 * a + j] = buf_load4(rv, off);
         }
     }

@@ -46,11 +46,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // pack the low halves / high halves of two words: (a.lo, b.lo) and (a.hi, b.hi)
+// (one v_perm_b32 byte select each: bytes 0-3 of the pair are a, 4-7 are b)
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 // two floats -> packed bf16 pair (round to nearest even), x in the low half
