@@ -123,7 +123,7 @@ struct ChunkStage {
   // (32-bit byte offsets: one sequence's keys span less than 2 GiB; the chunk
   // base plus a per-thread part, with the per-key steps of V as instruction
   // offsets)
-  __device__ __forceinline__ void load(buf_rsrc rk, buf_rsrc rv, buf_rsrc rb, int64_t key0,
+  __device__ __forceinline__ void load(buf_rsrc rk, buf_rsrc rv, buf_rsrc rb, int key0,
                                        int block) {
     const uint32_t cb = (uint32_t)key0 * (uint32_t)(D * 2);
 #pragma unroll
@@ -267,8 +267,10 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     qf[s] = as_bf16x8(w);
   }
 
-  const int cpb_log = a.bs == 2 * kChunk ? 1 : 0;   // chunks per block: 1 or 2
-  const int64_t own_c0 = branch_block0(p_begin, a.bs, a.window) << cpb_log;
+  // chunks per block: 1 or 2 (a scalar: the chunk walk's arithmetic stays in
+  // SGPRs, in 32 bits -- one sequence's keys span less than 2 GiB)
+  const int cpb_log = __builtin_amdgcn_readfirstlane(a.bs == 2 * kChunk ? 1 : 0);
+  const int own_c0 = (int)(branch_block0(p_begin, a.bs, a.window) << cpb_log);
   const int n_own = (int)(qt - own_c0 + 1);
   const int count = a.sel_count[tile];
   const int n_chunks = n_own + (count << cpb_log);
@@ -279,9 +281,9 @@ __global__ __launch_bounds__(NT) void attend_bf16_kernel(AttendArgs a) {
     return buf_load4(ri, (uint32_t)(((c - n_own) >> cpb_log) * 4));
   };
   // chunk c (block id j when selected) -> first key, bias block (-1: own block)
-  auto key0_of = [&](int c, int j) -> int64_t {
+  auto key0_of = [&](int c, int j) -> int {
     return c < n_own ? (own_c0 + c) * kChunk
-                     : ((int64_t)j << cpb_log) * kChunk + ((c - n_own) & cpb_log) * kChunk;
+                     : (j << cpb_log) * kChunk + ((c - n_own) & cpb_log) * kChunk;
   };
 
   f32x16 acc[D / 32];
