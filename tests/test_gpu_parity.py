@@ -52,6 +52,11 @@ PREFILL_CASES = {
     "window_covers_all_bf16": tiny(seq_len=700, dtype="bf16", gamma=8.0, window=11),
     # 64 < candidates <= 128 in the last tiles, full oracle parity
     "cand74_gqa4": W.get("prefill_8k").replace(seq_len=4800, n_heads=8, n_kv_heads=2),
+    # one query head per KV head at d = 128 (the two-wave attend workgroup and its
+    # four-buffer LDS ring), ragged, at both block sizes
+    "mha_d128_bs64_ragged": W.get("prefill_8k").replace(seq_len=1500, n_heads=2, n_kv_heads=2),
+    "mha_d128_bs128_ragged": W.get("prefill_64k").replace(seq_len=1700, n_heads=2, n_kv_heads=2,
+                                                          gamma=2.0),
     # more than 128 candidates in the last tiles (bf16, G >= 2: the long-row
     # routing kernel; G / 2 workgroups per tile whose unions are merged),
     # ragged tails
