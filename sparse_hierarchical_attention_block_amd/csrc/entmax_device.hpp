@@ -174,13 +174,25 @@ struct Stride16Reduce {   // lanes l, l^16, l^32, l^48 (one MFMA 16x16 C-fragmen
   }
 };
 
+// Slot i of a row held in registers: a float array, or MFMA accumulator
+// fragments of four (slot i is element i % 4 of fragment i / 4), read in
+// place so that no copy of the accumulators is made.
+template <int N>
+__device__ __forceinline__ float xget(const float (&x)[N], int i) { return x[i]; }
+template <int N>
+__device__ __forceinline__ float xget(const f32x4 (&x)[N], int i) { return x[i >> 2][i & 3]; }
+template <int N>
+__device__ __forceinline__ void xset(float (&x)[N], int i, float v) { x[i] = v; }
+template <int N>
+__device__ __forceinline__ void xset(f32x4 (&x)[N], int i, float v) { x[i >> 2][i & 3] = v; }
+
 // Support statistics of the register-held values at tau: count, s1, s2 and
 // the smallest positive y = x - tau (MODE as in entmax_tau).  Only the first
 // nact4 groups of four values are visited (nact4 is uniform across the wave,
 // so the skipped groups cost no VALU, and the loop leaves at the first
 // inactive group).
-template <int VPL, int mode>
-__device__ __forceinline__ void entmax_accumulate(const float (&xv)[VPL], float tau, float e,
+template <int VPL, int mode, typename XV>
+__device__ __forceinline__ void entmax_accumulate(const XV& xv, float tau, float e,
                                                   int nact4, int& kc, float& s1, float& s2,
                                                   float& ymin) {
   kc = 0;
@@ -192,7 +204,7 @@ __device__ __forceinline__ void entmax_accumulate(const float (&xv)[VPL], float 
     if (g4 < nact4) {   // the active groups come first
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const float y = xv[4 * g4 + ii] - tau;
+        const float y = xget(xv, 4 * g4 + ii) - tau;
         const bool in = y > 0.f;
         const float yp = fmaxf(y, 0.f);
         kc += in ? 1 : 0;
@@ -241,8 +253,8 @@ __device__ __forceinline__ bool entmax_update(float k, float s1, float s2, float
 // starts at max x - 1 and only grows, y <= 1, so [x - tau]_+ is the clamp of
 // x - tau to [0, 1], one subtraction with the clamp bit: three VALU
 // instructions per value against seven and a half for the full statistics.
-template <int VPL>
-__device__ __forceinline__ void entmax_sums15(const float (&xv)[VPL], float tau, int nact4,
+template <int VPL, typename XV>
+__device__ __forceinline__ void entmax_sums15(const XV& xv, float tau, int nact4,
                                               float& s1, float& s2) {
   s1 = 0.f;
   s2 = 0.f;
@@ -251,7 +263,7 @@ __device__ __forceinline__ void entmax_sums15(const float (&xv)[VPL], float tau,
     if (g4 < nact4) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const float yp = fminf(fmaxf(xv[4 * g4 + ii] - tau, 0.f), 1.f);
+        const float yp = fminf(fmaxf(xget(xv, 4 * g4 + ii) - tau, 0.f), 1.f);
         s1 += yp;
         s2 = fmaf(yp, yp, s2);
       }
@@ -267,14 +279,14 @@ constexpr float kEntmaxSumsStop = 1e-2f;
 // that lane set.  At alpha = 1.5 the first Newton steps use only the two sums;
 // once a step falls below kEntmaxSumsStop the passes gather the full support
 // statistics, so that the closed-form solve can end the search as before.
-template <int VPL, int mode, typename Red>
-__device__ __forceinline__ float entmax_tau_reg(const float (&xv)[VPL], Red red, float e, int nact4 = VPL / 4) {
+template <int VPL, int mode, typename XV, typename Red>
+__device__ __forceinline__ float entmax_tau_reg(const XV& xv, Red red, float e, int nact4 = VPL / 4) {
   float xmax = -INFINITY;
   static_for<0, VPL / 4>([&](auto G4) {
     constexpr int g4 = decltype(G4)::value;
     if (g4 < nact4)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) xmax = fmaxf(xmax, xv[4 * g4 + ii]);
+      for (int ii = 0; ii < 4; ++ii) xmax = fmaxf(xmax, xget(xv, 4 * g4 + ii));
   });
   xmax = red.max(xmax);
   float tau = xmax - 1.0f;

@@ -101,12 +101,13 @@ __device__ __forceinline__ void split3_bf16(float x0, float x1, uint32_t& hw, ui
 // the G rows of a position is a reduce-scatter over the lanes whose l16
 // differ in the bits of h = l16 % G: after it, the lane of head h holds the
 // sum for the slots s with s % G == h (slot s = 4 ct + i is candidate
-// 16 ct + 4 lg + i), which it writes.  Slots of candidate tiles at or past
+// 16 ct + 4 lg + i), which it writes.  xv: the row's slots, a float array or
+// the MFMA accumulator fragments themselves (xget / xset).  Slots of candidate tiles at or past
 // CT are never written (their j is at least t).
-template <int G, int MAXCT>
-__device__ __forceinline__ void route_rows_bias(const RouteArgs& a, float (&xv)[4 * MAXCT],
-                                                int CT, int t, int lg, int h, int64_t pos,
-                                                int64_t p_begin, int64_t tile, int* lflag) {
+template <int G, int MAXCT, typename XV>
+__device__ __forceinline__ void route_rows_bias(const RouteArgs& a, XV& xv, int CT, int t, int lg,
+                                                int h, int64_t pos, int64_t p_begin,
+                                                int64_t tile, int* lflag) {
   static_for<0, 3>([&](auto BB) {
     constexpr int bit = 1 << decltype(BB)::value;
     if constexpr (bit < G) {
@@ -114,9 +115,9 @@ __device__ __forceinline__ void route_rows_bias(const RouteArgs& a, float (&xv)[
       static_for<0, 4 * MAXCT / (2 * bit)>([&](auto K) {
         constexpr int s2 = 2 * bit * decltype(K)::value;
         if ((s2 >> 2) < CT) {
-          const float lo = xv[s2], hi = xv[s2 | bit];
+          const float lo = xget(xv, s2), hi = xget(xv, s2 | bit);
           const float send = up ? lo : hi, keep = up ? hi : lo;
-          xv[s2] = keep + lane_xor<bit>(send);
+          xset(xv, s2, keep + lane_xor<bit>(send));
         }
       });
     }
@@ -133,7 +134,7 @@ __device__ __forceinline__ void route_rows_bias(const RouteArgs& a, float (&xv)[
     constexpr int s2 = G * decltype(K)::value;
     constexpr int jc = 16 * (s2 >> 2) + (s2 & 3);     // j = jc + jl
     if ((s2 >> 2) < CT && jc + jl < t) {
-      const float pb = xv[s2] * invG;
+      const float pb = xget(xv, s2) * invG;
       buf_store4(prior_bias(pb, sl2), lp, voff + (uint32_t)jc * kQT * 4, 0u);
       if (pb > 0.f) lflag[jc + jl] = 1;
     }

@@ -147,23 +147,18 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
     }
   }
 
-  // ---- threshold, support bits, pbar and the Stage 2 bias ----
-  float xv[4 * kLongMaxCT];
+  // ---- threshold, support bits, pbar and the Stage 2 bias, in the accumulators ----
+  // (candidates past t in the last candidate tile become -inf; tiles at or
+  // past CT are never read)
   static_for<0, kLongMaxCT>([&](auto CTc) {
     constexpr int ct = decltype(CTc)::value;
-    if (ct < CT - 1) {   // every candidate of the tile exists
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xv[4 * ct + i] = X[ct][i];
-    } else if (ct == CT - 1) {
+    if (ct == CT - 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        xv[4 * ct + i] = 16 * ct + 4 * lg + i < t ? X[ct][i] : -INFINITY;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xv[4 * ct + i] = 0.f;
+        if (16 * ct + 4 * lg + i >= t) X[ct][i] = -INFINITY;
     }
   });
-  const float tau = entmax_tau_reg<4 * kLongMaxCT, MODE>(xv, Stride16Reduce{}, a.e, CT);
+  const float tau = entmax_tau_reg<4 * kLongMaxCT, MODE>(X, Stride16Reduce{}, a.e, CT);
   if (a.bits) {
     // ballots give, for each (ct, i), the bit of every (row, lg) pair
     uint32_t chunk[kLongMaxCT];
@@ -173,7 +168,7 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
       if (ct < CT) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint64_t mk = __ballot(xv[4 * ct + i] > tau);
+          const uint64_t mk = __ballot(X[ct][i] > tau);
 #pragma unroll
           for (int l2 = 0; l2 < 4; ++l2)
             chunk[ct] |= (uint32_t)((mk >> (16 * l2 + l16)) & 1ull) << (4 * l2 + i);
@@ -194,10 +189,10 @@ __global__ __launch_bounds__(kLongThreads) void route_long_kernel(RouteArgs a) {
     constexpr int ct = decltype(CTc)::value;
     if (ct < CT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[4 * ct + i] = entmax_prob<MODE>(xv[4 * ct + i] - tau, a.e);
+      for (int i = 0; i < 4; ++i) X[ct][i] = entmax_prob<MODE>(X[ct][i] - tau, a.e);
     }
   });
-  route_rows_bias<G, kLongMaxCT>(a, xv, CT, t, lg, h, pos, p_begin, tile, lflag);
+  route_rows_bias<G, kLongMaxCT>(a, X, CT, t, lg, h, pos, p_begin, tile, lflag);
   __syncthreads();
   if (threadIdx.x >= kWave) return;
   if (parts == 1) {

@@ -152,19 +152,15 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
 
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
-    float xv[4 * kTileMaxCT];
+    // the row's slots are the accumulators themselves: candidates past t in
+    // the last candidate tile become -inf; tiles at or past CT are never read
+    f32x4 (&xv)[kTileMaxCT] = X[rt];
     static_for<0, kTileMaxCT>([&](auto CTc) {
       constexpr int ct = decltype(CTc)::value;
-      if (ct < CT - 1) {   // every candidate of the tile exists
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xv[4 * ct + i] = X[rt][ct][i];
-      } else if (ct == CT - 1) {
+      if (ct == CT - 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          xv[4 * ct + i] = 16 * ct + 4 * lg + i < t ? X[rt][ct][i] : -INFINITY;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xv[4 * ct + i] = 0.f;
+          if (16 * ct + 4 * lg + i >= t) xv[ct][i] = -INFINITY;
       }
     });
     const float tau = entmax_tau_reg<4 * kTileMaxCT, MODE>(xv, Stride16Reduce{}, a.e, CT);
@@ -180,7 +176,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
         chunk[ct] = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint64_t mk = __ballot(ct < CT && xv[4 * ct + i] > tau);
+          const uint64_t mk = __ballot(ct < CT && xv[ct][i] > tau);
 #pragma unroll
           for (int l2 = 0; l2 < 4; ++l2)
             chunk[ct] |= (uint32_t)((mk >> (16 * l2 + l16)) & 1ull) << (4 * l2 + i);
@@ -200,7 +196,7 @@ __global__ __launch_bounds__(1024) void route_tile_kernel(RouteArgs a) {
       constexpr int ct = decltype(CTc)::value;
       if (ct < CT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[4 * ct + i] = entmax_prob<MODE>(xv[4 * ct + i] - tau, a.e);
+        for (int i = 0; i < 4; ++i) xv[ct][i] = entmax_prob<MODE>(xv[ct][i] - tau, a.e);
       }
     });
     route_rows_bias<G, kTileMaxCT>(a, xv, CT, t, lg, h, pos, p_begin, tile, uflag);
