@@ -659,20 +659,22 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
   constexpr int NBLK = D / 64;
   u32x4 pre[NBLK][4];
   float pre_l = 0.f, pre_d = 0.f, pre_b = 0.f;
+  // q and dO of one head through buffer resources over its n rows (32-bit
+  // offsets; rows past n read as zeros without a compare)
+  const uint32_t head_bytes = (uint32_t)(a.n * (D * 2));
   auto prefetch = [&](int64_t qt, int hh, bool branch) {
     const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
 #pragma unroll
     for (int m = 0; m < NBLK; ++m) {
       const int e = threadIdx.x + 256 * m;
-      const int which = e / (2 * D), e1 = e % (2 * D);
+      // q or dO: uniform within a wave (2 D threads per matrix)
+      const int which = __builtin_amdgcn_readfirstlane(e / (2 * D));
+      const int e1 = e % (2 * D);
       const int rb = e1 % 16, cb = e1 / 16;
-      const __bf16* src = (const __bf16*)(which ? a.dO : a.q) + (bh * a.n + qt * kBwdTile) * D;
+      const buf_rsrc rs = make_rsrc((const __bf16*)(which ? a.dO : a.q) + bh * a.n * D, head_bytes);
+      const uint32_t base = (uint32_t)qt * (kBwdTile * D * 2) + (uint32_t)(4 * rb * (D * 2) + 16 * cb);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = 4 * rb + rr;
-        pre[m][rr] = qt * kBwdTile + r < a.n ? *(const u32x4*)(src + r * D + 8 * cb)
-                                             : (u32x4){0u, 0u, 0u, 0u};
-      }
+      for (int rr = 0; rr < 4; ++rr) pre[m][rr] = buf_load16(rs, base + (uint32_t)(rr * (D * 2)));
     }
     // loads only: any arithmetic on a loaded value here would wait for all of them
     if (threadIdx.x < kBwdTile) {
