@@ -695,8 +695,12 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
       const int rb = e1 % 16, cb = e1 / 16;
       __bf16* dr = which ? Or : Qr;
       __bf16* dt = which ? Ot : Qt;
+      // 16-byte chunk c of row r sits at chunk c ^ ((r >> 4) & 3), i.e.
+      // cb ^ (rb >> 2) here: the 16 lanes of a store (rows 4 rb + rr) then
+      // cover all banks, as do the 16 rows of a fragment read
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) *(u32x4*)(dr + (4 * rb + rr) * RP + 8 * cb) = pre[m][rr];
+      for (int rr = 0; rr < 4; ++rr)
+        *(u32x4*)(dr + (4 * rb + rr) * RP + 8 * (cb ^ (rb >> 2))) = pre[m][rr];
       // queries 16 m' + 8 a' + 4 b' + [0, 4) go to columns 16 m' + 8 b' + 4 a' + [0, 4)
       const int col = 16 * (rb / 4) + 8 * (rb % 2) + 4 * ((rb / 2) % 2);
 #pragma unroll
@@ -748,15 +752,19 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
         f32x16 sv, dpv;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sv[i] = dpv[i] = 0.f;
-        // A fragments read one k-step ahead of their MFMAs
-        const int roff0 = (32 * qh + l32) * RP + 8 * lh;
-        u32x4 qa = *(const u32x4*)(Qr + roff0), oa = *(const u32x4*)(Or + roff0);
+        // A fragments read one k-step ahead of their MFMAs; chunk 2 s2 + lh of
+        // row 32 qh + l32 sits at 2 (s2 ^ qh) + (lh ^ (l32 >> 4)) (the swizzle
+        // above), so even and odd s2 step from two bases
+        const int rbase0 = (32 * qh + l32) * RP + 8 * (lh ^ (l32 >> 4));
+        const int roffE = rbase0 + 16 * qh, roffO = rbase0 - 16 * qh;
+        auto roff = [&](int s2) { return ((s2 & 1) ? roffO : roffE) + 16 * s2; };
+        u32x4 qa = *(const u32x4*)(Qr + roff(0)), oa = *(const u32x4*)(Or + roff(0));
 #pragma unroll
         for (int s2 = 0; s2 < D / 16; ++s2) {
           u32x4 qn = qa, on = oa;
           if (s2 + 1 < D / 16) {
-            qn = *(const u32x4*)(Qr + roff0 + 16 * (s2 + 1));
-            on = *(const u32x4*)(Or + roff0 + 16 * (s2 + 1));
+            qn = *(const u32x4*)(Qr + roff(s2 + 1));
+            on = *(const u32x4*)(Or + roff(s2 + 1));
           }
           sv = mfma32(as_bf16x8(qa), kf[s2], sv);
           dpv = mfma32(as_bf16x8(oa), vf[s2], dpv);
