@@ -337,14 +337,16 @@ void bwd_rows_mfma_kernel(BwdArgs a) {
     if (!full) return;
     // K^T in 4 x 4 blocks (4 keys x 4 d): four 8-byte loads, register
     // transposes, four 8-byte stores; keys 16 m + 8 a + 4 b + [0, 4) go to
-    // columns 16 m + 8 b + 4 a + [0, 4)
+    // columns 16 m + 8 b + 4 a + [0, 4), and 16-byte chunk c of row r sits at
+    // c ^ ((r >> 4) & 3) (rows 4 db + [0, 4): c ^ (db >> 2)), so the 16 lanes
+    // of a store (rows 4 apart) and of a fragment read cover all banks
     for (int e = threadIdx.x; e < (kBwdChunk / 4) * (D / 4); e += NT) {
       const int db = e % (D / 4), kb4 = e / (D / 4);
       u32x2 in[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         in[rr] = buf_load8(rk, (uint32_t)((key0 + 4 * kb4 + rr) * (D * 2) + db * 8));
-      const int col = 16 * (kb4 / 4) + 8 * (kb4 % 2) + 4 * ((kb4 / 2) % 2);
+      const int col = (16 * (kb4 / 4) + 8 * (kb4 % 2) + 4 * ((kb4 / 2) % 2)) ^ (8 * ((db >> 2) & 3));
       *(u32x2*)(Kt + (4 * db + 0) * VP + col) = (u32x2){pack_lo(in[0].x, in[1].x),
                                                         pack_lo(in[2].x, in[3].x)};
       *(u32x2*)(Kt + (4 * db + 1) * VP + col) = (u32x2){pack_hi(in[0].x, in[1].x),
@@ -469,16 +471,19 @@ void bwd_rows_mfma_kernel(BwdArgs a) {
     }
     csum = xor_reduce<32>(csum, DppAdd{});
     if (blk >= 0) bacc += csum;
-    {   // dQ^T += K^T dS^T, each A fragment read one MFMA ahead
+    {   // dQ^T += K^T dS^T, each A fragment read one MFMA ahead; chunk
+        // 2 ks + lh of row 32 dt + l32 sits at 2 (ks ^ (dt & 1)) + (lh ^ (l32 >> 4))
       constexpr int NQ = 4 * (D / 32);
-      u32x4 ka = *(const u32x4*)(Kt + l32 * VP + 8 * lh);
+      const __bf16* ktl = Kt + l32 * VP + 8 * (lh ^ (l32 >> 4));
+      auto kto = [&](int ks, int dt) { return (32 * dt) * VP + 16 * (ks ^ (dt & 1)); };
+      u32x4 ka = *(const u32x4*)(ktl + kto(0, 0));
 #pragma unroll
       for (int x = 0; x < NQ; ++x) {
         const int ks = x / (D / 32), dt = x % (D / 32);
         u32x4 kn = ka;
         if (x + 1 < NQ) {
           const int ks1 = (x + 1) / (D / 32), dt1 = (x + 1) % (D / 32);
-          kn = *(const u32x4*)(Kt + (32 * dt1 + l32) * VP + 16 * ks1 + 8 * lh);
+          kn = *(const u32x4*)(ktl + kto(ks1, dt1));
         }
         dqa[dt] = mfma32(as_bf16x8(ka), dsf[ks], dqa[dt]);
         ka = kn;
