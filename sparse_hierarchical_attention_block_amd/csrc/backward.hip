@@ -925,12 +925,26 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
   for (int hh = 0; hh < a.G; ++hh) {
     const int64_t bh = (int64_t)b * a.H + g * a.G + hh;
     __syncthreads();
-    // q rows, 16 bytes per load
+    // q rows, 16 bytes per load, all of a thread's loads issued before its stores
     constexpr int VE = 16 / (int)sizeof(T);
-    for (int e = tid; e < kBwdTile * D / VE; e += 256) {
-      const int r = e / (D / VE), c = (e % (D / VE)) * VE;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (p0 + r < a.n) w = *(const u32x4*)((const T*)a.q + (bh * a.n + p0 + r) * D + c);
+    constexpr int NQL = kBwdTile * D / VE / 256;
+    u32x4 wq[NQL];
+#pragma unroll
+    for (int k = 0; k < NQL; ++k) {
+      const int e = tid + 256 * k, r = e / (D / VE), c = (e % (D / VE)) * VE;
+      wq[k] = (u32x4){0u, 0u, 0u, 0u};
+      if (p0 + r < a.n) wq[k] = *(const u32x4*)((const T*)a.q + (bh * a.n + p0 + r) * D + c);
+    }
+    float tau2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t pos = p0 + rg + 32 * i;
+      tau2[i] = pos < a.n ? a.tau[bh * a.n + pos] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < NQL; ++k) {
+      const int e = tid + 256 * k, r = e / (D / VE), c = (e % (D / VE)) * VE;
+      const u32x4 w = wq[k];
       if constexpr (sizeof(T) == 2) {
         *(f32x4*)(Qh + r * QP + c) = (f32x4){bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
         *(f32x4*)(Qh + r * QP + c + 4) =
@@ -939,16 +953,10 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
         *(u32x4*)(Qh + r * QP + c) = w;
       }
     }
-    float tau2[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t pos = p0 + rg + 32 * i;
-      tau2[i] = pos < a.n ? a.tau[bh * a.n + pos] : 0.f;
-    }
     float* uh = ucg + (int64_t)hh * a.nb * kBwdTile;
     // phase A: u and the row sums of u and u dp
     float su[2] = {0.f, 0.f}, sud[2] = {0.f, 0.f};
-    load_s(0);
+    if (hh == 0 || cnt > kRtJ) load_s(0);   // one chunk: still held from the last head
     for (int j0 = 0; j0 < cnt; j0 += kRtJ) {
       __syncthreads();
       store_s();
@@ -1035,7 +1043,7 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
       }
     };
     load_b(0);
-    load_s(0);
+    if (cnt > kRtJ) load_s(0);   // one chunk: still held from phase A
     for (int j0 = 0; j0 < cnt; j0 += kRtJ) {
       __syncthreads();
       store_s();
