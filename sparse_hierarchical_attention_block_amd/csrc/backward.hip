@@ -1145,9 +1145,21 @@ __global__ __launch_bounds__(D) void bwd_dsum_kernel(BwdArgs a) {
   }
   __syncthreads();
   const int r = threadIdx.x;
+  // added in tile order, the rows of 16 tiles read before any is added
+  constexpr int kBatch = 16;
   float acc = 0.f;
-  for (int e = 0; e < a.slab_nq; ++e)
-    if (pos[e] >= 0) acc += a.dspart[((bg * a.slab + e) * a.nb + pos[e]) * D + r];
+  for (int e0 = 0; e0 < a.slab_nq; e0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = e0 + u;
+      v[u] = e < a.slab_nq && pos[e] >= 0 ? a.dspart[((bg * a.slab + e) * a.nb + pos[e]) * D + r]
+                                          : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (e0 + u < a.slab_nq && pos[e0 + u] >= 0) acc += v[u];
+  }
   a.ds[(bg * a.nb + j) * D + r] += acc;
 }
 
@@ -1163,8 +1175,18 @@ __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
     return;
   }
   const int64_t k0 = bg * a.n + j * a.bs;
+  // the block's key rows summed in order, read 16 at a time (the loads of a
+  // batch in flight together)
+  constexpr int kBatch = 16;
   float m = 0.f;
-  for (int t = 0; t < a.bs; ++t) m += ld<T>(a.k, (k0 + t) * D + r);
+  for (int t0 = 0; t0 < a.bs; t0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = t0 + u < a.bs ? ld<T>(a.k, (k0 + t0 + u) * D + r) : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (t0 + u < a.bs) m += v[u];
+  }
   mrow[r] = m / (float)a.bs;
   __shared__ float dsr[D];
   dsr[r] = a.ds[(bg * a.nb + j) * D + r];
@@ -1172,7 +1194,15 @@ __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
   float dm = 0.f;
   for (int c = 0; c < D; ++c) dm = fmaf(dsr[c], a.w_s[r * D + c], dm);
   dm /= (float)a.bs;
-  for (int t = 0; t < a.bs; ++t) a.dk[(k0 + t) * D + r] += dm;
+  // the block's dk rows likewise read 16 at a time before any is written back
+  for (int t0 = 0; t0 < a.bs; t0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = t0 + u < a.bs ? a.dk[(k0 + t0 + u) * D + r] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (t0 + u < a.bs) a.dk[(k0 + t0 + u) * D + r] = v[u] + dm;
+  }
 }
 
 // ---- dW_s = sum_j m_j^T ds_j ---------------------------------------------------------------
