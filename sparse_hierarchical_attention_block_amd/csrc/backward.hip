@@ -395,16 +395,38 @@ void bwd_rows_mfma_kernel(BwdArgs a) {
       }
   };
 
-  // pass 1: log2-sum-exp2 per query
+  // pass 1: log2-sum-exp2 per query.  It stages K only, and the next
+  // chunk's K is loaded into registers while the current one is computed.
+  constexpr int NPK = kBwdChunk * (D / 8) / NT;   // 16-byte pieces of K per thread
+  u32x4 kpre[NPK];
+  auto load_k = [&](int64_t key0) {
+#pragma unroll
+    for (int i = 0; i < NPK; ++i) {
+      const int e = threadIdx.x + NT * i, key = e / (D / 8), seg = e % (D / 8);
+      kpre[i] = buf_load16(rk, (uint32_t)((key0 + key) * (D * 2) + seg * 16));
+    }
+  };
   float m = -INFINITY, l = 0.f;
+  int64_t key0n = 0, blkn = -1;
+  if (n_chunks > 0) {
+    chunk(0, key0n, blkn);
+    load_k(key0n);
+  }
   for (int c = 0; c < n_chunks; ++c) {
-    int64_t key0, blk;
-    chunk(c, key0, blk);
+    const int64_t blk = blkn;
     const float bias2 =
         blk < 0 ? 0.f : a.sel_logp[(tile * a.nb + blk) * kBwdTile + qloc] * kLog2e;
     __syncthreads();
-    stage(key0, false);
+#pragma unroll
+    for (int i = 0; i < NPK; ++i) {
+      const int e = threadIdx.x + NT * i, key = e / (D / 8), seg = e % (D / 8);
+      *(u32x4*)(Ks + key * KP + seg * 8) = kpre[i];
+    }
     __syncthreads();
+    if (c + 1 < n_chunks) {
+      chunk(c + 1, key0n, blkn);
+      load_k(key0n);
+    }
     f32x16 st[2];
     scores(c, bias2, st);
     float cm = -INFINITY;
