@@ -67,6 +67,7 @@ struct BwdArgs {
   float* dspart;            // [B, Hkv, slab, nb, D] each tile's share of ds
   float* ds;                // [B, Hkv, nb, D]
   float* mean;              // [B, Hkv, nb, D]
+  float* dm;                // [B, Hkv, nb, D] (ds_j W_s^T) / bs per complete block, else 0
   float* wspart;            // [kWsSplit, D, D] slices of dW_s
   int64_t n, n_qt, nb;
   int64_t slab, slab_q0, slab_nq;   // slab capacity; this slab's first tile and size
@@ -614,9 +615,11 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(BwdArgs a) {
   }
   }
   if (valid) {
+    // plus the summaries' share of the key's block (zero for an incomplete block)
+    const float* dmr = a.dm + (bg * a.nb + kpos / a.bs) * D + sl * S;
 #pragma unroll
     for (int c = 0; c < S; ++c) {
-      a.dk[kbase + c] = dkv[c];
+      a.dk[kbase + c] = dkv[c] + dmr[c];
       a.dv[kbase + c] = dvv[c];
     }
   }
@@ -855,12 +858,14 @@ void bwd_keys_mfma_kernel(BwdArgs a) {
   if (kvalid) {
     float* dkr = a.dk + (bg * a.n + kpos) * D;
     float* dvr = a.dv + (bg * a.n + kpos) * D;
+    // plus the summaries' share of the key's block (zero for an incomplete block)
+    const float* dmr = a.dm + (bg * a.nb + kpos / a.bs) * D;
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int dcol = 32 * (NDT * dh + t) + 8 * (i / 4) + 4 * lh + (i % 4);
-        dkr[dcol] = dka[t][i] * a.rs;
+        dkr[dcol] = dka[t][i] * a.rs + dmr[dcol];
         dvr[dcol] = dva[t][i];
       }
   }
@@ -1185,15 +1190,17 @@ __global__ __launch_bounds__(D) void bwd_dsum_kernel(BwdArgs a) {
   a.ds[(bg * a.nb + j) * D + r] += acc;
 }
 
-// ---- block means, and dk += (ds_j W_s^T) / bs over the block ---------------------------------
+// ---- block means, and dm_j = (ds_j W_s^T) / bs, which the keys kernels add to the block's dk ---
 template <typename T, int D>
 __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
   const int64_t j = blockIdx.x % a.nb;
   const int64_t bg = blockIdx.x / a.nb;
   const int r = threadIdx.x;
   float* mrow = a.mean + (bg * a.nb + j) * D;
+  float* dmrow = a.dm + (bg * a.nb + j) * D;
   if (j >= a.n / a.bs) {   // incomplete block: no summary, no gradient
     mrow[r] = 0.f;
+    dmrow[r] = 0.f;
     return;
   }
   const int64_t k0 = bg * a.n + j * a.bs;
@@ -1215,16 +1222,7 @@ __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
   __syncthreads();
   float dm = 0.f;
   for (int c = 0; c < D; ++c) dm = fmaf(dsr[c], a.w_s[r * D + c], dm);
-  dm /= (float)a.bs;
-  // the block's dk rows likewise read 16 at a time before any is written back
-  for (int t0 = 0; t0 < a.bs; t0 += kBatch) {
-    float v[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) v[u] = t0 + u < a.bs ? a.dk[(k0 + t0 + u) * D + r] : 0.f;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (t0 + u < a.bs) a.dk[(k0 + t0 + u) * D + r] = v[u] + dm;
-  }
+  dmrow[r] = dm / (float)a.bs;
 }
 
 // ---- dW_s = sum_j m_j^T ds_j ---------------------------------------------------------------
@@ -1285,6 +1283,7 @@ BwdLayout bwd_layout(const Shape& s, int64_t n) {
   L.off_u = off;      off = al(off + per_slot);
   L.off_ds = off;     off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
   L.off_mean = off;   off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
+  L.off_dm = off;     off = al(off + sizeof(float) * s.B * s.Hkv * nb * s.d);
   L.off_dspart = off; off = al(off + sizeof(float) * s.B * s.Hkv * slab * nb * s.d);
   L.off_wspart = off; off = al(off + sizeof(float) * kWsSplit * s.d * s.d);
   L.slab = slab;
@@ -1321,6 +1320,7 @@ static hipError_t bwd_t(BwdArgs a, hipStream_t st) {
     if (nbc > 0)
       hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)(nbc * nbg)), dim3(D), 0, st, a);
   }
+  hipLaunchKernelGGL((bwd_means_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
   const int64_t nch = (a.n + kBwdChunk - 1) / kBwdChunk;
   if constexpr (sizeof(T) == 2) {
     const size_t lds_km = sizeof(__bf16) * (2 * kBwdTile * (D + 8) + 2 * D * (kBwdTile + 8)) +
@@ -1336,7 +1336,6 @@ static hipError_t bwd_t(BwdArgs a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_keys_kernel<T, D>), dim3((unsigned)(nch * nbg)), dim3(256), lds_k,
                        st, a);
   }
-  hipLaunchKernelGGL((bwd_means_kernel<T, D>), dim3((unsigned)(a.nb * nbg)), dim3(D), 0, st, a);
   hipLaunchKernelGGL((bwd_ws_kernel<D>), dim3((unsigned)((D * D + 255) / 256), kWsSplit),
                      dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_ws_sum_kernel<D>), dim3((unsigned)((D * D + 255) / 256)), dim3(256), 0,
@@ -1373,6 +1372,7 @@ hipError_t launch_prefill_backward(const Shape& s, const void* q, const void* k,
   a.ucoarse = (float*)(ws + L.off_u);
   a.ds = (float*)(ws + L.off_ds);
   a.mean = (float*)(ws + L.off_mean);
+  a.dm = (float*)(ws + L.off_dm);
   a.dspart = (float*)(ws + L.off_dspart);
   a.wspart = (float*)(ws + L.off_wspart);
   a.slab = L.slab;

@@ -77,7 +77,8 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* kc, const vo
 // Backward pass of the causal prefill (mean-pooled summaries): workspace
 // layout and launch.
 struct BwdLayout {
-  size_t off_lse, off_delta, off_dlogp, off_u, off_ds, off_mean, off_dspart, off_wspart, total;
+  size_t off_lse, off_delta, off_dlogp, off_u, off_ds, off_mean, off_dm, off_dspart, off_wspart,
+      total;
   int64_t slab;   // query tiles per slab of the per-tile arrays
 };
 BwdLayout bwd_layout(const Shape& s, int64_t n);
