@@ -1204,18 +1204,50 @@ __global__ __launch_bounds__(D) void bwd_means_kernel(BwdArgs a) {
     return;
   }
   const int64_t k0 = bg * a.n + j * a.bs;
-  // the block's key rows summed in order, read 16 at a time (the loads of a
-  // batch in flight together)
-  constexpr int kBatch = 16;
-  float m = 0.f;
-  for (int t0 = 0; t0 < a.bs; t0 += kBatch) {
-    float v[kBatch];
+  // The block's key rows in 16-byte pieces: thread t sums the VE columns of
+  // segment t % SEG over rows t / SEG + VE i (8 loads in flight at a time),
+  // then the VE row groups' partial sums are added in group order.  The
+  // pieces are copied into plain arrays before their halves or words are
+  // used (reading the vector's components directly compiled to the wrong
+  // component here).
+  constexpr int VE = 16 / (int)sizeof(T);   // values per 16 bytes
+  constexpr int SEG = D / VE;               // segments per row (D threads: VE row groups)
+  constexpr int kBatch = 8;
+  const int seg = r % SEG, rg = r / SEG;
+  float acc[VE];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) v[u] = t0 + u < a.bs ? ld<T>(a.k, (k0 + t0 + u) * D + r) : 0.f;
+  for (int v = 0; v < VE; ++v) acc[v] = 0.f;
+  const T* kb = (const T*)a.k + k0 * D + VE * seg;
+  for (int t0 = rg; t0 < a.bs; t0 += VE * kBatch) {
+    u32x4 w[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (t0 + u < a.bs) m += v[u];
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + VE * u;
+      w[u] = t < a.bs ? *(const u32x4*)(kb + (int64_t)t * D) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc[2 * h] += bf16_lo(ww[h]);
+          acc[2 * h + 1] += bf16_hi(ww[h]);
+        }
+      } else {
+        const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) acc[h] += __uint_as_float(ww[h]);
+      }
+    }
   }
+  __shared__ float part[VE][D];
+#pragma unroll
+  for (int v = 0; v < VE; ++v) part[rg][VE * seg + v] = acc[v];
+  __syncthreads();
+  float m = 0.f;
+#pragma unroll
+  for (int g2 = 0; g2 < VE; ++g2) m += part[g2][r];
   mrow[r] = m / (float)a.bs;
   __shared__ float dsr[D];
   dsr[r] = a.ds[(bg * a.nb + j) * D + r];
