@@ -1172,22 +1172,40 @@ __global__ __launch_bounds__(D) void bwd_dsum_kernel(BwdArgs a) {
   }
   __syncthreads();
   const int r = threadIdx.x;
-  // added in tile order, the rows of 16 tiles read before any is added
-  constexpr int kBatch = 16;
-  float acc = 0.f;
-  for (int e0 = 0; e0 < a.slab_nq; e0 += kBatch) {
-    float v[kBatch];
+  // 16 bytes per load: thread t adds the 4 columns of segment t % (D / 4)
+  // over the tiles of group t / (D / 4) (four contiguous ranges of the slab,
+  // each in tile order, 8 rows in flight at a time); the groups' sums are
+  // then added in group order
+  constexpr int NS = D / 4, kGroups = 4, kBatch = 8;
+  const int c4 = r % NS, grp = r / NS;
+  const int per = (int)((a.slab_nq + kGroups - 1) / kGroups);
+  const int e_lo = grp * per, e_hi = min((int)a.slab_nq, e_lo + per);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int e0 = e_lo; e0 < e_hi; e0 += kBatch) {
+    f32x4 v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int e = e0 + u;
-      v[u] = e < a.slab_nq && pos[e] >= 0 ? a.dspart[((bg * a.slab + e) * a.nb + pos[e]) * D + r]
-                                          : 0.f;
+      v[u] = e < e_hi && pos[e] >= 0
+                 ? *(const f32x4*)(a.dspart + ((bg * a.slab + e) * a.nb + pos[e]) * D + 4 * c4)
+                 : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
-      if (e0 + u < a.slab_nq && pos[e0 + u] >= 0) acc += v[u];
+      if (e0 + u < e_hi && pos[e0 + u] >= 0) {
+        const float w4[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) acc[k2] += w4[k2];
+      }
   }
-  a.ds[(bg * a.nb + j) * D + r] += acc;
+  __shared__ float part[kGroups][D];
+#pragma unroll
+  for (int k2 = 0; k2 < 4; ++k2) part[grp][4 * c4 + k2] = acc[k2];
+  __syncthreads();
+  float sum = 0.f;
+#pragma unroll
+  for (int g2 = 0; g2 < kGroups; ++g2) sum += part[g2][r];
+  a.ds[(bg * a.nb + j) * D + r] += sum;
 }
 
 // ---- block means, and dm_j = (ds_j W_s^T) / bs, which the keys kernels add to the block's dk ---
