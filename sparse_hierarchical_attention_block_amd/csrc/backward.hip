@@ -1144,7 +1144,7 @@ __global__ __launch_bounds__(256) void bwd_route_tile_kernel(BwdArgs a) {
 // ---- ds_j += the partial rows of this slab's tiles that list block j ---------------------------
 // One workgroup per (sequence, KV head, complete block); the tiles' list
 // positions of the block are found first (one binary search per tile, side
-// by side), then every thread adds its column over the tiles in order.
+// by side), then the listing tiles' partial rows are added in a fixed order.
 constexpr int kSlabMax = 256;   // tiles per slab (one search per thread)
 template <int D>
 __global__ __launch_bounds__(D) void bwd_dsum_kernel(BwdArgs a) {
